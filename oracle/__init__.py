@@ -1,0 +1,37 @@
+"""CPU oracle for query/Forecast-conditioned block selection and block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this package: only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg use it. It shares no code with the HIP library
+and never imports it; it receives plain numpy arrays.
+
+It is a slow, plain restatement of the method on the page "SparDA: Sparse
+Decoupled Attention for Efficient Long-Context LLM Inference" (picx.dev
+summary), section "Theoretical Foundation" (Eq. 1 block union, Eq. 2
+mean-pooled compressed keys) and section "Methodology" (Eq. 4 Forecast-driven
+top-k, Eq. 5 attention over the chosen blocks, "Compact Forecast Indexer", and
+the Eq. 6 group-summed softmax form of the query-driven selector). Arithmetic is
+fp64 from the compressed keys onward; the compressed keys themselves are formed
+in a fixed fp32 order and rounded to the key dtype, so they are one exact value.
+
+Pinned by the tests under tests/ marked "not gpu" (closed forms, library
+special cases, invariants and brute force). One reading has no pin of its own
+beyond brute force over its definition: which compressed entries belong to a
+64-token block ("parity unpinned" for that choice, see oracle.select).
+"""
+from .numerics import bf16_round, round_to
+from .compress import n_compressed, n_blocks, compressed_keys, append_compressed_keys
+from .select import (SOFTMAX_SUM, RAW_SUM, entry_scores, block_scores, block_entries,
+                     candidate_sets, top_k_blocks, select_blocks, SelectParams)
+from .attention import sparse_attention, lse_merge, split_attention_partials
+from .decode import decode_step, decode_unit
+from .prefill import prefill_tile_select, prefill_attention, prefill_chunk
+from .crosslayer import crosslayer_step
+
+__all__ = [
+    "bf16_round", "round_to", "n_compressed", "n_blocks", "compressed_keys",
+    "append_compressed_keys", "SOFTMAX_SUM", "RAW_SUM", "entry_scores", "block_scores",
+    "block_entries", "candidate_sets", "top_k_blocks", "select_blocks", "SelectParams",
+    "sparse_attention", "lse_merge", "split_attention_partials", "decode_step", "decode_unit",
+    "prefill_tile_select", "prefill_attention", "prefill_chunk", "crosslayer_step",
+]
