@@ -1,0 +1,228 @@
+"""Benchmark of the block-sparse decode hot path on one MI355X.
+
+A step is one decode step of the Forecast-scored 128K workload (batch 8, 32
+query heads, 8 KV heads, head_dim 128, bf16, top-k 64 + 1 initial + 2 local
+blocks): append the compressed-key window completed by the newest token, score
+and select blocks with the per-group Forecast vectors, and attend with the real
+queries over the selected blocks (split-K, merged with log-sum-exp weights).
+Inputs are seeded synthetic tensors resident in HBM before timing; R replicas
+at distinct addresses are rotated so the 256 MB last-level cache cannot serve
+one step's bytes from the previous step.
+
+Prints one JSON line: throughput (tokens/s = batch / step time), the achieved
+HBM bandwidth of the dominant kernel (decode attention) on its algorithmic
+bytes against the 8 TB/s peak, and the CPU oracle timed on the same inputs.
+Other workloads: --workload decode_gqa_bf16_32k | decode_tiny_f32_8k |
+crosslayer_bf16_64k | prefill_chunk_bf16_128k.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_forecast_bf16_128k")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--n-split", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import SparseDecoder
+
+    if args.workload.startswith("prefill"):
+        return bench_prefill(args)
+    w = synth.WORKLOADS[args.workload]
+    if w.layers > 1:
+        return bench_crosslayer(args, w)
+    return bench_decode(args, w)
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_decode(args, w):
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import SparseDecoder
+    from block_sparse_attention_12_amd import n_compressed, n_blocks
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_decode_inputs(w, device=dev)
+    T = w.T
+    lens_now = inp["seq_lens"]
+    lens_prev = lens_now - 1
+    dec = SparseDecoder(w.B, w.Hq, w.Hkv, T, w.top_k, w.n_init, w.n_local, w.selector,
+                        w.score_mode, device=dev, n_split=args.n_split)
+    sel_name = "F" if w.selector == "forecast" else "Q"
+    reps = []
+    for r in range(args.replicas):
+        rep = {k: (inp[k] if r == 0 else inp[k].clone()) for k in ("Q", "K", "V", sel_name)}
+        rep["Kc"] = dec.new_kc(inp["K"].dtype)
+        dec.build(rep["K"], rep["Kc"], lens_prev)        # windows up to the previous token
+        reps.append(rep)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        rep = reps[i % len(reps)]
+        if ev is not None:
+            ev[0].record(stream)
+        dec.append(rep["K"], rep["Kc"], lens_prev, lens_now)
+        if ev is not None:
+            ev[1].record(stream)
+        dec.select(rep[sel_name], rep["Kc"], lens_now)
+        if ev is not None:
+            ev[2].record(stream)
+        dec.attend(rep["Q"], rep["K"], rep["V"], lens_now)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(4) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    phases = {"append": [], "select": [], "attend": []}
+    for ev in evs:
+        phases["append"].append(ev[0].elapsed_time(ev[1]))
+        phases["select"].append(ev[1].elapsed_time(ev[2]))
+        phases["attend"].append(ev[2].elapsed_time(ev[3]))
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
+    mean = {k: sum(v) / len(v) for k, v in phases.items()}
+
+    # algorithmic bytes, from the actual selections and lengths
+    cnt = dec.cnt.cpu()
+    idx = dec.idx.cpu()
+    elem = inp["K"].element_size()
+    lens = [int(x) for x in lens_now.cpu()]
+    row = 128 * elem
+    attn_bytes = 0
+    for b in range(w.B):
+        L = lens[b]
+        for h in range(w.Hkv):
+            for blk in idx[b, h, :int(cnt[b, h])].tolist():
+                attn_bytes += 2 * row * max(0, min(64, L - 64 * blk))
+    attn_bytes += w.B * w.Hq * 128 * elem + w.B * w.Hq * (128 * 4 + 4)   # Q in, O + LSE out
+    sel_bytes = 0
+    for b in range(w.B):
+        L = lens[b]
+        nb = n_blocks(L)
+        n_cand = max(0, nb - w.n_local - min(w.n_init, nb))
+        if w.score_mode == "raw_sum":
+            sel_bytes += w.Hkv * 3 * n_cand * row
+        else:
+            sel_bytes += w.Hkv * n_compressed(L) * row
+    sel_in = inp[sel_name]
+    sel_bytes += sel_in.numel() * elem
+    new_entries = sum(n_compressed(L) - n_compressed(L - 1) for L in lens) * w.Hkv
+    append_bytes = new_entries * (32 * row + row)
+    step_bytes = attn_bytes + sel_bytes + append_bytes
+    attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
+
+    out = {
+        "metric": "sparse decode attn tokens/s and HBM GB/s (% of peak) at 128K ctx, 1 GPU",
+        "value": round(w.B / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), planted blocks)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.T, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k, "n_init": w.n_init,
+                   "n_local": w.n_local, "selector": w.selector, "score_mode": w.score_mode,
+                   "replicas": args.replicas, "n_split": args.n_split or "auto",
+                   "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "phase_ms": {k: round(v, 5) for k, v in mean.items()},
+        "step_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode attention (sparse_attn_decode)",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": attn_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, inp, lens, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(w, inp, lens, budget_s):
+    """The CPU oracle, as it is, on the same inputs: whole decode steps until the budget."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+
+    sel_name = "F" if w.selector == "forecast" else "Q"
+    Q = inp["Q"].float().cpu().numpy()
+    S = inp[sel_name].float().cpu().numpy()
+    p = oracle.SelectParams(w.top_k, w.n_init, w.n_local, w.score_mode)
+    Gs = S.shape[1] // w.Hkv
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    host = {}
+    for (b, h) in units:                               # setup, not timed
+        K = inp["K"][b, h].float().cpu().numpy()
+        V = inp["V"][b, h].float().cpu().numpy()
+        Kc = oracle.compressed_keys(K, lens[b] - 1, w.dtype)
+        host[(b, h)] = (K, V, Kc)
+    done, t_units = 0, 0.0
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            for (b, h) in units:
+                K, V, Kc = host[(b, h)]
+                L = lens[b]
+                Kc2 = oracle.append_compressed_keys(K, Kc, L - 1, L, w.dtype)
+                oracle.decode_unit(Q[b, h * w.G:(h + 1) * w.G], S[b, h * Gs:(h + 1) * Gs], K, V,
+                                   Kc2, L, p, 1.0)
+            done += 1
+        t_units = time.perf_counter() - t0
+    sec_per_step = t_units / done
+    return {"value": round(w.B / sec_per_step, 3), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} full decode steps of {w.name} (all {len(units)} units: append, "
+                      f"select, attend), numpy fp64, BLAS limited to 1 thread, {t_units:.1f} s"}
+
+
+def bench_crosslayer(args, w):
+    raise SystemExit("crosslayer bench: see bench_crosslayer below")
+
+
+def bench_prefill(args):
+    raise SystemExit("prefill bench not built yet")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""Python binding of libsparse_attn (MI355X / gfx950 block-sparse attention).
+
+Argument marshalling only: every step of the method runs in the HIP kernels of
+the shared library, reached through its C ABI (include/sparse_attn.h) with
+ctypes. PyTorch supplies device memory and the current HIP stream. There is no
+CPU or PyTorch fallback: if the library is not built, every call raises.
+
+Entry points (same names as the C ABI):
+    compress(K, Kc, lens_prev, lens_now)              compressed keys, Eq. 2
+    select(sel, Kc, seq_lens, T_cap, top_k, ...)      scores + top-k + union, Eq. 1/4/6
+    decode(Q, K, V, seq_lens, idx, cnt, ...)          sparse decode attention, Eq. 5
+    prefill_chunk(Q, q_start, K, V, Kc, ...)          tile-shared sparse prefill
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libsparse_attn.so")
+
+SA_OK = 0
+SA_ERR_INVALID_ARG = -1
+SA_ERR_UNSUPPORTED = -2
+SA_ERR_WORKSPACE = -3
+SA_ERR_CAPACITY = -4
+SA_ERR_HIP = -5
+SA_F32 = 0
+SA_BF16 = 1
+SA_SCORE_SOFTMAX_SUM = 0
+SA_SCORE_RAW_SUM = 1
+
+SCORE_MODES = {"softmax_sum": SA_SCORE_SOFTMAX_SUM, "raw_sum": SA_SCORE_RAW_SUM}
+
+# exported symbols, as declared in include/sparse_attn.h
+EXPORTS = [
+    "sparse_attn_abi_version", "sparse_attn_status_string", "sparse_attn_compress",
+    "sparse_attn_select_workspace_size", "sparse_attn_select",
+    "sparse_attn_decode_workspace_size", "sparse_attn_decode",
+    "sparse_attn_prefill_tile_cap", "sparse_attn_prefill_workspace_size",
+    "sparse_attn_prefill_chunk",
+]
+
+
+class SelectParams(ctypes.Structure):
+    _fields_ = [("block_size", ctypes.c_int32), ("cmp_kernel", ctypes.c_int32),
+                ("cmp_stride", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_init", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("score_mode", ctypes.c_int32)]
+
+
+def make_params(top_k: int, n_init: int = 1, n_local: int = 2, score_mode="softmax_sum",
+                block_size: int = 64, cmp_kernel: int = 32, cmp_stride: int = 16) -> SelectParams:
+    mode = SCORE_MODES[score_mode] if isinstance(score_mode, str) else int(score_mode)
+    return SelectParams(block_size, cmp_kernel, cmp_stride, top_k, n_init, n_local, mode)
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text} (status {status})")
+        self.status = status
+
+
+_lib = None
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_int = ctypes.c_int
+_PP = ctypes.POINTER(SelectParams)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsparse_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libsparse_attn.so not built ({LIB_PATH}); run __graft_entry__.build() "
+                           "or python block_sparse_attention_12_amd/_build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    L.sparse_attn_abi_version.restype = _int
+    L.sparse_attn_abi_version.argtypes = []
+    L.sparse_attn_status_string.restype = ctypes.c_char_p
+    L.sparse_attn_status_string.argtypes = [_int]
+    L.sparse_attn_compress.restype = _int
+    L.sparse_attn_compress.argtypes = [_vp, _vp, _int, _int, _int, _int, _i64, _i64, _vp, _vp, _i32, _vp]
+    L.sparse_attn_select_workspace_size.restype = _sz
+    L.sparse_attn_select_workspace_size.argtypes = [_int, _int, _int, _i64, _PP]
+    L.sparse_attn_select.restype = _int
+    L.sparse_attn_select.argtypes = [_vp, _int, _vp, _int, _int, _int, _int, _i64, _i64, _vp, _PP,
+                                     _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+    L.sparse_attn_decode_workspace_size.restype = _sz
+    L.sparse_attn_decode_workspace_size.argtypes = [_int, _int, _int, _i32, _i32]
+    L.sparse_attn_decode.restype = _int
+    L.sparse_attn_decode.argtypes = [_vp, _vp, _vp, _int, _int, _int, _int, _int, _i64, _vp, _vp, _vp,
+                                     _i32, _f32, _vp, _int, _vp, _i32, _vp, _sz, _vp]
+    L.sparse_attn_prefill_tile_cap.restype = _i32
+    L.sparse_attn_prefill_tile_cap.argtypes = [_i64, _i64, _PP]
+    L.sparse_attn_prefill_workspace_size.restype = _sz
+    L.sparse_attn_prefill_workspace_size.argtypes = [_int, _int, _i64, _i64, _PP]
+    L.sparse_attn_prefill_chunk.restype = _int
+    L.sparse_attn_prefill_chunk.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _int, _int, _int, _int,
+                                            _i64, _i64, _PP, _f32, _vp, _int, _vp, _vp, _i32, _vp,
+                                            _vp, _sz, _vp]
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().sparse_attn_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().sparse_attn_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != SA_OK:
+        raise SparseAttnError(fn, status, status_string(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _opt(t: Optional[torch.Tensor], name: str):
+    return None if t is None else _dev(t, name)
+
+
+def _stream(t: torch.Tensor, stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def n_compressed(L: int) -> int:
+    return 0 if L < 32 else (L - 32) // 16 + 1
+
+
+def n_blocks(L: int) -> int:
+    return (L + 63) // 64
+
+
+# ------------------------------------------------------------------ compress
+
+def compress(K: torch.Tensor, Kc: torch.Tensor, lens_prev: torch.Tensor, lens_now: torch.Tensor,
+             max_new_entries: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Write compressed-key entries [n_c(lens_prev), n_c(lens_now)) of Kc from K (in place)."""
+    B, Hkv, T_cap, d = K.shape
+    nc_cap = Kc.shape[2]
+    if Kc.dtype != K.dtype or Kc.shape[:2] != K.shape[:2] or Kc.shape[3] != d:
+        raise ValueError("Kc must be [B, Hkv, nc_cap, d] with K's dtype")
+    if max_new_entries is None:
+        max_new_entries = n_compressed(T_cap)
+    st = lib().sparse_attn_compress(_dev(K, "K"), _dev(Kc, "Kc"), _dtype_code(K), B, Hkv, d, T_cap,
+                                    nc_cap, _dev(lens_prev, "lens_prev"), _dev(lens_now, "lens_now"),
+                                    int(max_new_entries), _stream(K, stream))
+    _check("sparse_attn_compress", st)
+    return Kc
+
+
+# ------------------------------------------------------------------ select
+
+def select_workspace_size(B, Hkv, H_sel, T_cap, params: SelectParams) -> int:
+    return lib().sparse_attn_select_workspace_size(B, Hkv, H_sel, T_cap, ctypes.byref(params))
+
+
+def select(sel: torch.Tensor, Kc: torch.Tensor, seq_lens: torch.Tensor, T_cap: int, top_k: int,
+           n_init: int = 1, n_local: int = 2, score_mode="softmax_sum",
+           idx: Optional[torch.Tensor] = None, cnt: Optional[torch.Tensor] = None,
+           block_scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None):
+    """Block selection for every (sequence, KV head). Returns (idx, cnt, block_scores)."""
+    B, H_sel, d = sel.shape
+    _, Hkv, nc_cap, _ = Kc.shape
+    p = make_params(top_k, n_init, n_local, score_mode)
+    cap = top_k + n_init + n_local
+    dev = sel.device
+    if idx is None:
+        idx = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if block_scores is True:
+        block_scores = torch.empty((B, Hkv, n_blocks(T_cap)), dtype=torch.float32, device=dev)
+    need = select_workspace_size(B, Hkv, H_sel, T_cap, p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_select(_dev(sel, "sel"), H_sel, _dev(Kc, "Kc"), _dtype_code(Kc), B, Hkv, d,
+                                  T_cap, nc_cap, _dev(seq_lens, "seq_lens"), ctypes.byref(p),
+                                  _dev(idx, "idx"), idx.shape[-1], _dev(cnt, "cnt"),
+                                  _opt(block_scores if isinstance(block_scores, torch.Tensor) else None,
+                                       "block_scores"),
+                                  _opt(workspace, "workspace"), ws_bytes, _stream(sel, stream))
+    _check("sparse_attn_select", st)
+    return idx, cnt, (block_scores if isinstance(block_scores, torch.Tensor) else None)
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_workspace_size(B, Hq, Hkv, idx_cap, n_split=0) -> int:
+    return lib().sparse_attn_decode_workspace_size(B, Hq, Hkv, idx_cap, n_split)
+
+
+def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+           idx: torch.Tensor, cnt: torch.Tensor, scale: float = 1.0,
+           out_dtype=torch.float32, O: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, want_lse: bool = True, n_split: int = 0,
+           workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse decode attention over the selected blocks. Returns (O, lse)."""
+    B, Hq, d = Q.shape
+    _, Hkv, T_cap, _ = K.shape
+    dev = Q.device
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = decode_workspace_size(B, Hq, Hkv, idx.shape[-1], n_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(K), B, Hq, Hkv,
+                                  d, T_cap, _dev(seq_lens, "seq_lens"), _dev(idx, "idx"),
+                                  _dev(cnt, "cnt"), idx.shape[-1], float(scale), _dev(O, "O"),
+                                  _dtype_code(O), _opt(lse, "lse"), int(n_split),
+                                  _opt(workspace, "workspace"), ws_bytes, _stream(Q, stream))
+    _check("sparse_attn_decode", st)
+    return O, lse
+
+
+# ------------------------------------------------------------------ prefill
+
+def prefill_tile_cap(q_start: int, Tq: int, params: SelectParams) -> int:
+    return lib().sparse_attn_prefill_tile_cap(q_start, Tq, ctypes.byref(params))
+
+
+def prefill_workspace_size(Hq, Hkv, q_start, Tq, params: SelectParams) -> int:
+    return lib().sparse_attn_prefill_workspace_size(Hq, Hkv, q_start, Tq, ctypes.byref(params))
+
+
+def prefill_chunk(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tensor, Kc: torch.Tensor,
+                  top_k: int, n_init: int = 1, n_local: int = 4, score_mode="softmax_sum",
+                  scale: float = 1.0, out_dtype=torch.float32, O=None, lse=None, want_lse=True,
+                  tile_idx=None, tile_cnt=None, workspace=None, stream=None):
+    """Tile-shared sparse causal prefill of one chunk. Returns (O, lse, tile_idx, tile_cnt)."""
+    Tq, Hq, d = Q.shape
+    Hkv, T_cap = K.shape[-3], K.shape[-2]
+    nc_cap = Kc.shape[-2]
+    p = make_params(top_k, n_init, n_local, score_mode)
+    dev = Q.device
+    n_tiles = (Tq + 63) // 64
+    cap = prefill_tile_cap(q_start, Tq, p)
+    if O is None:
+        O = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    if tile_idx is None:
+        tile_idx = torch.empty((n_tiles, Hkv, cap), dtype=torch.int32, device=dev)
+    if tile_cnt is None:
+        tile_cnt = torch.empty((n_tiles, Hkv), dtype=torch.int32, device=dev)
+    need = prefill_workspace_size(Hq, Hkv, q_start, Tq, p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_prefill_chunk(_dev(Q, "Q"), int(q_start), Tq, _dev(K, "K"), _dev(V, "V"),
+                                         _dev(Kc, "Kc"), _dtype_code(K), Hq, Hkv, d, T_cap, nc_cap,
+                                         ctypes.byref(p), float(scale), _dev(O, "O"), _dtype_code(O),
+                                         _opt(lse, "lse"), _dev(tile_idx, "tile_idx"),
+                                         tile_idx.shape[-1], _dev(tile_cnt, "tile_cnt"),
+                                         _opt(workspace, "workspace"), ws_bytes, _stream(Q, stream))
+    _check("sparse_attn_prefill_chunk", st)
+    return O, lse, tile_idx, tile_cnt

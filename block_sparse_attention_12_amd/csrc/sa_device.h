@@ -1,0 +1,153 @@
+// Device-side helpers shared by the gfx950 kernels of libsparse_attn.
+//
+// Row layout used by every kernel: a row of d = 128 elements is read by 16
+// consecutive lanes ("a row group"), each lane owning 8 consecutive channels
+// (16 B of bf16 or 32 B of fp32). A 64-wide wavefront therefore covers 4 rows
+// per load instruction, and dot products are finished by a reduction across
+// the 16 lanes of a row group using DPP lane permutations (no LDS traffic).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kD = 128;            // head dimension supported
+constexpr int kRowLanes = 16;      // lanes per row
+constexpr int kLaneElems = 8;      // channels per lane
+constexpr int kBlock = 64;         // tokens per KV block
+constexpr int kCmpKernel = 32;     // compression window
+constexpr int kCmpStride = 16;     // compression stride
+
+typedef uint16_t bf16_t;
+
+__host__ __device__ __forceinline__ int64_t n_compressed(int64_t L) {
+    return L < kCmpKernel ? 0 : (L - kCmpKernel) / kCmpStride + 1;
+}
+__host__ __device__ __forceinline__ int64_t n_blocks(int64_t L) {
+    return (L + kBlock - 1) / kBlock;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---- 8-channel loads/stores of one lane's slice of a row -------------------
+
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t *p, float (&x)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// Raw (unconverted) register image of one lane's slice, so loads can be
+// issued early and converted later.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> { uint4 v; };
+template <> struct Raw8<float> { float4 a, b; };
+
+__device__ __forceinline__ void load_raw(const bf16_t *p, Raw8<bf16_t> &r) {
+    r.v = *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void load_raw(const float *p, Raw8<float> &r) {
+    r.a = reinterpret_cast<const float4 *>(p)[0];
+    r.b = reinterpret_cast<const float4 *>(p)[1];
+}
+__device__ __forceinline__ void unpack(const Raw8<bf16_t> &r, float (&x)[8]) {
+    x[0] = bf16_lo(r.v.x); x[1] = bf16_hi(r.v.x); x[2] = bf16_lo(r.v.y); x[3] = bf16_hi(r.v.y);
+    x[4] = bf16_lo(r.v.z); x[5] = bf16_hi(r.v.z); x[6] = bf16_lo(r.v.w); x[7] = bf16_hi(r.v.w);
+}
+__device__ __forceinline__ void unpack(const Raw8<float> &r, float (&x)[8]) {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
+__device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float (&x)[8]) {
+    uint4 v;
+    v.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
+    v.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+    v.z = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
+    v.w = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
+    *reinterpret_cast<uint4 *>(p) = v;
+}
+
+// ---- DPP lane permutations inside a 16-lane row ---------------------------
+
+// DPP controls (GCN/CDNA encoding)
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within each half row
+constexpr int kDppRowRor4 = 0x124;       // rotate right by 4 within the row
+constexpr int kDppRowRor8 = 0x128;       // rotate right by 8 within the row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Partner selection for the four reduction steps over a row group. Step s
+// pairs lanes that differ in bit (3 - s) of the lane's row position:
+//   s = 0: mirror (i <-> 15-i), s = 1: half mirror (i <-> 7-i),
+//   s = 2: xor 2, s = 3: xor 1.
+template <int S>
+__device__ __forceinline__ float partner(float v) {
+    if constexpr (S == 0) return dpp<kDppRowMirror>(v);
+    else if constexpr (S == 1) return dpp<kDppRowHalfMirror>(v);
+    else if constexpr (S == 2) return dpp<kDppQuadXor2>(v);
+    else return dpp<kDppQuadXor1>(v);
+}
+
+// Transposed sum over the 16 lanes of a row group of N partial values per
+// lane (N a power of two). After the call v[0 .. max(N/16,1)) holds totals:
+// for N >= 16 lane position i (= lane & 15) holds the totals of values
+// [i*N/16, (i+1)*N/16); for N < 16 it holds value (i >> (4 - log2 N)).
+// Each step halves the live values: the lane keeps the half selected by one
+// bit of its position and receives the partner's copy of that half, so the
+// whole reduction costs N-1 lane exchanges instead of 4N.
+template <int S, int N, int LIVE>
+__device__ __forceinline__ void transpose_reduce_step(float (&v)[N], int pos) {
+    if constexpr (S < 4) {
+        if constexpr (LIVE > 1) {
+            constexpr int H = LIVE / 2;
+            const bool upper = (pos >> (3 - S)) & 1;
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                const float keep = upper ? v[k + H] : v[k];
+                const float send = upper ? v[k] : v[k + H];
+                v[k] = keep + partner<S>(send);
+            }
+            transpose_reduce_step<S + 1, N, H>(v, pos);
+        } else {
+            v[0] = v[0] + partner<S>(v[0]);
+            transpose_reduce_step<S + 1, N, 1>(v, pos);
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void transpose_reduce16(float (&v)[N], int lane) {
+    transpose_reduce_step<0, N, N>(v, lane & 15);
+}
+
+// Full-wave helpers (64 lanes)
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+}  // namespace sa

@@ -1,0 +1,51 @@
+// Host-side launchers of libsparse_attn (one per kernel family). Argument
+// validation happens in sparse_attn_api.hip before any of these is called;
+// the launchers only size grids and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+
+// Scratch layout of sparse_attn_select (offsets in bytes inside the workspace).
+struct SelectWorkspace {
+    size_t logits_off, logits_bytes;   // [units][G][nc_pad] fp32 (softmax mode)
+    size_t stats_off, stats_bytes;     // [units][G][n_chunks] float2 (max, sum exp)
+    size_t bscore_off, bscore_bytes;   // [units][nb_cap] fp32
+    size_t total;
+    int64_t nc_pad;                    // row stride of the logits
+    int64_t nb_cap;
+    int n_chunks;
+};
+SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode);
+
+int launch_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int64_t T_cap,
+                    int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                    int32_t max_new_entries, hipStream_t stream);
+
+int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
+                  int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
+                  const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                  float *block_scores_out, void *workspace, hipStream_t stream);
+
+int decode_auto_split(int B, int Hkv, int32_t idx_cap);
+size_t decode_workspace_bytes(int B, int Hq, int32_t n_split);
+int launch_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq, int Hkv,
+                  int64_t T_cap, const int32_t *seq_lens, const int32_t *idx, const int32_t *cnt,
+                  int32_t idx_cap, float scale, void *O, int out_dtype, float *lse_out,
+                  int32_t n_split, void *workspace, hipStream_t stream);
+
+int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p);
+size_t prefill_workspace_bytes(int Hq, int Hkv, int64_t q_start, int64_t Tq,
+                               const sa_select_params &p);
+int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, const void *V,
+                   const void *Kc, int Hq, int Hkv, int64_t T_cap, int64_t nc_cap,
+                   const sa_select_params &p, float scale, void *O, int out_dtype, float *lse_out,
+                   int32_t *tile_idx, int32_t tile_idx_cap, int32_t *tile_cnt, void *workspace,
+                   hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,478 @@
+// Block selection: scoring of compressed keys, block aggregation, exact top-k
+// and the union with the initial and local blocks.
+//
+// Page: "SparDA: Sparse Decoupled Attention for Efficient Long-Context LLM
+// Inference" (picx.dev summary). Eq. 1 (union of init, local and top-k sets),
+// Eq. 4 (raw scores of one Forecast vector per GQA group, "Compact Forecast
+// Indexer": no per-head loop, no softmax) and Eq. 6 (the query-driven
+// selector: sum over the G heads of a group of each head's softmax over the
+// compressed entries).
+//
+// Kernels (all HBM or latency bound, no matrix cores: scoring is a
+// matrix-vector product per group):
+//   score_raw_kernel      RAW_SUM. The group's selector vectors are summed
+//                         once, then every block's three inside entries
+//                         (4b, 4b+1, 4b+2) are scored and max-reduced; the
+//                         straddling entry 4b+3 belongs to no block and is not
+//                         read. Writes one fp32 score per block.
+//   score_softmax_kernel  SOFTMAX_SUM. G dot products per entry, written as
+//                         fp32 logits, plus per 512-entry chunk and head the
+//                         running (max, sum of exp) for the softmax denominator.
+//   topk_kernel           one workgroup per (sequence, KV head): merges the
+//                         chunk denominators, forms block scores, finds the
+//                         exact k-th largest (score, -index) key by a 4-pass
+//                         8-bit radix select in LDS, and writes the union in
+//                         ascending block order with a workgroup prefix scan.
+#include <float.h>
+#include <math.h>
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+constexpr int kSelThreads = 256;
+constexpr int kSoftmaxChunk = 512;                  // entries per workgroup (softmax mode)
+constexpr int kRawChunkBlocks = 128;                // blocks per workgroup (raw mode)
+constexpr int kTopkThreads = 256;
+constexpr int64_t kMaxTopkBlocks = 32768;           // LDS key array limit
+
+SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
+    SelectWorkspace w{};
+    const int64_t units = (int64_t)B * Hkv;
+    const int64_t nc_cap = n_compressed(T_cap);
+    w.n_chunks = (int)((nc_cap + kSoftmaxChunk - 1) / kSoftmaxChunk);
+    w.nc_pad = (int64_t)w.n_chunks * kSoftmaxChunk;
+    w.nb_cap = n_blocks(T_cap);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    if (score_mode == SA_SCORE_SOFTMAX_SUM) {
+        w.logits_bytes = (size_t)units * G * w.nc_pad * sizeof(float);
+        w.logits_off = take(w.logits_bytes);
+        w.stats_bytes = (size_t)units * G * (w.n_chunks > 0 ? w.n_chunks : 1) * sizeof(float2);
+        w.stats_off = take(w.stats_bytes);
+    } else {
+        w.bscore_bytes = (size_t)units * (w.nb_cap > 0 ? w.nb_cap : 1) * sizeof(float);
+        w.bscore_off = take(w.bscore_bytes);
+    }
+    w.total = off;
+    return w;
+}
+
+__device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
+    return L < 0 ? 0 : (L > T_cap ? T_cap : L);
+}
+
+// ---------------------------------------------------------------- raw scores
+
+template <typename T>
+__global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
+    const T *__restrict__ sel, int H_sel, int Gs, const T *__restrict__ Kc, int Hkv,
+    int64_t nc_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ bscore,
+    int64_t nb_cap) {
+    const int unit = blockIdx.y;
+    const int b = unit / Hkv, kvh = unit % Hkv;
+    const int64_t L = clamp_len(seq_lens[b], T_cap);
+    const int64_t nc = n_compressed(L);
+    const int lane = threadIdx.x & 63;
+    const int lane16 = threadIdx.x & 15;
+    const int group = threadIdx.x >> 4;                 // 0..15
+
+    // group-summed selector slice (sum in head order)
+    float s[8];
+    {
+        const T *sp = sel + ((int64_t)b * H_sel + (int64_t)kvh * Gs) * kD + lane16 * kLaneElems;
+        load8(sp, s);
+        for (int g = 1; g < Gs; ++g) {
+            float x[8];
+            load8(sp + (int64_t)g * kD, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
+        }
+    }
+    const T *Kcu = Kc + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
+    float *bs = bscore + (int64_t)unit * nb_cap;
+    const int64_t chunk0 = (int64_t)blockIdx.x * kRawChunkBlocks;
+#pragma unroll 1
+    for (int it = 0; it < kRawChunkBlocks / 64; ++it) {
+        const int64_t blk0 = chunk0 + it * 64 + group * 4;      // this group's 4 blocks
+        Raw8<T> r[12];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int64_t j = 4 * (blk0 + q) + e;
+                if (j < nc) load_raw(Kcu + j * kD, r[q * 3 + e]);
+            }
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int64_t j = 4 * (blk0 + q) + e;
+                float acc = 0.f;
+                if (j < nc) {
+                    float x[8];
+                    unpack(r[q * 3 + e], x);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc = fmaf(s[c], x[c], acc);
+                }
+                v[q * 4 + e] = acc;
+            }
+            v[q * 4 + 3] = 0.f;
+        }
+        transpose_reduce16<16>(v, lane);
+        // lane position i holds block (i >> 2), inside entry (i & 3)
+        const int q = lane16 >> 2, e = lane16 & 3;
+        const int64_t blk = blk0 + q;
+        const int64_t j = 4 * blk + e;
+        float x = (e < 3 && j < nc) ? v[0] : -INFINITY;
+        x = fmaxf(x, dpp<kDppQuadXor1>(x));
+        x = fmaxf(x, dpp<kDppQuadXor2>(x));
+        if (e == 0 && blk < nb_cap) bs[blk] = x;
+    }
+    (void)lane;
+}
+
+// ---------------------------------------------------------------- softmax scores
+
+__device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    s = s * expf(m - M) + s2 * expf(m2 - M);
+    m = M;
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
+    const T *__restrict__ sel, int H_sel, const T *__restrict__ Kc, int Hkv, int64_t nc_cap,
+    int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ logits, int64_t nc_pad,
+    float2 *__restrict__ stats, int n_chunks) {
+    constexpr int EPI = 16 / G;                         // entries per row group per iteration
+    constexpr int PER_IT = 16 * EPI;                     // entries per workgroup iteration
+    __shared__ float2 s_ms[4][G];
+    const int unit = blockIdx.y;
+    const int b = unit / Hkv, kvh = unit % Hkv;
+    const int64_t L = clamp_len(seq_lens[b], T_cap);
+    const int64_t nc = n_compressed(L);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane16 = threadIdx.x & 15;
+    const int group = threadIdx.x >> 4;
+    float q[G][8];
+    {
+        const T *sp = sel + ((int64_t)b * H_sel + (int64_t)kvh * G) * kD + lane16 * kLaneElems;
+#pragma unroll
+        for (int g = 0; g < G; ++g) load8(sp + (int64_t)g * kD, q[g]);
+    }
+    const T *Kcu = Kc + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
+    const int my_e = lane16 / G, my_g = lane16 % G;     // value this lane ends up holding
+    float *lrow = logits + ((int64_t)unit * G + my_g) * nc_pad;
+    float m = -INFINITY, ssum = 0.f;
+    const int64_t base = (int64_t)blockIdx.x * kSoftmaxChunk;
+#pragma unroll 1
+    for (int it = 0; it < kSoftmaxChunk / PER_IT; ++it) {
+        const int64_t j0 = base + it * PER_IT + group * EPI;
+        Raw8<T> r[EPI];
+#pragma unroll
+        for (int e = 0; e < EPI; ++e)
+            if (j0 + e < nc) load_raw(Kcu + (j0 + e) * kD, r[e]);
+        float v[16];
+#pragma unroll
+        for (int e = 0; e < EPI; ++e) {
+            float x[8];
+            if (j0 + e < nc) unpack(r[e], x);
+            else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[c] = 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc = fmaf(q[g][c], x[c], acc);
+                v[e * G + g] = acc;
+            }
+        }
+        transpose_reduce16<16>(v, lane);
+        const int64_t j = j0 + my_e;
+        if (j < nc) {
+            const float x = v[0];
+            lrow[j] = x;
+            if (x > m) {
+                ssum = ssum * expf(m - x) + 1.f;
+                m = x;
+            } else {
+                ssum += expf(x - m);
+            }
+        }
+    }
+    // merge (max, sum) over lanes holding the same head: lane bits >= log2(G)
+#pragma unroll
+    for (int bit = G; bit < 64; bit <<= 1) {
+        const float m2 = shfl_xor(m, bit);
+        const float s2 = shfl_xor(ssum, bit);
+        merge_ms(m, ssum, m2, s2);
+    }
+    if (lane < G) s_ms[wave][lane] = make_float2(m, ssum);
+    __syncthreads();
+    if (threadIdx.x < G) {
+        float2 a = s_ms[0][threadIdx.x];
+        for (int w = 1; w < 4; ++w) merge_ms(a.x, a.y, s_ms[w][threadIdx.x].x, s_ms[w][threadIdx.x].y);
+        stats[((int64_t)unit * G + threadIdx.x) * n_chunks + blockIdx.x] = a;
+    }
+}
+
+// ---------------------------------------------------------------- top-k + union
+
+__device__ __forceinline__ uint32_t orderable(float x) {
+    if (x == 0.f) x = 0.f;                               // -0 and +0 tie
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of one int per thread over the workgroup; also returns the total.
+__device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) s_wave[wave] = v;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+        const int sw = s_wave[w];
+        if (w < wave) base += sw;
+        total += sw;
+    }
+    __syncthreads();
+    return base + v - x;
+}
+
+template <int G, bool SOFTMAX>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens, int top_k,
+    int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
+    const float2 *__restrict__ stats, int n_chunks, const float *__restrict__ bscore_in,
+    float *__restrict__ bscore_out, int32_t *__restrict__ idx_out, int idx_cap,
+    int32_t *__restrict__ cnt_out) {
+    extern __shared__ uint32_t s_keys[];                 // [nb_cap]
+    __shared__ uint32_t s_hist[256];
+    __shared__ float s_M[G > 0 ? G : 1], s_Zinv[G > 0 ? G : 1];
+    __shared__ int s_wave[kTopkThreads / 64];
+    __shared__ uint32_t s_digit, s_above;
+    const int unit = blockIdx.x;
+    const int b = unit / Hkv;
+    const int tid = threadIdx.x;
+    const int64_t L = clamp_len(seq_lens[b], T_cap);
+    const int64_t nc = n_compressed(L);
+    const int nb = (int)n_blocks(L);
+    const int init_hi = n_init < nb ? n_init : nb;
+    const int local_lo = nb - n_local > 0 ? nb - n_local : 0;
+    const int cand_lo = init_hi;
+    const int cand_hi = local_lo > cand_lo ? local_lo : cand_lo;
+    const int n_cand = cand_hi - cand_lo;
+
+    if constexpr (SOFTMAX) {
+        if (tid < G) {
+            const int used = (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk);
+            const float2 *st = stats + ((int64_t)unit * G + tid) * n_chunks;
+            float M = -INFINITY, Z = 0.f;
+            for (int c = 0; c < used; ++c) merge_ms(M, Z, st[c].x, st[c].y);
+            s_M[tid] = M;
+            s_Zinv[tid] = Z > 0.f ? 1.f / Z : 0.f;
+        }
+        __syncthreads();
+    }
+    // block scores and keys
+    for (int blk = tid; blk < nb_cap; blk += kTopkThreads) {
+        float score = -INFINITY;
+        if (blk < nb) {
+            if constexpr (SOFTMAX) {
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    const int64_t j = 4 * (int64_t)blk + e;
+                    if (j < nc) {
+                        float S = 0.f;
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            S += expf(logits[((int64_t)unit * G + g) * nc_pad + j] - s_M[g]) * s_Zinv[g];
+                        score = fmaxf(score, S);
+                    }
+                }
+            } else {
+                score = bscore_in[(int64_t)unit * nb_cap + blk];
+            }
+        }
+        if (bscore_out) bscore_out[(int64_t)unit * nb_cap + blk] = score;
+        s_keys[blk] = orderable(score);
+    }
+    __syncthreads();
+
+    // radix select of the top_k-th largest key among the candidates
+    const bool take_all = top_k >= n_cand;
+    const bool take_none = top_k <= 0;
+    uint32_t prefix = 0, mask = 0;
+    int remaining = top_k;
+    if (!take_all && !take_none) {
+#pragma unroll 1
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            s_hist[tid] = 0;
+            __syncthreads();
+            for (int blk = cand_lo + tid; blk < cand_hi; blk += kTopkThreads) {
+                const uint32_t key = s_keys[blk];
+                if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // counts above each bin, from the top: lane l owns bins 4l .. 4l+3
+                const uint32_t hb[4] = {s_hist[4 * tid], s_hist[4 * tid + 1], s_hist[4 * tid + 2],
+                                        s_hist[4 * tid + 3]};
+                const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
+                uint32_t incl = c;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t t = __shfl_down(incl, off, 64);
+                    if (tid + off < 64) incl += t;
+                }
+                uint32_t above = incl - c;               // keys in bins owned by higher lanes
+#pragma unroll
+                for (int k = 3; k >= 0; --k) {
+                    if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
+                        s_digit = 4 * tid + k;
+                        s_above = above;
+                    }
+                    above += hb[k];
+                }
+            }
+            __syncthreads();
+            prefix |= s_digit << shift;
+            mask |= 255u << shift;
+            remaining -= (int)s_above;
+            __syncthreads();
+        }
+    }
+    const uint32_t thr = prefix;        // exact key of the k-th largest candidate
+    const int take_eq = remaining;      // keys equal to thr that are taken, lowest ids first
+
+    // membership of block blk; eq_rank counts candidates equal to thr seen so far
+    auto in_union = [&](int blk, int &eq_rank) -> bool {
+        if (blk < init_hi || blk >= local_lo) return true;
+        if (blk < cand_lo || blk >= cand_hi || take_none) return false;
+        if (take_all) return true;
+        const uint32_t key = s_keys[blk];
+        if (key > thr) return true;
+        if (key == thr) return eq_rank++ < take_eq;
+        return false;
+    };
+
+    // union in ascending order: each thread owns a contiguous range of blocks
+    const int per = (nb + kTopkThreads - 1) / kTopkThreads;
+    const int lo = tid * per < nb ? tid * per : nb;
+    const int hi = lo + per < nb ? lo + per : nb;
+    int n_eq = 0;
+    if (!take_all && !take_none)
+        for (int blk = lo; blk < hi; ++blk)
+            n_eq += (blk >= cand_lo && blk < cand_hi && s_keys[blk] == thr) ? 1 : 0;
+    int unused;
+    const int eq_base = wg_exclusive_scan(n_eq, s_wave, unused);
+    int rank = eq_base, n_in = 0;
+    for (int blk = lo; blk < hi; ++blk) n_in += in_union(blk, rank) ? 1 : 0;
+    int total;
+    int pos = wg_exclusive_scan(n_in, s_wave, total);
+    int32_t *row = idx_out + (int64_t)unit * idx_cap;
+    rank = eq_base;
+    for (int blk = lo; blk < hi; ++blk) {
+        if (in_union(blk, rank)) {
+            if (pos < idx_cap) row[pos] = blk;
+            ++pos;
+        }
+    }
+    for (int i = total + tid; i < idx_cap; i += kTopkThreads) row[i] = -1;
+    if (tid == 0) cnt_out[unit] = total < idx_cap ? total : idx_cap;
+}
+
+template <typename T, int G>
+static void launch_softmax(const void *sel, int H_sel, const void *Kc, int B, int Hkv, int64_t T_cap,
+                           int64_t nc_cap, const int32_t *seq_lens, const sa_select_params &p,
+                           int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, float *bs_out,
+                           const SelectWorkspace &w, char *ws, hipStream_t stream) {
+    float *logits = (float *)(ws + w.logits_off);
+    float2 *stats = (float2 *)(ws + w.stats_off);
+    const unsigned units = (unsigned)(B * Hkv);
+    if (w.n_chunks > 0)
+        hipLaunchKernelGGL((score_softmax_kernel<T, G>), dim3((unsigned)w.n_chunks, units),
+                           dim3(kSelThreads), 0, stream, (const T *)sel, H_sel, (const T *)Kc, Hkv,
+                           nc_cap, T_cap, seq_lens, logits, w.nc_pad, stats, w.n_chunks);
+    const size_t lds = (size_t)(w.nb_cap > 0 ? w.nb_cap : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL((topk_kernel<G, true>), dim3(units), dim3(kTopkThreads), lds, stream, Hkv,
+                       T_cap, w.nb_cap, seq_lens, p.top_k, p.n_init, p.n_local, logits, w.nc_pad,
+                       stats, w.n_chunks, (const float *)nullptr, bs_out, idx_out, idx_cap, cnt_out);
+}
+
+template <typename T>
+static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B, int Hkv,
+                       int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
+                       const sa_select_params &p, int32_t *idx_out, int32_t idx_cap,
+                       int32_t *cnt_out, float *bs_out, const SelectWorkspace &w, char *ws,
+                       hipStream_t stream) {
+    float *bscore = (float *)(ws + w.bscore_off);
+    const unsigned units = (unsigned)(B * Hkv);
+    const unsigned chunks = (unsigned)((w.nb_cap + kRawChunkBlocks - 1) / kRawChunkBlocks);
+    if (chunks > 0)
+        hipLaunchKernelGGL(score_raw_kernel<T>, dim3(chunks, units), dim3(kSelThreads), 0, stream,
+                           (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap, seq_lens,
+                           bscore, w.nb_cap);
+    const size_t lds = (size_t)(w.nb_cap > 0 ? w.nb_cap : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL((topk_kernel<1, false>), dim3(units), dim3(kTopkThreads), lds, stream, Hkv,
+                       T_cap, w.nb_cap, seq_lens, p.top_k, p.n_init, p.n_local,
+                       (const float *)nullptr, (int64_t)0, (const float2 *)nullptr, 0,
+                       (const float *)bscore, bs_out, idx_out, idx_cap, cnt_out);
+}
+
+int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
+                  int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
+                  const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                  float *block_scores_out, void *workspace, hipStream_t stream) {
+    const SelectWorkspace w = select_workspace_layout(B, Hkv, G, T_cap, p.score_mode);
+    if (w.nb_cap > kMaxTopkBlocks) return SA_ERR_UNSUPPORTED;
+    char *ws = (char *)workspace;
+    const int H_sel = G * Hkv;
+    if (p.score_mode == SA_SCORE_RAW_SUM) {
+        if (dtype == SA_BF16)
+            launch_raw<bf16_t>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
+                               cnt_out, block_scores_out, w, ws, stream);
+        else
+            launch_raw<float>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
+                              cnt_out, block_scores_out, w, ws, stream);
+    } else {
+#define SA_SOFTMAX_CASE(GG)                                                                       \
+    case GG:                                                                                      \
+        if (dtype == SA_BF16)                                                                     \
+            launch_softmax<bf16_t, GG>(sel, H_sel, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, \
+                                       idx_cap, cnt_out, block_scores_out, w, ws, stream);        \
+        else                                                                                      \
+            launch_softmax<float, GG>(sel, H_sel, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out,  \
+                                      idx_cap, cnt_out, block_scores_out, w, ws, stream);         \
+        break;
+        switch (G) {
+            SA_SOFTMAX_CASE(1)
+            SA_SOFTMAX_CASE(2)
+            SA_SOFTMAX_CASE(4)
+            SA_SOFTMAX_CASE(8)
+            default: return SA_ERR_UNSUPPORTED;
+        }
+#undef SA_SOFTMAX_CASE
+    }
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace sa

@@ -1,0 +1,157 @@
+// C ABI entry points of libsparse_attn: argument validation, workspace sizing
+// and dispatch to the kernel launchers. Every check runs on the host before
+// any HIP call, so an invalid call enqueues nothing and returns a status.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == SA_F32 || dt == SA_BF16; }
+
+int check_params(const sa_select_params *p) {
+    if (!p) return SA_ERR_INVALID_ARG;
+    if (p->top_k < 0 || p->n_init < 0 || p->n_local < 0) return SA_ERR_INVALID_ARG;
+    if (p->score_mode != SA_SCORE_SOFTMAX_SUM && p->score_mode != SA_SCORE_RAW_SUM)
+        return SA_ERR_INVALID_ARG;
+    if (p->block_size != kBlock || p->cmp_kernel != kCmpKernel || p->cmp_stride != kCmpStride)
+        return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+int64_t union_cap(const sa_select_params *p) {
+    return (int64_t)p->top_k + p->n_init + p->n_local;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
+
+const char *sparse_attn_status_string(int status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID_ARG: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SA_ERR_CAPACITY: return "output or cache capacity too small";
+        case SA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int sparse_attn_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int d, int64_t T_cap,
+                         int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                         int32_t max_new_entries, void *stream) {
+    if (!K || !Kc || !lens_prev || !lens_now) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hkv <= 0 || d <= 0 || T_cap < 0 || nc_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    if (max_new_entries < 0) return SA_ERR_INVALID_ARG;
+    if (d != kD) return SA_ERR_UNSUPPORTED;
+    if (nc_cap < n_compressed(T_cap)) return SA_ERR_CAPACITY;
+    if ((int64_t)B * Hkv > 0x7fffffff) return SA_ERR_UNSUPPORTED;
+    if (max_new_entries == 0 || T_cap == 0) return SA_OK;
+    return launch_compress(K, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_prev, lens_now,
+                           max_new_entries, (hipStream_t)stream);
+}
+
+size_t sparse_attn_select_workspace_size(int B, int Hkv, int H_sel, int64_t T_cap,
+                                         const sa_select_params *p) {
+    if (!p || B <= 0 || Hkv <= 0 || H_sel <= 0 || H_sel % Hkv || T_cap < 0) return 0;
+    const int G = H_sel / Hkv;
+    return select_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total;
+}
+
+int sparse_attn_select(const void *sel, int H_sel, const void *Kc, int dtype, int B, int Hkv,
+                       int d, int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
+                       const sa_select_params *p, int32_t *idx_out, int32_t idx_cap,
+                       int32_t *cnt_out, float *block_scores_out, void *workspace,
+                       size_t ws_bytes, void *stream) {
+    if (!sel || !Kc || !seq_lens || !idx_out || !cnt_out) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hkv <= 0 || H_sel <= 0 || d <= 0 || T_cap < 0 || nc_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    int st = check_params(p);
+    if (st) return st;
+    if (H_sel % Hkv) return SA_ERR_INVALID_ARG;
+    const int G = H_sel / Hkv;
+    if (d != kD) return SA_ERR_UNSUPPORTED;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
+    if (n_blocks(T_cap) > 32768) return SA_ERR_UNSUPPORTED;
+    if (nc_cap < n_compressed(T_cap)) return SA_ERR_CAPACITY;
+    if (idx_cap < union_cap(p) || idx_cap <= 0) return SA_ERR_CAPACITY;
+    const size_t need = select_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total;
+    if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
+    return launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, seq_lens, *p, idx_out, idx_cap,
+                         cnt_out, block_scores_out, workspace, (hipStream_t)stream);
+}
+
+size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap, int32_t n_split) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || idx_cap <= 0) return 0;
+    const int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    return decode_workspace_bytes(B, Hq, s);
+}
+
+int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                       int Hkv, int d, int64_t T_cap, const int32_t *seq_lens, const int32_t *idx,
+                       const int32_t *cnt, int32_t idx_cap, float scale, void *O, int out_dtype,
+                       float *lse_out, int32_t n_split, void *workspace, size_t ws_bytes,
+                       void *stream) {
+    if (!Q || !K || !V || !seq_lens || !idx || !cnt || !O) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 ||
+        T_cap < 0 || idx_cap <= 0)
+        return SA_ERR_INVALID_ARG;
+    if (Hq % Hkv) return SA_ERR_INVALID_ARG;
+    if (!(scale == scale)) return SA_ERR_INVALID_ARG;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (n_split > 1024) return SA_ERR_UNSUPPORTED;
+    const int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    const size_t need = decode_workspace_bytes(B, Hq, s);
+    if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
+    return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale, O,
+                         out_dtype, lse_out, s, workspace, (hipStream_t)stream);
+}
+
+int32_t sparse_attn_prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params *p) {
+    if (!p || q_start < 0 || Tq <= 0) return 0;
+    return prefill_tile_cap(q_start, Tq, *p);
+}
+
+size_t sparse_attn_prefill_workspace_size(int Hq, int Hkv, int64_t q_start, int64_t Tq,
+                                          const sa_select_params *p) {
+    if (!p || Hq <= 0 || Hkv <= 0 || Hq % Hkv || q_start < 0 || Tq <= 0) return 0;
+    return prefill_workspace_bytes(Hq, Hkv, q_start, Tq, *p);
+}
+
+int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const void *K,
+                              const void *V, const void *Kc, int dtype, int Hq, int Hkv, int d,
+                              int64_t T_cap, int64_t nc_cap, const sa_select_params *p,
+                              float scale, void *O, int out_dtype, float *lse_out,
+                              int32_t *tile_idx_out, int32_t tile_idx_cap, int32_t *tile_cnt_out,
+                              void *workspace, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !Kc || !O || !tile_idx_out || !tile_cnt_out) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || Hq <= 0 || Hkv <= 0 || d <= 0 || Tq <= 0 ||
+        q_start < 0 || T_cap < 0 || nc_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    if (q_start % kBlock) return SA_ERR_INVALID_ARG;
+    if (Hq % Hkv) return SA_ERR_INVALID_ARG;
+    if (!(scale == scale)) return SA_ERR_INVALID_ARG;
+    int st = check_params(p);
+    if (st) return st;
+    if (d != kD || Hq / Hkv != 4 || dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (n_blocks(q_start + Tq) > 32768) return SA_ERR_UNSUPPORTED;
+    if (T_cap < q_start + Tq) return SA_ERR_CAPACITY;
+    if (nc_cap < n_compressed(q_start + Tq)) return SA_ERR_CAPACITY;
+    if (tile_idx_cap < prefill_tile_cap(q_start, Tq, *p)) return SA_ERR_CAPACITY;
+    const size_t need = prefill_workspace_bytes(Hq, Hkv, q_start, Tq, *p);
+    if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
+    return launch_prefill(Q, q_start, Tq, K, V, Kc, Hq, Hkv, T_cap, nc_cap, *p, scale, O, out_dtype,
+                          lse_out, tile_idx_out, tile_idx_cap, tile_cnt_out, workspace,
+                          (hipStream_t)stream);
+}
+
+}  // extern "C"

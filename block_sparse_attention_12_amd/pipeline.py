@@ -1,0 +1,113 @@
+"""Decode-step and prefill drivers over the C ABI (no arithmetic of their own).
+
+A decode step of one layer is: append the compressed-key entries completed by
+the new token (Eq. 2), select blocks with the query or Forecast (Eq. 4 / Eq. 6
+and the Eq. 1 union), and attend over them (Eq. 5). With cross-layer reuse one
+selection from the anchor layer serves several layers. Outputs, index buffers
+and workspaces are allocated once here so a step enqueues kernels only.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import (compress, select, decode, prefill_chunk, make_params, select_workspace_size,
+               decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
+
+
+class SparseDecoder:
+    """Buffers and calls for one decode configuration (fixed B, heads, capacity)."""
+
+    def __init__(self, B: int, Hq: int, Hkv: int, T_cap: int, top_k: int, n_init: int = 1,
+                 n_local: int = 2, selector: str = "query", score_mode: str = "softmax_sum",
+                 device="cuda", n_split: int = 0, out_dtype=torch.float32, want_lse: bool = True):
+        self.B, self.Hq, self.Hkv, self.T_cap = B, Hq, Hkv, T_cap
+        self.top_k, self.n_init, self.n_local = top_k, n_init, n_local
+        self.selector, self.score_mode, self.n_split = selector, score_mode, n_split
+        self.H_sel = Hq if selector == "query" else Hkv
+        self.cap = top_k + n_init + n_local
+        self.nc_cap = n_compressed(T_cap)
+        dev = torch.device(device)
+        self.device = dev
+        p = make_params(top_k, n_init, n_local, score_mode)
+        self.idx = torch.empty((B, Hkv, self.cap), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        sws = select_workspace_size(B, Hkv, self.H_sel, T_cap, p)
+        self.sel_ws = torch.empty(max(sws, 1), dtype=torch.uint8, device=dev)
+        dws = decode_workspace_size(B, Hq, Hkv, self.cap, n_split)
+        self.dec_ws = torch.empty(max(dws, 1), dtype=torch.uint8, device=dev)
+        self.O = torch.empty((B, Hq, 128), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
+
+    def new_kc(self, dtype) -> torch.Tensor:
+        return torch.empty((self.B, self.Hkv, self.nc_cap, 128), dtype=dtype, device=self.device)
+
+    def build(self, K, Kc, seq_lens):
+        zeros = torch.zeros_like(seq_lens)
+        compress(K, Kc, zeros, seq_lens, max_new_entries=self.nc_cap)
+
+    def append(self, K, Kc, lens_prev, lens_now, max_new_entries: int = 1):
+        compress(K, Kc, lens_prev, lens_now, max_new_entries=max_new_entries)
+
+    def select(self, sel, Kc, seq_lens, block_scores=None):
+        return select(sel, Kc, seq_lens, self.T_cap, self.top_k, self.n_init, self.n_local,
+                      self.score_mode, idx=self.idx, cnt=self.cnt, block_scores=block_scores,
+                      workspace=self.sel_ws)
+
+    def attend(self, Q, K, V, seq_lens, O: Optional[torch.Tensor] = None, lse=None, scale=1.0):
+        O = self.O if O is None else O
+        lse = self.lse if lse is None else lse
+        return decode(Q, K, V, seq_lens, self.idx, self.cnt, scale, O=O, lse=lse,
+                      want_lse=lse is not None, n_split=self.n_split, workspace=self.dec_ws)
+
+    def step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0):
+        """One single-layer decode step: append, select, attend."""
+        self.append(K, Kc, lens_prev, lens_now)
+        self.select(sel, Kc, lens_now)
+        return self.attend(Q, K, V, lens_now, scale=scale)
+
+    def crosslayer_step(self, layers: Sequence[dict], Kc, lens_prev, lens_now, outs=None,
+                        scale=1.0):
+        """One decode step where layer 0 (the anchor) selects for every layer.
+
+        layers: dicts with Q, K, V (K/V already hold the appended token).
+        outs: optional list of (O, lse) buffers per layer.
+        """
+        a = layers[0]
+        self.append(a["K"], Kc, lens_prev, lens_now)
+        self.select(a["Q"], Kc, lens_now)
+        res = []
+        for i, lay in enumerate(layers):
+            O, lse = (outs[i] if outs is not None else (None, None))
+            if O is None:
+                O = torch.empty_like(self.O)
+                lse = torch.empty_like(self.lse) if self.lse is not None else None
+            res.append(self.attend(lay["Q"], lay["K"], lay["V"], lens_now, O=O, lse=lse,
+                                   scale=scale))
+        return res
+
+
+class SparsePrefill:
+    """Buffers and call for chunked sparse prefill of one sequence."""
+
+    def __init__(self, Hq: int, Hkv: int, q_start: int, Tq: int, top_k: int, n_init: int = 1,
+                 n_local: int = 4, score_mode: str = "softmax_sum", device="cuda",
+                 out_dtype=torch.float32):
+        self.Hq, self.Hkv, self.q_start, self.Tq = Hq, Hkv, q_start, Tq
+        self.top_k, self.n_init, self.n_local, self.score_mode = top_k, n_init, n_local, score_mode
+        dev = torch.device(device)
+        p = make_params(top_k, n_init, n_local, score_mode)
+        self.cap = prefill_tile_cap(q_start, Tq, p)
+        n_tiles = (Tq + 63) // 64
+        self.tile_idx = torch.empty((n_tiles, Hkv, self.cap), dtype=torch.int32, device=dev)
+        self.tile_cnt = torch.empty((n_tiles, Hkv), dtype=torch.int32, device=dev)
+        ws = prefill_workspace_size(Hq, Hkv, q_start, Tq, p)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.O = torch.empty((Tq, Hq, 128), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+
+    def run(self, Q, K, V, Kc, scale=1.0):
+        return prefill_chunk(Q, self.q_start, K, V, Kc, self.top_k, self.n_init, self.n_local,
+                             self.score_mode, scale, O=self.O, lse=self.lse,
+                             tile_idx=self.tile_idx, tile_cnt=self.tile_cnt, workspace=self.ws)

@@ -1,0 +1,230 @@
+/*
+ * sparse_attn.h - C ABI of the MI355X (gfx950) block-sparse attention library
+ * (libsparse_attn.so).
+ *
+ * The method: keys are mean-pooled into compressed keys, a query (or one
+ * Forecast vector per GQA group) scores them, scores are aggregated to
+ * 64-token blocks, the top-k blocks are unioned with the initial and local
+ * blocks, and attention with an online softmax runs over only that union.
+ * Sources: the page "SparDA: Sparse Decoupled Attention for Efficient
+ * Long-Context LLM Inference" (picx.dev summary), sections "Theoretical
+ * Foundation" (Eq. 1, Eq. 2) and "Methodology" (Eq. 4, Eq. 5, "Compact
+ * Forecast Indexer", Eq. 6); tile-shared prefill selection and cross-layer
+ * index reuse follow the Kascade and CLSA abstracts on the pages "CoSA ..."
+ * and "HySparse2 ...".
+ *
+ * Common rules for every entry point:
+ *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *    The library never allocates or frees memory; scratch memory is a
+ *    caller-provided device workspace whose size the *_workspace_size
+ *    functions return (0 means no workspace is needed; then it may be NULL).
+ *  - Tensors are dense, row-major, innermost dimension last:
+ *      K, V  [B, Hkv, T_cap, d]     (prefill: B = 1)
+ *      Kc    [B, Hkv, nc_cap, d]    compressed keys, same dtype as K
+ *      Q     [B, Hq, d] (decode) or [Tq, Hq, d] (prefill chunk of one sequence)
+ *      sel   [B, H_sel, d]          selector vectors (Q itself, or Forecast F)
+ *    Every row of d elements starts 16-byte aligned (true for dense tensors
+ *    with d = 128). Only d = 128 is supported.
+ *  - dtype is SA_F32 or SA_BF16 and applies to all of Q, K, V, Kc and sel.
+ *    Arithmetic is fp32 (products, sums, softmax), outputs O are fp32 or bf16
+ *    (out_dtype), log-sum-exp outputs are fp32 natural logarithms.
+ *  - GQA: G = Hq / Hkv query heads share a KV head; query head h uses KV head
+ *    h / G. Hq must be a multiple of Hkv.
+ *  - seq_lens is a DEVICE int32 array [B]: the visible length L of each
+ *    sequence, 0 <= L <= T_cap. Kernels clamp values outside that range into
+ *    it so that no access leaves the tensors; the results are then undefined.
+ *  - Every call only enqueues work on the given hipStream_t (NULL = the
+ *    default stream) and returns without synchronising. Outputs are valid once
+ *    the stream reaches that point. Calls that share a workspace must be
+ *    ordered on one stream.
+ *  - Arguments are validated on the host before any HIP call. Every function
+ *    returns SA_OK (0) or a negative status; sparse_attn_status_string gives
+ *    its text. On an error nothing has been enqueued. A launch failure
+ *    reported by HIP returns SA_ERR_HIP.
+ *  - No global mutable state; calls on different streams with different
+ *    buffers may run concurrently.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_ABI_VERSION 1
+
+/* status codes */
+#define SA_OK               0
+#define SA_ERR_INVALID_ARG (-1)  /* null pointer, bad size, inconsistent shapes */
+#define SA_ERR_UNSUPPORTED (-2)  /* valid but not implemented (d != 128, GQA ratio, ...) */
+#define SA_ERR_WORKSPACE   (-3)  /* workspace missing or smaller than required */
+#define SA_ERR_CAPACITY    (-4)  /* an output or cache capacity is too small */
+#define SA_ERR_HIP         (-5)  /* a HIP launch reported an error */
+
+/* element types */
+#define SA_F32  0
+#define SA_BF16 1
+
+/* how the G selector heads of a group combine their scores of a compressed entry */
+#define SA_SCORE_SOFTMAX_SUM 0  /* sum over heads of each head's softmax over all entries (Eq. 6 form) */
+#define SA_SCORE_RAW_SUM     1  /* sum over heads of raw dot products (Eq. 4; one Forecast: its dot) */
+
+typedef struct sa_select_params {
+    int32_t block_size;  /* tokens per KV block: must be 64 */
+    int32_t cmp_kernel;  /* compression window l of Eq. 2: must be 32 */
+    int32_t cmp_stride;  /* compression stride s of Eq. 2: must be 16 */
+    int32_t top_k;       /* blocks chosen by score, >= 0 */
+    int32_t n_init;      /* initial blocks always kept, >= 0 */
+    int32_t n_local;     /* most recent blocks always kept, >= 0 */
+    int32_t score_mode;  /* SA_SCORE_SOFTMAX_SUM or SA_SCORE_RAW_SUM */
+} sa_select_params;
+
+/* Returns SPARSE_ATTN_ABI_VERSION of the loaded library. */
+int sparse_attn_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *sparse_attn_status_string(int status);
+
+/*
+ * sparse_attn_compress - Eq. 2: compressed entry j is the mean of keys
+ * 16j .. 16j+31 (kernel 32, stride 16). Only complete windows exist:
+ * n_c(L) = (L - 32) / 16 + 1 for L >= 32, else 0.
+ *
+ * Writes, for every sequence b, the entries j in [n_c(lens_prev[b]),
+ * n_c(lens_now[b])) of Kc from K; other entries are left untouched. A bulk
+ * build passes lens_prev = 0; a decode-time append passes the previous
+ * lengths, so only windows completed by the new tokens are formed.
+ * Each entry is one exact value: the window sum is the fp32 sum of two fp32
+ * partial sums of 16 consecutive keys each, accumulated in token order, then
+ * multiplied by 1/32 and rounded to the key dtype (round to nearest even).
+ *
+ *   K          [B, Hkv, T_cap, d] device, read
+ *   Kc         [B, Hkv, nc_cap, d] device, written; nc_cap >= n_c(T_cap)
+ *   lens_prev, lens_now   device int32 [B], lens_prev <= lens_now <= T_cap
+ *   max_new_entries  host hint: an upper bound on n_c(lens_now) - n_c(lens_prev)
+ *                    over the batch; sizes the launch only (any value >= 1
+ *                    gives correct results; pass n_c(T_cap) for a bulk build)
+ * Errors: SA_ERR_INVALID_ARG (null pointers, sizes <= 0, bad dtype),
+ *         SA_ERR_UNSUPPORTED (d != 128), SA_ERR_CAPACITY (nc_cap < n_c(T_cap)).
+ */
+int sparse_attn_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int d,
+                         int64_t T_cap, int64_t nc_cap, const int32_t *lens_prev,
+                         const int32_t *lens_now, int32_t max_new_entries, void *stream);
+
+/* Workspace bytes needed by sparse_attn_select (may be 0). */
+size_t sparse_attn_select_workspace_size(int B, int Hkv, int H_sel, int64_t T_cap,
+                                         const sa_select_params *p);
+
+/*
+ * sparse_attn_select - Eq. 4 / Eq. 6 scoring and top-k, Eq. 1 union, per
+ * (sequence b, KV head kvh) at visible length L = seq_lens[b].
+ *
+ * Scores: with H_sel = G * Hkv selector heads (the decode queries, G = Hq/Hkv)
+ * or H_sel = Hkv (one Forecast vector per group, "Compact Forecast Indexer"),
+ * the group's heads score every compressed entry j < n_c(L):
+ *   SOFTMAX_SUM: S_j = sum_h softmax_j(sel_h . Kc_j)    (softmax over j < n_c(L))
+ *   RAW_SUM:     S_j = sum_h sel_h . Kc_j
+ * Block b's score is the max of S_j over the entries whose window lies wholly
+ * inside the block (4b, 4b+1, 4b+2). With nb = ceil(L / 64) visible blocks,
+ * init = [0, min(n_init, nb)), local = [max(0, nb - n_local), nb), and the
+ * top_k blocks by score among the rest (ties to the lower block index) are
+ * unioned with init and local.
+ *
+ *   sel        [B, H_sel, d] device
+ *   Kc         [B, Hkv, nc_cap, d] device, valid for j < n_c(seq_lens[b])
+ *   T_cap      largest possible L; nc_cap >= n_c(T_cap)
+ *   idx_out    [B, Hkv, idx_cap] device int32: the union in ascending block
+ *              order, padded with -1; idx_cap >= top_k + n_init + n_local
+ *   cnt_out    [B, Hkv] device int32: number of valid entries of each row
+ *   block_scores_out  optional [B, Hkv, ceil(T_cap/64)] device fp32: each
+ *              block's score (-inf when no complete window lies inside it)
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, H_sel not Hkv or
+ *         a multiple of it with G in {1,2,4,8}, parameters other than
+ *         64/32/16, ceil(T_cap/64) > 32768), SA_ERR_CAPACITY (idx_cap, nc_cap),
+ *         SA_ERR_WORKSPACE.
+ */
+int sparse_attn_select(const void *sel, int H_sel, const void *Kc, int dtype, int B, int Hkv,
+                       int d, int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
+                       const sa_select_params *p, int32_t *idx_out, int32_t idx_cap,
+                       int32_t *cnt_out, float *block_scores_out, void *workspace,
+                       size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by sparse_attn_decode for this split count
+ * (n_split <= 0 asks the library's choice for this shape). */
+size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap,
+                                         int32_t n_split);
+
+/*
+ * sparse_attn_decode - Eq. 5 for one new token per sequence: query heads of
+ * KV head kvh attend, with softmax scale `scale`, to the tokens t < L of the
+ * blocks listed in idx[b, kvh, 0 .. cnt[b, kvh]) (any order, no duplicates).
+ * The query sits at position L - 1. The work of each (b, kvh) is split over
+ * n_split workgroups whose partial (max, sum, weighted values) are merged
+ * with log-sum-exp weights.
+ *
+ *   Q          [B, Hq, d] device
+ *   K, V       [B, Hkv, T_cap, d] device
+ *   idx, cnt   as written by sparse_attn_select (idx_cap columns)
+ *   O          [B, Hq, d] device, out_dtype SA_F32 or SA_BF16
+ *   lse_out    optional [B, Hq] device fp32: natural log of the softmax
+ *              denominator incl. scale (-inf when no token is selected)
+ *   n_split    workgroups per (b, kvh); <= 0 lets the library choose
+ * A (b, kvh) with cnt = 0 yields O = 0.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4),
+ *         SA_ERR_WORKSPACE.
+ */
+int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                       int Hkv, int d, int64_t T_cap, const int32_t *seq_lens,
+                       const int32_t *idx, const int32_t *cnt, int32_t idx_cap, float scale,
+                       void *O, int out_dtype, float *lse_out, int32_t n_split,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Columns needed per tile row of the prefill block sets: min(ceil(T/64),
+ * 64 * top_k + n_init + n_local) for a context of T = q_start + Tq tokens. */
+int32_t sparse_attn_prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params *p);
+
+/* Workspace bytes needed by sparse_attn_prefill_chunk. */
+size_t sparse_attn_prefill_workspace_size(int Hq, int Hkv, int64_t q_start, int64_t Tq,
+                                          const sa_select_params *p);
+
+/*
+ * sparse_attn_prefill_chunk - causal prefill of Tq new queries at positions
+ * q_start .. q_start+Tq-1 of one sequence whose context ends with them
+ * (L = q_start + Tq). q_start must be a multiple of 64. Tile t holds queries
+ * q_start+64t .. q_start+64t+63 (the last tile may be shorter), all inside
+ * block bt = q_start/64 + t.
+ *
+ * Selection per query p (L = p + 1), per KV head: Eq. 4 / Eq. 6 scores over
+ * entries j < n_c(p+1) with params->score_mode, block scores as in
+ * sparse_attn_select, top_k among blocks other than init and the local window
+ * [bt - n_local + 1, bt]. The tile's set is the union of its queries' top-k
+ * sets, init and the local window (ascending). Each query of the tile then
+ * attends causally (token t <= p) to that set, on matrix cores.
+ *
+ *   Q          [Tq, Hq, d] device
+ *   K, V       [Hkv, T_cap, d] device, T_cap >= q_start + Tq
+ *   Kc         [Hkv, nc_cap, d] device holding entries j < n_c(q_start + Tq)
+ *              (run sparse_attn_compress over the chunk first)
+ *   O          [Tq, Hq, d] device (out_dtype); lse_out optional [Tq, Hq] fp32
+ *   tile_idx_out [n_tiles, Hkv, tile_idx_cap] device int32, written (ascending,
+ *              -1 padded); tile_cnt_out [n_tiles, Hkv] device int32, written;
+ *              tile_idx_cap >= sparse_attn_prefill_tile_cap(...)
+ * Errors: SA_ERR_INVALID_ARG (incl. q_start % 64 != 0), SA_ERR_UNSUPPORTED
+ *         (d != 128, G != 4, dtype != SA_BF16, parameters other than 64/32/16),
+ *         SA_ERR_CAPACITY, SA_ERR_WORKSPACE.
+ */
+int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const void *K,
+                              const void *V, const void *Kc, int dtype, int Hq, int Hkv, int d,
+                              int64_t T_cap, int64_t nc_cap, const sa_select_params *p,
+                              float scale, void *O, int out_dtype, float *lse_out,
+                              int32_t *tile_idx_out, int32_t tile_idx_cap, int32_t *tile_cnt_out,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,159 @@
+"""The C-ABI library loads, exports every symbol its header declares, and its
+host-side validation rejects bad arguments with the documented status before
+any HIP call (so these run without a GPU; no call here reaches a kernel).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_12_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+FAKE = 0x1000          # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", src)))
+
+
+def test_header_declarations_match_binding_list():
+    assert declared_functions() == sorted(sa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = sa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert sa.abi_version() == 1
+    for code, text in ((0, "ok"), (-1, "invalid argument"), (-2, "unsupported configuration"),
+                       (-3, "workspace missing or too small"), (-4, "output or cache capacity too small"),
+                       (-5, "HIP launch error"), (7, "unknown status")):
+        assert sa.status_string(code) == text
+
+
+def _compress(**kw):
+    a = dict(K=FAKE, Kc=FAKE, dtype=sa.SA_BF16, B=2, Hkv=2, d=128, T_cap=1000, nc_cap=61,
+             lens_prev=FAKE, lens_now=FAKE, max_new=61, stream=None)
+    a.update(kw)
+    return sa.lib().sparse_attn_compress(a["K"], a["Kc"], a["dtype"], a["B"], a["Hkv"], a["d"],
+                                         a["T_cap"], a["nc_cap"], a["lens_prev"], a["lens_now"],
+                                         a["max_new"], a["stream"])
+
+
+def test_compress_validation():
+    assert _compress(K=None) == sa.SA_ERR_INVALID_ARG
+    assert _compress(lens_now=None) == sa.SA_ERR_INVALID_ARG
+    assert _compress(dtype=7) == sa.SA_ERR_INVALID_ARG
+    assert _compress(B=0) == sa.SA_ERR_INVALID_ARG
+    assert _compress(max_new=-1) == sa.SA_ERR_INVALID_ARG
+    assert _compress(d=64) == sa.SA_ERR_UNSUPPORTED
+    assert _compress(nc_cap=60) == sa.SA_ERR_CAPACITY           # n_c(1000) = 61
+    assert _compress(max_new=0) == sa.SA_OK                     # nothing to do: no launch
+
+
+def _select(**kw):
+    p = kw.pop("params", sa.make_params(16, 1, 2, "softmax_sum"))
+    a = dict(sel=FAKE, H_sel=8, Kc=FAKE, dtype=sa.SA_F32, B=1, Hkv=2, d=128, T_cap=8192,
+             nc_cap=511, seq_lens=FAKE, idx=FAKE, idx_cap=19, cnt=FAKE, bs=None, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    pp = None if p is None else ctypes.byref(p)
+    return sa.lib().sparse_attn_select(a["sel"], a["H_sel"], a["Kc"], a["dtype"], a["B"], a["Hkv"],
+                                       a["d"], a["T_cap"], a["nc_cap"], a["seq_lens"], pp, a["idx"],
+                                       a["idx_cap"], a["cnt"], a["bs"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
+
+
+def test_select_validation():
+    assert _select(sel=None) == sa.SA_ERR_INVALID_ARG
+    assert _select(params=None) == sa.SA_ERR_INVALID_ARG
+    assert _select(H_sel=7) == sa.SA_ERR_INVALID_ARG            # not a multiple of Hkv
+    assert _select(params=sa.make_params(-1)) == sa.SA_ERR_INVALID_ARG
+    assert _select(params=sa.make_params(16, score_mode=5)) == sa.SA_ERR_INVALID_ARG
+    assert _select(params=sa.make_params(16, block_size=128)) == sa.SA_ERR_UNSUPPORTED
+    assert _select(params=sa.make_params(16, cmp_stride=8)) == sa.SA_ERR_UNSUPPORTED
+    assert _select(H_sel=6) == sa.SA_ERR_UNSUPPORTED            # G = 3
+    assert _select(d=96) == sa.SA_ERR_UNSUPPORTED
+    assert _select(T_cap=64 * 32769) == sa.SA_ERR_UNSUPPORTED
+    assert _select(nc_cap=510) == sa.SA_ERR_CAPACITY
+    assert _select(idx_cap=18) == sa.SA_ERR_CAPACITY
+    assert _select(ws=None) == sa.SA_ERR_WORKSPACE
+    need = sa.select_workspace_size(1, 2, 8, 8192, sa.make_params(16))
+    assert need > 0
+    assert _select(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+
+
+def test_select_workspace_sizes():
+    soft = sa.select_workspace_size(8, 8, 32, 131072, sa.make_params(64, 1, 2, "softmax_sum"))
+    raw = sa.select_workspace_size(8, 8, 8, 131072, sa.make_params(64, 1, 2, "raw_sum"))
+    assert soft >= 64 * 4 * 8191 * 4                          # logits of every entry and head
+    assert raw >= 64 * 2048 * 4                                # one score per block
+    assert sa.select_workspace_size(8, 8, 7, 1000, sa.make_params(4)) == 0   # invalid -> 0
+
+
+def _decode(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=sa.SA_BF16, B=2, Hq=8, Hkv=2, d=128, T_cap=4096,
+             lens=FAKE, idx=FAKE, cnt=FAKE, idx_cap=19, scale=1.0, O=FAKE, out_dtype=sa.SA_F32,
+             lse=None, n_split=4, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return sa.lib().sparse_attn_decode(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["Hq"], a["Hkv"],
+                                       a["d"], a["T_cap"], a["lens"], a["idx"], a["cnt"],
+                                       a["idx_cap"], a["scale"], a["O"], a["out_dtype"], a["lse"],
+                                       a["n_split"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_decode_validation():
+    assert _decode(O=None) == sa.SA_ERR_INVALID_ARG
+    assert _decode(idx_cap=0) == sa.SA_ERR_INVALID_ARG
+    assert _decode(Hq=7) == sa.SA_ERR_INVALID_ARG
+    assert _decode(out_dtype=3) == sa.SA_ERR_INVALID_ARG
+    assert _decode(scale=float("nan")) == sa.SA_ERR_INVALID_ARG
+    assert _decode(Hq=16) == sa.SA_ERR_UNSUPPORTED              # G = 8
+    assert _decode(d=64) == sa.SA_ERR_UNSUPPORTED
+    assert _decode(ws=None) == sa.SA_ERR_WORKSPACE
+    assert _decode(ws_bytes=sa.decode_workspace_size(2, 8, 2, 19, 4) - 1) == sa.SA_ERR_WORKSPACE
+    assert sa.decode_workspace_size(2, 8, 2, 19, 1) == 0        # one split writes O directly
+
+
+def _prefill(**kw):
+    p = kw.pop("params", sa.make_params(32, 1, 4))
+    a = dict(Q=FAKE, q_start=1024, Tq=256, K=FAKE, V=FAKE, Kc=FAKE, dtype=sa.SA_BF16, Hq=32, Hkv=8,
+             d=128, T_cap=1280, nc_cap=79, O=FAKE, out_dtype=sa.SA_F32, lse=None, tidx=FAKE,
+             tcap=20, tcnt=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return sa.lib().sparse_attn_prefill_chunk(a["Q"], a["q_start"], a["Tq"], a["K"], a["V"], a["Kc"],
+                                              a["dtype"], a["Hq"], a["Hkv"], a["d"], a["T_cap"],
+                                              a["nc_cap"], ctypes.byref(p), 1.0, a["O"],
+                                              a["out_dtype"], a["lse"], a["tidx"], a["tcap"],
+                                              a["tcnt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_validation():
+    assert sa.prefill_tile_cap(1024, 256, sa.make_params(32, 1, 4)) == 20       # nb(1280) = 20
+    assert sa.prefill_tile_cap(129024, 2048, sa.make_params(32, 1, 4)) == 2048
+    assert _prefill(q_start=1000) == sa.SA_ERR_INVALID_ARG                       # not block aligned
+    assert _prefill(Tq=0) == sa.SA_ERR_INVALID_ARG
+    assert _prefill(tidx=None) == sa.SA_ERR_INVALID_ARG
+    assert _prefill(dtype=sa.SA_F32) == sa.SA_ERR_UNSUPPORTED
+    assert _prefill(Hq=16) == sa.SA_ERR_UNSUPPORTED
+    assert _prefill(T_cap=1279) == sa.SA_ERR_CAPACITY
+    assert _prefill(nc_cap=78) == sa.SA_ERR_CAPACITY                             # n_c(1280) = 79
+    assert _prefill(tcap=19) == sa.SA_ERR_CAPACITY
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    K = torch.zeros(1, 1, 64, 128)
+    with pytest.raises(ValueError):
+        sa.compress(K, torch.zeros(1, 1, 3, 128), torch.zeros(1, dtype=torch.int32),
+                    torch.zeros(1, dtype=torch.int32))
