@@ -229,7 +229,7 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Te
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = decode_workspace_size(B, Hq, Hkv, idx.shape[-1], n_split)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)   # merge counters start at 0
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().sparse_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(K), B, Hq, Hkv,
                                   d, T_cap, _dev(seq_lens, "seq_lens"), _dev(idx, "idx"),

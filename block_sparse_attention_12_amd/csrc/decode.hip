@@ -10,19 +10,26 @@
 //
 // Mapping of a 256-thread workgroup: wave w owns rows 16w .. 16w+15 of every
 // block; inside a wave, row group r = lane / 16 takes rows 16w + 4i + r
-// (i = 0..3) and each lane owns 8 channels. One block costs each lane 4 K and
-// 4 V loads of 16 B, all issued before any arithmetic. Logits for 4 rows x 4
-// heads are reduced across the 16 lanes of a row by the DPP transposed
-// reduction, leaving one logit per lane; the online softmax keeps a running
-// max per head (wave-uniform) and per-lane partial sums, so no workgroup
-// barrier is needed inside the block loop. Probabilities reach the lanes that
-// hold the matching V rows through a wave-private LDS slot. The four waves'
-// states are merged once at the end through LDS.
+// (i = 0..3) and each lane owns 8 channels. A block costs each lane 4 K and
+// 4 V loads of 16 B. Loads of the next block are issued before the current
+// block is computed (two register buffers), and the share's block ids are
+// fetched once into lanes and broadcast with readlane, so the only waits in
+// the loop are for data already in flight.
 //
-// With n_split > 1 each workgroup writes (max, sum, weighted values) to the
-// workspace and combine_kernel merges them with log-sum-exp weights; with
-// n_split = 1 the workgroup writes O directly. Logits are kept in base-2 units
-// (q is pre-multiplied by scale * log2 e) so every exponential is one exp2.
+// Logits for 4 rows x 4 heads are reduced across the 16 lanes of a row by the
+// DPP transposed reduction, leaving one logit per lane (bf16 inputs use the
+// packed bf16 dot product for q.k). The online softmax keeps a running max per
+// head (wave-uniform) and per-lane partial sums, so no workgroup barrier is
+// needed inside the block loop; probabilities reach the lanes holding the
+// matching V rows through a wave-private LDS slot. Logits are in base-2 units
+// (scaled by scale * log2 e) so each exponential is one exp2.
+//
+// Split merge: every workgroup writes (max, sum, weighted values) for its 4
+// heads and combine_kernel, launched next on the same stream, merges the
+// n_split partials with log-sum-exp weights. (Merging inside the last
+// workgroup of a unit would need a device-scope release fence per workgroup,
+// which on this multi-die part writes back L2 and serialises the grid.) With
+// n_split = 1 the workgroup writes O directly.
 #include <math.h>
 
 #include "sa_device.h"
@@ -33,45 +40,80 @@ namespace sa {
 constexpr int kDecThreads = 256;
 constexpr int kDecG = 4;
 constexpr int kPartStride = kD + 4;          // acc[128], max, sum, 2 pad (16 B aligned rows)
+constexpr int kMaxSplit = 64;                // splits per (b, kvh) (4 heads x 64 = one per thread)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// a split holds at most 64 blocks (one block id per lane)
+int decode_min_split(int32_t idx_cap) { return (idx_cap + 63) / 64; }
+
 int decode_auto_split(int B, int Hkv, int32_t idx_cap) {
     const int units = B * Hkv;
-    const int target = 2048;                              // workgroups in flight over 256 CUs
+    const int target = 512;                               // ~2 workgroups per CU
     int s = (target + units - 1) / units;
-    int max_s = idx_cap / 2 > 1 ? idx_cap / 2 : 1;       // at least ~2 blocks per split
+    int max_s = idx_cap / 4 > 1 ? idx_cap / 4 : 1;       // at least ~4 blocks per split
     if (s > max_s) s = max_s;
     if (s > 64) s = 64;
     if (s < 1) s = 1;
-    return s;
+    return decode_min_split(idx_cap) > s ? decode_min_split(idx_cap) : s;
 }
 
+// workspace: the split partials [B * Hq][n_split][kPartStride] fp32
 size_t decode_workspace_bytes(int B, int Hq, int32_t n_split) {
     if (n_split <= 1) return 0;
     return (size_t)B * Hq * n_split * kPartStride * sizeof(float);
 }
 
-template <int G>
-__device__ __forceinline__ float pick(const float (&a)[G], int i) {
-    float r = a[0];
+// q for this lane's 8 channels of the group's heads: packed bf16 pairs (bf16
+// inputs, used with dot2) or fp32 values (fp32 inputs).
+template <typename T> struct QFrag;
+template <> struct QFrag<bf16_t> { uint32_t w[kDecG][4]; };
+template <> struct QFrag<float> { float w[kDecG][8]; };
+
+__device__ __forceinline__ void load_q(const bf16_t *p, QFrag<bf16_t> &q) {
 #pragma unroll
-    for (int g = 1; g < G; ++g) r = (i == g) ? a[g] : r;
-    return r;
+    for (int g = 0; g < kDecG; ++g) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(p + (int64_t)g * kD);
+        q.w[g][0] = v.x; q.w[g][1] = v.y; q.w[g][2] = v.z; q.w[g][3] = v.w;
+    }
+}
+__device__ __forceinline__ void load_q(const float *p, QFrag<float> &q) {
+#pragma unroll
+    for (int g = 0; g < kDecG; ++g) load8(p + (int64_t)g * kD, q.w[g]);
+}
+__device__ __forceinline__ float qk(const QFrag<bf16_t> &q, int g, const Raw8<bf16_t> &k) {
+    float a = dot2_bf16(q.w[g][0], k.v.x, 0.f);
+    a = dot2_bf16(q.w[g][1], k.v.y, a);
+    a = dot2_bf16(q.w[g][2], k.v.z, a);
+    return dot2_bf16(q.w[g][3], k.v.w, a);
+}
+__device__ __forceinline__ float qk(const QFrag<float> &q, int g, const Raw8<float> &k) {
+    float x[8];
+    unpack(k, x);
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a = fmaf(q.w[g][c], x[c], a);
+    return a;
 }
 
-__device__ __forceinline__ void store_out(float *O, int64_t i, float x) { O[i] = x; }
+template <typename T>
+struct BlockRegs {
+    Raw8<T> k[4], v[4];
+    int64_t t0;
+};
 
 template <typename T, bool DIRECT>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int idx_cap, float qscale, int n_split,
-    float *__restrict__ part, void *__restrict__ O, int out_bf16, float *__restrict__ lse) {
+    float *__restrict__ part, void *__restrict__ O, int out_bf16,
+    float *__restrict__ lse) {
     constexpr int G = kDecG;
     __shared__ __align__(16) float s_p[4][64];
     __shared__ float s_m[4][G], s_l[4][G];
     __shared__ __align__(16) float s_acc[4][G][kD];
+
 
     const int split = blockIdx.x, unit = blockIdx.y;
     const int b = unit / Hkv, kvh = unit % Hkv;
@@ -82,83 +124,73 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     int n = cnt[unit];
     n = n < 0 ? 0 : (n > idx_cap ? idx_cap : n);
     const int per = (n + n_split - 1) / n_split;
-    const int e_lo = split * per;
-    const int e_hi = e_lo + per < n ? e_lo + per : n;
+    const int e_lo = split * per < n ? split * per : n;
+    const int nblk = (e_lo + per < n ? e_lo + per : n) - e_lo;
 
-    float q[G][8];
-    {
-        const T *qp = Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + lane16 * kLaneElems;
+    QFrag<T> q;
+    load_q(Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + lane16 * kLaneElems, q);
+    float acc[G][8];
+    float m_my = -INFINITY, l_lane = 0.f;     // this lane's head: running max, partial sum
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            load8(qp + (int64_t)g * kD, q[g]);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) q[g][c] *= qscale;
-        }
-    }
-    float m_run[G], acc[G][8];
-    float l_lane = 0.f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_run[g] = -INFINITY;
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
-    }
-    const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-    const T *Vu = V + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-    const int32_t *irow = idx + (int64_t)unit * idx_cap;
-    const int my_head = lane16 & 3;
+    // per-unit K/V windows of L rows: rows at or past L read as zeros
+    constexpr uint32_t kRowBytes = kD * sizeof(T);
+    const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
+    const int32_t *irow = idx + (int64_t)unit * idx_cap + e_lo;
     const int my_row = 16 * wave + 4 * (lane16 >> 2) + rgrp;   // row of the logit this lane holds
+    const int row0 = 16 * wave + rgrp;                          // first row this lane loads
+    const uint32_t row_lane_off = row0 * kRowBytes + lane_off;
+    const int64_t nb = n_blocks(L);
 
-#pragma unroll 1
-    for (int e = e_lo; e < e_hi; ++e) {
-        const int64_t t0 = (int64_t)irow[e] * kBlock;
-        Raw8<T> kr[4], vr[4];
-        bool ok[4];
+    // block id of iteration it (a uniform scalar load), or -1 (no rows) past
+    // the share or out of range
+    auto block_id = [&](int it) -> int {
+        const int blk = it < nblk ? irow[it] : -1;
+        return (blk >= 0 && blk < nb) ? blk : -1;
+    };
+    // Issues the block's K/V loads unconditionally: id -1 maps every row to an
+    // out-of-range offset, which reads zeros and moves no bytes, so the wait
+    // counts stay exact (one block in flight behind the current one).
+    auto issue = [&](BlockRegs<T> &r, int blk) {
+        r.t0 = (int64_t)blk * kBlock;
+        const uint32_t base = blk < 0 ? 0xffffffffu : (uint32_t)blk * (kBlock * kRowBytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t t = t0 + 16 * wave + 4 * i + rgrp;
-            ok[i] = t >= 0 && t < L;
-            if (ok[i]) {
-                load_raw(Ku + t * kD, kr[i]);
-                load_raw(Vu + t * kD, vr[i]);
-            }
+            const uint32_t off = blk < 0 ? 0xffffffffu : base + row_lane_off + i * (4 * kRowBytes);
+            load_raw(rK, off, r.k[i]);
+            load_raw(rV, off, r.v[i]);
         }
+    };
+    auto process = [&](const BlockRegs<T> &r) {
         float v[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float k8[8];
-            if (ok[i]) unpack(kr[i], k8);
-            else {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) k8[c] = 0.f;
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float a = 0.f;
-#pragma unroll
-                for (int c = 0; c < 8; ++c) a = fmaf(q[g][c], k8[c], a);
-                v[i * G + g] = a;
-            }
-        }
+            for (int g = 0; g < G; ++g) v[i * G + g] = qk(q, g, r.k[i]);
         transpose_reduce16<16>(v, lane);
-        const int64_t my_t = t0 + my_row;
-        const float x = (my_t >= 0 && my_t < L) ? v[0] : -INFINITY;
+        const int64_t my_t = r.t0 + my_row;
+        const float x = (my_t >= 0 && my_t < L) ? v[0] * qscale : -INFINITY;
         // block max per head over the wave (lanes sharing lane & 3)
         float mx = fmaxf(x, dpp<kDppRowRor4>(x));
         mx = fmaxf(mx, dpp<kDppRowRor8>(mx));
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
+        // running max of this lane's head (lanes of one head agree), its
+        // rescale factor, and the four heads' factors broadcast from lanes 0..3
+        const float m_new = fmaxf(m_my, mx);
+        const float alpha_me = (m_my == -INFINITY) ? 0.f : exp2f(m_my - m_new);
+        m_my = m_new;
+        const float p = (x == -INFINITY) ? 0.f : exp2f(x - m_new);
+        l_lane = l_lane * alpha_me + p;
         float alpha[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float mb = __shfl(mx, g, 64);
-            const float mn = fmaxf(m_run[g], mb);
-            alpha[g] = (m_run[g] == -INFINITY) ? 0.f : exp2f(m_run[g] - mn);
-            m_run[g] = mn;
-        }
-        const float my_m = pick<G>(m_run, my_head);
-        const float p = (x == -INFINITY) ? 0.f : exp2f(x - my_m);
-        l_lane = l_lane * pick<G>(alpha, my_head) + p;
+        for (int g = 0; g < G; ++g)
+            alpha[g] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, alpha_me), g));
         s_p[wave][lane] = p;
         __builtin_amdgcn_wave_barrier();
         float pr[16];
@@ -177,9 +209,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             for (int c = 0; c < 8; ++c) acc[g][c] *= alpha[g];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (!ok[i]) continue;
             float v8[8];
-            unpack(vr[i], v8);
+            unpack(r.v[i], v8);                    // rows past L are zeros and have p = 0
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const float pg = pr[i * G + g];
@@ -187,6 +218,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(pg, v8[c], acc[g][c]);
             }
         }
+    };
+
+    // sched_barrier keeps the compiler from sinking a prefetch below the
+    // compute it is meant to overlap
+    BlockRegs<T> bufA, bufB;
+    issue(bufA, block_id(0));
+#pragma unroll 1
+    for (int it = 0; it < nblk; it += 2) {
+        issue(bufB, block_id(it + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        process(bufA);
+        issue(bufA, block_id(it + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + 1 < nblk) process(bufB);
     }
 
     // ---- merge inside the wave: l over lanes of one head, acc over row groups
@@ -213,7 +258,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     }
     if (lane < G) {
-        s_m[wave][lane] = pick<G>(m_run, lane);
+        s_m[wave][lane] = m_my;                 // lane g < 4 holds head g's max
         s_l[wave][lane] = l;                    // lane g < 4 holds head g's sum
     }
     __syncthreads();
@@ -234,44 +279,91 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         a1 = fmaf(wt, s_acc[w][g][c2 + 1], a1);
     }
     const int64_t row = (int64_t)b * Hq + (int64_t)kvh * G + g;   // query head row
-    if constexpr (DIRECT) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        if (out_bf16) {
-            uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
-            reinterpret_cast<uint32_t *>(O)[(row * kD + c2) / 2] = w;
-        } else {
-            reinterpret_cast<float2 *>(O)[(row * kD + c2) / 2] = make_float2(a0 * inv, a1 * inv);
-        }
-        if (lse && (tid & 63) == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
-    } else {
+    if constexpr (!DIRECT) {
         float *dst = part + (row * n_split + split) * kPartStride;
         reinterpret_cast<float2 *>(dst)[c2 / 2] = make_float2(a0, a1);
         if ((tid & 63) == 0) {
             dst[kD] = M;
             dst[kD + 1] = lsum;
         }
+        return;
     }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (out_bf16) {
+        const uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
+        reinterpret_cast<uint32_t *>(O)[(row * kD + c2) / 2] = w;
+    } else {
+        reinterpret_cast<float2 *>(O)[(row * kD + c2) / 2] = make_float2(a0 * inv, a1 * inv);
+    }
+    if (lse && (tid & 63) == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-__global__ __launch_bounds__(kD) void combine_kernel(const float *__restrict__ part, int n_split,
-                                                     void *__restrict__ O, int out_bf16,
-                                                     float *__restrict__ lse) {
-    const int64_t row = blockIdx.x;
-    const int c = threadIdx.x;
-    const float *p = part + row * n_split * kPartStride;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[s * kPartStride + kD]);
-    float lsum = 0.f, a = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-        const float ms = p[s * kPartStride + kD];
-        const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        lsum = fmaf(wt, p[s * kPartStride + kD + 1], lsum);
-        a = fmaf(wt, p[s * kPartStride + c], a);
+// Merges the n_split partials of one (b, kvh) unit's 4 heads: every (head,
+// split) max and sum is loaded by its own thread, the per-head weights are
+// formed in LDS, then each thread gathers its two channels from all splits
+// with 8 loads in flight at a time.
+__global__ __launch_bounds__(kDecThreads) void combine_kernel(
+    const float *__restrict__ part, int n_split, int Hq, int Hkv, void *__restrict__ O,
+    int out_bf16, float *__restrict__ lse) {
+    constexpr int G = kDecG;
+    __shared__ float s_w[G * kMaxSplit], s_l[G * kMaxSplit];
+    __shared__ float s_M[G], s_L[G];
+    const int unit = blockIdx.x;
+    const int b = unit / Hkv, kvh = unit % Hkv;
+    const int tid = threadIdx.x;
+    const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;
+    const float *up = part + row0 * n_split * kPartStride;
+    if (tid < G * n_split) {
+        const float *ps = up + tid * kPartStride;        // (head tid / n_split, split tid % n_split)
+        s_w[tid] = ps[kD];
+        s_l[tid] = ps[kD + 1];
     }
-    const float o = lsum > 0.f ? a / lsum : 0.f;
-    if (out_bf16) reinterpret_cast<bf16_t *>(O)[row * kD + c] = (bf16_t)f32_to_bf16_bits(o);
-    else reinterpret_cast<float *>(O)[row * kD + c] = o;
-    if (lse && c == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+    __syncthreads();
+    if (tid < G) {
+        float Mg = -INFINITY;
+        for (int s = 0; s < n_split; ++s) Mg = fmaxf(Mg, s_w[tid * n_split + s]);
+        float Lg = 0.f;
+        for (int s = 0; s < n_split; ++s) {
+            const float ms = s_w[tid * n_split + s];
+            const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - Mg);
+            s_w[tid * n_split + s] = wt;
+            Lg = fmaf(wt, s_l[tid * n_split + s], Lg);
+        }
+        s_M[tid] = Mg;
+        s_L[tid] = Lg;
+    }
+    __syncthreads();
+    const int g = tid >> 6;
+    const int c2 = (tid & 63) * 2;
+    const float *pg = up + (int64_t)g * n_split * kPartStride + c2;
+    const float *wg = &s_w[g * n_split];
+    float a0 = 0.f, a1 = 0.f;
+    int s0 = 0;
+    for (; s0 + 8 <= n_split; s0 += 8) {
+        float2 a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = *reinterpret_cast<const float2 *>(pg + (s0 + k) * kPartStride);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            a0 = fmaf(wg[s0 + k], a[k].x, a0);
+            a1 = fmaf(wg[s0 + k], a[k].y, a1);
+        }
+    }
+    for (; s0 < n_split; ++s0) {
+        const float2 a = *reinterpret_cast<const float2 *>(pg + s0 * kPartStride);
+        a0 = fmaf(wg[s0], a.x, a0);
+        a1 = fmaf(wg[s0], a.y, a1);
+    }
+    const float lsum = s_L[g], M = s_M[g];
+    const int64_t row = row0 + g;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if (out_bf16) {
+        const uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
+        reinterpret_cast<uint32_t *>(O)[(row * kD + c2) / 2] = w;
+    } else {
+        reinterpret_cast<float2 *>(O)[(row * kD + c2) / 2] = make_float2(a0 * inv, a1 * inv);
+    }
+    if (lse && (tid & 63) == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
 template <typename T>
@@ -289,10 +381,9 @@ static void launch_decode_t(const void *Q, const void *K, const void *V, int B, 
     } else {
         hipLaunchKernelGGL((decode_kernel<T, false>), grid, dim3(kDecThreads), 0, stream,
                            (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens, idx,
-                           cnt, idx_cap, qscale, n_split, (float *)ws, (void *)nullptr, 0,
-                           (float *)nullptr);
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(B * Hq)), dim3(kD), 0, stream,
-                           (const float *)ws, n_split, O, out_bf16, lse);
+                           cnt, idx_cap, qscale, n_split, (float *)ws, O, out_bf16, lse);
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(B * Hkv)), dim3(kDecThreads), 0, stream,
+                           (const float *)ws, n_split, Hq, Hkv, O, out_bf16, lse);
     }
 }
 

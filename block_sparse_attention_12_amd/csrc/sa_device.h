@@ -147,6 +147,38 @@ __device__ __forceinline__ void transpose_reduce16(float (&v)[N], int lane) {
     transpose_reduce_step<0, N, N>(v, lane & 15);
 }
 
+// ---- buffer loads: 32-bit offsets from an SGPR resource; reads at or past
+// num_bytes return zeros (hardware range check), so tails need no branches.
+typedef int sa_v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)num_bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<bf16_t> &x) {
+    const sa_v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    x.v = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<float> &x) {
+    const sa_v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const sa_v4i b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, 0);
+    x.a = make_float4(__int_as_float(a.x), __int_as_float(a.y), __int_as_float(a.z), __int_as_float(a.w));
+    x.b = make_float4(__int_as_float(b.x), __int_as_float(b.y), __int_as_float(b.z), __int_as_float(b.w));
+}
+// byte offset of a row, or an out-of-range offset (reads zeros) if it does not fit
+__device__ __forceinline__ uint32_t row_offset(int64_t row, uint32_t row_bytes, uint32_t lane_off) {
+    const int64_t o = row * (int64_t)row_bytes + lane_off;
+    return (o < 0 || o > 0x7fffffffLL) ? 0xffffffffu : (uint32_t)o;
+}
+
+// bf16 pair dot product accumulated in fp32: a.lo*b.lo + a.hi*b.hi + c
+// (v_dot2c_f32_bf16; bf16 products are exact in fp32).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // Full-wave helpers (64 lanes)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -33,6 +33,7 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   float *block_scores_out, void *workspace, hipStream_t stream);
 
 int decode_auto_split(int B, int Hkv, int32_t idx_cap);
+int decode_min_split(int32_t idx_cap);
 size_t decode_workspace_bytes(int B, int Hq, int32_t n_split);
 int launch_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq, int Hkv,
                   int64_t T_cap, const int32_t *seq_lens, const int32_t *idx, const int32_t *cnt,

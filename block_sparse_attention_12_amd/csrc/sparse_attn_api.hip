@@ -92,7 +92,8 @@ int sparse_attn_select(const void *sel, int H_sel, const void *Kc, int dtype, in
 
 size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap, int32_t n_split) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || idx_cap <= 0) return 0;
-    const int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    if (s < decode_min_split(idx_cap)) s = decode_min_split(idx_cap);
     return decode_workspace_bytes(B, Hq, s);
 }
 
@@ -108,8 +109,10 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
     if (Hq % Hkv) return SA_ERR_INVALID_ARG;
     if (!(scale == scale)) return SA_ERR_INVALID_ARG;
     if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
-    if (n_split > 1024) return SA_ERR_UNSUPPORTED;
-    const int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    if (n_split > 64 || idx_cap > 64 * 64) return SA_ERR_UNSUPPORTED;
+    if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    if (s < decode_min_split(idx_cap)) s = decode_min_split(idx_cap);
     const size_t need = decode_workspace_bytes(B, Hq, s);
     if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
     return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale, O,

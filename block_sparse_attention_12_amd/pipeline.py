@@ -36,7 +36,7 @@ class SparseDecoder:
         sws = select_workspace_size(B, Hkv, self.H_sel, T_cap, p)
         self.sel_ws = torch.empty(max(sws, 1), dtype=torch.uint8, device=dev)
         dws = decode_workspace_size(B, Hq, Hkv, self.cap, n_split)
-        self.dec_ws = torch.empty(max(dws, 1), dtype=torch.uint8, device=dev)
+        self.dec_ws = torch.zeros(max(dws, 1), dtype=torch.uint8, device=dev)  # counters start at 0
         self.O = torch.empty((B, Hq, 128), dtype=out_dtype, device=dev)
         self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
 

@@ -171,9 +171,15 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap
  *   O          [B, Hq, d] device, out_dtype SA_F32 or SA_BF16
  *   lse_out    optional [B, Hq] device fp32: natural log of the softmax
  *              denominator incl. scale (-inf when no token is selected)
- *   n_split    workgroups per (b, kvh); <= 0 lets the library choose
- * A (b, kvh) with cnt = 0 yields O = 0.
- * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4),
+ *   n_split    workgroups per (b, kvh), at most 64; <= 0 lets the library
+ *              choose. A split holds at most 64 blocks, so the count is
+ *              raised to at least ceil(idx_cap / 64) (idx_cap <= 4096).
+ *   workspace  required when the split count is above 1: the split
+ *              partials (fp32), merged by a second kernel on the same stream.
+ * A (b, kvh) with cnt = 0 yields O = 0 and LSE = -inf.
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4,
+ *         n_split > 64, idx_cap > 4096, one (b, kvh) cache slice of
+ *         T_cap * d elements taking 2 GiB or more),
  *         SA_ERR_WORKSPACE.
  */
 int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,

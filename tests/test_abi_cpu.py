@@ -119,6 +119,8 @@ def test_decode_validation():
     assert _decode(out_dtype=3) == sa.SA_ERR_INVALID_ARG
     assert _decode(scale=float("nan")) == sa.SA_ERR_INVALID_ARG
     assert _decode(Hq=16) == sa.SA_ERR_UNSUPPORTED              # G = 8
+    assert _decode(n_split=65) == sa.SA_ERR_UNSUPPORTED
+    assert _decode(idx_cap=4097) == sa.SA_ERR_UNSUPPORTED
     assert _decode(d=64) == sa.SA_ERR_UNSUPPORTED
     assert _decode(ws=None) == sa.SA_ERR_WORKSPACE
     assert _decode(ws_bytes=sa.decode_workspace_size(2, 8, 2, 19, 4) - 1) == sa.SA_ERR_WORKSPACE
