@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--n-split", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (slower on this stack: a graph "
+                         "launch costs more than the launch gaps it removes)")
     return ap.parse_args()
 
 
@@ -91,37 +94,52 @@ def bench_decode(args, w):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
-        rep = reps[i % len(reps)]
-        if ev is not None:
-            ev[0].record(stream)
-        dec.append(rep["K"], rep["Kc"], lens_prev, lens_now)
-        if ev is not None:
-            ev[1].record(stream)
-        dec.select(rep[sel_name], rep["Kc"], lens_now)
-        if ev is not None:
-            ev[2].record(stream)
-        dec.attend(rep["Q"], rep["K"], rep["V"], lens_now)
-        if ev is not None:
-            ev[3].record(stream)
+    def phases_of(rep):
+        return {
+            "append": lambda: dec.append(rep["K"], rep["Kc"], lens_prev, lens_now),
+            "select": lambda: dec.select(rep[sel_name], rep["Kc"], lens_now),
+            "attend": lambda: dec.attend(rep["Q"], rep["K"], rep["V"], lens_now),
+        }
 
+    def whole_step(rep):
+        for f in phases_of(rep).values():
+            f()
+
+    if not args.graph:
+        steps_fn = [lambda rep=rep: whole_step(rep) for rep in reps]
+    else:
+        graphs = [dec.capture(lambda rep=rep: whole_step(rep)) for rep in reps]
+        steps_fn = [g.replay for g in graphs]
     for i in range(args.warmup):
-        step(i)
+        steps_fn[i % len(reps)]()
     torch.cuda.synchronize()
-    evs = [_events(4) for _ in range(args.steps)]
+    ev0, ev1 = _events(2)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        steps_fn[i % len(reps)]()
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    phases = {"append": [], "select": [], "attend": []}
-    for ev in evs:
-        phases["append"].append(ev[0].elapsed_time(ev[1]))
-        phases["select"].append(ev[1].elapsed_time(ev[2]))
-        phases["attend"].append(ev[2].elapsed_time(ev[3]))
-    gpu_ms = evs[0][0].elapsed_time(evs[-1][3]) / args.steps
-    mean = {k: sum(v) / len(v) for k, v in phases.items()}
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-phase GPU time: each phase captured on its own, replays bracketed by events
+    mean = {}
+    n_ph = max(10, min(args.steps, 100))
+    for name in ("append", "select", "attend"):
+        fns = [phases_of(rep)[name] for rep in reps]
+        if args.graph:
+            fns = [dec.capture(f).replay for f in fns]
+        for i in range(3):
+            fns[i % len(fns)]()
+        evs = [_events(2) for _ in range(n_ph)]
+        for i in range(n_ph):
+            evs[i][0].record(stream)
+            fns[i % len(fns)]()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        mean[name] = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ph
 
     # algorithmic bytes, from the actual selections and lengths
     cnt = dec.cnt.cpu()
@@ -164,12 +182,14 @@ def bench_decode(args, w):
                    "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k, "n_init": w.n_init,
                    "n_local": w.n_local, "selector": w.selector, "score_mode": w.score_mode,
                    "replicas": args.replicas, "n_split": args.n_split or "auto",
+                   "launch": "hip graph per step" if args.graph else "eager, one stream",
                    "parallelism": "none (1 GPU)"},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "phase_ms": {k: round(v, 5) for k, v in mean.items()},
         "step_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "decode attention (sparse_attn_decode)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "sparse_attn_decode (decode_kernel + combine_kernel)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": attn_bytes},

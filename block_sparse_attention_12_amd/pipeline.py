@@ -67,6 +67,23 @@ class SparseDecoder:
         self.select(sel, Kc, lens_now)
         return self.attend(Q, K, V, lens_now, scale=scale)
 
+    def capture(self, fn, warmup: int = 2):
+        """Capture fn() (a sequence of the calls above on fixed buffers) into a
+        HIP graph; returns the torch.cuda.CUDAGraph to replay. Every call only
+        enqueues kernels on the current stream (no allocation, no memset), so
+        the captured graph is the same kernel sequence with its launch gaps
+        removed."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
     def crosslayer_step(self, layers: Sequence[dict], Kc, lens_prev, lens_now, outs=None,
                         scale=1.0):
         """One decode step where layer 0 (the anchor) selects for every layer.
