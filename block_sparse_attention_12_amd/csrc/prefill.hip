@@ -1,8 +1,463 @@
-// Chunked sparse prefill (placeholder until the matrix-core kernels land).
+// Chunked sparse prefill on matrix cores.
+//
+// Page "SparDA: Sparse Decoupled Attention for Efficient Long-Context LLM
+// Inference" (picx.dev summary): per query, Eq. 6's group-summed softmax
+// scores over the compressed keys (or raw Eq. 4 scores), block scores, top-k
+// and the Eq. 1 union; Eq. 5 attention over the chosen blocks. Sharing one
+// block set per 64-query tile follows the Kascade abstract on the page
+// "CoSA ..." ("tile-level operations" for prefill).
+//
+// One sequence, queries q_start .. q_start+Tq-1 (q_start a multiple of 64).
+// Tile t = queries q_start+64t .. +63, all inside block bt = q_start/64 + t.
+// A workgroup owns one (tile, KV head): 64 queries x 4 heads = 256 rows of
+// the attention; wave w takes queries 16w .. 16w+15, i.e. 64 rows, as four
+// 16-row tiles (row = 4 * query + head).
+//
+// Both dense contractions use v_mfma_f32_16x16x32_bf16 in the transposed form
+// S^T = K Q^T (keys as M, rows as N), so each lane ends up with 16 scores of a
+// single row (4 key tiles x 4 consecutive keys) and no data movement is
+// needed between the score and the value products:
+//   O^T = V^T P^T, with P converted in registers to the B operand. The key
+//   order inside each K = 32 step is permuted identically on both operands.
+// K (or compressed-key) chunks are staged in LDS with an XOR swizzle of their
+// 16-byte chunks (conflict-free 16-row reads); V is staged transposed with a
+// padded row so the A operand of V^T reads are conflict-free.
+//
+// Kernels:
+//   prefill_score_kernel  per (tile, KV head), two sweeps over the compressed
+//                         keys: per-row softmax max / sum over the entries the
+//                         row's query can see, then the group-summed
+//                         probabilities, max-reduced over each block's three
+//                         inside entries, written as one score per (query,
+//                         KV head, block).
+//   topk (select.hip)     per (query, KV head): top-k among the blocks that
+//                         are neither initial nor in the local window, plus
+//                         init and local.
+//   prefill_union_kernel  per (tile, KV head): union of its 64 queries' sets.
+//   prefill_attn_kernel   per (tile, KV head): causal flash attention over the
+//                         union, online softmax in fp32, P rounded to bf16 for
+//                         the value product, fp32 accumulation.
+// Workgroups are numbered tile * Hkv + kvh so the tiles of one KV head land on
+// the same XCD (round-robin dispatch over 8 XCDs) and share its L2.
+#include <math.h>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kPfThreads = 256;
+constexpr int kPfG = 4;
+constexpr int kVtStride = 68;          // bf16 per transposed V row (64 keys + pad)
+constexpr float kLog2eF = 1.44269504088896340736f;
+constexpr float kLn2F = 0.69314718055994530942f;
+
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ---- LDS staging of a 64-row x 128-channel bf16 tile (K or compressed K):
+// row r's 16-byte chunk c is stored at chunk position c ^ (r % 16).
+__device__ __forceinline__ void stage_rows_swizzled(bf16_t *lds, __amdgpu_buffer_rsrc_t src,
+                                                    int64_t row0, int tid) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int id = r * kPfThreads + tid;           // 1024 chunks of 16 B
+        const int row = id >> 4, chunk = id & 15;
+        const uint32_t off = row_offset(row0 + row, kD * 2, chunk * 16);
+        Raw8<bf16_t> x;
+        load_raw(src, off, x);
+        *reinterpret_cast<uint4 *>(lds + row * kD + ((chunk ^ (row & 15)) * 8)) = x.v;
+    }
+}
+
+// A operand (rows as M) from a swizzled LDS tile: row m_row, channels 32 ks + 8 g .. +8
+__device__ __forceinline__ bf16x8_t lds_frag_rows(const bf16_t *lds, int m_row, int ks, int g) {
+    const int chunk = (4 * ks + g) ^ (m_row & 15);
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + m_row * kD + chunk * 8));
+}
+
+// ---- V staged transposed: Vt[channel][key], row stride kVtStride bf16
+__device__ __forceinline__ void stage_v_transposed(bf16_t *vt, __amdgpu_buffer_rsrc_t src,
+                                                   int64_t row0, int tid) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int id = r * kPfThreads + tid;
+        const int key = id >> 4, chunk = id & 15;
+        const uint32_t off = row_offset(row0 + key, kD * 2, chunk * 16);
+        Raw8<bf16_t> x;
+        load_raw(src, off, x);
+        const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            vt[(chunk * 8 + 2 * j) * kVtStride + key] = (bf16_t)(w[j] & 0xffffu);
+            vt[(chunk * 8 + 2 * j + 1) * kVtStride + key] = (bf16_t)(w[j] >> 16);
+        }
+    }
+}
+
+// A operand of V^T for the value product: channel row ch, permuted keys of
+// step kk: 32kk + 4g .. +3 and 32kk + 16 + 4g .. +3
+__device__ __forceinline__ bf16x8_t vt_frag(const bf16_t *vt, int ch, int kk, int g) {
+    const uint2 lo = *reinterpret_cast<const uint2 *>(vt + ch * kVtStride + 32 * kk + 4 * g);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(vt + ch * kVtStride + 32 * kk + 16 + 4 * g);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Q rows of this wave as B operands: qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
+// (zeros for rows past the chunk). Row = 4 * query + head inside the wave.
+__device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[4][4], const bf16_t *Q, int Hq, int kvh,
+                                             int64_t q_first, int64_t Tq, int wave, int lane) {
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);     // query index in the chunk
+        const int h = c16 & 3;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qi < Tq)
+                v = *reinterpret_cast<const uint4 *>(Q + (qi * Hq + (int64_t)kvh * kPfG + h) * kD +
+                                                     32 * ks + 8 * g);
+            qf[rt][ks] = as_bf16x8(v);
+        }
+    }
+}
+
+// S^T tile of 64 keys (from a swizzled LDS tile) x this wave's 64 rows:
+// s[mt][rt][i] = score of row 16 rt + (l%16) with key 16 mt + 4 g + i
+__device__ __forceinline__ void scores_64x64(f32x4_t (&s)[4][4], const bf16_t *ldsK,
+                                             const bf16x8_t (&qf)[4][4], int lane) {
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) s[mt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const bf16x8_t a = lds_frag_rows(ldsK, 16 * mt + c16, ks, g);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) s[mt][rt] = mfma16(a, qf[rt][ks], s[mt][rt]);
+        }
+}
+
+// ------------------------------------------------------------------ scoring
+
+// Visible compressed entries for a query at position p: n_c(p + 1).
+__global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
+    const bf16_t *__restrict__ Q, const bf16_t *__restrict__ Kc, int Hq, int Hkv, int64_t q_start,
+    int64_t Tq, int64_t nc_cap, int raw_mode, float *__restrict__ bscore, int64_t nb_cap,
+    int32_t *__restrict__ qlens) {
+    __shared__ __align__(16) bf16_t sK[64 * kD];
+    const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t q_first = (int64_t)tile * 64;                  // query index of the tile start
+    const int64_t bt = q_start / kBlock + tile;
+    if (kvh == 0 && tid < 64 && q_first + tid < Tq) qlens[q_first + tid] = (int32_t)(q_start + q_first + tid + 1);
+
+    bf16x8_t qf[4][4];
+    load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
+    // visible entries of this lane's row in each row tile
+    int64_t nvis[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);
+        nvis[rt] = qi < Tq ? n_compressed(q_start + qi + 1) : 0;
+    }
+    const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)kvh * nc_cap * kD,
+                                                (uint32_t)(nc_cap * kD * 2));
+    const int n_chunks = (int)(bt / 16) + 1;                     // every block <= bt is covered
+
+    // sweep 1: per-row max and sum of exp over visible entries (base 2)
+    float m[4], z[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; z[rt] = 0.f; }
+    if (!raw_mode) {
+        for (int c = 0; c < n_chunks; ++c) {
+            __syncthreads();
+            stage_rows_swizzled(sK, rKc, (int64_t)c * 64, tid);
+            __syncthreads();
+            f32x4_t s[4][4];
+            scores_64x64(s, sK, qf, lane);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float x[16];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t j = (int64_t)c * 64 + 16 * mt + 4 * g + i;
+                        const float v = j < nvis[rt] ? s[mt][rt][i] * kLog2eF : -INFINITY;
+                        x[mt * 4 + i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                const float mn = fmaxf(m[rt], mx);
+                if (mn != -INFINITY) {
+                    float acc = (m[rt] == -INFINITY) ? 0.f : z[rt] * exp2f(m[rt] - mn);
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) acc += (x[k] == -INFINITY) ? 0.f : exp2f(x[k] - mn);
+                    z[rt] = acc;
+                    m[rt] = mn;
+                }
+            }
+        }
+        // merge the 4 lanes (g = 0..3) that share a row
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int sh = 16; sh <= 32; sh <<= 1) {
+                const float m2 = shfl_xor(m[rt], sh), z2 = shfl_xor(z[rt], sh);
+                const float mn = fmaxf(m[rt], m2);
+                if (mn != -INFINITY) {
+                    z[rt] = ((m[rt] == -INFINITY) ? 0.f : z[rt] * exp2f(m[rt] - mn)) +
+                            ((m2 == -INFINITY) ? 0.f : z2 * exp2f(m2 - mn));
+                    m[rt] = mn;
+                }
+            }
+        }
+    }
+    float zinv[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) zinv[rt] = z[rt] > 0.f ? 1.f / z[rt] : 0.f;
+
+    // sweep 2: group-summed scores, max over each block's inside entries
+    for (int c = 0; c < n_chunks; ++c) {
+        __syncthreads();
+        stage_rows_swizzled(sK, rKc, (int64_t)c * 64, tid);
+        __syncthreads();
+        f32x4_t s[4][4];
+        scores_64x64(s, sK, qf, lane);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t j = (int64_t)c * 64 + 16 * mt + 4 * g + i;
+                    const bool vis = j < nvis[rt];
+                    float pv;
+                    if (raw_mode) pv = vis ? s[mt][rt][i] : 0.f;
+                    else pv = vis ? exp2f(s[mt][rt][i] * kLog2eF - m[rt]) * zinv[rt] : 0.f;
+                    // sum over the 4 heads of the query (lanes 4k .. 4k+3 of the row group)
+                    pv += dpp<kDppQuadXor1>(pv);
+                    pv += dpp<kDppQuadXor2>(pv);
+                    v[i] = vis ? pv : -INFINITY;
+                }
+                const float bs = fmaxf(fmaxf(v[0], v[1]), v[2]);   // entries 4b, 4b+1, 4b+2
+                const int64_t blk = (int64_t)c * 16 + 4 * mt + g;
+                if ((c16 & 3) == 0 && qi < Tq && blk < nb_cap)
+                    bscore[(qi * Hkv + kvh) * nb_cap + blk] = bs;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ union
+
+__global__ __launch_bounds__(kPfThreads) void prefill_union_kernel(
+    const int32_t *__restrict__ qidx, const int32_t *__restrict__ qcnt, int qcap, int Hkv,
+    int64_t q_start, int64_t Tq, int32_t *__restrict__ tile_idx, int tile_cap,
+    int32_t *__restrict__ tile_cnt) {
+    __shared__ uint32_t s_bits[32768 / 32];
+    __shared__ int s_wave[kPfThreads / 64];
+    const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+    const int tid = threadIdx.x;
+    const int64_t bt = q_start / kBlock + tile;
+    const int nb = (int)bt + 1;
+    const int words = (nb + 31) / 32;
+    for (int w = tid; w < words; w += kPfThreads) s_bits[w] = 0u;
+    __syncthreads();
+    const int64_t q_first = (int64_t)tile * 64;
+    const int nq = (int)(Tq - q_first < 64 ? Tq - q_first : 64);
+    for (int e = tid; e < nq * qcap; e += kPfThreads) {
+        const int q = e / qcap, k = e % qcap;
+        const int64_t unit = (q_first + q) * Hkv + kvh;
+        if (k < qcnt[unit]) {
+            const int blk = qidx[unit * qcap + k];
+            if (blk >= 0 && blk < nb) atomicOr(&s_bits[blk >> 5], 1u << (blk & 31));
+        }
+    }
+    __syncthreads();
+    // ascending compaction: thread t owns words t*per .. t*per+per-1
+    const int per = (words + kPfThreads - 1) / kPfThreads;
+    const int lo = tid * per < words ? tid * per : words;
+    const int hi = lo + per < words ? lo + per : words;
+    int n = 0;
+    for (int w = lo; w < hi; ++w) n += __popc(s_bits[w]);
+    // workgroup exclusive scan
+    const int lane = tid & 63, wave = tid >> 6;
+    int v = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) s_wave[wave] = v;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kPfThreads / 64; ++w) {
+        if (w < wave) base += s_wave[w];
+        total += s_wave[w];
+    }
+    int pos = base + v - n;
+    int32_t *row = tile_idx + (int64_t)blockIdx.x * tile_cap;
+    for (int w = lo; w < hi; ++w) {
+        uint32_t bits = s_bits[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (pos < tile_cap) row[pos] = w * 32 + b;
+            ++pos;
+        }
+    }
+    for (int i = total + tid; i < tile_cap; i += kPfThreads) row[i] = -1;
+    if (tid == 0) tile_cnt[blockIdx.x] = total < tile_cap ? total : tile_cap;
+}
+
+// ------------------------------------------------------------------ attention
+
+__global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
+    const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
+    int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
+    int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
+    int out_bf16, float *__restrict__ lse) {
+    __shared__ __align__(16) bf16_t sK[64 * kD];
+    __shared__ __align__(16) bf16_t sVt[kD * kVtStride];
+    const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int64_t q_first = (int64_t)tile * 64;
+    const int64_t bt = q_start / kBlock + tile;
+
+    bf16x8_t qf[4][4];
+    load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
+    int qloc[4];                                   // query offset inside the tile, per row tile
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) qloc[rt] = 16 * wave + 4 * rt + (c16 >> 2);
+
+    f32x4_t o[8][4];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[4], lsum[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; lsum[rt] = 0.f; }
+
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
+    const int32_t *ids = tile_idx + (int64_t)blockIdx.x * tile_cap;
+    int n = tile_cnt[blockIdx.x];
+    n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
+
+    for (int e = 0; e < n; ++e) {
+        const int64_t blk = ids[e];
+        __syncthreads();
+        stage_rows_swizzled(sK, rK, blk * kBlock, tid);
+        stage_v_transposed(sVt, rV, blk * kBlock, tid);
+        __syncthreads();
+        f32x4_t s[4][4];
+        scores_64x64(s, sK, qf, lane);
+        const bool diag = blk == bt;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * mt + 4 * g + i;
+                    float x = s[mt][rt][i] * qscale;
+                    if (diag && key > qloc[rt]) x = -INFINITY;          // causal: key t <= query p
+                    s[mt][rt][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float mn = fmaxf(m[rt], mx);
+            const float alpha = (m[rt] == -INFINITY) ? 0.f : exp2f(m[rt] - mn);
+            m[rt] = mn;
+            float ps = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = s[mt][rt][i];
+                    const float p = (x == -INFINITY) ? 0.f : exp2f(x - mn);
+                    s[mt][rt][i] = p;
+                    ps += p;
+                }
+            lsum[rt] = lsum[rt] * alpha + ps;
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[ct][rt][i] *= alpha;
+        }
+        // P as B operands: step kk holds keys 32kk + 4g + i (mt = 2kk) then 32kk + 16 + 4g + i
+        bf16x8_t pb[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4_t &a = s[2 * kk][rt];
+                const f32x4_t &b = s[2 * kk + 1][rt];
+                pb[kk][rt] = as_bf16x8(make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                  pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])));
+            }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8_t a = vt_frag(sVt, 16 * ct + c16, kk, g);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[kk][rt], o[ct][rt]);
+            }
+    }
+
+    // finish: total sum per row over the 4 lanes sharing it, then write
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        float l = lsum[rt];
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+        const int64_t qi = q_first + qloc[rt];
+        if (qi >= Tq) continue;
+        const int h = c16 & 3;
+        const int64_t orow = qi * Hq + (int64_t)kvh * kPfG + h;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int ch = 16 * ct + 4 * g;
+            const f32x4_t &v = o[ct][rt];
+            if (out_bf16) {
+                uint2 w = make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
+                *reinterpret_cast<uint2 *>(reinterpret_cast<bf16_t *>(O) + orow * kD + ch) = w;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(O) + orow * kD + ch) =
+                    make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            }
+        }
+        if (lse && g == 0) lse[orow] = l > 0.f ? (m[rt] + log2f(l)) * kLn2F : -INFINITY;
+    }
+}
+
+// ------------------------------------------------------------------ host side
 
 int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p) {
     const int64_t nb = n_blocks(q_start + Tq);
@@ -10,12 +465,60 @@ int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p)
     return (int32_t)(nb < u ? nb : u);
 }
 
-size_t prefill_workspace_bytes(int, int, int64_t, int64_t, const sa_select_params &) { return 0; }
+struct PrefillWorkspace {
+    size_t bscore_off, qlens_off, qidx_off, qcnt_off, total;
+    int64_t nb_cap;
+    int qcap;
+};
 
-int launch_prefill(const void *, int64_t, int64_t, const void *, const void *, const void *, int,
-                   int, int64_t, int64_t, const sa_select_params &, float, void *, int, float *,
-                   int32_t *, int32_t, int32_t *, void *, hipStream_t) {
-    return SA_ERR_UNSUPPORTED;
+static PrefillWorkspace prefill_layout(int Hkv, int64_t q_start, int64_t Tq, const sa_select_params &p) {
+    PrefillWorkspace w{};
+    w.nb_cap = n_blocks(q_start + Tq);
+    w.qcap = p.top_k + p.n_init + p.n_local;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    w.bscore_off = take((size_t)Tq * Hkv * w.nb_cap * sizeof(float));
+    w.qlens_off = take((size_t)Tq * sizeof(int32_t));
+    w.qidx_off = take((size_t)Tq * Hkv * w.qcap * sizeof(int32_t));
+    w.qcnt_off = take((size_t)Tq * Hkv * sizeof(int32_t));
+    w.total = off;
+    return w;
+}
+
+size_t prefill_workspace_bytes(int Hq, int Hkv, int64_t q_start, int64_t Tq, const sa_select_params &p) {
+    (void)Hq;
+    return prefill_layout(Hkv, q_start, Tq, p).total;
+}
+
+int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, const void *V,
+                   const void *Kc, int Hq, int Hkv, int64_t T_cap, int64_t nc_cap,
+                   const sa_select_params &p, float scale, void *O, int out_dtype, float *lse_out,
+                   int32_t *tile_idx, int32_t tile_idx_cap, int32_t *tile_cnt, void *workspace,
+                   hipStream_t stream) {
+    const PrefillWorkspace w = prefill_layout(Hkv, q_start, Tq, p);
+    char *ws = (char *)workspace;
+    float *bscore = (float *)(ws + w.bscore_off);
+    int32_t *qlens = (int32_t *)(ws + w.qlens_off);
+    int32_t *qidx = (int32_t *)(ws + w.qidx_off);
+    int32_t *qcnt = (int32_t *)(ws + w.qcnt_off);
+    const int n_tiles = (int)((Tq + 63) / 64);
+    const dim3 grid((unsigned)(n_tiles * Hkv));
+    const int raw = p.score_mode == SA_SCORE_RAW_SUM ? 1 : 0;
+    hipLaunchKernelGGL(prefill_score_kernel, grid, dim3(kPfThreads), 0, stream, (const bf16_t *)Q,
+                       (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, raw, bscore, w.nb_cap, qlens);
+    launch_topk_raw((int)(Tq * Hkv), Hkv, q_start + Tq, w.nb_cap, qlens, p, bscore, qidx, w.qcap,
+                    qcnt, stream);
+    hipLaunchKernelGGL(prefill_union_kernel, grid, dim3(kPfThreads), 0, stream, (const int32_t *)qidx,
+                       (const int32_t *)qcnt, w.qcap, Hkv, q_start, Tq, tile_idx, tile_idx_cap, tile_cnt);
+    hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPfThreads), 0, stream, (const bf16_t *)Q,
+                       (const bf16_t *)K, (const bf16_t *)V, Hq, Hkv, q_start, Tq, T_cap,
+                       (const int32_t *)tile_idx, tile_idx_cap, (const int32_t *)tile_cnt,
+                       scale * kLog2eF, O, out_dtype == SA_BF16 ? 1 : 0, lse_out);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
 }  // namespace sa

@@ -32,6 +32,10 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
                   float *block_scores_out, void *workspace, hipStream_t stream);
 
+void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
+                     const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,
+                     int32_t *cnt_out, hipStream_t stream);
+
 int decode_auto_split(int B, int Hkv, int32_t idx_cap);
 int decode_min_split(int32_t idx_cap);
 size_t decode_workspace_bytes(int B, int Hq, int32_t n_split);

@@ -400,6 +400,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     if (tid == 0) cnt_out[unit] = total < idx_cap ? total : idx_cap;
 }
 
+// Top-k + union over precomputed raw block scores, one workgroup per unit
+// (used by the prefill path: a unit is one (query, KV head) there, with its
+// own visible length in seq_lens).
+void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
+                     const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,
+                     int32_t *cnt_out, hipStream_t stream) {
+    const size_t lds = (size_t)(nb_cap > 0 ? nb_cap : 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL((topk_kernel<1, false>), dim3((unsigned)n_units), dim3(kTopkThreads), lds,
+                       stream, Hkv, T_cap, nb_cap, seq_lens, p.top_k, p.n_init, p.n_local,
+                       (const float *)nullptr, (int64_t)0, (const float2 *)nullptr, 0, bscore,
+                       (float *)nullptr, idx_out, idx_cap, cnt_out);
+}
+
 template <typename T, int G>
 static void launch_softmax(const void *sel, int H_sel, const void *Kc, int B, int Hkv, int64_t T_cap,
                            int64_t nc_cap, const int32_t *seq_lens, const sa_select_params &p,

@@ -79,3 +79,28 @@ def oracle_kc(K: np.ndarray, lens, dtype, nc_cap):
             c = oracle.compressed_keys(K[b, h], int(lens[b]), dtype)
             out[b, h, :c.shape[0]] = c
     return out
+
+
+def tile_union_ok(gpu_union, ref_union, per_query, k, cand):
+    """Tile block sets: exact, or every differing block is inside some query's
+    near-tie band (the query's k-th and (k+1)-th candidate scores differ by
+    less than 1e-5 relative and the block scores within 1e-5 of the k-th)."""
+    gpu_union = list(gpu_union)
+    if gpu_union == list(ref_union):
+        return True, "exact"
+    if gpu_union != sorted(set(gpu_union)):
+        return False, "not ascending / duplicates"
+    diff = set(gpu_union) ^ set(ref_union)
+    for b in diff:
+        explained = False
+        for top, BS in per_query:
+            if len(cand) <= k or k <= 0:
+                continue
+            order = oracle.top_k_blocks(BS, cand, len(cand))
+            s_k, s_k1 = BS[order[k - 1]], BS[order[k]]
+            if rel_close(s_k, s_k1) and rel_close(BS[b], s_k):
+                explained = True
+                break
+        if not explained:
+            return False, f"block {b} differs outside any near-tie band"
+    return True, "near tie"

@@ -1,0 +1,115 @@
+"""GPU parity of the chunked sparse prefill (tile-shared selection + causal
+attention on matrix cores) against the CPU oracle.
+
+Tile block sets must match the oracle's union of per-query top-k sets exactly
+(near ties excepted, per query); outputs are compared with the oracle's
+attention over the GPU's own tile sets, within the bf16 tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_12_amd as sa
+import oracle
+import synth
+from oracle import SelectParams
+from oracle.attention import block_tokens
+from parity import assert_close, to_np, tile_union_ok
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(T, q_start, Hq=8, Hkv=2, seed=0, T_cap=None):
+    w = synth.PrefillWorkload("t", Hq=Hq, Hkv=Hkv, d=128, T=T, q_start=q_start, dtype="bf16",
+                              top_k=32, n_init=1, n_local=4, seed=seed)
+    inp = synth.make_prefill_inputs(w, device=DEV)
+    if T_cap is not None and T_cap > T:
+        pad = torch.zeros((1, Hkv, T_cap - T, 128), dtype=torch.bfloat16, device=DEV)
+        inp["K"] = torch.cat([inp["K"], pad], dim=2).contiguous()
+        inp["V"] = torch.cat([inp["V"], pad], dim=2).contiguous()
+    K, V = inp["K"][0].contiguous(), inp["V"][0].contiguous()
+    nc = oracle.n_compressed(K.shape[1])
+    Kc = torch.zeros((1, Hkv, nc, 128), dtype=torch.bfloat16, device=DEV)
+    lens = torch.tensor([T], dtype=torch.int32, device=DEV)
+    sa.compress(inp["K"], Kc, torch.zeros_like(lens), lens)
+    return inp["Q"], K, V, Kc[0].contiguous()
+
+
+def _check(Q, K, V, Kc, q_start, k, n_local, mode, tiles=None, queries_per_tile=None):
+    Tq, Hq, _ = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    O, lse, tidx, tcnt = sa.prefill_chunk(Q, q_start, K, V, Kc, k, 1, n_local, mode)
+    torch.cuda.synchronize()
+    Qn, Kn, Vn, Kcn = to_np(Q), to_np(K), to_np(V), to_np(Kc)
+    On, Ln = to_np(O), lse.cpu().numpy()
+    tidx, tcnt = tidx.cpu().numpy(), tcnt.cpu().numpy()
+    n_tiles = (Tq + 63) // 64
+    p = SelectParams(top_k=k, n_init=1, n_local=n_local, score_mode=mode)
+    todo = tiles if tiles is not None else [(t, h) for t in range(n_tiles) for h in range(Hkv)]
+    kinds = []
+    for (t, h) in todo:
+        n = int(tcnt[t, h])
+        got = tidx[t, h, :n].tolist()
+        assert np.all(tidx[t, h, n:] == -1)
+        lo, hi = 64 * t, min(64 * t + 64, Tq)
+        pos = np.arange(q_start + lo, q_start + hi)
+        ref, per_q = oracle.prefill_tile_select(Qn[lo:hi, G * h:G * h + G], Kcn[h], pos, p,
+                                                return_per_query=True)
+        nb = oracle.n_blocks(int(pos[-1]) + 1)
+        _, _, cand = oracle.candidate_sets(nb, 1, n_local)
+        ok, why = tile_union_ok(got, ref, per_q, k, cand)
+        assert ok, ((t, h), why)
+        kinds.append(why)
+        qs = range(lo, hi) if queries_per_tile is None else \
+            np.linspace(lo, hi - 1, queries_per_tile).astype(int).tolist()
+        for i in qs:
+            o, l = oracle.sparse_attention(Qn[i, G * h:G * h + G], Kn[h], Vn[h],
+                                           block_tokens(got, q_start + i + 1), 1.0)
+            assert_close(On[i, G * h:G * h + G], o, "bf16", f"O tile {t} kvh {h} query {i}")
+            assert_close(Ln[i, G * h:G * h + G], l, "bf16", f"LSE tile {t} query {i}")
+    return kinds
+
+
+@pytest.mark.parametrize("mode", ["softmax_sum", "raw_sum"])
+def test_prefill_small_parity(mode):
+    Q, K, V, Kc = _inputs(T=4096, q_start=3584, seed=1)
+    kinds = _check(Q, K, V, Kc, 3584, 5, 4, mode)
+    assert kinds.count("exact") >= len(kinds) - 1
+
+
+def test_prefill_partial_last_tile_and_padded_capacity():
+    Q, K, V, Kc = _inputs(T=3000, q_start=2560, seed=2, T_cap=3100)   # Tq = 440: 6 full + 1 partial tile
+    _check(Q, K, V, Kc, 2560, 6, 4, "softmax_sum")
+
+
+def test_prefill_chunk_at_start_of_sequence():
+    Q, K, V, Kc = _inputs(T=700, q_start=0, seed=3)      # early tiles have no candidates at all
+    _check(Q, K, V, Kc, 0, 3, 4, "softmax_sum")
+
+
+def test_prefill_dense_limit_equals_causal_sdpa():
+    T, q_start = 1500, 1024
+    Q, K, V, Kc = _inputs(T=T, q_start=q_start, seed=4)
+    O, lse, tidx, tcnt = sa.prefill_chunk(Q, q_start, K, V, Kc, 10 ** 4, 1, 4, "softmax_sum")
+    Tq, Hq = Q.shape[:2]
+    qt = Q.double().permute(1, 0, 2)[None].cpu()
+    kt = K.double().repeat_interleave(4, 0)[None].cpu()
+    vt = V.double().repeat_interleave(4, 0)[None].cpu()
+    causal = torch.arange(T)[None, :] <= (q_start + torch.arange(Tq))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=causal,
+                                                           scale=1.0)[0].permute(1, 0, 2).numpy()
+    assert_close(to_np(O), ref, "bf16", "dense causal prefill")
+
+
+def test_prefill_chunk_bf16_128k_full_sampled():
+    w = synth.PREFILL_WORKLOADS["prefill_chunk_bf16_128k"]
+    inp = synth.make_prefill_inputs(w, device=DEV)
+    K, V = inp["K"][0].contiguous(), inp["V"][0].contiguous()
+    Kc = torch.zeros((1, w.Hkv, oracle.n_compressed(w.T), 128), dtype=torch.bfloat16, device=DEV)
+    lens = torch.tensor([w.T], dtype=torch.int32, device=DEV)
+    sa.compress(inp["K"], Kc, torch.zeros_like(lens), lens)
+    kinds = _check(inp["Q"], K, V, Kc[0].contiguous(), w.q_start, w.top_k, w.n_local, "softmax_sum",
+                   tiles=[(0, 0), (13, 3), (31, 7)], queries_per_tile=6)
+    print(f"prefill_chunk_bf16_128k sampled tiles: {kinds}", flush=True)
