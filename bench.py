@@ -237,11 +237,165 @@ def cpu_baseline_decode(w, inp, lens, budget_s):
 
 
 def bench_crosslayer(args, w):
-    raise SystemExit("crosslayer bench: see bench_crosslayer below")
+    """One decode step of the cross-layer workload: layer 0 appends its compressed
+    keys and selects; all layers attend over that selection. The 16 appended
+    tokens' keys and values are in the cache from the start; a step advances
+    the lengths by one, and the 16-step cycle repeats."""
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import SparseDecoder
+    from block_sparse_attention_12_amd import n_compressed
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T_cap = w.T + w.steps
+    layers = []
+    for l in range(w.layers):
+        inp = synth.make_decode_inputs(w, device=dev, T_cap=T_cap, layer=l)
+        qs = synth.make_decode_queries(w, w.steps, device=dev, seed_offset=100 + l)
+        layers.append(dict(K=inp["K"], V=inp["V"], qs=qs))
+        del inp
+    dec = SparseDecoder(w.B, w.Hq, w.Hkv, T_cap, w.top_k, w.n_init, w.n_local, "query",
+                        w.score_mode, device=dev, n_split=args.n_split)
+    Kc = dec.new_kc(layers[0]["K"].dtype)
+    lens = [torch.full((w.B,), w.T + s, dtype=torch.int32, device=dev) for s in range(w.steps + 1)]
+    dec.build(layers[0]["K"], Kc, lens[0])
+    outs = [(torch.empty_like(dec.O), torch.empty_like(dec.lse)) for _ in range(w.layers)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = i % w.steps
+        lay = [dict(Q=L["qs"][s], K=L["K"], V=L["V"]) for L in layers]
+        dec.crosslayer_step(lay, Kc, lens[s], lens[s + 1], outs=outs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = _events(2)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    # bytes of the last step (L = T + steps): anchor scan + 4 attentions
+    cnt, idx = dec.cnt.cpu(), dec.idx.cpu()
+    L = w.T + w.steps
+    row = 128 * 2
+    attn = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for blk in idx[b, h, :int(cnt[b, h])].tolist():
+                attn += 2 * row * max(0, min(64, L - 64 * blk))
+    attn = attn * w.layers + w.layers * w.B * w.Hq * (128 * 2 + 128 * 4 + 4)
+    scan = w.B * w.Hkv * n_compressed(L) * row + w.B * w.Hq * row
+    step_bytes = attn + scan
+    out = {
+        "metric": "cross-layer sparse decode tokens/s (4 layers share one selection) and HBM GB/s",
+        "value": round(w.B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.name, "batch": w.B, "context": f"{w.T}..{w.T + w.steps}",
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "layers": w.layers,
+                   "top_k": w.top_k, "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5), "step_bytes": step_bytes,
+        "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_prefill(args):
-    raise SystemExit("prefill bench not built yet")
+    """One chunk of sparse prefill: tile selection (scores on matrix cores, exact
+    per-query top-k, tile unions) and causal attention over the unions."""
+    import numpy as np
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import SparsePrefill
+    from block_sparse_attention_12_amd import compress, n_compressed
+
+    w = synth.PREFILL_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_prefill_inputs(w, device=dev)
+    lens = torch.tensor([w.T], dtype=torch.int32, device=dev)
+    reps = []
+    for r in range(max(1, min(args.replicas, 2))):
+        K = inp["K"] if r == 0 else inp["K"].clone()
+        V = inp["V"] if r == 0 else inp["V"].clone()
+        Kc = torch.empty((1, w.Hkv, n_compressed(w.T), 128), dtype=torch.bfloat16, device=dev)
+        compress(K, Kc, torch.zeros_like(lens), lens)
+        reps.append(dict(Q=inp["Q"] if r == 0 else inp["Q"].clone(), K=K[0], V=V[0], Kc=Kc[0]))
+    pf = SparsePrefill(w.Hq, w.Hkv, w.q_start, w.Tq, w.top_k, w.n_init, w.n_local, "softmax_sum",
+                       device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        r = reps[i % len(reps)]
+        pf.run(r["Q"], r["K"], r["V"], r["Kc"])
+
+    def attend(i):
+        r = reps[i % len(reps)]
+        pf.attend(r["Q"], r["K"], r["V"])
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = _events(2)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    evs = [_events(2) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        attend(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+
+    # algorithmic FLOPs from the tile sets: QK^T and PV over unmasked query-key pairs
+    tidx, tcnt = pf.tile_idx.cpu().numpy(), pf.tile_cnt.cpu().numpy()
+    pairs = 0
+    n_tiles = (w.Tq + 63) // 64
+    for t in range(n_tiles):
+        nq = min(64, w.Tq - 64 * t)
+        bt = w.q_start // 64 + t
+        for h in range(w.Hkv):
+            blocks = tidx[t, h, :tcnt[t, h]]
+            full = int((blocks < bt).sum())
+            pairs += full * 64 * nq + (nq * (nq + 1) // 2 if bt in blocks else 0)
+    G = w.Hq // w.Hkv
+    attn_flops = pairs * G * 128 * 4
+    sel_flops = sum(n_compressed(w.q_start + i + 1) for i in range(w.Tq)) * w.Hq * 128 * 2 * 2
+    attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+    out = {
+        "metric": "sparse chunked-prefill tokens/s and MFMA TFLOP/s (% of bf16 peak), 1 GPU",
+        "value": round(w.Tq / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.name, "context": w.T, "chunk": f"{w.q_start}..{w.T - 1}",
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k,
+                   "n_init": w.n_init, "n_local": w.n_local, "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "phase_ms": {"select": round(gpu_ms - attn_ms, 5), "attend": round(attn_ms, 5)},
+        "mean_union_blocks": round(float(tcnt.mean()), 1),
+        "attn_tflop": round(attn_flops / 1e12, 4), "select_tflop": round(sel_flops / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel (sparse_attn_prefill_attend)",
+                     "achieved": round(attn_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": attn_flops},
+    }
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

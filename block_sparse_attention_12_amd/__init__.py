@@ -41,7 +41,7 @@ EXPORTS = [
     "sparse_attn_select_workspace_size", "sparse_attn_select",
     "sparse_attn_decode_workspace_size", "sparse_attn_decode",
     "sparse_attn_prefill_tile_cap", "sparse_attn_prefill_workspace_size",
-    "sparse_attn_prefill_chunk",
+    "sparse_attn_prefill_chunk", "sparse_attn_prefill_attend",
 ]
 
 
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_prefill_chunk.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _int, _int, _int, _int,
                                             _i64, _i64, _PP, _f32, _vp, _int, _vp, _vp, _i32, _vp,
                                             _vp, _sz, _vp]
+    L.sparse_attn_prefill_attend.restype = _int
+    L.sparse_attn_prefill_attend.argtypes = [_vp, _i64, _i64, _vp, _vp, _int, _int, _int, _int, _i64,
+                                             _vp, _i32, _vp, _f32, _vp, _int, _vp, _vp]
     _lib = L
     return L
 
@@ -282,3 +285,23 @@ def prefill_chunk(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tenso
                                          _opt(workspace, "workspace"), ws_bytes, _stream(Q, stream))
     _check("sparse_attn_prefill_chunk", st)
     return O, lse, tile_idx, tile_cnt
+
+
+def prefill_attend(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tensor,
+                   tile_idx: torch.Tensor, tile_cnt: torch.Tensor, scale: float = 1.0,
+                   out_dtype=torch.float32, O=None, lse=None, want_lse=True, stream=None):
+    """Causal attention of a prefill chunk over given tile block sets. Returns (O, lse)."""
+    Tq, Hq, d = Q.shape
+    Hkv, T_cap = K.shape[-3], K.shape[-2]
+    dev = Q.device
+    if O is None:
+        O = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    st = lib().sparse_attn_prefill_attend(_dev(Q, "Q"), int(q_start), Tq, _dev(K, "K"), _dev(V, "V"),
+                                          _dtype_code(K), Hq, Hkv, d, T_cap,
+                                          _dev(tile_idx, "tile_idx"), tile_idx.shape[-1],
+                                          _dev(tile_cnt, "tile_cnt"), float(scale), _dev(O, "O"),
+                                          _dtype_code(O), _opt(lse, "lse"), _stream(Q, stream))
+    _check("sparse_attn_prefill_attend", st)
+    return O, lse

@@ -514,10 +514,19 @@ int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, co
                     qcnt, stream);
     hipLaunchKernelGGL(prefill_union_kernel, grid, dim3(kPfThreads), 0, stream, (const int32_t *)qidx,
                        (const int32_t *)qcnt, w.qcap, Hkv, q_start, Tq, tile_idx, tile_idx_cap, tile_cnt);
-    hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPfThreads), 0, stream, (const bf16_t *)Q,
-                       (const bf16_t *)K, (const bf16_t *)V, Hq, Hkv, q_start, Tq, T_cap,
-                       (const int32_t *)tile_idx, tile_idx_cap, (const int32_t *)tile_cnt,
-                       scale * kLog2eF, O, out_dtype == SA_BF16 ? 1 : 0, lse_out);
+    return launch_prefill_attend(Q, q_start, Tq, K, V, Hq, Hkv, T_cap, tile_idx, tile_idx_cap,
+                                 tile_cnt, scale, O, out_dtype, lse_out, stream);
+}
+
+int launch_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void *K, const void *V,
+                          int Hq, int Hkv, int64_t T_cap, const int32_t *tile_idx,
+                          int32_t tile_idx_cap, const int32_t *tile_cnt, float scale, void *O,
+                          int out_dtype, float *lse_out, hipStream_t stream) {
+    const int n_tiles = (int)((Tq + 63) / 64);
+    hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(n_tiles * Hkv)), dim3(kPfThreads), 0,
+                       stream, (const bf16_t *)Q, (const bf16_t *)K, (const bf16_t *)V, Hq, Hkv,
+                       q_start, Tq, T_cap, tile_idx, tile_idx_cap, tile_cnt, scale * kLog2eF, O,
+                       out_dtype == SA_BF16 ? 1 : 0, lse_out);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -53,4 +53,9 @@ int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, co
                    int32_t *tile_idx, int32_t tile_idx_cap, int32_t *tile_cnt, void *workspace,
                    hipStream_t stream);
 
+int launch_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void *K, const void *V,
+                          int Hq, int Hkv, int64_t T_cap, const int32_t *tile_idx,
+                          int32_t tile_idx_cap, const int32_t *tile_cnt, float scale, void *O,
+                          int out_dtype, float *lse_out, hipStream_t stream);
+
 }  // namespace sa

@@ -158,4 +158,23 @@ int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const 
                           (hipStream_t)stream);
 }
 
+int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void *K,
+                               const void *V, int dtype, int Hq, int Hkv, int d, int64_t T_cap,
+                               const int32_t *tile_idx, int32_t tile_idx_cap,
+                               const int32_t *tile_cnt, float scale, void *O, int out_dtype,
+                               float *lse_out, void *stream) {
+    if (!Q || !K || !V || !O || !tile_idx || !tile_cnt) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || Hq <= 0 || Hkv <= 0 || d <= 0 || Tq <= 0 ||
+        q_start < 0 || T_cap < 0 || tile_idx_cap <= 0)
+        return SA_ERR_INVALID_ARG;
+    if (q_start % kBlock) return SA_ERR_INVALID_ARG;
+    if (Hq % Hkv) return SA_ERR_INVALID_ARG;
+    if (!(scale == scale)) return SA_ERR_INVALID_ARG;
+    if (d != kD || Hq / Hkv != 4 || dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+    if (T_cap * d * 2 > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (T_cap < q_start + Tq) return SA_ERR_CAPACITY;
+    return launch_prefill_attend(Q, q_start, Tq, K, V, Hq, Hkv, T_cap, tile_idx, tile_idx_cap,
+                                 tile_cnt, scale, O, out_dtype, lse_out, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (compress, select, decode, prefill_chunk, make_params, select_workspace_size,
+from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
+               select_workspace_size,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
 
@@ -128,3 +129,8 @@ class SparsePrefill:
         return prefill_chunk(Q, self.q_start, K, V, Kc, self.top_k, self.n_init, self.n_local,
                              self.score_mode, scale, O=self.O, lse=self.lse,
                              tile_idx=self.tile_idx, tile_cnt=self.tile_cnt, workspace=self.ws)
+
+    def attend(self, Q, K, V, scale=1.0, O=None, lse=None):
+        """Attention only, over the tile sets of the last run (reuse across layers)."""
+        return prefill_attend(Q, self.q_start, K, V, self.tile_idx, self.tile_cnt, scale,
+                              O=self.O if O is None else O, lse=self.lse if lse is None else lse)

@@ -229,6 +229,27 @@ int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const 
                               int32_t *tile_idx_out, int32_t tile_idx_cap, int32_t *tile_cnt_out,
                               void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * sparse_attn_prefill_attend - the attention half of sparse_attn_prefill_chunk
+ * over caller-given tile block sets, e.g. the sets one anchor layer selected,
+ * reused by the following layers (top-k indices computed in anchor layers and
+ * reused in later layers, for prefill and decode: Kascade abstract on the page
+ * "CoSA ..."). Each query of tile t attends causally (t <= p) to the blocks
+ * tile_idx[t, kvh, 0 .. tile_cnt[t, kvh]) (ascending, each <= the tile's
+ * block, no duplicates).
+ *
+ *   Q [Tq, Hq, d], K/V [Hkv, T_cap, d] device bf16; O [Tq, Hq, d] (out_dtype),
+ *   lse_out optional [Tq, Hq] fp32; tile_idx [n_tiles, Hkv, tile_idx_cap],
+ *   tile_cnt [n_tiles, Hkv] device int32.
+ * Errors: SA_ERR_INVALID_ARG (incl. q_start % 64 != 0), SA_ERR_UNSUPPORTED
+ *         (d != 128, G != 4, dtype != SA_BF16), SA_ERR_CAPACITY (T_cap).
+ */
+int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void *K,
+                               const void *V, int dtype, int Hq, int Hkv, int d, int64_t T_cap,
+                               const int32_t *tile_idx, int32_t tile_idx_cap,
+                               const int32_t *tile_cnt, float scale, void *O, int out_dtype,
+                               float *lse_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

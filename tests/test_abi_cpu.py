@@ -159,3 +159,21 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         sa.compress(K, torch.zeros(1, 1, 3, 128), torch.zeros(1, dtype=torch.int32),
                     torch.zeros(1, dtype=torch.int32))
+
+
+def test_prefill_attend_validation():
+    L = sa.lib()
+
+    def call(**kw):
+        a = dict(Q=FAKE, q_start=1024, Tq=256, K=FAKE, V=FAKE, dtype=sa.SA_BF16, Hq=32, Hkv=8, d=128,
+                 T_cap=1280, tidx=FAKE, tcap=20, tcnt=FAKE, O=FAKE, out=sa.SA_F32, lse=None)
+        a.update(kw)
+        return L.sparse_attn_prefill_attend(a["Q"], a["q_start"], a["Tq"], a["K"], a["V"], a["dtype"],
+                                            a["Hq"], a["Hkv"], a["d"], a["T_cap"], a["tidx"], a["tcap"],
+                                            a["tcnt"], 1.0, a["O"], a["out"], a["lse"], None)
+    assert call(tidx=None) == sa.SA_ERR_INVALID_ARG
+    assert call(q_start=65) == sa.SA_ERR_INVALID_ARG
+    assert call(tcap=0) == sa.SA_ERR_INVALID_ARG
+    assert call(Hq=8) == sa.SA_ERR_UNSUPPORTED
+    assert call(dtype=sa.SA_F32) == sa.SA_ERR_UNSUPPORTED
+    assert call(T_cap=1000) == sa.SA_ERR_CAPACITY

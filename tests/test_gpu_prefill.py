@@ -113,3 +113,27 @@ def test_prefill_chunk_bf16_128k_full_sampled():
     kinds = _check(inp["Q"], K, V, Kc[0].contiguous(), w.q_start, w.top_k, w.n_local, "softmax_sum",
                    tiles=[(0, 0), (13, 3), (31, 7)], queries_per_tile=6)
     print(f"prefill_chunk_bf16_128k sampled tiles: {kinds}", flush=True)
+
+
+def test_prefill_attend_reuses_tile_sets_across_layers():
+    """Attention of another layer over the anchor layer's tile sets (and the
+    anchor's own attention, recomputed, is bit-identical to the chunk call)."""
+    T, q_start = 3000, 2432
+    Q, K, V, Kc = _inputs(T=T, q_start=q_start, seed=5)
+    Q2, K2, V2, _ = _inputs(T=T, q_start=q_start, seed=6)
+    O, lse, tidx, tcnt = sa.prefill_chunk(Q, q_start, K, V, Kc, 6, 1, 4, "softmax_sum")
+    O1, _ = sa.prefill_attend(Q, q_start, K, V, tidx, tcnt)
+    assert torch.equal(O1, O)
+    O2, L2 = sa.prefill_attend(Q2, q_start, K2, V2, tidx, tcnt)
+    torch.cuda.synchronize()
+    Qn, Kn, Vn = to_np(Q2), to_np(K2), to_np(V2)
+    ti, tc = tidx.cpu().numpy(), tcnt.cpu().numpy()
+    On, Ln = to_np(O2), L2.cpu().numpy()
+    for i in range(0, Q.shape[0], 7):
+        t = i // 64
+        for h in range(2):
+            blocks = ti[t, h, :tc[t, h]].tolist()
+            o, l = oracle.sparse_attention(Qn[i, 4 * h:4 * h + 4], Kn[h], Vn[h],
+                                           block_tokens(blocks, q_start + i + 1), 1.0)
+            assert_close(On[i, 4 * h:4 * h + 4], o, "bf16", f"reuse query {i}")
+            assert_close(Ln[i, 4 * h:4 * h + 4], l, "bf16", f"reuse lse {i}")
