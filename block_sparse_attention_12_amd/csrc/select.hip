@@ -33,9 +33,8 @@ namespace sa {
 
 constexpr int kSelThreads = 256;
 constexpr int kSoftmaxChunk = 512;                  // entries per workgroup (softmax mode)
-constexpr int kRawChunkBlocks = 128;                // blocks per workgroup (raw mode)
-constexpr int kTopkThreads = 256;
-constexpr int64_t kMaxTopkBlocks = 32768;           // LDS key array limit
+constexpr int kRawChunkBlocks = 256;                // blocks per workgroup (raw mode)
+constexpr int64_t kMaxTopkBlocks = 32768;           // 1024 threads x 32 blocks
 
 SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
     SelectWorkspace w{};
@@ -70,6 +69,11 @@ __device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
 // ---------------------------------------------------------------- raw scores
 
 template <typename T>
+struct RawIter {                         // one iteration: 4 blocks x 3 inside entries per row group
+    Raw8<T> r[12];
+};
+
+template <typename T>
 __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const T *__restrict__ sel, int H_sel, int Gs, const T *__restrict__ Kc, int Hkv,
     int64_t nc_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ bscore,
@@ -81,43 +85,69 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const int lane = threadIdx.x & 63;
     const int lane16 = threadIdx.x & 15;
     const int group = threadIdx.x >> 4;                 // 0..15
-
-    // group-summed selector slice (sum in head order)
-    float s[8];
-    {
-        const T *sp = sel + ((int64_t)b * H_sel + (int64_t)kvh * Gs) * kD + lane16 * kLaneElems;
-        load8(sp, s);
-        for (int g = 1; g < Gs; ++g) {
-            float x[8];
-            load8(sp + (int64_t)g * kD, x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-        }
-    }
-    const T *Kcu = Kc + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
-    float *bs = bscore + (int64_t)unit * nb_cap;
+    constexpr uint32_t kRowBytes = kD * sizeof(T);
+    // rows at or past n_c(L) read as zeros
+    const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)unit * nc_cap * kD,
+                                                (uint32_t)(nc * kRowBytes));
+    const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
     const int64_t chunk0 = (int64_t)blockIdx.x * kRawChunkBlocks;
-#pragma unroll 1
-    for (int it = 0; it < kRawChunkBlocks / 64; ++it) {
-        const int64_t blk0 = chunk0 + it * 64 + group * 4;      // this group's 4 blocks
-        Raw8<T> r[12];
+    auto issue = [&](RawIter<T> &it, int64_t blk0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int e = 0; e < 3; ++e) {
-                const int64_t j = 4 * (blk0 + q) + e;
-                if (j < nc) load_raw(Kcu + j * kD, r[q * 3 + e]);
+            for (int e = 0; e < 3; ++e)
+                load_raw(rKc, row_offset(4 * (blk0 + q) + e, kRowBytes, lane_off), it.r[q * 3 + e]);
+    };
+    // first rows go out before the selector is even loaded
+    RawIter<T> bufA, bufB;
+    issue(bufA, chunk0 + group * 4);
+
+    // group-summed selector slice (sum in head order)
+    float s[8];
+    uint32_t s_bf[4];                       // the single selector as bf16 pairs (Gs == 1, bf16)
+    {
+        const T *sp = sel + ((int64_t)b * H_sel + (int64_t)kvh * Gs) * kD + lane16 * kLaneElems;
+        Raw8<T> raw[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+            if (g < Gs) load_raw(sp + (int64_t)g * kD, raw[g]);
+        unpack(raw[0], s);
+#pragma unroll
+        for (int g = 1; g < 8; ++g) {
+            if (g < Gs) {
+                float x[8];
+                unpack(raw[g], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
             }
+        }
+        if constexpr (sizeof(T) == 2) {
+            const Raw8<bf16_t> &r0 = reinterpret_cast<const Raw8<bf16_t> &>(raw[0]);
+            s_bf[0] = r0.v.x; s_bf[1] = r0.v.y; s_bf[2] = r0.v.z; s_bf[3] = r0.v.w;
+        }
+    }
+    const bool use_dot2 = sizeof(T) == 2 && Gs == 1;
+    float *bs = bscore + (int64_t)unit * nb_cap;
+
+    auto process = [&](const RawIter<T> &it, int64_t blk0) {
         float v[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
             for (int e = 0; e < 3; ++e) {
-                const int64_t j = 4 * (blk0 + q) + e;
                 float acc = 0.f;
-                if (j < nc) {
+                if constexpr (sizeof(T) == 2) {
+                    if (use_dot2) {
+                        const Raw8<bf16_t> &k8 = reinterpret_cast<const Raw8<bf16_t> &>(it.r[q * 3 + e]);
+                        acc = dot2_bf16(s_bf[0], k8.v.x, acc);
+                        acc = dot2_bf16(s_bf[1], k8.v.y, acc);
+                        acc = dot2_bf16(s_bf[2], k8.v.z, acc);
+                        acc = dot2_bf16(s_bf[3], k8.v.w, acc);
+                    }
+                }
+                if (!use_dot2) {
                     float x[8];
-                    unpack(r[q * 3 + e], x);
+                    unpack(it.r[q * 3 + e], x);
 #pragma unroll
                     for (int c = 0; c < 8; ++c) acc = fmaf(s[c], x[c], acc);
                 }
@@ -134,8 +164,23 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
         x = fmaxf(x, dpp<kDppQuadXor1>(x));
         x = fmaxf(x, dpp<kDppQuadXor2>(x));
         if (e == 0 && blk < nb_cap) bs[blk] = x;
+    };
+
+    // iterations of 64 blocks; the next iteration's rows are in flight while
+    // the current ones are reduced (sched_barrier keeps the prefetch in place)
+    constexpr int kIters = kRawChunkBlocks / 64;
+#pragma unroll
+    for (int it = 0; it < kIters; it += 2) {
+        const int64_t b0 = chunk0 + it * 64 + group * 4;
+        if (it + 1 < kIters) issue(bufB, b0 + 64);
+        __builtin_amdgcn_sched_barrier(0);
+        process(bufA, b0);
+        if (it + 1 < kIters) {
+            if (it + 2 < kIters) issue(bufA, b0 + 128);
+            __builtin_amdgcn_sched_barrier(0);
+            process(bufB, b0 + 64);
+        }
     }
-    (void)lane;
 }
 
 // ---------------------------------------------------------------- softmax scores
@@ -235,6 +280,7 @@ __device__ __forceinline__ uint32_t orderable(float x) {
 }
 
 // Exclusive prefix sum of one int per thread over the workgroup; also returns the total.
+template <int NT>
 __device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int v = x;
@@ -248,7 +294,7 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total)
     int base = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const int sw = s_wave[w];
         if (w < wave) base += sw;
         total += sw;
@@ -257,17 +303,21 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total)
     return base + v - x;
 }
 
-template <int G, bool SOFTMAX>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+// Thread t owns PER consecutive blocks [t*PER, t*PER + PER): their 32-bit
+// orderable keys stay in registers for the whole kernel, so the radix passes
+// are register compares plus LDS histogram atomics, and the ascending
+// compaction needs only two workgroup prefix scans.
+template <int G, bool SOFTMAX, int NT, int PER>
+__global__ __launch_bounds__(NT) void topk_kernel(
     int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens, int top_k,
     int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
     const float2 *__restrict__ stats, int n_chunks, const float *__restrict__ bscore_in,
     float *__restrict__ bscore_out, int32_t *__restrict__ idx_out, int idx_cap,
     int32_t *__restrict__ cnt_out) {
-    extern __shared__ uint32_t s_keys[];                 // [nb_cap]
     __shared__ uint32_t s_hist[256];
-    __shared__ float s_M[G > 0 ? G : 1], s_Zinv[G > 0 ? G : 1];
-    __shared__ int s_wave[kTopkThreads / 64];
+    __shared__ float s_M[G], s_Zinv[G];
+    __shared__ float2 s_st[G * 64];
+    __shared__ int s_wave[NT / 64];
     __shared__ uint32_t s_digit, s_above;
     const int unit = blockIdx.x;
     const int b = unit / Hkv;
@@ -280,42 +330,95 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const int cand_lo = init_hi;
     const int cand_hi = local_lo > cand_lo ? local_lo : cand_lo;
     const int n_cand = cand_hi - cand_lo;
+    const int blk0 = tid * PER;                     // first block of this thread
 
+    float score[PER];
     if constexpr (SOFTMAX) {
+        // per-head softmax max / denominator from the chunk partials (<= 64 chunks)
+        const int used = (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk);
+        if (used <= 64) {
+            for (int i = tid; i < G * used; i += NT)
+                s_st[i] = stats[((int64_t)unit * G + i / used) * n_chunks + i % used];
+            __syncthreads();
+        }
         if (tid < G) {
-            const int used = (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk);
-            const float2 *st = stats + ((int64_t)unit * G + tid) * n_chunks;
             float M = -INFINITY, Z = 0.f;
-            for (int c = 0; c < used; ++c) merge_ms(M, Z, st[c].x, st[c].y);
+            const float2 *st = stats + ((int64_t)unit * G + tid) * n_chunks;
+            for (int c = 0; c < used; ++c) {
+                const float2 v = used <= 64 ? s_st[tid * used + c] : st[c];   // > 64: long contexts
+                merge_ms(M, Z, v.x, v.y);
+            }
             s_M[tid] = M;
             s_Zinv[tid] = Z > 0.f ? 1.f / Z : 0.f;
         }
         __syncthreads();
-    }
-    // block scores and keys
-    for (int blk = tid; blk < nb_cap; blk += kTopkThreads) {
-        float score = -INFINITY;
-        if (blk < nb) {
-            if constexpr (SOFTMAX) {
+        // entries 4*blk0 .. 4*blk0 + 4*PER - 1, eight blocks (32 entries) at a time
 #pragma unroll
-                for (int e = 0; e < 3; ++e) {
-                    const int64_t j = 4 * (int64_t)blk + e;
-                    if (j < nc) {
-                        float S = 0.f;
+        for (int sub = 0; sub < PER; sub += 8) {
+            float S[32];
 #pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            S += expf(logits[((int64_t)unit * G + g) * nc_pad + j] - s_M[g]) * s_Zinv[g];
-                        score = fmaxf(score, S);
+            for (int k = 0; k < 32; ++k) S[k] = 0.f;
+            const int64_t j0 = 4 * (int64_t)(blk0 + sub);
+#pragma unroll
+            for (int g0 = 0; g0 < G; g0 += (G >= 8 ? 2 : (G < 4 ? G : 4))) {
+                constexpr int GC = G >= 8 ? 2 : (G < 4 ? G : 4);   // heads per load group
+                float4 lg[GC][8];
+#pragma unroll
+                for (int gg = 0; gg < GC; ++gg)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        lg[gg][q] = (j0 + 4 * q < nc)
+                                        ? *reinterpret_cast<const float4 *>(
+                                              logits + ((int64_t)unit * G + g0 + gg) * nc_pad + j0 + 4 * q)
+                                        : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+                for (int gg = 0; gg < GC; ++gg) {
+                    const float Mg = s_M[g0 + gg], Zi = s_Zinv[g0 + gg];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        S[4 * q + 0] += expf(lg[gg][q].x - Mg) * Zi;
+                        S[4 * q + 1] += expf(lg[gg][q].y - Mg) * Zi;
+                        S[4 * q + 2] += expf(lg[gg][q].z - Mg) * Zi;
                     }
                 }
-            } else {
-                score = bscore_in[(int64_t)unit * nb_cap + blk];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                float best = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                    if (j0 + 4 * q + e < nc) best = fmaxf(best, S[4 * q + e]);
+                score[sub + q] = (blk0 + sub + q < nb) ? best : -INFINITY;
             }
         }
-        if (bscore_out) bscore_out[(int64_t)unit * nb_cap + blk] = score;
-        s_keys[blk] = orderable(score);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PER; q += 4) {
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (blk0 + q + 3 < nb_cap)
+                v = *reinterpret_cast<const float4 *>(bscore_in + (int64_t)unit * nb_cap + blk0 + q);
+            else {
+                float t[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    t[e] = (blk0 + q + e < nb_cap) ? bscore_in[(int64_t)unit * nb_cap + blk0 + q + e] : -INFINITY;
+                v = make_float4(t[0], t[1], t[2], t[3]);
+            }
+            score[q] = v.x; score[q + 1] = v.y; score[q + 2] = v.z; score[q + 3] = v.w;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (blk0 + q >= nb) score[q] = -INFINITY;
     }
-    __syncthreads();
+    uint32_t key[PER];
+    bool cand[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int blk = blk0 + q;
+        if (bscore_out && blk < nb_cap) bscore_out[(int64_t)unit * nb_cap + blk] = score[q];
+        key[q] = orderable(score[q]);
+        cand[q] = blk >= cand_lo && blk < cand_hi;
+    }
 
     // radix select of the top_k-th largest key among the candidates
     const bool take_all = top_k >= n_cand;
@@ -325,12 +428,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     if (!take_all && !take_none) {
 #pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
-            s_hist[tid] = 0;
+            for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
             __syncthreads();
-            for (int blk = cand_lo + tid; blk < cand_hi; blk += kTopkThreads) {
-                const uint32_t key = s_keys[blk];
-                if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-            }
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                if (cand[q] && (key[q] & mask) == prefix) atomicAdd(&s_hist[(key[q] >> shift) & 255u], 1u);
             __syncthreads();
             if (tid < 64) {
                 // counts above each bin, from the top: lane l owns bins 4l .. 4l+3
@@ -357,47 +459,61 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
             prefix |= s_digit << shift;
             mask |= 255u << shift;
             remaining -= (int)s_above;
-            __syncthreads();
         }
     }
     const uint32_t thr = prefix;        // exact key of the k-th largest candidate
     const int take_eq = remaining;      // keys equal to thr that are taken, lowest ids first
 
-    // membership of block blk; eq_rank counts candidates equal to thr seen so far
-    auto in_union = [&](int blk, int &eq_rank) -> bool {
-        if (blk < init_hi || blk >= local_lo) return true;
-        if (blk < cand_lo || blk >= cand_hi || take_none) return false;
-        if (take_all) return true;
-        const uint32_t key = s_keys[blk];
-        if (key > thr) return true;
-        if (key == thr) return eq_rank++ < take_eq;
-        return false;
-    };
-
-    // union in ascending order: each thread owns a contiguous range of blocks
-    const int per = (nb + kTopkThreads - 1) / kTopkThreads;
-    const int lo = tid * per < nb ? tid * per : nb;
-    const int hi = lo + per < nb ? lo + per : nb;
+    // ascending compaction over this thread's consecutive blocks
     int n_eq = 0;
     if (!take_all && !take_none)
-        for (int blk = lo; blk < hi; ++blk)
-            n_eq += (blk >= cand_lo && blk < cand_hi && s_keys[blk] == thr) ? 1 : 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) n_eq += (cand[q] && key[q] == thr) ? 1 : 0;
     int unused;
-    const int eq_base = wg_exclusive_scan(n_eq, s_wave, unused);
-    int rank = eq_base, n_in = 0;
-    for (int blk = lo; blk < hi; ++blk) n_in += in_union(blk, rank) ? 1 : 0;
+    int rank = wg_exclusive_scan<NT>(n_eq, s_wave, unused);
+    bool in[PER];
+    int n_in = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int blk = blk0 + q;
+        bool x;
+        if (blk >= nb) x = false;
+        else if (blk < init_hi || blk >= local_lo) x = true;
+        else if (take_none) x = false;
+        else if (take_all) x = true;
+        else if (key[q] > thr) x = true;
+        else if (key[q] == thr) x = rank++ < take_eq;
+        else x = false;
+        in[q] = x;
+        n_in += x ? 1 : 0;
+    }
     int total;
-    int pos = wg_exclusive_scan(n_in, s_wave, total);
+    int pos = wg_exclusive_scan<NT>(n_in, s_wave, total);
     int32_t *row = idx_out + (int64_t)unit * idx_cap;
-    rank = eq_base;
-    for (int blk = lo; blk < hi; ++blk) {
-        if (in_union(blk, rank)) {
-            if (pos < idx_cap) row[pos] = blk;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (in[q]) {
+            if (pos < idx_cap) row[pos] = blk0 + q;
             ++pos;
         }
-    }
-    for (int i = total + tid; i < idx_cap; i += kTopkThreads) row[i] = -1;
+    for (int i = total + tid; i < idx_cap; i += NT) row[i] = -1;
     if (tid == 0) cnt_out[unit] = total < idx_cap ? total : idx_cap;
+}
+
+// Launch shape for the block count: keys of PER consecutive blocks per thread.
+template <int G, bool SOFTMAX>
+static void launch_topk(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
+                        const sa_select_params &p, const float *logits, int64_t nc_pad,
+                        const float2 *stats, int n_chunks, const float *bscore, float *bs_out,
+                        int32_t *idx_out, int idx_cap, int32_t *cnt_out, hipStream_t stream) {
+#define SA_TOPK(NT, PER)                                                                          \
+    hipLaunchKernelGGL((topk_kernel<G, SOFTMAX, NT, PER>), dim3((unsigned)n_units), dim3(NT), 0,   \
+                       stream, Hkv, T_cap, nb_cap, seq_lens, p.top_k, p.n_init, p.n_local, logits, \
+                       nc_pad, stats, n_chunks, bscore, bs_out, idx_out, idx_cap, cnt_out)
+    if (nb_cap <= 256 * 8) SA_TOPK(256, 8);
+    else if (nb_cap <= 1024 * 8) SA_TOPK(1024, 8);
+    else SA_TOPK(1024, 32);
+#undef SA_TOPK
 }
 
 // Top-k + union over precomputed raw block scores, one workgroup per unit
@@ -406,11 +522,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
                      const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,
                      int32_t *cnt_out, hipStream_t stream) {
-    const size_t lds = (size_t)(nb_cap > 0 ? nb_cap : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((topk_kernel<1, false>), dim3((unsigned)n_units), dim3(kTopkThreads), lds,
-                       stream, Hkv, T_cap, nb_cap, seq_lens, p.top_k, p.n_init, p.n_local,
-                       (const float *)nullptr, (int64_t)0, (const float2 *)nullptr, 0, bscore,
-                       (float *)nullptr, idx_out, idx_cap, cnt_out);
+    launch_topk<1, false>(n_units, Hkv, T_cap, nb_cap, seq_lens, p, nullptr, 0, nullptr, 0, bscore,
+                          nullptr, idx_out, idx_cap, cnt_out, stream);
 }
 
 template <typename T, int G>
@@ -425,10 +538,8 @@ static void launch_softmax(const void *sel, int H_sel, const void *Kc, int B, in
         hipLaunchKernelGGL((score_softmax_kernel<T, G>), dim3((unsigned)w.n_chunks, units),
                            dim3(kSelThreads), 0, stream, (const T *)sel, H_sel, (const T *)Kc, Hkv,
                            nc_cap, T_cap, seq_lens, logits, w.nc_pad, stats, w.n_chunks);
-    const size_t lds = (size_t)(w.nb_cap > 0 ? w.nb_cap : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((topk_kernel<G, true>), dim3(units), dim3(kTopkThreads), lds, stream, Hkv,
-                       T_cap, w.nb_cap, seq_lens, p.top_k, p.n_init, p.n_local, logits, w.nc_pad,
-                       stats, w.n_chunks, (const float *)nullptr, bs_out, idx_out, idx_cap, cnt_out);
+    launch_topk<G, true>(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, logits, w.nc_pad, stats,
+                         w.n_chunks, nullptr, bs_out, idx_out, idx_cap, cnt_out, stream);
 }
 
 template <typename T>
@@ -444,11 +555,8 @@ static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B
         hipLaunchKernelGGL(score_raw_kernel<T>, dim3(chunks, units), dim3(kSelThreads), 0, stream,
                            (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap, seq_lens,
                            bscore, w.nb_cap);
-    const size_t lds = (size_t)(w.nb_cap > 0 ? w.nb_cap : 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL((topk_kernel<1, false>), dim3(units), dim3(kTopkThreads), lds, stream, Hkv,
-                       T_cap, w.nb_cap, seq_lens, p.top_k, p.n_init, p.n_local,
-                       (const float *)nullptr, (int64_t)0, (const float2 *)nullptr, 0,
-                       (const float *)bscore, bs_out, idx_out, idx_cap, cnt_out);
+    launch_topk<1, false>(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, nullptr, 0, nullptr, 0,
+                          bscore, bs_out, idx_out, idx_cap, cnt_out, stream);
 }
 
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
