@@ -57,12 +57,53 @@ def main():
     import synth
     from block_sparse_attention_12_amd.pipeline import SparseDecoder
 
+    if args.workload == "copy_calibration":
+        return copy_calibration(args)
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
     w = synth.WORKLOADS[args.workload]
     if w.layers > 1:
         return bench_crosslayer(args, w)
     return bench_decode(args, w)
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch recorded from profiler counters in profiles/<name>_traffic.md,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["sources"].split(","):
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def copy_calibration(args):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch),
+    used to scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler
+    run: bytes per counter unit = 2^30 / counter value of this copy."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(max(1, args.steps)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": a.numel() * 4,
+                                           "bytes_written_per_launch": b.numel() * 4,
+                                           "launches": max(1, args.steps)}}), flush=True)
 
 
 def _events(n):
@@ -191,7 +232,8 @@ def bench_decode(args, w):
         "roofline": {"bound": "hbm",
                      "kernel": "sparse_attn_decode (decode_kernel + combine_kernel)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"{w.name}_decode"),
                      "bytes_per_launch": attn_bytes},
     }
     if not args.no_cpu_baseline:

@@ -11,10 +11,10 @@
 // Mapping of a 256-thread workgroup: wave w owns rows 16w .. 16w+15 of every
 // block; inside a wave, row group r = lane / 16 takes rows 16w + 4i + r
 // (i = 0..3) and each lane owns 8 channels. A block costs each lane 4 K and
-// 4 V loads of 16 B. Loads of the next block are issued before the current
-// block is computed (two register buffers), and the share's block ids are
-// fetched once into lanes and broadcast with readlane, so the only waits in
-// the loop are for data already in flight.
+// 4 V loads of 16 B. Loads of the next two blocks are in flight while a block
+// is computed (three register buffers); block ids are uniform scalar loads,
+// and the loads of an absent block use an out-of-range offset, so every wait
+// in the loop is for data already in flight.
 //
 // Logits for 4 rows x 4 heads are reduced across the 16 lanes of a row by the
 // DPP transposed reduction, leaving one logit per lane (bf16 inputs use the
@@ -203,10 +203,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
         }
         __builtin_amdgcn_wave_barrier();
+        // rescale only when some head's running max moved (wave-uniform test)
+        if (alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[g][c] *= alpha[g];
+                for (int c = 0; c < 8; ++c) acc[g][c] *= alpha[g];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float v8[8];
@@ -220,18 +223,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     };
 
-    // sched_barrier keeps the compiler from sinking a prefetch below the
-    // compute it is meant to overlap
-    BlockRegs<T> bufA, bufB;
+    // Three register buffers: blocks it+1 and it+2 are in flight while block it
+    // is computed. sched_barrier keeps the compiler from sinking a prefetch
+    // below the compute it is meant to overlap.
+    BlockRegs<T> bufA, bufB, bufC;
     issue(bufA, block_id(0));
+    issue(bufB, block_id(1));
 #pragma unroll 1
-    for (int it = 0; it < nblk; it += 2) {
-        issue(bufB, block_id(it + 1));
+    for (int it = 0; it < nblk; it += 3) {
+        issue(bufC, block_id(it + 2));
         __builtin_amdgcn_sched_barrier(0);
         process(bufA);
-        issue(bufA, block_id(it + 2));
+        issue(bufA, block_id(it + 3));
         __builtin_amdgcn_sched_barrier(0);
         if (it + 1 < nblk) process(bufB);
+        issue(bufB, block_id(it + 4));
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + 2 < nblk) process(bufC);
     }
 
     // ---- merge inside the wave: l over lanes of one head, acc over row groups
