@@ -51,7 +51,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kPfThreads = 256;
 constexpr int kPfG = 4;
-constexpr int kVtStride = 68;          // bf16 per transposed V row (64 keys + pad)
 constexpr float kLog2eF = 1.44269504088896340736f;
 constexpr float kLn2F = 0.69314718055994530942f;
 
@@ -82,31 +81,50 @@ __device__ __forceinline__ bf16x8_t lds_frag_rows(const bf16_t *lds, int m_row, 
     return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + m_row * kD + chunk * 8));
 }
 
-// ---- V staged transposed: Vt[channel][key], row stride kVtStride bf16
-__device__ __forceinline__ void stage_v_transposed(bf16_t *vt, __amdgpu_buffer_rsrc_t src,
-                                                   int64_t row0, int tid) {
+// ---- DMA of one 64-row x 128-channel bf16 tile straight into LDS, in the same
+// swizzled row-major layout as above. Each 16-byte load of lane i of a wave lands
+// at the instruction's LDS base + 16 i; instruction r of wave w fills chunk slots
+// (4r + w) * 64 + lane, and each slot fetches the source chunk that belongs there.
+// Rows outside the buffer read as zeros (buffer range check).
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma_tile_swizzled(bf16_t *lds, __amdgpu_buffer_rsrc_t src,
+                                                  int64_t row0, int wave, int lane) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int id = r * kPfThreads + tid;
-        const int key = id >> 4, chunk = id & 15;
-        const uint32_t off = row_offset(row0 + key, kD * 2, chunk * 16);
-        Raw8<bf16_t> x;
-        load_raw(src, off, x);
-        const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            vt[(chunk * 8 + 2 * j) * kVtStride + key] = (bf16_t)(w[j] & 0xffffu);
-            vt[(chunk * 8 + 2 * j + 1) * kVtStride + key] = (bf16_t)(w[j] >> 16);
-        }
+        const int slot0 = (4 * r + wave) * 64;
+        const int row = (slot0 >> 4) + (lane >> 4);
+        const int chunk = (lane & 15) ^ (row & 15);
+        const uint32_t off = row_offset(row0 + row, kD * 2, chunk * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t *)(lds + slot0 * 8), 16, off, 0, 0, 0);
     }
 }
 
-// A operand of V^T for the value product: channel row ch, permuted keys of
-// step kk: 32kk + 4g .. +3 and 32kk + 16 + 4g .. +3
-__device__ __forceinline__ bf16x8_t vt_frag(const bf16_t *vt, int ch, int kk, int g) {
-    const uint2 lo = *reinterpret_cast<const uint2 *>(vt + ch * kVtStride + 32 * kk + 4 * g);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(vt + ch * kVtStride + 32 * kk + 16 + 4 * g);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+// A operand of V^T for the value product from a swizzled row-major V tile:
+// channel row 16 ct + (l%16), permuted keys of step kk: slots 0..3 hold keys
+// 32kk + 4g .. +3, slots 4..7 keys 32kk + 16 + 4g .. +3. ds_read_b64_tr_b16
+// transposes inside each 16-lane group: output lane i, element j comes from
+// source lane 4j + i/4, element i%4, so source lane s reads key row
+// key0 + s/4 at channels 16 ct + 4 (s%4) .. +3.
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ bf16x8_t vt_frag_tr(const bf16_t *lds, int ct, int kk, int g, int c16) {
+    s16x4_t h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int row = 32 * kk + 16 * half + 4 * g + (c16 >> 2);
+        const int ch = 16 * ct + 4 * (c16 & 3);
+        const int elem = row * kD + (((ch >> 3) ^ (row & 15)) << 3) + (ch & 7);
+        h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + elem));
+    }
+    typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+    const s16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Two fp32 values to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -332,18 +350,44 @@ __global__ __launch_bounds__(kPfThreads) void prefill_union_kernel(
 
 // ------------------------------------------------------------------ attention
 
+// LDS ring: kPfStages stages, each holding the K tile and the V tile of one block.
+constexpr int kPfStages = 3;
+constexpr int kPfStageElems = 2 * 64 * kD;
+// A row's softmax reference only moves when a block's row max exceeds it by more
+// than this (log2 units): probabilities then stay below 2^64, far from fp32 /
+// bf16 overflow, and the rescaling of the output accumulators is rare. The result is the same: numerator and
+// denominator share the reference.
+constexpr float kRescaleSlack = 64.f;
+// Passes over a tile's blocks: each redo raises some reference by more than the
+// slack and the second pass can no longer outgrow any (the cap only bounds the loop).
+constexpr int kPfMaxPasses = 4;
+
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// wait until at most 8 / 0 vector-memory operations of this wave are in flight.
+constexpr int kWaitVm8 = 0x0F78;
+constexpr int kWaitVm0 = 0x0F70;
+
+// LDS-only workgroup barrier: orders LDS accesses without waiting for the
+// in-flight DMA of later blocks (that wait is explicit, per wave, before it).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    __shared__ __align__(16) bf16_t sK[64 * kD];
-    __shared__ __align__(16) bf16_t sVt[kD * kVtStride];
+    __shared__ __align__(16) bf16_t ring[kPfStages * kPfStageElems];
+    __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int64_t q_first = (int64_t)tile * 64;
     const int64_t bt = q_start / kBlock + tile;
+    if (tid < kPfMaxPasses) s_redo[tid] = 0;
 
     bf16x8_t qf[4][4];
     load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
@@ -351,12 +395,17 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qloc[rt] = 16 * wave + 4 * rt + (c16 >> 2);
 
+    // Rows the DMA does not fill (past the end of K / V) must hold finite values:
+    // zero the ring once.
+    for (int i = tid; i < kPfStages * kPfStageElems / 8; i += kPfThreads)
+        reinterpret_cast<uint4 *>(ring)[i] = make_uint4(0u, 0u, 0u, 0u);
+
     f32x4_t o[8][4];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[4], lsum[4];
+    float m[4], lsum[4];                           // reference (log2 units) and partial sum per row
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; lsum[rt] = 0.f; }
 
@@ -365,69 +414,166 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
     const int32_t *ids = tile_idx + (int64_t)blockIdx.x * tile_cap;
     int n = tile_cnt[blockIdx.x];
     n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
+    __syncthreads();                               // ring zeroed before any DMA lands
 
-    for (int e = 0; e < n; ++e) {
-        const int64_t blk = ids[e];
-        __syncthreads();
-        stage_rows_swizzled(sK, rK, blk * kBlock, tid);
-        stage_v_transposed(sVt, rV, blk * kBlock, tid);
-        __syncthreads();
-        f32x4_t s[4][4];
-        scores_64x64(s, sK, qf, lane);
-        const bool diag = blk == bt;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = 16 * mt + 4 * g + i;
-                    float x = s[mt][rt][i] * qscale;
-                    if (diag && key > qloc[rt]) x = -INFINITY;          // causal: key t <= query p
-                    s[mt][rt][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float mn = fmaxf(m[rt], mx);
-            const float alpha = (m[rt] == -INFINITY) ? 0.f : exp2f(m[rt] - mn);
-            m[rt] = mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float x = s[mt][rt][i];
-                    const float p = (x == -INFINITY) ? 0.f : exp2f(x - mn);
-                    s[mt][rt][i] = p;
-                    ps += p;
-                }
-            lsum[rt] = lsum[rt] * alpha + ps;
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[ct][rt][i] *= alpha;
-        }
-        // P as B operands: step kk holds keys 32kk + 4g + i (mt = 2kk) then 32kk + 16 + 4g + i
+    auto dma_block = [&](int stage, int64_t blk) {
+        bf16_t *base = ring + stage * kPfStageElems;
+        dma_tile_swizzled(base, rK, blk * kBlock, wave, lane);
+        dma_tile_swizzled(base + 64 * kD, rV, blk * kBlock, wave, lane);
+    };
+
+    // Probabilities relative to the row references, packed to bf16 as B operands
+    // (step kk holds keys 32kk + 4g + i (mt = 2kk) then 32kk + 16 + 4g + i), and
+    // the value product for one block.
+    auto accumulate_block = [&](const f32x4_t (&sc)[4][4], const bf16_t *sV) {
         bf16x8_t pb[2][4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int rt = 0; rt < 4; ++rt) {
+            const float nm = -m[rt];
+            float ps = 0.f;
+            float p[4][4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const f32x4_t &a = s[2 * kk][rt];
-                const f32x4_t &b = s[2 * kk + 1][rt];
-                pb[kk][rt] = as_bf16x8(make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                                                  pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])));
-            }
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][rt][i], qscale, nm));
+                    ps += p[mt][i];
+                }
+            lsum[rt] += ps;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                pb[kk][rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[2 * kk][0], p[2 * kk][1]),
+                                                  cvt_pk_bf16(p[2 * kk][2], p[2 * kk][3]),
+                                                  cvt_pk_bf16(p[2 * kk + 1][0], p[2 * kk + 1][1]),
+                                                  cvt_pk_bf16(p[2 * kk + 1][2], p[2 * kk + 1][3])));
+        }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_t a = vt_frag(sVt, 16 * ct + c16, kk, g);
+                const bf16x8_t a = vt_frag_tr(sV, ct, kk, g, c16);
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[kk][rt], o[ct][rt]);
             }
+    };
+
+    // One half block (32 keys): scores S^T = K Q^T, causal mask on the diagonal
+    // block, probabilities against the row references, value product. The
+    // accumulators are never touched outside the matrix cores: when a row max
+    // outgrows its reference by more than the slack, the reference is raised,
+    // this pass's sums are void (redo) and the workgroup runs the blocks again
+    // with the raised references, which no block can then outgrow.
+    bool redo = false;
+    auto half_step = [&](const bf16_t *sK, const bf16_t *sV, int hh, bool diag) {
+        f32x4_t s[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8_t a = lds_frag_rows(sK, 32 * hh + 16 * j + c16, ks, g);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
+            }
+        if (diag) {                                // causal: key <= query inside the tile's own block
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                int q = qloc[rt] - 32 * hh - 4 * g;
+                asm volatile("" : "+v"(q));        // computed here, not hoisted out of the loop as masks
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * j + i > q) s[j][rt][i] = -INFINITY;
+            }
+        }
+        float lmx[4];
+        bool fresh = false, grow = false;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                                   fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
+            lmx[rt] = mx * qscale;
+            fresh |= m[rt] == -INFINITY;
+            grow |= lmx[rt] > m[rt] + kRescaleSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(fresh | grow)) {
+            // Raise references to the row max (over the 4 lanes sharing a row).
+            // A row seeing its first keys has zero sums, so only a row that had
+            // a finite reference voids the pass.
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float mx = lmx[rt];
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                if (m[rt] == -INFINITY) m[rt] = mx;
+                else if (mx > m[rt] + kRescaleSlack) { m[rt] = mx; redo = true; }
+            }
+        }
+        // probabilities as bf16 B operands: keys 32hh + 4g + i (j = 0), then
+        // 32hh + 16 + 4g + i (j = 1). A row with no visible key so far keeps a
+        // -inf reference and gets zeros.
+        bf16x8_t pb[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
+            float p[2][4];
+            float ps = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[j][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][rt][i], qscale, nm));
+                    ps += p[j][i];
+                }
+            lsum[rt] += ps;
+            pb[rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
+                                          cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const bf16x8_t a = vt_frag_tr(sV, ct, hh, g, c16);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[rt], o[ct][rt]);
+        }
+    };
+
+    for (int pass = 0; pass < kPfMaxPasses; ++pass) {
+        if (pass > 0) {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) lsum[rt] = 0.f;
+            redo = false;
+        }
+        if (n > 0) dma_block(0, ids[0]);
+        if (n > 1) dma_block(1, ids[1]);
+        int st = 0;                                // stage of block e
+        for (int e = 0; e < n; ++e) {
+            // this wave's DMA of block e is done (block e+1's 8 loads may still
+            // fly); after the barrier every wave's is, and every wave has
+            // finished block e-1, whose stage the DMA of block e+2 reuses
+            if (e + 1 < n) __builtin_amdgcn_s_waitcnt(kWaitVm8);
+            else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            lds_barrier();
+            if (e + 2 < n) dma_block(st == 0 ? 2 : st - 1, ids[e + 2]);
+            const bf16_t *sK = ring + st * kPfStageElems;
+            const bf16_t *sV = sK + 64 * kD;
+            const bool diag = ids[e] == bt;
+            st = st == kPfStages - 1 ? 0 : st + 1;
+            half_step(sK, sV, 0, diag);
+            half_step(sK, sV, 1, diag);
+        }
+        // workgroup-wide: run again if any wave voided its sums
+        __syncthreads();
+        if (redo && lane == 0) s_redo[pass] = 1;
+        __syncthreads();
+        if (s_redo[pass] == 0) break;
     }
 
     // finish: total sum per row over the 4 lanes sharing it, then write

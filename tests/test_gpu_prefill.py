@@ -137,3 +137,51 @@ def test_prefill_attend_reuses_tile_sets_across_layers():
                                            block_tokens(blocks, q_start + i + 1), 1.0)
             assert_close(On[i, 4 * h:4 * h + 4], o, "bf16", f"reuse query {i}")
             assert_close(Ln[i, 4 * h:4 * h + 4], l, "bf16", f"reuse lse {i}")
+
+
+def test_prefill_attend_large_logit_jump_between_blocks():
+    """A later block whose scores exceed a row's first block by far more than the
+    kernel's lazy-reference slack (hundreds of log2 units): the workgroup must
+    redo its pass with raised references and still match the oracle; also in
+    the diagonal block of one tile."""
+    T, q_start = 2048, 1024
+    Q, K, V, _ = _inputs(T=T, q_start=q_start, seed=7)
+    Hkv, Tq = K.shape[0], Q.shape[0]
+    n_tiles = Tq // 64
+    # a shared direction u: every query gets +0.5 u, blocks 9 and 20 get keys
+    # along u (block 20 = tile 4's own block, larger still), so their scores
+    # jump by ~150 and ~300 nats over block 0's
+    gen = torch.Generator().manual_seed(70)
+    u = torch.randn(128, generator=gen, dtype=torch.float64)
+    u = (u / u.norm()).to(DEV)
+    Q = (Q.double() + 0.5 * u).to(torch.bfloat16).contiguous()
+    K = K.clone()
+    for b, mag in ((9, 300.0), (20, 600.0)):
+        K[:, 64 * b:64 * b + 64] = (mag * u + 0.05 * K[:, 64 * b:64 * b + 64].double()).to(torch.bfloat16)
+    cap = 8
+    tidx = torch.full((n_tiles, Hkv, cap), -1, dtype=torch.int32)
+    tcnt = torch.zeros((n_tiles, Hkv), dtype=torch.int32)
+    sets = {}
+    for t in range(n_tiles):
+        bt = q_start // 64 + t
+        blocks = sorted({0, 3, 9, bt - 1, bt} | ({20} if bt >= 20 else set()))
+        sets[t] = blocks
+        for h in range(Hkv):
+            tidx[t, h, :len(blocks)] = torch.tensor(blocks, dtype=torch.int32)
+            tcnt[t, h] = len(blocks)
+    O, L = sa.prefill_attend(Q, q_start, K, V, tidx.to(DEV), tcnt.to(DEV))
+    torch.cuda.synchronize()
+    Qn, Kn, Vn = to_np(Q), to_np(K), to_np(V)
+    On, Ln = to_np(O), L.cpu().numpy()
+    jumped = 0
+    for i in list(range(0, Tq, 5)) + list(range(256, 320)):
+        t = i // 64
+        for h in range(Hkv):
+            q = Qn[i, 4 * h:4 * h + 4]
+            first = (q @ Kn[h, 0:64].T).max(axis=1)
+            later = (q @ Kn[h, 64 * 9:64 * 10].T).max(axis=1)
+            jumped += int(np.any((later - first) / np.log(2) > 128))
+            o, l = oracle.sparse_attention(q, Kn[h], Vn[h], block_tokens(sets[t], q_start + i + 1), 1.0)
+            assert_close(On[i, 4 * h:4 * h + 4], o, "bf16", f"jump query {i} kvh {h}")
+            assert_close(Ln[i, 4 * h:4 * h + 4], l, "bf16", f"jump lse {i} kvh {h}")
+    assert jumped > 50, jumped                    # the case really exercises the raised references
