@@ -41,6 +41,8 @@
 // the same XCD (round-robin dispatch over 8 XCDs) and share its L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -350,9 +352,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_union_kernel(
 
 // ------------------------------------------------------------------ attention
 
-// LDS ring: kPfStages stages, each holding the K tile and the V tile of one block.
-constexpr int kPfStages = 3;
-constexpr int kPfStageElems = 2 * 64 * kD;
+// LDS ring of 3 stages, each holding the K tile and the V tile of one block.
 // A row's softmax reference only moves when a block's row max exceeds it by more
 // than this (log2 units): probabilities then stay below 2^64, far from fp32 /
 // bf16 overflow, and the rescaling of the output accumulators is rare. The result is the same: numerator and
@@ -363,16 +363,19 @@ constexpr float kRescaleSlack = 64.f;
 constexpr int kPfMaxPasses = 4;
 
 // s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
-// wait until at most 8 / 0 vector-memory operations of this wave are in flight.
-constexpr int kWaitVm8 = 0x0F78;
-constexpr int kWaitVm0 = 0x0F70;
+// every LDS access of this wave done and at most 8 / 0 vector-memory
+// operations (the DMA of later blocks) still in flight.
+constexpr int kWaitVm8Lgkm0 = 0x0078;
+constexpr int kWaitVm0Lgkm0 = 0x0070;
 
-// LDS-only workgroup barrier: orders LDS accesses without waiting for the
-// in-flight DMA of later blocks (that wait is explicit, per wave, before it).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+// Workgroup barrier for the block ring. The explicit wait before it covers what
+// the next stage reuse needs (this wave's LDS reads done, its DMA of the block
+// about to be read landed); no fence, so the DMA of later blocks keeps flying.
+// The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    asm volatile("" ::: "memory");
 }
 
 __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
@@ -380,7 +383,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    __shared__ __align__(16) bf16_t ring[kPfStages * kPfStageElems];
+    // The ring's stages are separate LDS objects so the compiler can tell that
+    // reads of one stage do not depend on the DMA still filling the others.
+    __shared__ __align__(16) bf16_t sK0[64 * kD], sV0[64 * kD], sK1[64 * kD], sV1[64 * kD],
+        sK2[64 * kD], sV2[64 * kD];
     __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -397,8 +403,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
 
     // Rows the DMA does not fill (past the end of K / V) must hold finite values:
     // zero the ring once.
-    for (int i = tid; i < kPfStages * kPfStageElems / 8; i += kPfThreads)
-        reinterpret_cast<uint4 *>(ring)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < 64 * kD / 8; i += kPfThreads) {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4 *>(sK0)[i] = z;
+        reinterpret_cast<uint4 *>(sV0)[i] = z;
+        reinterpret_cast<uint4 *>(sK1)[i] = z;
+        reinterpret_cast<uint4 *>(sV1)[i] = z;
+        reinterpret_cast<uint4 *>(sK2)[i] = z;
+        reinterpret_cast<uint4 *>(sV2)[i] = z;
+    }
 
     f32x4_t o[8][4];
 #pragma unroll
@@ -411,16 +424,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
 
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
-    const int32_t *ids = tile_idx + (int64_t)blockIdx.x * tile_cap;
+    // block ids through the constant address space: scalar loads, whose waits
+    // do not also wait for the ring's DMA
+    typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+    const_i32_t *ids = (const_i32_t *)(tile_idx + (int64_t)blockIdx.x * tile_cap);
     int n = tile_cnt[blockIdx.x];
     n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
     __syncthreads();                               // ring zeroed before any DMA lands
 
-    auto dma_block = [&](int stage, int64_t blk) {
-        bf16_t *base = ring + stage * kPfStageElems;
-        dma_tile_swizzled(base, rK, blk * kBlock, wave, lane);
-        dma_tile_swizzled(base + 64 * kD, rV, blk * kBlock, wave, lane);
+    auto stage_k = [&](auto S) -> bf16_t * {
+        constexpr int st = decltype(S)::value;
+        if constexpr (st == 0) return sK0;
+        else if constexpr (st == 1) return sK1;
+        else return sK2;
     };
+    auto stage_v = [&](auto S) -> bf16_t * {
+        constexpr int st = decltype(S)::value;
+        if constexpr (st == 0) return sV0;
+        else if constexpr (st == 1) return sV1;
+        else return sV2;
+    };
+    auto dma_block = [&](auto S, int64_t blk) {
+        dma_tile_swizzled(stage_k(S), rK, blk * kBlock, wave, lane);
+        dma_tile_swizzled(stage_v(S), rV, blk * kBlock, wave, lane);
+    };
+    const std::integral_constant<int, 0> kSt0{};
+    const std::integral_constant<int, 1> kSt1{};
+    const std::integral_constant<int, 2> kSt2{};
 
     // Probabilities relative to the row references, packed to bf16 as B operands
     // (step kk holds keys 32kk + 4g + i (mt = 2kk) then 32kk + 16 + 4g + i), and
@@ -551,23 +581,31 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
             for (int rt = 0; rt < 4; ++rt) lsum[rt] = 0.f;
             redo = false;
         }
-        if (n > 0) dma_block(0, ids[0]);
-        if (n > 1) dma_block(1, ids[1]);
-        int st = 0;                                // stage of block e
-        for (int e = 0; e < n; ++e) {
-            // this wave's DMA of block e is done (block e+1's 8 loads may still
-            // fly); after the barrier every wave's is, and every wave has
-            // finished block e-1, whose stage the DMA of block e+2 reuses
-            if (e + 1 < n) __builtin_amdgcn_s_waitcnt(kWaitVm8);
-            else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            lds_barrier();
-            if (e + 2 < n) dma_block(st == 0 ? 2 : st - 1, ids[e + 2]);
-            const bf16_t *sK = ring + st * kPfStageElems;
-            const bf16_t *sV = sK + 64 * kD;
-            const bool diag = ids[e] == bt;
-            st = st == kPfStages - 1 ? 0 : st + 1;
-            half_step(sK, sV, 0, diag);
-            half_step(sK, sV, 1, diag);
+        // (an id of -1 fetches nothing: every row is out of range and reads as zeros)
+        dma_block(kSt0, n > 0 ? ids[0] : -1);
+        dma_block(kSt1, n > 1 ? ids[1] : -1);
+        // Block e sits in stage e % 3. Before the barrier: this wave's DMA of
+        // block e landed (block e+1's 8 loads may still fly); after it every
+        // wave's has, and every wave has finished block e-1, whose stage the
+        // DMA of block e+2 then reuses.
+        int e = 0;
+        auto block_step = [&](auto S) {
+            constexpr int st = decltype(S)::value;
+            const std::integral_constant<int, (st + 2) % 3> S2{};
+            __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
+            ring_barrier();
+            dma_block(S2, e + 2 < n ? ids[__builtin_amdgcn_readfirstlane(e + 2)] : -1);
+            const bool diag = ids[__builtin_amdgcn_readfirstlane(e)] == bt;
+            half_step(stage_k(S), stage_v(S), 0, diag);
+            half_step(stage_k(S), stage_v(S), 1, diag);
+            ++e;
+        };
+        while (e < n) {
+            block_step(kSt0);
+            if (e >= n) break;
+            block_step(kSt1);
+            if (e >= n) break;
+            block_step(kSt2);
         }
         // workgroup-wide: run again if any wave voided its sums
         __syncthreads();
