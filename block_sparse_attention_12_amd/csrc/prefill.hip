@@ -368,6 +368,19 @@ constexpr int kPfMaxPasses = 4;
 constexpr int kWaitVm8Lgkm0 = 0x0078;
 constexpr int kWaitVm0Lgkm0 = 0x0070;
 
+// Scheduling hint for one region: its LDS reads first, then each of its
+// N_MFMA matrix instructions followed by up to 6 vector ALU instructions, so the
+// vector work issues while the matrix core is busy.
+template <int N_MFMA, int N_DS>
+__device__ __forceinline__ void interleave_mfma_valu() {
+    __builtin_amdgcn_sched_group_barrier(0x100, N_DS, 0);        // DS reads
+#pragma unroll
+    for (int i = 0; i < N_MFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);       // VALU
+    }
+}
+
 // Workgroup barrier for the block ring. The explicit wait before it covers what
 // the next stage reuse needs (this wave's LDS reads done, its DMA of the block
 // about to be read landed); no fence, so the DMA of later blocks keeps flying.
@@ -452,50 +465,9 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
     const std::integral_constant<int, 1> kSt1{};
     const std::integral_constant<int, 2> kSt2{};
 
-    // Probabilities relative to the row references, packed to bf16 as B operands
-    // (step kk holds keys 32kk + 4g + i (mt = 2kk) then 32kk + 16 + 4g + i), and
-    // the value product for one block.
-    auto accumulate_block = [&](const f32x4_t (&sc)[4][4], const bf16_t *sV) {
-        bf16x8_t pb[2][4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const float nm = -m[rt];
-            float ps = 0.f;
-            float p[4][4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][rt][i], qscale, nm));
-                    ps += p[mt][i];
-                }
-            lsum[rt] += ps;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                pb[kk][rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[2 * kk][0], p[2 * kk][1]),
-                                                  cvt_pk_bf16(p[2 * kk][2], p[2 * kk][3]),
-                                                  cvt_pk_bf16(p[2 * kk + 1][0], p[2 * kk + 1][1]),
-                                                  cvt_pk_bf16(p[2 * kk + 1][2], p[2 * kk + 1][3])));
-        }
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8_t a = vt_frag_tr(sV, ct, kk, g, c16);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[kk][rt], o[ct][rt]);
-            }
-    };
-
-    // One half block (32 keys): scores S^T = K Q^T, causal mask on the diagonal
-    // block, probabilities against the row references, value product. The
-    // accumulators are never touched outside the matrix cores: when a row max
-    // outgrows its reference by more than the slack, the reference is raised,
-    // this pass's sums are void (redo) and the workgroup runs the blocks again
-    // with the raised references, which no block can then outgrow.
-    bool redo = false;
-    auto half_step = [&](const bf16_t *sK, const bf16_t *sV, int hh, bool diag) {
-        f32x4_t s[2][4];
+    // Scores S^T = K Q^T of one half block (32 keys, 32hh .. 32hh+31 of the tile):
+    // s[j][rt][i] = score of row 16 rt + (l%16) with key 32hh + 16j + 4g + i.
+    auto half_scores = [&](f32x4_t (&s)[2][4], const bf16_t *sK, int hh, int g, int c16) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -508,48 +480,33 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
             }
-        if (diag) {                                // causal: key <= query inside the tile's own block
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                int q = qloc[rt] - 32 * hh - 4 * g;
-                asm volatile("" : "+v"(q));        // computed here, not hoisted out of the loop as masks
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * j + i > q) s[j][rt][i] = -INFINITY;
-            }
-        }
-        float lmx[4];
-        bool fresh = false, grow = false;
+    };
+    // causal mask inside the tile's own block: key <= query
+    auto mask_causal = [&](f32x4_t (&s)[2][4], int hh) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
-                                   fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
-            lmx[rt] = mx * qscale;
-            fresh |= m[rt] == -INFINITY;
-            grow |= lmx[rt] > m[rt] + kRescaleSlack;
-        }
-        if (__builtin_amdgcn_ballot_w64(fresh | grow)) {
-            // Raise references to the row max (over the 4 lanes sharing a row).
-            // A row seeing its first keys has zero sums, so only a row that had
-            // a finite reference voids the pass.
+            int q = qloc[rt] - 32 * hh - 4 * g;
+            asm volatile("" : "+v"(q));            // compared here, not hoisted as lane masks
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                float mx = lmx[rt];
-                mx = fmaxf(mx, shfl_xor(mx, 16));
-                mx = fmaxf(mx, shfl_xor(mx, 32));
-                if (m[rt] == -INFINITY) m[rt] = mx;
-                else if (mx > m[rt] + kRescaleSlack) { m[rt] = mx; redo = true; }
-            }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * j + i > q) s[j][rt][i] = -INFINITY;
         }
-        // probabilities as bf16 B operands: keys 32hh + 4g + i (j = 0), then
-        // 32hh + 16 + 4g + i (j = 1). A row with no visible key so far keeps a
-        // -inf reference and gets zeros.
-        bf16x8_t pb[4];
+    };
+    auto half_max = [&](const f32x4_t (&s)[2][4], int rt) {
+        return fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                     fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
+    };
+    // Probabilities against the row references as bf16 B operands (keys
+    // 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i), row sums; the lane's
+    // running row max feeds the end-of-pass check.
+    float mrun[4];
+    auto half_probs = [&](bf16x8_t (&pb)[4], const f32x4_t (&s)[2][4]) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const float nm = m[rt] == -INFINITY ? 0.f : -m[rt];
+            mrun[rt] = fmaxf(mrun[rt], half_max(s, rt));
+            const float nm = -m[rt];
             float p[2][4];
             float ps = 0.f;
 #pragma unroll
@@ -563,6 +520,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
             pb[rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
+    };
+    auto half_values = [&](const bf16x8_t (&pb)[4], const bf16_t *sV, int hh, int g, int c16) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const bf16x8_t a = vt_frag_tr(sV, ct, hh, g, c16);
@@ -570,17 +529,28 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
             for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[rt], o[ct][rt]);
         }
     };
+    auto half_accumulate = [&](const f32x4_t (&s)[2][4], const bf16_t *sV, int hh) {
+        bf16x8_t pb[4];
+        half_probs(pb, s);
+        half_values(pb, sV, hh, g, c16);
+    };
 
+    // The block steps have no branches. References: the row max of the first
+    // half block; a row whose max later exceeds its reference by more than the
+    // slack (checked once per pass, from the running maxima) gets the larger
+    // reference and the workgroup runs its blocks again (the pass's sums are
+    // void; the accumulators are never rescaled, so they stay in the matrix
+    // cores' registers). No block can outgrow the raised references.
+    // The tile's own block, last in the ascending set, takes the causal mask.
+    const bool last_diag = n > 0 && ids[n - 1] == bt;
+    const int n_main = last_diag ? n - 1 : n;
     for (int pass = 0; pass < kPfMaxPasses; ++pass) {
-        if (pass > 0) {
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) lsum[rt] = 0.f;
-            redo = false;
-        }
+        for (int rt = 0; rt < 4; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
         // (an id of -1 fetches nothing: every row is out of range and reads as zeros)
         dma_block(kSt0, n > 0 ? ids[0] : -1);
         dma_block(kSt1, n > 1 ? ids[1] : -1);
@@ -588,6 +558,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
         // block e landed (block e+1's 8 loads may still fly); after it every
         // wave's has, and every wave has finished block e-1, whose stage the
         // DMA of block e+2 then reuses.
+        if (pass == 0 && n > 0) {
+            __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
+            ring_barrier();
+            f32x4_t s[2][4];
+            half_scores(s, sK0, 0, g, c16);
+            if (n == 1 && last_diag) mask_causal(s, 0);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                float mx = half_max(s, rt) * qscale;
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                m[rt] = mx == -INFINITY ? 0.f : mx;
+            }
+        }
         int e = 0;
         auto block_step = [&](auto S) {
             constexpr int st = decltype(S)::value;
@@ -595,21 +579,57 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
             __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
             ring_barrier();
             dma_block(S2, e + 2 < n ? ids[__builtin_amdgcn_readfirstlane(e + 2)] : -1);
-            const bool diag = ids[__builtin_amdgcn_readfirstlane(e)] == bt;
-            half_step(stage_k(S), stage_v(S), 0, diag);
-            half_step(stage_k(S), stage_v(S), 1, diag);
+            // Software pipeline over the two halves, so that the matrix cores
+            // run while the vector units compute probabilities:
+            //   scores h0 | scores h1 + probs h0 | values h0 + probs h1 | values h1
+            f32x4_t s0[2][4], s1[2][4];
+            bf16x8_t pb0[4], pb1[4];
+            // lane fields recomputed per step: LDS addresses are not kept live
+            // across the loop for every stage
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int lg = ln >> 4, lc = ln & 15;
+            half_scores(s0, stage_k(S), 0, lg, lc);
+            half_probs(pb0, s0);
+            half_values(pb0, stage_v(S), 0, lg, lc);
+            __builtin_amdgcn_sched_barrier(0);
+            half_scores(s1, stage_k(S), 1, lg, lc);
+            half_probs(pb1, s1);
+            half_values(pb1, stage_v(S), 1, lg, lc);
             ++e;
         };
-        while (e < n) {
+        while (e < n_main) {
             block_step(kSt0);
-            if (e >= n) break;
+            if (e >= n_main) break;
             block_step(kSt1);
-            if (e >= n) break;
+            if (e >= n_main) break;
             block_step(kSt2);
         }
-        // workgroup-wide: run again if any wave voided its sums
+        if (last_diag) {                           // e = n - 1, stage e % 3
+            __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+            ring_barrier();
+            const int st = e % 3;
+            const bf16_t *sK = st == 0 ? sK0 : (st == 1 ? sK1 : sK2);
+            const bf16_t *sV = st == 0 ? sV0 : (st == 1 ? sV1 : sV2);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                f32x4_t s[2][4];
+                half_scores(s, sK, hh, g, c16);
+                mask_causal(s, hh);
+                half_accumulate(s, sV, hh);
+            }
+        }
+        // end of pass: raise references a row outgrew; workgroup-wide redo
+        bool redo = false;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float mx = mrun[rt] * qscale;
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            if (mx > m[rt] + kRescaleSlack) { m[rt] = mx; redo = true; }
+        }
         __syncthreads();
-        if (redo && lane == 0) s_redo[pass] = 1;
+        if (redo) s_redo[pass] = 1;
         __syncthreads();
         if (s_redo[pass] == 0) break;
     }
