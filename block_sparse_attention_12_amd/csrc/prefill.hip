@@ -391,7 +391,7 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_attn_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
@@ -410,6 +410,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
 
     bf16x8_t qf[4][4];
     load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
+    // The query fragments only feed the matrix cores: keep them in AGPRs and the
+    // VGPRs free for the vector work and LDS prefetch.
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qf[rt][ks]));
     int qloc[4];                                   // query offset inside the tile, per row tile
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qloc[rt] = 16 * wave + 4 * rt + (c16 >> 2);
@@ -589,12 +595,19 @@ __global__ __launch_bounds__(kPfThreads) void prefill_attn_kernel(
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int lg = ln >> 4, lc = ln & 15;
+            // Software pipeline over the two halves, so that the matrix cores
+            // run while the vector units compute probabilities:
+            //   scores h0 | scores h1 + probs h0 | values h0 + probs h1 | values h1
             half_scores(s0, stage_k(S), 0, lg, lc);
-            half_probs(pb0, s0);
-            half_values(pb0, stage_v(S), 0, lg, lc);
             __builtin_amdgcn_sched_barrier(0);
             half_scores(s1, stage_k(S), 1, lg, lc);
+            half_probs(pb0, s0);
+            interleave_mfma_valu<32, 8>();
+            __builtin_amdgcn_sched_barrier(0);
+            half_values(pb0, stage_v(S), 0, lg, lc);
             half_probs(pb1, s1);
+            interleave_mfma_valu<32, 16>();
+            __builtin_amdgcn_sched_barrier(0);
             half_values(pb1, stage_v(S), 1, lg, lc);
             ++e;
         };
