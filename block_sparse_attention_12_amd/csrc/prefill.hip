@@ -352,43 +352,43 @@ __global__ __launch_bounds__(kPfThreads) void prefill_union_kernel(
 
 // ------------------------------------------------------------------ attention
 
-// LDS ring of 3 stages, each holding the K tile and the V tile of one block.
 // A row's softmax reference only moves when a block's row max exceeds it by more
 // than this (log2 units): probabilities then stay below 2^64, far from fp32 /
-// bf16 overflow, and the rescaling of the output accumulators is rare. The result is the same: numerator and
-// denominator share the reference.
+// bf16 overflow. The result does not depend on the reference: numerator and
+// denominator share it.
 constexpr float kRescaleSlack = 64.f;
 // Passes over a tile's blocks: each redo raises some reference by more than the
 // slack and the second pass can no longer outgrow any (the cap only bounds the loop).
 constexpr int kPfMaxPasses = 4;
+constexpr int kPfTileElems = 64 * kD;             // one 64 x 128 bf16 tile (16 KB)
 
-// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
-// every LDS access of this wave done and at most 8 / 0 vector-memory
-// operations (the DMA of later blocks) still in flight.
-constexpr int kWaitVm8Lgkm0 = 0x0078;
-constexpr int kWaitVm0Lgkm0 = 0x0070;
-
-// Scheduling hint for one region: its LDS reads first, then each of its
-// N_MFMA matrix instructions followed by up to 6 vector ALU instructions, so the
-// vector work issues while the matrix core is busy.
-template <int N_MFMA, int N_DS>
-__device__ __forceinline__ void interleave_mfma_valu() {
-    __builtin_amdgcn_sched_group_barrier(0x100, N_DS, 0);        // DS reads
+// Global -> register half of the block staging: this thread's 4 K and 4 V chunks
+// of one block, in the swizzled order of the LDS tile (thread (w, l), load r
+// fills chunk slot (4r + w) * 64 + l). Rows outside the buffer read as zeros.
+struct BlockRegs {
+    Raw8<bf16_t> k[4], v[4];
+};
+__device__ __forceinline__ void load_block_regs(BlockRegs &br, __amdgpu_buffer_rsrc_t rK,
+                                                __amdgpu_buffer_rsrc_t rV, int64_t blk, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < N_MFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);       // VALU
+    for (int r = 0; r < 4; ++r) {
+        const int slot0 = (4 * r + wave) * 64;
+        const int row = (slot0 >> 4) + (lane >> 4);
+        const int chunk = (lane & 15) ^ (row & 15);
+        const uint32_t off = row_offset(blk * kBlock + row, kD * 2, chunk * 16);
+        load_raw(rK, off, br.k[r]);
+        load_raw(rV, off, br.v[r]);
     }
 }
-
-// Workgroup barrier for the block ring. The explicit wait before it covers what
-// the next stage reuse needs (this wave's LDS reads done, its DMA of the block
-// about to be read landed); no fence, so the DMA of later blocks keeps flying.
-// The empty asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void ring_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+// Register -> LDS half: 16 B per lane, consecutive lanes to consecutive slots.
+__device__ __forceinline__ void store_block_lds(bf16_t *sK, bf16_t *sV, const BlockRegs &br, int wave,
+                                                int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int slot = (4 * r + wave) * 64 + lane;
+        *reinterpret_cast<uint4 *>(sK + slot * 8) = br.k[r].v;
+        *reinterpret_cast<uint4 *>(sV + slot * 8) = br.v[r].v;
+    }
 }
 
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_attn_kernel(
@@ -396,10 +396,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    // The ring's stages are separate LDS objects so the compiler can tell that
-    // reads of one stage do not depend on the DMA still filling the others.
-    __shared__ __align__(16) bf16_t sK0[64 * kD], sV0[64 * kD], sK1[64 * kD], sV1[64 * kD],
-        sK2[64 * kD], sV2[64 * kD];
+    // two stages, each the K tile then the V tile of one block
+    __shared__ __align__(16) bf16_t ring[2 * 2 * kPfTileElems];
+    // this wave's query fragments (B operands of the score product), one 1 KB
+    // row of 64 lanes x 16 B per (row tile, channel step): sQ[wave][4 rt + ks][lane]
+    __shared__ uint4 sQ[4][16][64];
     __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -408,84 +409,50 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int64_t bt = q_start / kBlock + tile;
     if (tid < kPfMaxPasses) s_redo[tid] = 0;
 
-    bf16x8_t qf[4][4];
-    load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
-    // The query fragments only feed the matrix cores: keep them in AGPRs and the
-    // VGPRs free for the vector work and LDS prefetch.
+    {
+        bf16x8_t qf[4][4];
+        load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qf[rt][ks]));
+            for (int ks = 0; ks < 4; ++ks) sQ[wave][4 * rt + ks][lane] = __builtin_bit_cast(uint4, qf[rt][ks]);
+    }
     int qloc[4];                                   // query offset inside the tile, per row tile
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qloc[rt] = 16 * wave + 4 * rt + (c16 >> 2);
 
-    // Rows the DMA does not fill (past the end of K / V) must hold finite values:
-    // zero the ring once.
-    for (int i = tid; i < 64 * kD / 8; i += kPfThreads) {
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        reinterpret_cast<uint4 *>(sK0)[i] = z;
-        reinterpret_cast<uint4 *>(sV0)[i] = z;
-        reinterpret_cast<uint4 *>(sK1)[i] = z;
-        reinterpret_cast<uint4 *>(sV1)[i] = z;
-        reinterpret_cast<uint4 *>(sK2)[i] = z;
-        reinterpret_cast<uint4 *>(sV2)[i] = z;
-    }
-
     f32x4_t o[8][4];
+    float m[4], lsum[4], mrun[4];                  // reference (log2 units), partial sum, running max
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[4], lsum[4];                           // reference (log2 units) and partial sum per row
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; lsum[rt] = 0.f; }
+    for (int rt = 0; rt < 4; ++rt) m[rt] = -INFINITY;
 
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
-    // block ids through the constant address space: scalar loads, whose waits
-    // do not also wait for the ring's DMA
-    typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+    typedef const __attribute__((address_space(4))) int32_t const_i32_t;   // scalar loads
     const_i32_t *ids = (const_i32_t *)(tile_idx + (int64_t)blockIdx.x * tile_cap);
     int n = tile_cnt[blockIdx.x];
     n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
-    __syncthreads();                               // ring zeroed before any DMA lands
+    auto blk_at = [&](int e) -> int64_t { return ids[__builtin_amdgcn_readfirstlane(e)]; };
 
-    auto stage_k = [&](auto S) -> bf16_t * {
-        constexpr int st = decltype(S)::value;
-        if constexpr (st == 0) return sK0;
-        else if constexpr (st == 1) return sK1;
-        else return sK2;
-    };
-    auto stage_v = [&](auto S) -> bf16_t * {
-        constexpr int st = decltype(S)::value;
-        if constexpr (st == 0) return sV0;
-        else if constexpr (st == 1) return sV1;
-        else return sV2;
-    };
-    auto dma_block = [&](auto S, int64_t blk) {
-        dma_tile_swizzled(stage_k(S), rK, blk * kBlock, wave, lane);
-        dma_tile_swizzled(stage_v(S), rV, blk * kBlock, wave, lane);
-    };
-    const std::integral_constant<int, 0> kSt0{};
-    const std::integral_constant<int, 1> kSt1{};
-    const std::integral_constant<int, 2> kSt2{};
-
-    // Scores S^T = K Q^T of one half block (32 keys, 32hh .. 32hh+31 of the tile):
+    // Scores S^T = K Q^T of one half block (keys 32hh .. 32hh+31 of the block):
     // s[j][rt][i] = score of row 16 rt + (l%16) with key 32hh + 16j + 4g + i.
-    auto half_scores = [&](f32x4_t (&s)[2][4], const bf16_t *sK, int hh, int g, int c16) {
+    auto half_scores = [&](f32x4_t (&s)[2][4], const bf16_t *sK, int hh) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8_t qb[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) qb[rt] = as_bf16x8(sQ[wave][4 * rt + ks][lane]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const bf16x8_t a = lds_frag_rows(sK, 32 * hh + 16 * j + c16, ks, g);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
+                for (int rt = 0; rt < 4; ++rt) s[j][rt] = mfma16(a, qb[rt], s[j][rt]);
             }
+        }
     };
     // causal mask inside the tile's own block: key <= query
     auto mask_causal = [&](f32x4_t (&s)[2][4], int hh) {
@@ -505,50 +472,61 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
                      fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
     };
     // Probabilities against the row references as bf16 B operands (keys
-    // 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i), row sums; the lane's
-    // running row max feeds the end-of-pass check.
-    float mrun[4];
+    // 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i), row sums, running max.
     auto half_probs = [&](bf16x8_t (&pb)[4], const f32x4_t (&s)[2][4]) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            mrun[rt] = fmaxf(mrun[rt], half_max(s, rt));
             const float nm = -m[rt];
             float p[2][4];
-            float ps = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[j][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][rt][i], qscale, nm));
-                    ps += p[j][i];
-                }
-            lsum[rt] += ps;
+                for (int i = 0; i < 4; ++i) p[j][i] = __builtin_fmaf(s[j][rt][i], qscale, nm);
+            // running max of the exponents (relative to the reference)
+            mrun[rt] = fmaxf(fmaxf(fmaxf(mrun[rt], fmaxf(p[0][0], p[0][1])), fmaxf(p[0][2], p[0][3])),
+                             fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[j][i] = __builtin_amdgcn_exp2f(p[j][i]);
+            lsum[rt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
             pb[rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
     };
-    auto half_values = [&](const bf16x8_t (&pb)[4], const bf16_t *sV, int hh, int g, int c16) {
+    // One block: scores and probabilities of both halves, then the value
+    // product O^T += V^T P^T with each accumulator's two steps back to back.
+    auto block_compute = [&](const bf16_t *sK, const bf16_t *sV, bool diag) {
+        bf16x8_t pb[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            f32x4_t s[2][4];
+            half_scores(s, sK, hh);
+            if (diag) mask_causal(s, hh);
+            half_probs(pb[hh], s);
+        }
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const bf16x8_t a = vt_frag_tr(sV, ct, hh, g, c16);
+            const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
+            const bf16x8_t a1 = vt_frag_tr(sV, ct, 1, g, c16);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = mfma16(a, pb[rt], o[ct][rt]);
+            for (int rt = 0; rt < 4; ++rt) {
+                o[ct][rt] = mfma16(a0, pb[0][rt], o[ct][rt]);
+                o[ct][rt] = mfma16(a1, pb[1][rt], o[ct][rt]);
+            }
         }
     };
-    auto half_accumulate = [&](const f32x4_t (&s)[2][4], const bf16_t *sV, int hh) {
-        bf16x8_t pb[4];
-        half_probs(pb, s);
-        half_values(pb, sV, hh, g, c16);
-    };
 
-    // The block steps have no branches. References: the row max of the first
-    // half block; a row whose max later exceeds its reference by more than the
-    // slack (checked once per pass, from the running maxima) gets the larger
-    // reference and the workgroup runs its blocks again (the pass's sums are
-    // void; the accumulators are never rescaled, so they stay in the matrix
-    // cores' registers). No block can outgrow the raised references.
-    // The tile's own block, last in the ascending set, takes the causal mask.
-    const bool last_diag = n > 0 && ids[n - 1] == bt;
+    // Blocks go through a 2-stage LDS ring: block e sits in stage e % 2. Step e:
+    // barrier (block e staged by every wave; every wave done with block e-1),
+    // issue the loads of block e+1 into registers, compute block e, then store
+    // block e+1 into the other stage. The loop body has no branches: the
+    // reference of a row is the max of its first half block; a row whose running
+    // max later exceeds it by more than the slack (checked once per pass) gets
+    // the larger reference and the workgroup runs its blocks again (the pass's
+    // sums are void; accumulators are never rescaled). The tile's own block,
+    // last in the ascending set, takes the causal mask after the loop.
+    const bool last_diag = n > 0 && blk_at(n - 1) == bt;
     const int n_main = last_diag ? n - 1 : n;
     for (int pass = 0; pass < kPfMaxPasses; ++pass) {
 #pragma unroll
@@ -557,18 +535,15 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
             for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
-        // (an id of -1 fetches nothing: every row is out of range and reads as zeros)
-        dma_block(kSt0, n > 0 ? ids[0] : -1);
-        dma_block(kSt1, n > 1 ? ids[1] : -1);
-        // Block e sits in stage e % 3. Before the barrier: this wave's DMA of
-        // block e landed (block e+1's 8 loads may still fly); after it every
-        // wave's has, and every wave has finished block e-1, whose stage the
-        // DMA of block e+2 then reuses.
-        if (pass == 0 && n > 0) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
-            ring_barrier();
+        BlockRegs br;
+        if (n > 0) {
+            load_block_regs(br, rK, rV, blk_at(0), wave, lane);
+            store_block_lds(ring, ring + kPfTileElems, br, wave, lane);
+        }
+        if (pass == 0 && n > 0) {                  // references from the first half block
+            __syncthreads();
             f32x4_t s[2][4];
-            half_scores(s, sK0, 0, g, c16);
+            half_scores(s, ring, 0);
             if (n == 1 && last_diag) mask_causal(s, 0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
@@ -578,68 +553,32 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
                 m[rt] = mx == -INFINITY ? 0.f : mx;
             }
         }
-        int e = 0;
-        auto block_step = [&](auto S) {
-            constexpr int st = decltype(S)::value;
-            const std::integral_constant<int, (st + 2) % 3> S2{};
-            __builtin_amdgcn_s_waitcnt(kWaitVm8Lgkm0);
-            ring_barrier();
-            dma_block(S2, e + 2 < n ? ids[__builtin_amdgcn_readfirstlane(e + 2)] : -1);
-            // Software pipeline over the two halves, so that the matrix cores
-            // run while the vector units compute probabilities:
-            //   scores h0 | scores h1 + probs h0 | values h0 + probs h1 | values h1
-            f32x4_t s0[2][4], s1[2][4];
-            bf16x8_t pb0[4], pb1[4];
-            // lane fields recomputed per step: LDS addresses are not kept live
-            // across the loop for every stage
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int lg = ln >> 4, lc = ln & 15;
-            // Software pipeline over the two halves, so that the matrix cores
-            // run while the vector units compute probabilities:
-            //   scores h0 | scores h1 + probs h0 | values h0 + probs h1 | values h1
-            half_scores(s0, stage_k(S), 0, lg, lc);
-            __builtin_amdgcn_sched_barrier(0);
-            half_scores(s1, stage_k(S), 1, lg, lc);
-            half_probs(pb0, s0);
-            interleave_mfma_valu<32, 8>();
-            __builtin_amdgcn_sched_barrier(0);
-            half_values(pb0, stage_v(S), 0, lg, lc);
-            half_probs(pb1, s1);
-            interleave_mfma_valu<32, 16>();
-            __builtin_amdgcn_sched_barrier(0);
-            half_values(pb1, stage_v(S), 1, lg, lc);
-            ++e;
-        };
-        while (e < n_main) {
-            block_step(kSt0);
-            if (e >= n_main) break;
-            block_step(kSt1);
-            if (e >= n_main) break;
-            block_step(kSt2);
-        }
-        if (last_diag) {                           // e = n - 1, stage e % 3
-            __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
-            ring_barrier();
-            const int st = e % 3;
-            const bf16_t *sK = st == 0 ? sK0 : (st == 1 ? sK1 : sK2);
-            const bf16_t *sV = st == 0 ? sV0 : (st == 1 ? sV1 : sV2);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                f32x4_t s[2][4];
-                half_scores(s, sK, hh, g, c16);
-                mask_causal(s, hh);
-                half_accumulate(s, sV, hh);
+        for (int e = 0; e < n_main; ++e) {
+            __syncthreads();
+            const bf16_t *sK = ring + (e & 1) * 2 * kPfTileElems;
+            const bf16_t *sV = sK + kPfTileElems;
+            const bool more = e + 1 < n;
+            if (more) load_block_regs(br, rK, rV, blk_at(e + 1), wave, lane);
+            block_compute(sK, sV, false);
+            if (more) {
+                bf16_t *nK = ring + ((e + 1) & 1) * 2 * kPfTileElems;
+                store_block_lds(nK, nK + kPfTileElems, br, wave, lane);
             }
+        }
+        if (last_diag) {                           // block n-1, staged by the loop (or the prologue)
+            __syncthreads();
+            const bf16_t *sK = ring + (n_main & 1) * 2 * kPfTileElems;
+            const bf16_t *sV = sK + kPfTileElems;
+            block_compute(sK, sV, true);
         }
         // end of pass: raise references a row outgrew; workgroup-wide redo
         bool redo = false;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            float mx = mrun[rt] * qscale;
+            float mx = mrun[rt];
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
-            if (mx > m[rt] + kRescaleSlack) { m[rt] = mx; redo = true; }
+            if (mx > kRescaleSlack) { m[rt] += mx; redo = true; }
         }
         __syncthreads();
         if (redo) s_redo[pass] = 1;
