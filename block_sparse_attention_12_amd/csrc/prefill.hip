@@ -361,46 +361,48 @@ constexpr float kRescaleSlack = 64.f;
 // slack and the second pass can no longer outgrow any (the cap only bounds the loop).
 constexpr int kPfMaxPasses = 4;
 constexpr int kPfTileElems = 64 * kD;             // one 64 x 128 bf16 tile (16 KB)
+// Attention workgroup: 8 waves (two per SIMD, so one wave's vector work overlaps
+// the other's matrix work), each owning 32 rows = 8 queries x 4 heads, as two
+// 16-row tiles (row = 4 * query + head).
+constexpr int kAtWaves = 8;
+constexpr int kAtThreads = 64 * kAtWaves;
+constexpr int kAtRt = 2;
 
-// Global -> register half of the block staging: this thread's 4 K and 4 V chunks
-// of one block, in the swizzled order of the LDS tile (thread (w, l), load r
-// fills chunk slot (4r + w) * 64 + l). Rows outside the buffer read as zeros.
+// Global -> register half of the block staging: this thread's 2 K and 2 V chunks
+// of one block, in the swizzled order of the LDS tile (thread t, load r fills
+// chunk slot 512 r + t). Rows outside the buffer read as zeros.
 struct BlockRegs {
-    Raw8<bf16_t> k[4], v[4];
+    Raw8<bf16_t> k[2], v[2];
 };
 __device__ __forceinline__ void load_block_regs(BlockRegs &br, __amdgpu_buffer_rsrc_t rK,
-                                                __amdgpu_buffer_rsrc_t rV, int64_t blk, int wave, int lane) {
+                                                __amdgpu_buffer_rsrc_t rV, int64_t blk, int tid) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int slot0 = (4 * r + wave) * 64;
-        const int row = (slot0 >> 4) + (lane >> 4);
-        const int chunk = (lane & 15) ^ (row & 15);
+    for (int r = 0; r < 2; ++r) {
+        const int slot = kAtThreads * r + tid;
+        const int row = slot >> 4;
+        const int chunk = (slot & 15) ^ (row & 15);
         const uint32_t off = row_offset(blk * kBlock + row, kD * 2, chunk * 16);
         load_raw(rK, off, br.k[r]);
         load_raw(rV, off, br.v[r]);
     }
 }
-// Register -> LDS half: 16 B per lane, consecutive lanes to consecutive slots.
-__device__ __forceinline__ void store_block_lds(bf16_t *sK, bf16_t *sV, const BlockRegs &br, int wave,
-                                                int lane) {
+// Register -> LDS half: 16 B per thread, consecutive threads to consecutive slots.
+__device__ __forceinline__ void store_block_lds(bf16_t *sK, bf16_t *sV, const BlockRegs &br, int tid) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int slot = (4 * r + wave) * 64 + lane;
+    for (int r = 0; r < 2; ++r) {
+        const int slot = kAtThreads * r + tid;
         *reinterpret_cast<uint4 *>(sK + slot * 8) = br.k[r].v;
         *reinterpret_cast<uint4 *>(sV + slot * 8) = br.v[r].v;
     }
 }
 
-__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_attn_kernel(
+__global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
     // two stages, each the K tile then the V tile of one block
     __shared__ __align__(16) bf16_t ring[2 * 2 * kPfTileElems];
-    // this wave's query fragments (B operands of the score product), one 1 KB
-    // row of 64 lanes x 16 B per (row tile, channel step): sQ[wave][4 rt + ks][lane]
-    __shared__ uint4 sQ[4][16][64];
     __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -409,22 +411,28 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int64_t bt = q_start / kBlock + tile;
     if (tid < kPfMaxPasses) s_redo[tid] = 0;
 
-    {
-        bf16x8_t qf[4][4];
-        load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
+    // query fragments (B operands): qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
+    int qloc[kAtRt];                               // query offset inside the tile, per row tile
+    bf16x8_t qf[kAtRt][4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < kAtRt; ++rt) {
+        qloc[rt] = 8 * wave + 4 * rt + (c16 >> 2);
+        const int64_t qi = q_first + qloc[rt];
+        const int h = c16 & 3;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) sQ[wave][4 * rt + ks][lane] = __builtin_bit_cast(uint4, qf[rt][ks]);
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (qi < Tq)
+                v = *reinterpret_cast<const uint4 *>(Q + (qi * Hq + (int64_t)kvh * kPfG + h) * kD +
+                                                     32 * ks + 8 * g);
+            qf[rt][ks] = as_bf16x8(v);
+        }
     }
-    int qloc[4];                                   // query offset inside the tile, per row tile
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) qloc[rt] = 16 * wave + 4 * rt + (c16 >> 2);
 
-    f32x4_t o[8][4];
-    float m[4], lsum[4], mrun[4];                  // reference (log2 units), partial sum, running max
+    f32x4_t o[8][kAtRt];
+    float m[kAtRt], lsum[kAtRt], mrun[kAtRt];      // reference (log2 units), partial sum, running max
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) m[rt] = -INFINITY;
+    for (int rt = 0; rt < kAtRt; ++rt) m[rt] = -INFINITY;
 
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)kvh * T_cap * kD, (uint32_t)(T_cap * kD * 2));
@@ -436,28 +444,24 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 
     // Scores S^T = K Q^T of one half block (keys 32hh .. 32hh+31 of the block):
     // s[j][rt][i] = score of row 16 rt + (l%16) with key 32hh + 16j + 4g + i.
-    auto half_scores = [&](f32x4_t (&s)[2][4], const bf16_t *sK, int hh) {
+    auto half_scores = [&](f32x4_t (&s)[2][kAtRt], const bf16_t *sK, int hh) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8_t qb[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) qb[rt] = as_bf16x8(sQ[wave][4 * rt + ks][lane]);
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const bf16x8_t a = lds_frag_rows(sK, 32 * hh + 16 * j + c16, ks, g);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) s[j][rt] = mfma16(a, qb[rt], s[j][rt]);
+                for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
             }
-        }
     };
     // causal mask inside the tile's own block: key <= query
-    auto mask_causal = [&](f32x4_t (&s)[2][4], int hh) {
+    auto mask_causal = [&](f32x4_t (&s)[2][kAtRt], int hh) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < kAtRt; ++rt) {
             int q = qloc[rt] - 32 * hh - 4 * g;
             asm volatile("" : "+v"(q));            // compared here, not hoisted as lane masks
 #pragma unroll
@@ -467,22 +471,18 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
                     if (16 * j + i > q) s[j][rt][i] = -INFINITY;
         }
     };
-    auto half_max = [&](const f32x4_t (&s)[2][4], int rt) {
-        return fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
-                     fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3])));
-    };
-    // Probabilities against the row references as bf16 B operands (keys
-    // 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i), row sums, running max.
-    auto half_probs = [&](bf16x8_t (&pb)[4], const f32x4_t (&s)[2][4]) {
+    // Exponents against the row references (running max kept), probabilities as
+    // bf16 B operands (keys 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i),
+    // row sums.
+    auto half_probs = [&](bf16x8_t (&pb)[kAtRt], const f32x4_t (&s)[2][kAtRt]) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < kAtRt; ++rt) {
             const float nm = -m[rt];
             float p[2][4];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) p[j][i] = __builtin_fmaf(s[j][rt][i], qscale, nm);
-            // running max of the exponents (relative to the reference)
             mrun[rt] = fmaxf(fmaxf(fmaxf(mrun[rt], fmaxf(p[0][0], p[0][1])), fmaxf(p[0][2], p[0][3])),
                              fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
 #pragma unroll
@@ -497,10 +497,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
     // One block: scores and probabilities of both halves, then the value
     // product O^T += V^T P^T with each accumulator's two steps back to back.
     auto block_compute = [&](const bf16_t *sK, const bf16_t *sV, bool diag) {
-        bf16x8_t pb[2][4];
+        bf16x8_t pb[2][kAtRt];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            f32x4_t s[2][4];
+            f32x4_t s[2][kAtRt];
             half_scores(s, sK, hh);
             if (diag) mask_causal(s, hh);
             half_probs(pb[hh], s);
@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
             const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
             const bf16x8_t a1 = vt_frag_tr(sV, ct, 1, g, c16);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+            for (int rt = 0; rt < kAtRt; ++rt) {
                 o[ct][rt] = mfma16(a0, pb[0][rt], o[ct][rt]);
                 o[ct][rt] = mfma16(a1, pb[1][rt], o[ct][rt]);
             }
@@ -532,22 +532,23 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < kAtRt; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
+        for (int rt = 0; rt < kAtRt; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
         BlockRegs br;
         if (n > 0) {
-            load_block_regs(br, rK, rV, blk_at(0), wave, lane);
-            store_block_lds(ring, ring + kPfTileElems, br, wave, lane);
+            load_block_regs(br, rK, rV, blk_at(0), tid);
+            store_block_lds(ring, ring + kPfTileElems, br, tid);
         }
         if (pass == 0 && n > 0) {                  // references from the first half block
             __syncthreads();
-            f32x4_t s[2][4];
+            f32x4_t s[2][kAtRt];
             half_scores(s, ring, 0);
             if (n == 1 && last_diag) mask_causal(s, 0);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                float mx = half_max(s, rt) * qscale;
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                                 fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3]))) * qscale;
                 mx = fmaxf(mx, shfl_xor(mx, 16));
                 mx = fmaxf(mx, shfl_xor(mx, 32));
                 m[rt] = mx == -INFINITY ? 0.f : mx;
@@ -558,23 +559,22 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
             const bf16_t *sK = ring + (e & 1) * 2 * kPfTileElems;
             const bf16_t *sV = sK + kPfTileElems;
             const bool more = e + 1 < n;
-            if (more) load_block_regs(br, rK, rV, blk_at(e + 1), wave, lane);
+            if (more) load_block_regs(br, rK, rV, blk_at(e + 1), tid);
             block_compute(sK, sV, false);
             if (more) {
                 bf16_t *nK = ring + ((e + 1) & 1) * 2 * kPfTileElems;
-                store_block_lds(nK, nK + kPfTileElems, br, wave, lane);
+                store_block_lds(nK, nK + kPfTileElems, br, tid);
             }
         }
         if (last_diag) {                           // block n-1, staged by the loop (or the prologue)
             __syncthreads();
             const bf16_t *sK = ring + (n_main & 1) * 2 * kPfTileElems;
-            const bf16_t *sV = sK + kPfTileElems;
-            block_compute(sK, sV, true);
+            block_compute(sK, sK + kPfTileElems, true);
         }
         // end of pass: raise references a row outgrew; workgroup-wide redo
         bool redo = false;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < kAtRt; ++rt) {
             float mx = mrun[rt];
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 
     // finish: total sum per row over the 4 lanes sharing it, then write
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < kAtRt; ++rt) {
         float l = lsum[rt];
         l += shfl_xor(l, 16);
         l += shfl_xor(l, 32);
@@ -679,7 +679,7 @@ int launch_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void
                           int32_t tile_idx_cap, const int32_t *tile_cnt, float scale, void *O,
                           int out_dtype, float *lse_out, hipStream_t stream) {
     const int n_tiles = (int)((Tq + 63) / 64);
-    hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(n_tiles * Hkv)), dim3(kPfThreads), 0,
+    hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)(n_tiles * Hkv)), dim3(kAtThreads), 0,
                        stream, (const bf16_t *)Q, (const bf16_t *)K, (const bf16_t *)V, Hq, Hkv,
                        q_start, Tq, T_cap, tile_idx, tile_idx_cap, tile_cnt, scale * kLog2eF, O,
                        out_dtype == SA_BF16 ? 1 : 0, lse_out);
