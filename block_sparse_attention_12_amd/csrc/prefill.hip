@@ -9,19 +9,24 @@
 //
 // One sequence, queries q_start .. q_start+Tq-1 (q_start a multiple of 64).
 // Tile t = queries q_start+64t .. +63, all inside block bt = q_start/64 + t.
-// A workgroup owns one (tile, KV head): 64 queries x 4 heads = 256 rows of
-// the attention; wave w takes queries 16w .. 16w+15, i.e. 64 rows, as four
-// 16-row tiles (row = 4 * query + head).
+// A workgroup owns one (tile, KV head): 64 queries x 4 heads = 256 rows
+// (row = 4 * query + head). The scoring kernel gives each of 4 waves 64 rows;
+// the attention kernel gives each of 8 waves (two per SIMD) 32 rows.
 //
 // Both dense contractions use v_mfma_f32_16x16x32_bf16 in the transposed form
-// S^T = K Q^T (keys as M, rows as N), so each lane ends up with 16 scores of a
-// single row (4 key tiles x 4 consecutive keys) and no data movement is
-// needed between the score and the value products:
-//   O^T = V^T P^T, with P converted in registers to the B operand. The key
-//   order inside each K = 32 step is permuted identically on both operands.
-// K (or compressed-key) chunks are staged in LDS with an XOR swizzle of their
-// 16-byte chunks (conflict-free 16-row reads); V is staged transposed with a
-// padded row so the A operand of V^T reads are conflict-free.
+// S^T = K Q^T (keys as M, rows as N), so each lane ends up with the scores of a
+// single row and no data movement is needed between the score and the value
+// products: O^T = V^T P^T, with P converted in registers to the B operand. The
+// key order inside each K = 32 step is permuted identically on both operands.
+// K (or compressed-key) tiles sit in LDS row-major with an XOR swizzle of their
+// 16-byte chunks (conflict-free 16-row reads); V tiles row-major with their own
+// swizzle, read as V^T operands with ds_read_b64_tr_b16.
+//
+// Softmax: a row's reference (log2 units) is the max of its first half block;
+// probabilities are taken against it without rescaling the accumulators. A
+// row whose scores outgrow the reference by more than 2^64 voids the pass and
+// the workgroup runs its blocks again with the raised reference (the result
+// does not depend on the reference, only overflow does).
 //
 // Kernels:
 //   prefill_score_kernel  per (tile, KV head), two sweeps over the compressed
@@ -34,14 +39,14 @@
 //                         are neither initial nor in the local window, plus
 //                         init and local.
 //   prefill_union_kernel  per (tile, KV head): union of its 64 queries' sets.
-//   prefill_attn_kernel   per (tile, KV head): causal flash attention over the
-//                         union, online softmax in fp32, P rounded to bf16 for
-//                         the value product, fp32 accumulation.
+//   prefill_attn_kernel   per (tile, KV head): causal attention over the union,
+//                         blocks staged through a 2-stage LDS ring (loads of
+//                         the next block in registers during the current one),
+//                         softmax in fp32, P rounded to bf16 for the value
+//                         product, fp32 accumulation.
 // Workgroups are numbered tile * Hkv + kvh so the tiles of one KV head land on
 // the same XCD (round-robin dispatch over 8 XCDs) and share its L2.
 #include <math.h>
-
-#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -83,23 +88,10 @@ __device__ __forceinline__ bf16x8_t lds_frag_rows(const bf16_t *lds, int m_row, 
     return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + m_row * kD + chunk * 8));
 }
 
-// ---- DMA of one 64-row x 128-channel bf16 tile straight into LDS, in the same
-// swizzled row-major layout as above. Each 16-byte load of lane i of a wave lands
-// at the instruction's LDS base + 16 i; instruction r of wave w fills chunk slots
-// (4r + w) * 64 + lane, and each slot fetches the source chunk that belongs there.
-// Rows outside the buffer read as zeros (buffer range check).
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ void dma_tile_swizzled(bf16_t *lds, __amdgpu_buffer_rsrc_t src,
-                                                  int64_t row0, int wave, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int slot0 = (4 * r + wave) * 64;
-        const int row = (slot0 >> 4) + (lane >> 4);
-        const int chunk = (lane & 15) ^ (row & 15);
-        const uint32_t off = row_offset(row0 + row, kD * 2, chunk * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t *)(lds + slot0 * 8), 16, off, 0, 0, 0);
-    }
-}
+// V tiles use their own swizzle: chunk c of row r at c ^ 2 (r % 8). A transposed
+// read of 8 rows x 32 bytes (one half of a ds_read_b64_tr_b16) then touches 16
+// distinct chunks, all 64 banks once.
+__device__ __forceinline__ int vt_swizzle(int row) { return 2 * (row & 7); }
 
 // A operand of V^T for the value product from a swizzled row-major V tile:
 // channel row 16 ct + (l%16), permuted keys of step kk: slots 0..3 hold keys
@@ -115,7 +107,7 @@ __device__ __forceinline__ bf16x8_t vt_frag_tr(const bf16_t *lds, int ct, int kk
     for (int half = 0; half < 2; ++half) {
         const int row = 32 * kk + 16 * half + 4 * g + (c16 >> 2);
         const int ch = 16 * ct + 4 * (c16 & 3);
-        const int elem = row * kD + (((ch >> 3) ^ (row & 15)) << 3) + (ch & 7);
+        const int elem = row * kD + (((ch >> 3) ^ vt_swizzle(row)) << 3) + (ch & 7);
         h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + elem));
     }
     typedef __attribute__((ext_vector_type(8))) short s16x8_t;
@@ -380,10 +372,9 @@ __device__ __forceinline__ void load_block_regs(BlockRegs &br, __amdgpu_buffer_r
     for (int r = 0; r < 2; ++r) {
         const int slot = kAtThreads * r + tid;
         const int row = slot >> 4;
-        const int chunk = (slot & 15) ^ (row & 15);
-        const uint32_t off = row_offset(blk * kBlock + row, kD * 2, chunk * 16);
-        load_raw(rK, off, br.k[r]);
-        load_raw(rV, off, br.v[r]);
+        const int64_t grow = blk * kBlock + row;
+        load_raw(rK, row_offset(grow, kD * 2, ((slot & 15) ^ (row & 15)) * 16), br.k[r]);
+        load_raw(rV, row_offset(grow, kD * 2, ((slot & 15) ^ vt_swizzle(row)) * 16), br.v[r]);
     }
 }
 // Register -> LDS half: 16 B per thread, consecutive threads to consecutive slots.
