@@ -430,12 +430,12 @@ def bench_prefill(args):
                    "n_init": w.n_init, "n_local": w.n_local, "parallelism": "none (1 GPU)"},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "phase_ms": {"select": round(gpu_ms - attn_ms, 5), "attend": round(attn_ms, 5)},
-        "mean_union_blocks": round(float(tcnt.mean()), 1),
+        "mean_union_blocks": round(float(tcnt.mean()), 1), "max_union_blocks": int(tcnt.max()),
         "attn_tflop": round(attn_flops / 1e12, 4), "select_tflop": round(sel_flops / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel (sparse_attn_prefill_attend)",
                      "achieved": round(attn_tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": attn_flops},
+                     "traffic": recorded_traffic(f"{w.name}_attn"), "flops_per_launch": attn_flops},
     }
     print(json.dumps(out), flush=True)
 
