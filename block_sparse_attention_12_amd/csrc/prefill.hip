@@ -67,21 +67,6 @@ __device__ __forceinline__ f32x4_t mfma16(const bf16x8_t &a, const bf16x8_t &b, 
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4 &v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// ---- LDS staging of a 64-row x 128-channel bf16 tile (K or compressed K):
-// row r's 16-byte chunk c is stored at chunk position c ^ (r % 16).
-__device__ __forceinline__ void stage_rows_swizzled(bf16_t *lds, __amdgpu_buffer_rsrc_t src,
-                                                    int64_t row0, int tid) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int id = r * kPfThreads + tid;           // 1024 chunks of 16 B
-        const int row = id >> 4, chunk = id & 15;
-        const uint32_t off = row_offset(row0 + row, kD * 2, chunk * 16);
-        Raw8<bf16_t> x;
-        load_raw(src, off, x);
-        *reinterpret_cast<uint4 *>(lds + row * kD + ((chunk ^ (row & 15)) * 8)) = x.v;
-    }
-}
-
 // A operand (rows as M) from a swizzled LDS tile: row m_row, channels 32 ks + 8 g .. +8
 __device__ __forceinline__ bf16x8_t lds_frag_rows(const bf16_t *lds, int m_row, int ks, int g) {
     const int chunk = (4 * ks + g) ^ (m_row & 15);
@@ -125,14 +110,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
-// Q rows of this wave as B operands: qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
-// (zeros for rows past the chunk). Row = 4 * query + head inside the wave.
-__device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[4][4], const bf16_t *Q, int Hq, int kvh,
-                                             int64_t q_first, int64_t Tq, int wave, int lane) {
+// Row mapping shared by the scoring and attention kernels: 8 waves per
+// workgroup (two per SIMD, so one wave's vector work overlaps the other's
+// matrix work), each owning 32 rows = 8 queries x 4 heads of the tile as two
+// 16-row tiles (row = 4 * query + head).
+constexpr int kAtWaves = 8;
+constexpr int kAtThreads = 64 * kAtWaves;
+constexpr int kAtRt = 2;
+constexpr int kPfTileElems = 64 * kD;             // one 64 x 128 bf16 tile (16 KB)
+
+// This wave's query rows as B operands: qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
+// (zeros for queries past the chunk); qloc[rt] = the lane's query offset in the tile.
+__device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[kAtRt][4], int (&qloc)[kAtRt], const bf16_t *Q,
+                                             int Hq, int kvh, int64_t q_first, int64_t Tq, int wave,
+                                             int lane) {
     const int g = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);     // query index in the chunk
+    for (int rt = 0; rt < kAtRt; ++rt) {
+        qloc[rt] = 8 * wave + 4 * rt + (c16 >> 2);
+        const int64_t qi = q_first + qloc[rt];
         const int h = c16 & 3;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -145,33 +141,59 @@ __device__ __forceinline__ void load_q_frags(bf16x8_t (&qf)[4][4], const bf16_t 
     }
 }
 
-// S^T tile of 64 keys (from a swizzled LDS tile) x this wave's 64 rows:
-// s[mt][rt][i] = score of row 16 rt + (l%16) with key 16 mt + 4 g + i
-__device__ __forceinline__ void scores_64x64(f32x4_t (&s)[4][4], const bf16_t *ldsK,
-                                             const bf16x8_t (&qf)[4][4], int lane) {
-    const int g = lane >> 4, c16 = lane & 15;
+// A 64 x 128 tile staged global -> registers -> LDS: this thread's two 16-byte
+// chunks, thread t's load r filling chunk slot 512 r + t of the tile, each slot
+// fetching the source chunk that the swizzle puts there (K swizzle c ^ (r%16),
+// or the V swizzle). Rows outside the buffer read as zeros.
+struct TileRegs {
+    Raw8<bf16_t> c[2];
+};
+__device__ __forceinline__ int vt_swizzle(int row);
+template <bool V_SWIZZLE>
+__device__ __forceinline__ void load_tile_regs(TileRegs &tr, __amdgpu_buffer_rsrc_t src, int64_t row0,
+                                               int tid) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int r = 0; r < 2; ++r) {
+        const int slot = kAtThreads * r + tid;
+        const int row = slot >> 4;
+        const int sw = V_SWIZZLE ? vt_swizzle(row) : (row & 15);
+        load_raw(src, row_offset(row0 + row, kD * 2, ((slot & 15) ^ sw) * 16), tr.c[r]);
+    }
+}
+__device__ __forceinline__ void store_tile_lds(bf16_t *lds, const TileRegs &tr, int tid) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) s[mt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4 *>(lds + (kAtThreads * r + tid) * 8) = tr.c[r].v;
+}
+
+// Scores S^T = K Q^T of half a tile (keys 32hh .. 32hh+31) for this wave's rows:
+// s[j][rt][i] = score of row 16 rt + (l%16) with key 32hh + 16j + 4g + i.
+__device__ __forceinline__ void half_scores(f32x4_t (&s)[2][kAtRt], const bf16_t *sK,
+                                            const bf16x8_t (&qf)[kAtRt][4], int hh, int g, int c16) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const bf16x8_t a = lds_frag_rows(ldsK, 16 * mt + c16, ks, g);
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8_t a = lds_frag_rows(sK, 32 * hh + 16 * j + c16, ks, g);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) s[mt][rt] = mfma16(a, qf[rt][ks], s[mt][rt]);
+            for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
         }
 }
 
 // ------------------------------------------------------------------ scoring
 
-// Visible compressed entries for a query at position p: n_c(p + 1).
-__global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
+// Visible compressed entries for a query at position p: n_c(p + 1). The
+// compressed keys go through a 2-stage LDS ring of 64-entry chunks (the next
+// chunk's loads held in registers during the current one). Chunks below what
+// the tile's first query sees need no visibility mask; the rest take it.
+__global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_score_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ Kc, int Hq, int Hkv, int64_t q_start,
     int64_t Tq, int64_t nc_cap, int raw_mode, float *__restrict__ bscore, int64_t nb_cap,
     int32_t *__restrict__ qlens) {
-    __shared__ __align__(16) bf16_t sK[64 * kD];
+    __shared__ __align__(16) bf16_t ring[2 * kPfTileElems];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -179,104 +201,140 @@ __global__ __launch_bounds__(kPfThreads) void prefill_score_kernel(
     const int64_t bt = q_start / kBlock + tile;
     if (kvh == 0 && tid < 64 && q_first + tid < Tq) qlens[q_first + tid] = (int32_t)(q_start + q_first + tid + 1);
 
-    bf16x8_t qf[4][4];
-    load_q_frags(qf, Q, Hq, kvh, q_first, Tq, wave, lane);
-    // visible entries of this lane's row in each row tile
-    int64_t nvis[4];
+    int qloc[kAtRt];
+    bf16x8_t qf[kAtRt][4];
+    load_q_frags(qf, qloc, Q, Hq, kvh, q_first, Tq, wave, lane);
+    int nvis[kAtRt];                                             // visible entries of the lane's row
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);
-        nvis[rt] = qi < Tq ? n_compressed(q_start + qi + 1) : 0;
+    for (int rt = 0; rt < kAtRt; ++rt) {
+        const int64_t qi = q_first + qloc[rt];
+        nvis[rt] = qi < Tq ? (int)n_compressed(q_start + qi + 1) : 0;
     }
     const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)kvh * nc_cap * kD,
                                                 (uint32_t)(nc_cap * kD * 2));
     const int n_chunks = (int)(bt / 16) + 1;                     // every block <= bt is covered
+    const int vis_min = (int)n_compressed(q_start + q_first + 1);
+    const int n_full = vis_min / 64 < n_chunks ? vis_min / 64 : n_chunks;
 
-    // sweep 1: per-row max and sum of exp over visible entries (base 2)
-    float m[4], z[4];
+    // scores of chunk c: s[mt][rt][i] for entry 64c + 16 mt + 4g + i; masked
+    // entries (past the row's visible count) are -inf
+    auto chunk_scores = [&](f32x4_t (&s)[4][kAtRt], const bf16_t *sK, int c, bool masked) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; z[rt] = 0.f; }
-    if (!raw_mode) {
+        for (int hh = 0; hh < 2; ++hh) {
+            f32x4_t h[2][kAtRt];
+            half_scores(h, sK, qf, hh, g, c16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int rt = 0; rt < kAtRt; ++rt) s[2 * hh + j][rt] = h[j][rt];
+        }
+        if (masked) {
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                const int lim = nvis[rt] - 64 * c - 4 * g;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * mt + i >= lim) s[mt][rt][i] = -INFINITY;
+            }
+        }
+    };
+    // one sweep over the chunks: body(s, c) per chunk
+    auto sweep = [&](auto body) {
+        TileRegs rk;
+        load_tile_regs<false>(rk, rKc, 0, tid);
+        store_tile_lds(ring, rk, tid);
         for (int c = 0; c < n_chunks; ++c) {
             __syncthreads();
-            stage_rows_swizzled(sK, rKc, (int64_t)c * 64, tid);
-            __syncthreads();
-            f32x4_t s[4][4];
-            scores_64x64(s, sK, qf, lane);
+            const bf16_t *sK = ring + (c & 1) * kPfTileElems;
+            const bool more = c + 1 < n_chunks;
+            if (more) load_tile_regs<false>(rk, rKc, (int64_t)(c + 1) * 64, tid);
+            f32x4_t s[4][kAtRt];
+            if (c < n_full) {
+                chunk_scores(s, sK, c, false);
+                body(s, c);
+            } else {
+                chunk_scores(s, sK, c, true);
+                body(s, c);
+            }
+            if (more) store_tile_lds(ring + ((c + 1) & 1) * kPfTileElems, rk, tid);
+        }
+        __syncthreads();                           // ring free for the next sweep
+    };
+
+    // sweep 1 (softmax mode): per-row max and sum of exp over visible entries
+    // (base 2), online per lane, then merged over the 4 lanes sharing a row
+    float m[kAtRt], z[kAtRt];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+    for (int rt = 0; rt < kAtRt; ++rt) { m[rt] = -INFINITY; z[rt] = 0.f; }
+    if (!raw_mode) {
+        sweep([&](f32x4_t (&s)[4][kAtRt], int) {
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt) {
                 float x[16];
-                float mx = -INFINITY;
+                float mx = m[rt];
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int64_t j = (int64_t)c * 64 + 16 * mt + 4 * g + i;
-                        const float v = j < nvis[rt] ? s[mt][rt][i] * kLog2eF : -INFINITY;
-                        x[mt * 4 + i] = v;
-                        mx = fmaxf(mx, v);
+                        x[4 * mt + i] = s[mt][rt][i] * kLog2eF;
+                        mx = fmaxf(mx, x[4 * mt + i]);
                     }
-                const float mn = fmaxf(m[rt], mx);
-                if (mn != -INFINITY) {
-                    float acc = (m[rt] == -INFINITY) ? 0.f : z[rt] * exp2f(m[rt] - mn);
+                if (mx != -INFINITY) {
+                    float acc = z[rt] * __builtin_amdgcn_exp2f(m[rt] - mx);
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) acc += (x[k] == -INFINITY) ? 0.f : exp2f(x[k] - mn);
+                    for (int k = 0; k < 16; ++k) acc += __builtin_amdgcn_exp2f(x[k] - mx);
                     z[rt] = acc;
-                    m[rt] = mn;
+                    m[rt] = mx;
                 }
             }
-        }
-        // merge the 4 lanes (g = 0..3) that share a row
+        });
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < kAtRt; ++rt) {
 #pragma unroll
             for (int sh = 16; sh <= 32; sh <<= 1) {
                 const float m2 = shfl_xor(m[rt], sh), z2 = shfl_xor(z[rt], sh);
                 const float mn = fmaxf(m[rt], m2);
                 if (mn != -INFINITY) {
-                    z[rt] = ((m[rt] == -INFINITY) ? 0.f : z[rt] * exp2f(m[rt] - mn)) +
-                            ((m2 == -INFINITY) ? 0.f : z2 * exp2f(m2 - mn));
+                    z[rt] = z[rt] * __builtin_amdgcn_exp2f(m[rt] - mn) + z2 * __builtin_amdgcn_exp2f(m2 - mn);
                     m[rt] = mn;
                 }
             }
         }
     }
-    float zinv[4];
+    float zinv[kAtRt];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) zinv[rt] = z[rt] > 0.f ? 1.f / z[rt] : 0.f;
+    for (int rt = 0; rt < kAtRt; ++rt) zinv[rt] = z[rt] > 0.f ? 1.f / z[rt] : 0.f;
 
-    // sweep 2: group-summed scores, max over each block's inside entries
-    for (int c = 0; c < n_chunks; ++c) {
-        __syncthreads();
-        stage_rows_swizzled(sK, rKc, (int64_t)c * 64, tid);
-        __syncthreads();
-        f32x4_t s[4][4];
-        scores_64x64(s, sK, qf, lane);
+    // sweep 2: probabilities (or raw scores) summed over the 4 heads of a query
+    // (lanes 4k .. 4k+3 of a row group), max over each block's inside entries
+    // 4b, 4b+1, 4b+2 (lane g holds block 16c + 4mt + g), one score per
+    // (query, KV head, block)
+    sweep([&](f32x4_t (&s)[4][kAtRt], int c) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int64_t qi = q_first + 16 * wave + 4 * rt + (c16 >> 2);
+        for (int rt = 0; rt < kAtRt; ++rt) {
+            const int64_t qi = q_first + qloc[rt];
+            const float nm = -m[rt];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                float v[4];
+                float v[3];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t j = (int64_t)c * 64 + 16 * mt + 4 * g + i;
-                    const bool vis = j < nvis[rt];
-                    float pv;
-                    if (raw_mode) pv = vis ? s[mt][rt][i] : 0.f;
-                    else pv = vis ? exp2f(s[mt][rt][i] * kLog2eF - m[rt]) * zinv[rt] : 0.f;
-                    // sum over the 4 heads of the query (lanes 4k .. 4k+3 of the row group)
+                for (int i = 0; i < 3; ++i) {
+                    const float x = s[mt][rt][i];
+                    float pv = raw_mode ? (x == -INFINITY ? 0.f : x)
+                                        : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2eF, nm)) * zinv[rt];
                     pv += dpp<kDppQuadXor1>(pv);
                     pv += dpp<kDppQuadXor2>(pv);
-                    v[i] = vis ? pv : -INFINITY;
+                    v[i] = x == -INFINITY ? -INFINITY : pv;
                 }
-                const float bs = fmaxf(fmaxf(v[0], v[1]), v[2]);   // entries 4b, 4b+1, 4b+2
+                const float bs = fmaxf(fmaxf(v[0], v[1]), v[2]);
                 const int64_t blk = (int64_t)c * 16 + 4 * mt + g;
                 if ((c16 & 3) == 0 && qi < Tq && blk < nb_cap)
                     bscore[(qi * Hkv + kvh) * nb_cap + blk] = bs;
             }
         }
-    }
+    });
 }
 
 // ------------------------------------------------------------------ union
@@ -352,40 +410,6 @@ constexpr float kRescaleSlack = 64.f;
 // Passes over a tile's blocks: each redo raises some reference by more than the
 // slack and the second pass can no longer outgrow any (the cap only bounds the loop).
 constexpr int kPfMaxPasses = 4;
-constexpr int kPfTileElems = 64 * kD;             // one 64 x 128 bf16 tile (16 KB)
-// Attention workgroup: 8 waves (two per SIMD, so one wave's vector work overlaps
-// the other's matrix work), each owning 32 rows = 8 queries x 4 heads, as two
-// 16-row tiles (row = 4 * query + head).
-constexpr int kAtWaves = 8;
-constexpr int kAtThreads = 64 * kAtWaves;
-constexpr int kAtRt = 2;
-
-// Global -> register half of the block staging: this thread's 2 K and 2 V chunks
-// of one block, in the swizzled order of the LDS tile (thread t, load r fills
-// chunk slot 512 r + t). Rows outside the buffer read as zeros.
-struct BlockRegs {
-    Raw8<bf16_t> k[2], v[2];
-};
-__device__ __forceinline__ void load_block_regs(BlockRegs &br, __amdgpu_buffer_rsrc_t rK,
-                                                __amdgpu_buffer_rsrc_t rV, int64_t blk, int tid) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int slot = kAtThreads * r + tid;
-        const int row = slot >> 4;
-        const int64_t grow = blk * kBlock + row;
-        load_raw(rK, row_offset(grow, kD * 2, ((slot & 15) ^ (row & 15)) * 16), br.k[r]);
-        load_raw(rV, row_offset(grow, kD * 2, ((slot & 15) ^ vt_swizzle(row)) * 16), br.v[r]);
-    }
-}
-// Register -> LDS half: 16 B per thread, consecutive threads to consecutive slots.
-__device__ __forceinline__ void store_block_lds(bf16_t *sK, bf16_t *sV, const BlockRegs &br, int tid) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int slot = kAtThreads * r + tid;
-        *reinterpret_cast<uint4 *>(sK + slot * 8) = br.k[r].v;
-        *reinterpret_cast<uint4 *>(sV + slot * 8) = br.v[r].v;
-    }
-}
 
 __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
@@ -402,23 +426,9 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     const int64_t bt = q_start / kBlock + tile;
     if (tid < kPfMaxPasses) s_redo[tid] = 0;
 
-    // query fragments (B operands): qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
     int qloc[kAtRt];                               // query offset inside the tile, per row tile
     bf16x8_t qf[kAtRt][4];
-#pragma unroll
-    for (int rt = 0; rt < kAtRt; ++rt) {
-        qloc[rt] = 8 * wave + 4 * rt + (c16 >> 2);
-        const int64_t qi = q_first + qloc[rt];
-        const int h = c16 & 3;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (qi < Tq)
-                v = *reinterpret_cast<const uint4 *>(Q + (qi * Hq + (int64_t)kvh * kPfG + h) * kD +
-                                                     32 * ks + 8 * g);
-            qf[rt][ks] = as_bf16x8(v);
-        }
-    }
+    load_q_frags(qf, qloc, Q, Hq, kvh, q_first, Tq, wave, lane);
 
     f32x4_t o[8][kAtRt];
     float m[kAtRt], lsum[kAtRt], mrun[kAtRt];      // reference (log2 units), partial sum, running max
@@ -433,22 +443,6 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
     auto blk_at = [&](int e) -> int64_t { return ids[__builtin_amdgcn_readfirstlane(e)]; };
 
-    // Scores S^T = K Q^T of one half block (keys 32hh .. 32hh+31 of the block):
-    // s[j][rt][i] = score of row 16 rt + (l%16) with key 32hh + 16j + 4g + i.
-    auto half_scores = [&](f32x4_t (&s)[2][kAtRt], const bf16_t *sK, int hh) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8_t a = lds_frag_rows(sK, 32 * hh + 16 * j + c16, ks, g);
-#pragma unroll
-                for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
-            }
-    };
     // causal mask inside the tile's own block: key <= query
     auto mask_causal = [&](f32x4_t (&s)[2][kAtRt], int hh) {
 #pragma unroll
@@ -492,7 +486,7 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             f32x4_t s[2][kAtRt];
-            half_scores(s, sK, hh);
+            half_scores(s, sK, qf, hh, g, c16);
             if (diag) mask_causal(s, hh);
             half_probs(pb[hh], s);
         }
@@ -526,15 +520,23 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int rt = 0; rt < kAtRt; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < kAtRt; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
-        BlockRegs br;
+        TileRegs rk, rv;
+        auto load_block = [&](int64_t blk) {
+            load_tile_regs<false>(rk, rK, blk * kBlock, tid);
+            load_tile_regs<true>(rv, rV, blk * kBlock, tid);
+        };
+        auto store_block = [&](bf16_t *stage) {
+            store_tile_lds(stage, rk, tid);
+            store_tile_lds(stage + kPfTileElems, rv, tid);
+        };
         if (n > 0) {
-            load_block_regs(br, rK, rV, blk_at(0), tid);
-            store_block_lds(ring, ring + kPfTileElems, br, tid);
+            load_block(blk_at(0));
+            store_block(ring);
         }
         if (pass == 0 && n > 0) {                  // references from the first half block
             __syncthreads();
             f32x4_t s[2][kAtRt];
-            half_scores(s, ring, 0);
+            half_scores(s, ring, qf, 0, g, c16);
             if (n == 1 && last_diag) mask_causal(s, 0);
 #pragma unroll
             for (int rt = 0; rt < kAtRt; ++rt) {
@@ -550,12 +552,9 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             const bf16_t *sK = ring + (e & 1) * 2 * kPfTileElems;
             const bf16_t *sV = sK + kPfTileElems;
             const bool more = e + 1 < n;
-            if (more) load_block_regs(br, rK, rV, blk_at(e + 1), tid);
+            if (more) load_block(blk_at(e + 1));
             block_compute(sK, sV, false);
-            if (more) {
-                bf16_t *nK = ring + ((e + 1) & 1) * 2 * kPfTileElems;
-                store_block_lds(nK, nK + kPfTileElems, br, tid);
-            }
+            if (more) store_block(ring + ((e + 1) & 1) * 2 * kPfTileElems);
         }
         if (last_diag) {                           // block n-1, staged by the loop (or the prologue)
             __syncthreads();
@@ -655,7 +654,7 @@ int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, co
     const int n_tiles = (int)((Tq + 63) / 64);
     const dim3 grid((unsigned)(n_tiles * Hkv));
     const int raw = p.score_mode == SA_SCORE_RAW_SUM ? 1 : 0;
-    hipLaunchKernelGGL(prefill_score_kernel, grid, dim3(kPfThreads), 0, stream, (const bf16_t *)Q,
+    hipLaunchKernelGGL(prefill_score_kernel, grid, dim3(kAtThreads), 0, stream, (const bf16_t *)Q,
                        (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, raw, bscore, w.nb_cap, qlens);
     launch_topk_raw((int)(Tq * Hkv), Hkv, q_start + Tq, w.nb_cap, qlens, p, bscore, qidx, w.qcap,
                     qcnt, stream);
