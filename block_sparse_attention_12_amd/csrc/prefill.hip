@@ -410,17 +410,14 @@ constexpr float kRescaleSlack = 64.f;
 // Passes over a tile's blocks: each redo raises some reference by more than the
 // slack and the second pass can no longer outgrow any (the cap only bounds the loop).
 constexpr int kPfMaxPasses = 4;
-// s_waitcnt immediates: lgkmcnt(0) with vmcnt and expcnt at their maxima; all zero
-constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int kWaitAll0 = 0x0070;
 
 __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ K, const bf16_t *__restrict__ V,
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    // three stages, each the K tile then the V tile of one block
-    __shared__ __align__(16) bf16_t ring[3 * 2 * kPfTileElems];
+    // two stages, each the K tile then the V tile of one block
+    __shared__ __align__(16) bf16_t ring[2 * 2 * kPfTileElems];
     __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -482,25 +479,40 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
     };
-    // Ping-pong schedule. Waves 0-3 (group A, one per SIMD) and 4-7 (group B)
-    // alternate between a matrix phase and a vector phase, group B one phase
-    // behind, so on every SIMD one wave issues matrix work while the other does
-    // its softmax:
-    //   matrix phase of block e: O^T += V^T P^T for block e-1, then S^T = K Q^T
-    //                            for block e (both halves)
-    //   vector phase of block e: causal mask (tile's own block), exponents,
-    //                            probabilities as bf16 B operands, row sums
-    // Global phase t ends with a workgroup barrier; a wave of group B is in its
-    // phase t-1. Block b lives in ring stage b % 3: read by group A in phases
-    // 2b (K) and 2b+2 (V), by group B in 2b+1 and 2b+3; stored (from registers
-    // loaded two phases earlier) in phase 2b-2, after block b-3's last read in
-    // phase 2b-3. References: the row max of the first half block; a row whose
-    // running max later exceeds it by more than the slack (checked once per
-    // pass) gets the larger reference and the workgroup runs its blocks again
-    // (the pass's sums are void; accumulators are never rescaled).
-    const bool grp_b = wave >= 4;
+    // One block: scores and probabilities of both halves, then the value
+    // product O^T += V^T P^T with each accumulator's two steps back to back.
+    auto block_compute = [&](const bf16_t *sK, const bf16_t *sV, bool diag) {
+        bf16x8_t pb[2][kAtRt];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            f32x4_t s[2][kAtRt];
+            half_scores(s, sK, qf, hh, g, c16);
+            if (diag) mask_causal(s, hh);
+            half_probs(pb[hh], s);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
+            const bf16x8_t a1 = vt_frag_tr(sV, ct, 1, g, c16);
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                o[ct][rt] = mfma16(a0, pb[0][rt], o[ct][rt]);
+                o[ct][rt] = mfma16(a1, pb[1][rt], o[ct][rt]);
+            }
+        }
+    };
+
+    // Blocks go through a 2-stage LDS ring: block e sits in stage e % 2. Step e:
+    // barrier (block e staged by every wave; every wave done with block e-1),
+    // issue the loads of block e+1 into registers, compute block e, then store
+    // block e+1 into the other stage. The loop body has no branches: the
+    // reference of a row is the max of its first half block; a row whose running
+    // max later exceeds it by more than the slack (checked once per pass) gets
+    // the larger reference and the workgroup runs its blocks again (the pass's
+    // sums are void; accumulators are never rescaled). The tile's own block,
+    // last in the ascending set, takes the causal mask after the loop.
     const bool last_diag = n > 0 && blk_at(n - 1) == bt;
-    auto stage = [&](int b) { return ring + (b % 3) * 2 * kPfTileElems; };
+    const int n_main = last_diag ? n - 1 : n;
     for (int pass = 0; pass < kPfMaxPasses; ++pass) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
@@ -509,79 +521,45 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
         for (int rt = 0; rt < kAtRt; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
         TileRegs rk, rv;
-        auto load_block = [&](int b) {
-            const int64_t blk = blk_at(b);
+        auto load_block = [&](int64_t blk) {
             load_tile_regs<false>(rk, rK, blk * kBlock, tid);
             load_tile_regs<true>(rv, rV, blk * kBlock, tid);
         };
-        auto store_block = [&](bf16_t *st) {
-            store_tile_lds(st, rk, tid);
-            store_tile_lds(st + kPfTileElems, rv, tid);
+        auto store_block = [&](bf16_t *stage) {
+            store_tile_lds(stage, rk, tid);
+            store_tile_lds(stage + kPfTileElems, rv, tid);
         };
         if (n > 0) {
-            load_block(0);
-            store_block(stage(0));
+            load_block(blk_at(0));
+            store_block(ring);
         }
-        if (n > 1) load_block(1);
-        __builtin_amdgcn_s_waitcnt(kWaitAll0);     // query fragments and block 1 in registers
-        __syncthreads();
-
-        f32x4_t s[2][2][kAtRt];                    // scores of the current block, both halves
-        bf16x8_t pb[2][kAtRt];                     // probabilities of the previous vector phase
-        for (int t = 0; t < 2 * n + 2; ++t) {
-            const int tp = t - (grp_b ? 1 : 0);    // this wave's phase
-            if (tp >= 0 && tp <= 2 * n) {
-                const int e = tp >> 1;
-                if ((tp & 1) == 0) {               // matrix phase of block e
-                    if (e >= 1) {
-                        const bf16_t *sV = stage(e - 1) + kPfTileElems;
+        if (pass == 0 && n > 0) {                  // references from the first half block
+            __syncthreads();
+            f32x4_t s[2][kAtRt];
+            half_scores(s, ring, qf, 0, g, c16);
+            if (n == 1 && last_diag) mask_causal(s, 0);
 #pragma unroll
-                        for (int ct = 0; ct < 8; ++ct) {
-                            const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
-                            const bf16x8_t a1 = vt_frag_tr(sV, ct, 1, g, c16);
-#pragma unroll
-                            for (int rt = 0; rt < kAtRt; ++rt) {
-                                o[ct][rt] = mfma16(a0, pb[0][rt], o[ct][rt]);
-                                o[ct][rt] = mfma16(a1, pb[1][rt], o[ct][rt]);
-                            }
-                        }
-                    }
-                    if (e < n) {
-                        const bf16_t *sK = stage(e);
-                        half_scores(s[0], sK, qf, 0, g, c16);
-                        half_scores(s[1], sK, qf, 1, g, c16);
-                    }
-                } else {                           // vector phase of block e < n
-                    if (last_diag && e == n - 1) {
-                        mask_causal(s[0], 0);
-                        mask_causal(s[1], 1);
-                    }
-                    if (pass == 0 && e == 0) {     // references from the first half block
-#pragma unroll
-                        for (int rt = 0; rt < kAtRt; ++rt) {
-                            float mx = fmaxf(fmaxf(fmaxf(s[0][0][rt][0], s[0][0][rt][1]),
-                                                   fmaxf(s[0][0][rt][2], s[0][0][rt][3])),
-                                             fmaxf(fmaxf(s[0][1][rt][0], s[0][1][rt][1]),
-                                                   fmaxf(s[0][1][rt][2], s[0][1][rt][3]))) * qscale;
-                            mx = fmaxf(mx, shfl_xor(mx, 16));
-                            mx = fmaxf(mx, shfl_xor(mx, 32));
-                            m[rt] = mx == -INFINITY ? 0.f : mx;
-                        }
-                    }
-                    half_probs(pb[0], s[0]);
-                    half_probs(pb[1], s[1]);
-                }
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
+                                 fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3]))) * qscale;
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                m[rt] = mx == -INFINITY ? 0.f : mx;
             }
-            if ((t & 1) == 0) {                    // staging: store block t/2+1, load t/2+2
-                const int b = (t >> 1) + 1;
-                if (b < n) store_block(stage(b));
-                if (b + 1 < n) load_block(b + 1);
-            }
-            // phase barrier: this wave's LDS accesses done; loads in flight stay in flight
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+        }
+        for (int e = 0; e < n_main; ++e) {
+            __syncthreads();
+            const bf16_t *sK = ring + (e & 1) * 2 * kPfTileElems;
+            const bf16_t *sV = sK + kPfTileElems;
+            const bool more = e + 1 < n;
+            if (more) load_block(blk_at(e + 1));
+            block_compute(sK, sV, false);
+            if (more) store_block(ring + ((e + 1) & 1) * 2 * kPfTileElems);
+        }
+        if (last_diag) {                           // block n-1, staged by the loop (or the prologue)
+            __syncthreads();
+            const bf16_t *sK = ring + (n_main & 1) * 2 * kPfTileElems;
+            block_compute(sK, sK + kPfTileElems, true);
         }
         // end of pass: raise references a row outgrew; workgroup-wide redo
         bool redo = false;
