@@ -106,6 +106,49 @@ def copy_calibration(args):
                                            "launches": max(1, args.steps)}}), flush=True)
 
 
+def measured_stream_read_gbs(dev, gib=4, reps=5, launches=5):
+    """HBM stream-read ceiling measured with the library's stream-read kernel
+    (a whole-GPU grid reading a 4 GiB buffer once per launch, 5 launches back to
+    back per timing): median GB/s."""
+    import statistics
+    import torch
+    from block_sparse_attention_12_amd import stream_read
+    buf = torch.ones((gib << 30) // 4, dtype=torch.int32, device=dev)
+    out = stream_read(buf)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0, e1 = _events(2)
+        e0.record(stream)
+        for _ in range(launches):
+            stream_read(buf, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / launches)
+    del buf
+    return round((gib << 30) / 1e9 / (statistics.median(times) * 1e-3), 1)
+
+
+def measured_matmul_tflops(dev, n=8192, reps=10):
+    """bf16 dense GEMM ceiling measured with torch.matmul (the vendor library) on
+    n x n x n: median TFLOP/s."""
+    import statistics
+    import torch
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = torch.matmul(a, b)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0, e1 = _events(2)
+        e0.record(stream)
+        torch.matmul(a, b, out=c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return round(2.0 * n ** 3 / (statistics.median(times) * 1e-3) / 1e12, 1)
+
+
 def _events(n):
     import torch
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -236,6 +279,10 @@ def bench_decode(args, w):
                      "traffic": recorded_traffic(f"{w.name}_decode"),
                      "bytes_per_launch": attn_bytes},
     }
+    ceil = measured_stream_read_gbs(dev)
+    out["roofline"]["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
+                                           "GB/s": ceil, "frac": round(attn_gbs / ceil, 4),
+                                           "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, inp, lens, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -260,7 +307,8 @@ def cpu_baseline_decode(w, inp, lens, budget_s):
         Kc = oracle.compressed_keys(K, lens[b] - 1, w.dtype)
         host[(b, h)] = (K, V, Kc)
     done, t_units = 0, 0.0
-    with threadpoolctl.threadpool_limits(1):
+    n_threads = min(len(os.sched_getaffinity(0)), 16)
+    with threadpoolctl.threadpool_limits(n_threads):
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < budget_s:
             for (b, h) in units:
@@ -272,10 +320,11 @@ def cpu_baseline_decode(w, inp, lens, budget_s):
             done += 1
         t_units = time.perf_counter() - t0
     sec_per_step = t_units / done
-    return {"value": round(w.B / sec_per_step, 3), "unit": "tokens/s", "cores": 1,
+    return {"value": round(w.B / sec_per_step, 3), "unit": "tokens/s", "cores": n_threads,
             "kind": "oracle",
             "sample": f"{done} full decode steps of {w.name} (all {len(units)} units: append, "
-                      f"select, attend), numpy fp64, BLAS limited to 1 thread, {t_units:.1f} s"}
+                      f"select, attend), numpy fp64, BLAS threads = {n_threads} (CPU affinity, "
+                      f"at most 16), {t_units:.1f} s"}
 
 
 def bench_crosslayer(args, w):
@@ -347,6 +396,9 @@ def bench_crosslayer(args, w):
         "gpu_ms_per_step": round(gpu_ms, 5), "step_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
     }
+    ceil = measured_stream_read_gbs(dev)
+    out["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)", "GB/s": ceil,
+                               "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
     print(json.dumps(out), flush=True)
 
 
@@ -437,6 +489,9 @@ def bench_prefill(args):
                      "unit": "TFLOP/s", "frac": round(attn_tf / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(f"{w.name}_attn"), "flops_per_launch": attn_flops},
     }
+    ceil = measured_matmul_tflops(dev)
+    out["roofline"]["measured_ceiling"] = {"what": "bf16 GEMM 8192^3 (torch.matmul)",
+                                           "TFLOP/s": ceil, "frac": round(attn_tf / ceil, 4)}
     print(json.dumps(out), flush=True)
 
 

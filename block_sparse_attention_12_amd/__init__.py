@@ -42,6 +42,7 @@ EXPORTS = [
     "sparse_attn_decode_workspace_size", "sparse_attn_decode",
     "sparse_attn_prefill_tile_cap", "sparse_attn_prefill_workspace_size",
     "sparse_attn_prefill_chunk", "sparse_attn_prefill_attend",
+    "sparse_attn_stream_read_blocks", "sparse_attn_stream_read",
 ]
 
 
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_prefill_attend.restype = _int
     L.sparse_attn_prefill_attend.argtypes = [_vp, _i64, _i64, _vp, _vp, _int, _int, _int, _int, _i64,
                                              _vp, _i32, _vp, _f32, _vp, _int, _vp, _vp]
+    L.sparse_attn_stream_read_blocks.restype = _int
+    L.sparse_attn_stream_read_blocks.argtypes = []
+    L.sparse_attn_stream_read.restype = _int
+    L.sparse_attn_stream_read.argtypes = [_vp, _sz, _vp, _vp]
     _lib = L
     return L
 
@@ -305,3 +310,16 @@ def prefill_attend(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tens
                                           _dtype_code(O), _opt(lse, "lse"), _stream(Q, stream))
     _check("sparse_attn_prefill_attend", st)
     return O, lse
+
+
+def stream_read(buf: torch.Tensor, xor_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Reads a contiguous device buffer once (HBM stream-read ceiling measurement).
+    Returns the per-workgroup XOR words (int32 view of uint32)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    if xor_out is None:
+        xor_out = torch.empty(lib().sparse_attn_stream_read_blocks(), dtype=torch.int32, device=buf.device)
+    st = lib().sparse_attn_stream_read(_dev(buf, "buf"), nbytes, _dev(xor_out, "xor_out"), _stream(buf, stream))
+    _check("sparse_attn_stream_read", st)
+    return xor_out

@@ -58,4 +58,7 @@ int launch_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void
                           int32_t tile_idx_cap, const int32_t *tile_cnt, float scale, void *O,
                           int out_dtype, float *lse_out, hipStream_t stream);
 
+constexpr int kStreamReadBlocks = 2048;   // workgroups of the stream-read grid
+int launch_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, hipStream_t stream);
+
 }  // namespace sa

@@ -177,4 +177,12 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                  tile_cnt, scale, O, out_dtype, lse_out, (hipStream_t)stream);
 }
 
+int sparse_attn_stream_read_blocks(void) { return kStreamReadBlocks; }
+
+int sparse_attn_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, void *stream) {
+    if (!buf || !xor_out || bytes == 0 || bytes % 16 != 0) return SA_ERR_INVALID_ARG;
+    if ((uintptr_t)buf % 16 != 0) return SA_ERR_INVALID_ARG;
+    return launch_stream_read(buf, bytes, xor_out, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -250,6 +250,22 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                const int32_t *tile_cnt, float scale, void *O, int out_dtype,
                                float *lse_out, void *stream);
 
+/*
+ * sparse_attn_stream_read - measurement utility, not a step of the method: reads
+ * a device buffer once with a whole-GPU grid (the HBM stream-read ceiling that
+ * the bandwidth-bound kernels are compared against, next to the vendor peak).
+ * Each of the sparse_attn_stream_read_blocks() workgroups writes the XOR of the
+ * 32-bit words it read to xor_out[workgroup]; the XOR over all of xor_out is the
+ * XOR of the whole buffer.
+ *
+ *   buf      device pointer, 16-byte aligned, caller-owned, read only
+ *   bytes    > 0, multiple of 16
+ *   xor_out  device uint32 [sparse_attn_stream_read_blocks()], written
+ * Errors: SA_ERR_INVALID_ARG (null pointer, size or alignment), SA_ERR_HIP.
+ */
+int sparse_attn_stream_read_blocks(void);
+int sparse_attn_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

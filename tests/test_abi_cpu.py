@@ -177,3 +177,13 @@ def test_prefill_attend_validation():
     assert call(Hq=8) == sa.SA_ERR_UNSUPPORTED
     assert call(dtype=sa.SA_F32) == sa.SA_ERR_UNSUPPORTED
     assert call(T_cap=1000) == sa.SA_ERR_CAPACITY
+
+
+def test_stream_read_validation():
+    L = sa.lib()
+    assert L.sparse_attn_stream_read_blocks() > 0
+    assert L.sparse_attn_stream_read(None, 1024, FAKE, None) == sa.SA_ERR_INVALID_ARG
+    assert L.sparse_attn_stream_read(FAKE, 0, FAKE, None) == sa.SA_ERR_INVALID_ARG
+    assert L.sparse_attn_stream_read(FAKE, 1000, FAKE, None) == sa.SA_ERR_INVALID_ARG   # not a multiple of 16
+    assert L.sparse_attn_stream_read(FAKE + 8, 1024, FAKE, None) == sa.SA_ERR_INVALID_ARG  # misaligned
+    assert L.sparse_attn_stream_read(FAKE, 1024, None, None) == sa.SA_ERR_INVALID_ARG

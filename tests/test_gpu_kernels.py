@@ -260,3 +260,16 @@ def test_graph_replay_matches_eager_step():
         assert torch.equal(dec.O, ref_O), r
         assert torch.equal(Kc, ref_kc), r
         _ = (inp["Q"].float() * 2).sum().item()  # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 24) + 16 * 777])
+def test_stream_read_xor_matches_host(nbytes):
+    """The stream-read measurement kernel reads every word exactly once: the XOR
+    of its per-workgroup words equals the XOR of the buffer."""
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    out = sa.stream_read(host.to("cuda"))
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert got == want
