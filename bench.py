@@ -62,6 +62,8 @@ def main():
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
     w = synth.WORKLOADS[args.workload]
+    if w.lookahead:
+        return bench_lookahead(args, w)
     if w.layers > 1:
         return bench_crosslayer(args, w)
     return bench_decode(args, w)
@@ -285,6 +287,94 @@ def bench_decode(args, w):
                                            "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, inp, lens, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_lookahead(args, w):
+    """A decode step through w.layers layers of the 128K Forecast workload, each
+    layer appending, selecting with its own Forecast and attending. Measured
+    in order on one stream and with layer l+1's selection on a second stream
+    while layer l attends; both as eager launches and as one captured graph per
+    step. value = sequences / step time of the lookahead graph."""
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import LookaheadDecoder
+    from block_sparse_attention_12_amd import n_blocks
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    la = LookaheadDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, device=dev,
+                          n_split=args.n_split)
+    layers = []
+    for l in range(w.layers):
+        inp = synth.make_decode_inputs(w, device=dev, layer=l)
+        lens = inp["seq_lens"]
+        Kc = la.new_kc(inp["K"].dtype)
+        la.build(inp["K"], Kc, lens - 1)
+        layers.append(dict(Q=inp["Q"], F=inp["F"], K=inp["K"], V=inp["V"], Kc=Kc))
+        del inp
+    lens_now = lens
+    lens_prev = lens_now - 1
+    outs = [(torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)) for _ in range(w.layers)]
+    stream = torch.cuda.current_stream()
+
+    def run(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(2)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+    def seq():
+        la.step(layers, lens_prev, lens_now, outs, lookahead=False)
+
+    def ahead():
+        la.step(layers, lens_prev, lens_now, outs, lookahead=True)
+
+    res = {"eager_in_order": run(seq, args.steps), "eager_lookahead": run(ahead, args.steps)}
+    g_seq = la.dec[0].capture(seq)
+    g_ahead = la.dec[0].capture(ahead)
+    res["graph_in_order"] = run(g_seq.replay, args.steps)
+    res["graph_lookahead"] = run(g_ahead.replay, args.steps)
+    ms_step, gpu_ms = res["graph_lookahead"]
+    row = 128 * 2
+    L = w.T
+    idx = la.dec[(w.layers - 1) % 2].idx.cpu().numpy()
+    cnt = la.dec[(w.layers - 1) % 2].cnt.cpu().numpy()
+    per_layer_kv = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for blk in idx[b, h, :int(cnt[b, h])].tolist():
+                per_layer_kv += 2 * row * max(0, min(64, L - 64 * blk))
+    nb = n_blocks(L)
+    scan = w.B * w.Hkv * (nb - w.n_init - w.n_local) * 3 * row      # inside entries of candidates
+    step_bytes = w.layers * (per_layer_kv + scan + w.B * w.Hq * (row + 128 * 4 + 4))
+    out = {
+        "metric": "decode tokens/s through 4 Forecast-selected layers at 128K (lookahead selection), 1 GPU",
+        "value": round(w.B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), planted blocks)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.T, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "layers": w.layers, "top_k": w.top_k,
+                   "selector": "forecast", "launch": "one hip graph per step, two streams",
+                   "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "modes_ms_per_step": {k: {"wall": round(v[0], 5), "gpu": round(v[1], 5)} for k, v in res.items()},
+        "hidden_selection_us_per_step": round((res["graph_in_order"][1] - gpu_ms) * 1e3, 2),
+        "per_layer_us": round(gpu_ms * 1e3 / w.layers, 2),
+        "step_bytes": step_bytes, "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+    }
+    ceil = measured_stream_read_gbs(dev)
+    out["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)", "GB/s": ceil,
+                               "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
     print(json.dumps(out), flush=True)
 
 

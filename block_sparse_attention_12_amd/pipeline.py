@@ -106,6 +106,78 @@ class SparseDecoder:
         return res
 
 
+class LookaheadDecoder:
+    """A decode step through several layers, each selecting its own blocks with
+    its own Forecast (Eq. 4 with F_l, one vector per GQA group), where layer
+    l+1's append and selection run on a second stream while layer l attends:
+    the Forecast of the next layer is available before this layer's attention,
+    so selection leaves the critical path (the lookahead the SparDA page
+    describes between the Forecast and its use one layer later). Two sets of
+    selection buffers alternate between layers; every dependency is an event
+    (selection of layer l+1 waits for attention of layer l-1, which last read
+    that buffer set; attention of layer l waits for its selection).
+    """
+
+    def __init__(self, B: int, Hq: int, Hkv: int, T_cap: int, top_k: int, n_init: int = 1,
+                 n_local: int = 2, device="cuda", n_split: int = 0, out_dtype=torch.float32):
+        self.dec = [SparseDecoder(B, Hq, Hkv, T_cap, top_k, n_init, n_local, "forecast", "raw_sum",
+                                  device=device, n_split=n_split, out_dtype=out_dtype)
+                    for _ in range(2)]
+        self.device = torch.device(device)
+        self.side = torch.cuda.Stream(device=self.device)   # default priority
+
+    def new_kc(self, dtype) -> torch.Tensor:
+        return self.dec[0].new_kc(dtype)
+
+    def build(self, K, Kc, seq_lens):
+        self.dec[0].build(K, Kc, seq_lens)
+
+    def step(self, layers: Sequence[dict], lens_prev, lens_now, outs, scale=1.0,
+             lookahead: bool = True):
+        """layers: dicts with F (Forecast, [B, Hkv, d]), Q, K, V (K/V already hold
+        the new token) and Kc (that layer's compressed keys); outs: list of
+        (O, lse) per layer. With lookahead=False everything runs in order on the
+        current stream (the same calls, for comparison)."""
+        main = torch.cuda.current_stream(self.device)
+        n = len(layers)
+        if not lookahead:
+            for l, lay in enumerate(layers):
+                d = self.dec[l % 2]
+                d.append(lay["K"], lay["Kc"], lens_prev, lens_now)
+                d.select(lay["F"], lay["Kc"], lens_now)
+                d.attend(lay["Q"], lay["K"], lay["V"], lens_now, O=outs[l][0], lse=outs[l][1],
+                         scale=scale)
+            return outs
+        side = self.side
+        side.wait_stream(main)                     # the step's inputs are in place
+
+        def select_on_side(l):
+            d, lay = self.dec[l % 2], layers[l]
+            with torch.cuda.stream(side):
+                d.append(lay["K"], lay["Kc"], lens_prev, lens_now)
+                d.select(lay["F"], lay["Kc"], lens_now)
+                ev = torch.cuda.Event()
+                ev.record(side)
+            return ev
+
+        sel_done = select_on_side(0)
+        att_done = [None] * n
+        for l, lay in enumerate(layers):
+            main.wait_event(sel_done)
+            if l + 1 < n:
+                if l >= 1:
+                    side.wait_event(att_done[l - 1])   # buffers of layer l+1 = those of l-1
+                next_done = select_on_side(l + 1)
+            self.dec[l % 2].attend(lay["Q"], lay["K"], lay["V"], lens_now, O=outs[l][0],
+                                   lse=outs[l][1], scale=scale)
+            att_done[l] = torch.cuda.Event()
+            att_done[l].record(main)
+            if l + 1 < n:
+                sel_done = next_done
+        main.wait_stream(side)                     # join: the side stream is idle after the step
+        return outs
+
+
 class SparsePrefill:
     """Buffers and call for chunked sparse prefill of one sequence."""
 

@@ -47,8 +47,10 @@ class DecodeWorkload:
     score_mode: str         # "softmax_sum" or "raw_sum"
     planted: int            # planted blocks per (sequence, KV head)
     seed: int
-    layers: int = 1         # layers sharing one selection (cross-layer reuse)
+    layers: int = 1         # layers sharing one selection (cross-layer reuse), or decoded per step
     steps: int = 0          # appended decode steps (cross-layer workload only)
+    lookahead: bool = False # each layer selects with its own Forecast; layer l+1's selection
+                            # runs while layer l attends
 
     @property
     def G(self) -> int:
@@ -95,6 +97,12 @@ WORKLOADS = {
         "decode_forecast_bf16_128k", B=8, Hq=32, Hkv=8, d=128, T=131072, dtype="bf16",
         top_k=64, n_init=1, n_local=2, selector="forecast", score_mode="raw_sum",
         planted=8, seed=3),
+    # the 128K Forecast decode through 4 layers, each with its own selection,
+    # layer l+1's selection overlapped with layer l's attention
+    "lookahead_forecast_bf16_128k": DecodeWorkload(
+        "lookahead_forecast_bf16_128k", B=8, Hq=32, Hkv=8, d=128, T=131072, dtype="bf16",
+        top_k=64, n_init=1, n_local=2, selector="forecast", score_mode="raw_sum",
+        planted=8, seed=3, layers=4, lookahead=True),
     # cross-layer reuse: 4 layers share layer 0's selection, 16 appended steps
     "crosslayer_bf16_64k": DecodeWorkload(
         "crosslayer_bf16_64k", B=32, Hq=32, Hkv=8, d=128, T=65536, dtype="bf16",
