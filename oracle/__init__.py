@@ -27,6 +27,7 @@ from .attention import sparse_attention, lse_merge, split_attention_partials
 from .decode import decode_step, decode_unit
 from .prefill import prefill_tile_select, prefill_attention, prefill_chunk
 from .crosslayer import crosslayer_step
+from .quality import block_mass, recall, rest_bucket_distribution, mass_optimal_blocks
 
 __all__ = [
     "bf16_round", "round_to", "n_compressed", "n_blocks", "compressed_keys",
@@ -34,4 +35,5 @@ __all__ = [
     "block_entries", "candidate_sets", "top_k_blocks", "select_blocks", "SelectParams",
     "sparse_attention", "lse_merge", "split_attention_partials", "decode_step", "decode_unit",
     "prefill_tile_select", "prefill_attention", "prefill_chunk", "crosslayer_step",
+    "block_mass", "recall", "rest_bucket_distribution", "mass_optimal_blocks",
 ]
