@@ -42,6 +42,7 @@ EXPORTS = [
     "sparse_attn_decode_workspace_size", "sparse_attn_decode",
     "sparse_attn_prefill_tile_cap", "sparse_attn_prefill_workspace_size",
     "sparse_attn_prefill_chunk", "sparse_attn_prefill_attend",
+    "sparse_attn_block_mass_workspace_size", "sparse_attn_block_mass",
     "sparse_attn_stream_read_blocks", "sparse_attn_stream_read",
 ]
 
@@ -107,6 +108,11 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_prefill_attend.restype = _int
     L.sparse_attn_prefill_attend.argtypes = [_vp, _i64, _i64, _vp, _vp, _int, _int, _int, _int, _i64,
                                              _vp, _i32, _vp, _f32, _vp, _int, _vp, _vp]
+    L.sparse_attn_block_mass_workspace_size.restype = _sz
+    L.sparse_attn_block_mass_workspace_size.argtypes = [_int, _int, _i64]
+    L.sparse_attn_block_mass.restype = _int
+    L.sparse_attn_block_mass.argtypes = [_vp, _vp, _int, _int, _int, _int, _int, _i64, _vp, _f32, _vp,
+                                         _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp]
     L.sparse_attn_stream_read_blocks.restype = _int
     L.sparse_attn_stream_read_blocks.argtypes = []
     L.sparse_attn_stream_read.restype = _int
@@ -323,3 +329,28 @@ def stream_read(buf: torch.Tensor, xor_out: Optional[torch.Tensor] = None, strea
     st = lib().sparse_attn_stream_read(_dev(buf, "buf"), nbytes, _dev(xor_out, "xor_out"), _stream(buf, stream))
     _check("sparse_attn_stream_read", st)
     return xor_out
+
+
+def block_mass(Q: torch.Tensor, K: torch.Tensor, seq_lens: torch.Tensor, scale: float = 1.0,
+               idx: Optional[torch.Tensor] = None, cnt: Optional[torch.Tensor] = None,
+               mass: Optional[torch.Tensor] = None, recall: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Exact attention mass per 64-token block of each head's decode query, and
+    the recall of (idx, cnt) if given. Returns (mass [B, Hq, nb], recall or None)."""
+    B, Hq, d = Q.shape
+    Hkv, T_cap = K.shape[1], K.shape[2]
+    nb = n_blocks(T_cap)
+    if mass is None:
+        mass = torch.empty((B, Hq, nb), dtype=torch.float32, device=Q.device)
+    if idx is not None and recall is None:
+        recall = torch.empty((B, Hq), dtype=torch.float32, device=Q.device)
+    ws_need = lib().sparse_attn_block_mass_workspace_size(B, Hq, mass.shape[-1])
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=Q.device)
+    st = lib().sparse_attn_block_mass(_dev(Q, "Q"), _dev(K, "K"), _dtype_code(K), B, Hq, Hkv, d, T_cap,
+                                      _dev(seq_lens, "seq_lens"), float(scale), _dev(mass, "mass"),
+                                      mass.shape[-1], _opt(idx, "idx"), _opt(cnt, "cnt"),
+                                      idx.shape[-1] if idx is not None else 0, _opt(recall, "recall"),
+                                      _dev(workspace, "workspace"), workspace.numel(), _stream(Q, stream))
+    _check("sparse_attn_block_mass", st)
+    return mass, recall

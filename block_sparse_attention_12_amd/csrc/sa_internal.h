@@ -58,6 +58,12 @@ int launch_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const void
                           int32_t tile_idx_cap, const int32_t *tile_cnt, float scale, void *O,
                           int out_dtype, float *lse_out, hipStream_t stream);
 
+size_t block_mass_workspace_bytes(int B, int Hq, int64_t nb_cap);
+int launch_block_mass(const void *Q, const void *K, int dtype, int B, int Hq, int Hkv, int64_t T_cap,
+                      const int32_t *seq_lens, float scale, float *mass, int64_t nb_cap,
+                      const int32_t *idx, const int32_t *cnt, int idx_cap, float *recall,
+                      void *workspace, hipStream_t stream);
+
 constexpr int kStreamReadBlocks = 2048;   // workgroups of the stream-read grid
 int launch_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, hipStream_t stream);
 

@@ -177,6 +177,28 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                  tile_cnt, scale, O, out_dtype, lse_out, (hipStream_t)stream);
 }
 
+size_t sparse_attn_block_mass_workspace_size(int B, int Hq, int64_t mass_cap) {
+    if (B <= 0 || Hq <= 0 || mass_cap <= 0) return 0;
+    return block_mass_workspace_bytes(B, Hq, mass_cap);
+}
+
+int sparse_attn_block_mass(const void *Q, const void *K, int dtype, int B, int Hq, int Hkv, int d,
+                           int64_t T_cap, const int32_t *seq_lens, float scale, float *mass_out,
+                           int64_t mass_cap, const int32_t *idx, const int32_t *cnt,
+                           int32_t idx_cap, float *recall_out, void *workspace, size_t ws_bytes,
+                           void *stream) {
+    if (!Q || !K || !seq_lens || !mass_out) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || T_cap <= 0) return SA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0 || !(scale == scale)) return SA_ERR_INVALID_ARG;
+    if (idx && (!cnt || !recall_out || idx_cap <= 0)) return SA_ERR_INVALID_ARG;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (mass_cap < n_blocks(T_cap)) return SA_ERR_CAPACITY;
+    if (!workspace || ws_bytes < block_mass_workspace_bytes(B, Hq, mass_cap)) return SA_ERR_WORKSPACE;
+    return launch_block_mass(Q, K, dtype, B, Hq, Hkv, T_cap, seq_lens, scale, mass_out, mass_cap,
+                             idx, cnt, idx_cap, recall_out, workspace, (hipStream_t)stream);
+}
+
 int sparse_attn_stream_read_blocks(void) { return kStreamReadBlocks; }
 
 int sparse_attn_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, void *stream) {

@@ -251,6 +251,34 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                float *lse_out, void *stream);
 
 /*
+ * sparse_attn_block_mass - selection quality, not a step of the sparse path:
+ * the exact attention mass of every 64-token block for the decode query of
+ * each head (the sum of the block's dense attention probabilities, the
+ * quantity the CoSA abstract on the page "CoSA ..." reduces block selection
+ * to), and optionally the recall of a selected block set (the mass it
+ * captures: one minus the rest bucket of Eq. 7 on the page "SparDA ...",
+ * section "Training"). Reads every visible key.
+ *
+ *   Q [B, Hq, d], K [B, Hkv, T_cap, d] device, dtype SA_F32 or SA_BF16; the
+ *   query of sequence b sits at position seq_lens[b] - 1 and sees t < seq_lens[b]
+ *   (lengths clamped to [0, T_cap]); probabilities softmax_t(scale * q . k_t).
+ *   mass_out  [B, Hq, mass_cap] device fp32, written (0 past a sequence's
+ *             block count); mass_cap >= ceil(T_cap / 64)
+ *   idx, cnt  optional block sets as produced by sparse_attn_select
+ *             ([B, Hkv, idx_cap], [B, Hkv]); then recall_out [B, Hq] device
+ *             fp32 is written (ids outside the sequence's blocks count 0)
+ *   workspace >= sparse_attn_block_mass_workspace_size(B, Hq, mass_cap) bytes
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4),
+ *         SA_ERR_CAPACITY (mass_cap), SA_ERR_WORKSPACE.
+ */
+size_t sparse_attn_block_mass_workspace_size(int B, int Hq, int64_t mass_cap);
+int sparse_attn_block_mass(const void *Q, const void *K, int dtype, int B, int Hq, int Hkv, int d,
+                           int64_t T_cap, const int32_t *seq_lens, float scale, float *mass_out,
+                           int64_t mass_cap, const int32_t *idx, const int32_t *cnt,
+                           int32_t idx_cap, float *recall_out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
+/*
  * sparse_attn_stream_read - measurement utility, not a step of the method: reads
  * a device buffer once with a whole-GPU grid (the HBM stream-read ceiling that
  * the bandwidth-bound kernels are compared against, next to the vendor peak).

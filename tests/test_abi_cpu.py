@@ -187,3 +187,28 @@ def test_stream_read_validation():
     assert L.sparse_attn_stream_read(FAKE, 1000, FAKE, None) == sa.SA_ERR_INVALID_ARG   # not a multiple of 16
     assert L.sparse_attn_stream_read(FAKE + 8, 1024, FAKE, None) == sa.SA_ERR_INVALID_ARG  # misaligned
     assert L.sparse_attn_stream_read(FAKE, 1024, None, None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_block_mass_validation():
+    L = sa.lib()
+
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, dtype=sa.SA_BF16, B=2, Hq=8, Hkv=2, d=128, T_cap=1000, lens=FAKE,
+                 mass=FAKE, mass_cap=16, idx=None, cnt=None, idx_cap=0, recall=None, ws=FAKE,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sparse_attn_block_mass(a["Q"], a["K"], a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                        a["T_cap"], a["lens"], 1.0, a["mass"], a["mass_cap"], a["idx"],
+                                        a["cnt"], a["idx_cap"], a["recall"], a["ws"], a["ws_bytes"], None)
+    assert call(Q=None) == sa.SA_ERR_INVALID_ARG
+    assert call(mass=None) == sa.SA_ERR_INVALID_ARG
+    assert call(dtype=9) == sa.SA_ERR_INVALID_ARG
+    assert call(Hq=7) == sa.SA_ERR_INVALID_ARG
+    assert call(idx=FAKE) == sa.SA_ERR_INVALID_ARG                   # set without cnt / recall
+    assert call(Hq=16) == sa.SA_ERR_UNSUPPORTED                      # G = 8
+    assert call(d=64) == sa.SA_ERR_UNSUPPORTED
+    assert call(mass_cap=15) == sa.SA_ERR_CAPACITY                   # ceil(1000 / 64) = 16
+    need = L.sparse_attn_block_mass_workspace_size(2, 8, 16)
+    assert need == 2 * 2 * 8 * 16 * 4
+    assert call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ws=None) == sa.SA_ERR_WORKSPACE
