@@ -281,6 +281,7 @@ def bench_decode(args, w):
                      "traffic": recorded_traffic(f"{w.name}_decode"),
                      "bytes_per_launch": attn_bytes},
     }
+    out["selection_quality"] = selection_quality(w, reps[0], dec, sel_name, lens_now)
     ceil = measured_stream_read_gbs(dev)
     out["roofline"]["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
                                            "GB/s": ceil, "frac": round(attn_gbs / ceil, 4),
@@ -288,6 +289,42 @@ def bench_decode(args, w):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, inp, lens, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def selection_quality(w, rep, dec, sel_name, lens):
+    """Recall of the dense attention mass by the selected blocks (exact block
+    masses from sparse_attn_block_mass on the first replica, the selection made
+    by that replica's step), next to the best recall any set of the same shape
+    (init + local + k candidates) could reach: the k candidates of largest mass,
+    taken on the host from the kernel's masses."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_12_amd import block_mass
+
+    dec.select(rep[sel_name], rep["Kc"], lens)
+    ev0, ev1 = _events(2)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    mass, rec = block_mass(rep["Q"], rep["K"], lens, 1.0, idx=dec.idx, cnt=dec.cnt)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    M, R = mass.cpu().numpy().astype(np.float64), rec.cpu().numpy()
+    best = []
+    for b in range(w.B):
+        nb = -(-int(lens[b]) // 64)
+        cand = np.arange(w.n_init, nb - w.n_local)
+        for hq in range(w.Hq):
+            m = M[b, hq, :nb]
+            top = np.sort(m[cand])[::-1][:w.top_k].sum() if len(cand) else 0.0
+            best.append(m[:w.n_init].sum() + m[nb - w.n_local:].sum() + top)
+    best = np.array(best)
+    return {"recall_mean": round(float(R.mean()), 4), "recall_min": round(float(R.min()), 4),
+            "mass_optimal_recall_mean": round(float(best.mean()), 4),
+            "uniform_share": round((w.top_k + w.n_init + w.n_local) / (-(-w.T // 64)), 4),
+            "block_mass_ms": round(ev0.elapsed_time(ev1), 4),
+            "note": "dense attention mass of each query head captured by its KV head's selected "
+                    "blocks (mean / min over heads); synthetic queries are independent of the "
+                    "selector except along planted directions"}
 
 
 def bench_lookahead(args, w):
