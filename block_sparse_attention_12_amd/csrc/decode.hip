@@ -40,7 +40,6 @@ namespace sa {
 constexpr int kDecThreads = 256;
 constexpr int kDecG = 4;
 constexpr int kPartStride = kD + 4;          // acc[128], max, sum, 2 pad (16 B aligned rows)
-constexpr int kMaxSplit = 64;                // splits per (b, kvh) (4 heads x 64 = one per thread)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -306,64 +305,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if (lse && (tid & 63) == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-// Merges the n_split partials of one (b, kvh) unit's 4 heads: every (head,
-// split) max and sum is loaded by its own thread, the per-head weights are
-// formed in LDS, then each thread gathers its two channels from all splits
-// with 8 loads in flight at a time.
+// Merges the n_split partials of one (b, kvh) unit's 4 heads. Thread
+// (head g, channels 2c, 2c+1) loads, for eight splits at a time, each split's
+// (max, sum) pair (the same address on every lane of the wave, one cache line)
+// and its own two weighted-value channels, all sixteen loads in flight at once,
+// and merges them with log-sum-exp weights against the running maximum. Up to
+// eight splits this is one memory round trip and no workgroup barrier.
 __global__ __launch_bounds__(kDecThreads) void combine_kernel(
     const float *__restrict__ part, int n_split, int Hq, int Hkv, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
     constexpr int G = kDecG;
-    __shared__ float s_w[G * kMaxSplit], s_l[G * kMaxSplit];
-    __shared__ float s_M[G], s_L[G];
     const int unit = blockIdx.x;
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int tid = threadIdx.x;
-    const int64_t row0 = (int64_t)b * Hq + (int64_t)kvh * G;
-    const float *up = part + row0 * n_split * kPartStride;
-    if (tid < G * n_split) {
-        const float *ps = up + tid * kPartStride;        // (head tid / n_split, split tid % n_split)
-        s_w[tid] = ps[kD];
-        s_l[tid] = ps[kD + 1];
-    }
-    __syncthreads();
-    if (tid < G) {
-        float Mg = -INFINITY;
-        for (int s = 0; s < n_split; ++s) Mg = fmaxf(Mg, s_w[tid * n_split + s]);
-        float Lg = 0.f;
-        for (int s = 0; s < n_split; ++s) {
-            const float ms = s_w[tid * n_split + s];
-            const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - Mg);
-            s_w[tid * n_split + s] = wt;
-            Lg = fmaf(wt, s_l[tid * n_split + s], Lg);
-        }
-        s_M[tid] = Mg;
-        s_L[tid] = Lg;
-    }
-    __syncthreads();
     const int g = tid >> 6;
     const int c2 = (tid & 63) * 2;
-    const float *pg = up + (int64_t)g * n_split * kPartStride + c2;
-    const float *wg = &s_w[g * n_split];
-    float a0 = 0.f, a1 = 0.f;
-    int s0 = 0;
-    for (; s0 + 8 <= n_split; s0 += 8) {
-        float2 a[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) a[k] = *reinterpret_cast<const float2 *>(pg + (s0 + k) * kPartStride);
+    const int64_t row = (int64_t)b * Hq + (int64_t)kvh * G + g;
+    const float *pg = part + row * n_split * kPartStride;
+    float M = -INFINITY, lsum = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int s0 = 0; s0 < n_split; s0 += 8) {
+        float2 ml[8], a[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            a0 = fmaf(wg[s0 + k], a[k].x, a0);
-            a1 = fmaf(wg[s0 + k], a[k].y, a1);
+            if (s0 + k < n_split) {
+                const float *ps = pg + (int64_t)(s0 + k) * kPartStride;
+                ml[k] = *reinterpret_cast<const float2 *>(ps + kD);
+                a[k] = *reinterpret_cast<const float2 *>(ps + c2);
+            } else {
+                ml[k] = make_float2(-INFINITY, 0.f);
+                a[k] = make_float2(0.f, 0.f);
+            }
         }
+        float Mc = M;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) Mc = fmaxf(Mc, ml[k].x);
+        if (Mc == -INFINITY) continue;                      // nothing seen yet
+        const float w_old = (M == -INFINITY) ? 0.f : exp2f(M - Mc);
+        lsum *= w_old;
+        a0 *= w_old;
+        a1 *= w_old;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float wt = (ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - Mc);
+            lsum = fmaf(wt, ml[k].y, lsum);
+            a0 = fmaf(wt, a[k].x, a0);
+            a1 = fmaf(wt, a[k].y, a1);
+        }
+        M = Mc;
     }
-    for (; s0 < n_split; ++s0) {
-        const float2 a = *reinterpret_cast<const float2 *>(pg + s0 * kPartStride);
-        a0 = fmaf(wg[s0], a.x, a0);
-        a1 = fmaf(wg[s0], a.y, a1);
-    }
-    const float lsum = s_L[g], M = s_M[g];
-    const int64_t row = row0 + g;
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if (out_bf16) {
         const uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);

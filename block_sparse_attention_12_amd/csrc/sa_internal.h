@@ -65,6 +65,7 @@ int launch_block_mass(const void *Q, const void *K, int dtype, int B, int Hq, in
                       void *workspace, hipStream_t stream);
 
 constexpr int kStreamReadBlocks = 2048;   // workgroups of the stream-read grid
+constexpr int kMaxSplit = 64;              // decode workgroups per (b, kvh); 64 blocks per split
 int launch_stream_read(const void *buf, size_t bytes, uint32_t *xor_out, hipStream_t stream);
 
 }  // namespace sa

@@ -19,10 +19,12 @@
 //                         fp32 logits, plus per 512-entry chunk and head the
 //                         running (max, sum of exp) for the softmax denominator.
 //   topk_kernel           one workgroup per (sequence, KV head): merges the
-//                         chunk denominators, forms block scores, finds the
-//                         exact k-th largest (score, -index) key by a 4-pass
-//                         8-bit radix select in LDS, and writes the union in
-//                         ascending block order with a workgroup prefix scan.
+//                         chunk denominators, forms block scores, buckets the
+//                         candidates by value (256 buckets over their range),
+//                         ranks the boundary bucket exactly in LDS (a 4-pass
+//                         8-bit radix select of the exact k-th (score, -index)
+//                         key when the bucketing degenerates), and writes the
+//                         union in ascending block order with a prefix scan.
 #include <float.h>
 #include <math.h>
 
@@ -35,6 +37,8 @@ constexpr int kSelThreads = 256;
 constexpr int kSoftmaxChunk = 512;                  // entries per workgroup (softmax mode)
 constexpr int kRawChunkBlocks = 256;                // blocks per workgroup (raw mode)
 constexpr int64_t kMaxTopkBlocks = 32768;           // 1024 threads x 32 blocks
+constexpr int kBoundaryCap = 512;                   // boundary-bucket candidates ranked in LDS
+constexpr int kBucketMinUnits = 1024;               // top-k grids this large take the bucket path
 
 SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
     SelectWorkspace w{};
@@ -304,21 +308,26 @@ __device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total)
 }
 
 // Thread t owns PER consecutive blocks [t*PER, t*PER + PER): their 32-bit
-// orderable keys stay in registers for the whole kernel, so the radix passes
-// are register compares plus LDS histogram atomics, and the ascending
-// compaction needs only two workgroup prefix scans.
+// orderable keys stay in registers for the whole kernel, so the bucket (and,
+// when needed, radix) passes are register compares plus LDS histogram atomics,
+// and the ascending compaction is one workgroup prefix scan.
 template <int G, bool SOFTMAX, int NT, int PER>
 __global__ __launch_bounds__(NT) void topk_kernel(
     int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens, int top_k,
     int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
     const float2 *__restrict__ stats, int n_chunks, const float *__restrict__ bscore_in,
     float *__restrict__ bscore_out, int32_t *__restrict__ idx_out, int idx_cap,
-    int32_t *__restrict__ cnt_out) {
+    int32_t *__restrict__ cnt_out, int use_buckets) {
     __shared__ uint32_t s_hist[256];
     __shared__ float s_M[G], s_Zinv[G];
     __shared__ float2 s_st[G * 64];
+    constexpr int kSelWords = NT * PER / 32;        // one bit per block this workgroup covers
     __shared__ int s_wave[NT / 64];
-    __shared__ uint32_t s_digit, s_above;
+    __shared__ uint32_t s_digit, s_above, s_nbnd;
+    __shared__ float s_lo[NT / 64], s_hi[NT / 64];
+    __shared__ uint32_t s_sel[kSelWords];
+    __shared__ uint32_t s_bkey[kBoundaryCap];
+    __shared__ int s_bblk[kBoundaryCap];
     const int unit = blockIdx.x;
     const int b = unit / Hkv;
     const int tid = threadIdx.x;
@@ -420,12 +429,129 @@ __global__ __launch_bounds__(NT) void topk_kernel(
         cand[q] = blk >= cand_lo && blk < cand_hi;
     }
 
-    // radix select of the top_k-th largest key among the candidates
     const bool take_all = top_k >= n_cand;
     const bool take_none = top_k <= 0;
+    const bool choose = !take_all && !take_none;
+
+    // Bin of the histogram that holds the `remaining`-th largest counted key
+    // (bins scanned from the top), and the count of keys in the bins above it.
+    auto boundary_bin = [&](int remaining) {
+        if (tid < 64) {
+            // lane l owns bins 4l .. 4l+3; counts above each bin, from the top
+            const uint32_t hb[4] = {s_hist[4 * tid], s_hist[4 * tid + 1], s_hist[4 * tid + 2],
+                                    s_hist[4 * tid + 3]};
+            const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t t = __shfl_down(incl, off, 64);
+                if (tid + off < 64) incl += t;
+            }
+            uint32_t above = incl - c;                   // keys in bins owned by higher lanes
+#pragma unroll
+            for (int k = 3; k >= 0; --k) {
+                if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
+                    s_digit = 4 * tid + k;
+                    s_above = above;
+                }
+                above += hb[k];
+            }
+        }
+        __syncthreads();
+    };
+
+    // Fast path (grids of many units, where the kernel is throughput bound;
+    // with few units its longer chain of dependent steps costs more than the
+    // radix passes it saves): 256 equal-width value buckets over the
+    // candidates' [min, max].
+    // A bucket index is a monotone function of the score (fp32 subtraction of
+    // a constant and multiplication by a positive constant are monotone under
+    // rounding), so every candidate in a bucket above the one holding the k-th
+    // largest score is taken, and only that boundary bucket's candidates are
+    // ranked exactly (score, then lower block id) in LDS. Degenerate ranges
+    // (all scores equal, non-finite) and boundary buckets above kBoundaryCap
+    // fall back to the radix select of the exact k-th key below.
+    int bin[PER];
+    bool fast = false;
+    int bstar = 0;
+    if (choose && use_buckets) {
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (cand[q]) {
+                lo = fminf(lo, score[q]);
+                hi = fmaxf(hi, score[q]);
+            }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            lo = fminf(lo, shfl_xor(lo, off));
+            hi = fmaxf(hi, shfl_xor(hi, off));
+        }
+        if ((tid & 63) == 0) {
+            s_lo[tid >> 6] = lo;
+            s_hi[tid >> 6] = hi;
+        }
+        for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+        for (int i = tid; i < kSelWords; i += NT) s_sel[i] = 0;
+        if (tid == 0) s_nbnd = 0;
+        __syncthreads();
+        lo = s_lo[0];
+        hi = s_hi[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) {
+            lo = fminf(lo, s_lo[w]);
+            hi = fmaxf(hi, s_hi[w]);
+        }
+        const float range = hi - lo;
+        const float inv = 256.f / range;
+        fast = range > 0.f && range <= FLT_MAX && inv <= FLT_MAX;   // same on every thread
+        if (fast) {
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                int bq = -1;
+                if (cand[q]) {
+                    bq = (int)((score[q] - lo) * inv);
+                    bq = bq < 0 ? 0 : (bq > 255 ? 255 : bq);
+                    atomicAdd(&s_hist[bq], 1u);
+                }
+                bin[q] = bq;
+            }
+            __syncthreads();
+            boundary_bin(top_k);
+            bstar = (int)s_digit;
+            const int c = (int)s_hist[bstar];
+            const int r = top_k - (int)s_above;             // taken from the boundary bucket, >= 1
+            if (c <= kBoundaryCap) {
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if (bin[q] == bstar) {
+                        const uint32_t slot = atomicAdd(&s_nbnd, 1u);
+                        s_bkey[slot] = key[q];
+                        s_bblk[slot] = blk0 + q;
+                    }
+                __syncthreads();
+                for (int i = tid; i < c; i += NT) {
+                    const uint32_t ki = s_bkey[i];
+                    const int bi = s_bblk[i];
+                    int rank = 0;
+                    for (int j = 0; j < c; ++j) {
+                        const uint32_t kj = s_bkey[j];
+                        rank += (kj > ki || (kj == ki && s_bblk[j] < bi)) ? 1 : 0;
+                    }
+                    if (rank < r) atomicOr(&s_sel[bi >> 5], 1u << (bi & 31));
+                }
+                __syncthreads();
+            } else {
+                fast = false;
+            }
+        }
+    }
+
+    // Fallback: radix select of the top_k-th largest key among the candidates
+    // (four 8-bit digits of the orderable key, most significant first).
     uint32_t prefix = 0, mask = 0;
     int remaining = top_k;
-    if (!take_all && !take_none) {
+    if (choose && !fast) {
 #pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
             for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
@@ -434,28 +560,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
             for (int q = 0; q < PER; ++q)
                 if (cand[q] && (key[q] & mask) == prefix) atomicAdd(&s_hist[(key[q] >> shift) & 255u], 1u);
             __syncthreads();
-            if (tid < 64) {
-                // counts above each bin, from the top: lane l owns bins 4l .. 4l+3
-                const uint32_t hb[4] = {s_hist[4 * tid], s_hist[4 * tid + 1], s_hist[4 * tid + 2],
-                                        s_hist[4 * tid + 3]};
-                const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
-                uint32_t incl = c;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t t = __shfl_down(incl, off, 64);
-                    if (tid + off < 64) incl += t;
-                }
-                uint32_t above = incl - c;               // keys in bins owned by higher lanes
-#pragma unroll
-                for (int k = 3; k >= 0; --k) {
-                    if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
-                        s_digit = 4 * tid + k;
-                        s_above = above;
-                    }
-                    above += hb[k];
-                }
-            }
-            __syncthreads();
+            boundary_bin(remaining);
             prefix |= s_digit << shift;
             mask |= 255u << shift;
             remaining -= (int)s_above;
@@ -463,14 +568,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     }
     const uint32_t thr = prefix;        // exact key of the k-th largest candidate
     const int take_eq = remaining;      // keys equal to thr that are taken, lowest ids first
-
-    // ascending compaction over this thread's consecutive blocks
-    int n_eq = 0;
-    if (!take_all && !take_none)
+    int rank = 0;
+    if (choose && !fast) {
+        int n_eq = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) n_eq += (cand[q] && key[q] == thr) ? 1 : 0;
-    int unused;
-    int rank = wg_exclusive_scan<NT>(n_eq, s_wave, unused);
+        int unused;
+        rank = wg_exclusive_scan<NT>(n_eq, s_wave, unused);
+    }
+
+    // ascending compaction over this thread's consecutive blocks
     bool in[PER];
     int n_in = 0;
 #pragma unroll
@@ -481,6 +588,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(
         else if (blk < init_hi || blk >= local_lo) x = true;
         else if (take_none) x = false;
         else if (take_all) x = true;
+        else if (fast) x = bin[q] > bstar || (bin[q] == bstar && ((s_sel[blk >> 5] >> (blk & 31)) & 1u));
         else if (key[q] > thr) x = true;
         else if (key[q] == thr) x = rank++ < take_eq;
         else x = false;
@@ -506,10 +614,12 @@ static void launch_topk(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, con
                         const sa_select_params &p, const float *logits, int64_t nc_pad,
                         const float2 *stats, int n_chunks, const float *bscore, float *bs_out,
                         int32_t *idx_out, int idx_cap, int32_t *cnt_out, hipStream_t stream) {
+    const int use_buckets = n_units >= kBucketMinUnits ? 1 : 0;
 #define SA_TOPK(NT, PER)                                                                          \
     hipLaunchKernelGGL((topk_kernel<G, SOFTMAX, NT, PER>), dim3((unsigned)n_units), dim3(NT), 0,   \
                        stream, Hkv, T_cap, nb_cap, seq_lens, p.top_k, p.n_init, p.n_local, logits, \
-                       nc_pad, stats, n_chunks, bscore, bs_out, idx_out, idx_cap, cnt_out)
+                       nc_pad, stats, n_chunks, bscore, bs_out, idx_out, idx_cap, cnt_out,          \
+                       use_buckets)
     if (nb_cap <= 256 * 8) SA_TOPK(256, 8);
     else if (nb_cap <= 1024 * 8) SA_TOPK(1024, 8);
     else SA_TOPK(1024, 32);

@@ -109,7 +109,7 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
     if (Hq % Hkv) return SA_ERR_INVALID_ARG;
     if (!(scale == scale)) return SA_ERR_INVALID_ARG;
     if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
-    if (n_split > 64 || idx_cap > 64 * 64) return SA_ERR_UNSUPPORTED;
+    if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
     if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
     if (s < decode_min_split(idx_cap)) s = decode_min_split(idx_cap);

@@ -150,6 +150,77 @@ def test_select_exact_ties_go_to_lower_index():
         _check_select(selq, K, [T], T, k, 1, 2, "softmax_sum", dt, exact=True)
 
 
+@pytest.mark.parametrize("mode", ["raw_sum", "softmax_sum"])
+@pytest.mark.parametrize("outlier", [False, True])
+def test_select_many_exact_ties_at_the_threshold(mode, outlier):
+    """Block scores that take four values only (every key of block b is
+    v_b * e_0), so the k-th largest sits in a run of ~150 exactly equal
+    scores: ties must go to the lower block ids. With one outlier block far
+    above the rest, every other score lands in the lowest value bucket and the
+    top-k falls back to the exact radix select; without it, the boundary
+    bucket is ranked directly."""
+    dt = "bf16"
+    nb = 600
+    T = 64 * nb
+    g = torch.Generator().manual_seed(21)
+    v = (torch.randint(0, 4, (2, nb), generator=g).float() * 0.25)
+    if outlier:
+        # far above the rest, yet small enough that the others' softmax terms
+        # stay normal fp32 numbers (no underflow to equal zeros)
+        v[:, 300] = 1000.0 if mode == "raw_sum" else 40.0
+    K = torch.zeros((1, 2, T, 128))
+    K[0, :, :, 0] = v.repeat_interleave(64, dim=1)
+    K = K.to(TD[dt])
+    if mode == "raw_sum":
+        sel = torch.zeros((1, 2, 128))
+        sel[..., 0] = 1.0
+    else:
+        sel = torch.zeros((1, 8, 128))
+        sel[..., 0] = 0.5
+    for k in (1, 100, 300):
+        _check_select(sel.to(TD[dt]), K, [T], T, k, 1, 2, mode, dt, exact=True)
+
+
+@pytest.mark.parametrize("mode", ["raw_sum", "softmax_sum"])
+@pytest.mark.parametrize("pattern", ["four_values", "outlier", "all_equal"])
+def test_select_ties_on_a_grid_of_many_units(mode, pattern):
+    """1024 (sequence, KV head) units, the grid size from which the top-k
+    buckets candidates by value before ranking: exact ties at the threshold
+    (four score values), one far outlier, and all scores equal (a range that
+    does not bucket, handled by the radix select). Sampled units are compared
+    with the oracle exactly; every unit's count is checked."""
+    dt = "bf16"
+    B, Hkv, nb = 512, 2, 40
+    T = 64 * nb
+    g = torch.Generator().manual_seed(22)
+    if pattern == "all_equal":
+        v = torch.full((B, Hkv, nb), 0.5)
+    else:
+        v = torch.randint(0, 4, (B, Hkv, nb), generator=g).float() * 0.25
+        if pattern == "outlier":
+            v[:, :, 17] = 1000.0 if mode == "raw_sum" else 40.0
+    K = torch.zeros((B, Hkv, T, 128), dtype=TD[dt])
+    K[..., 0] = v.repeat_interleave(64, dim=2).to(TD[dt])
+    G = 1 if mode == "raw_sum" else 4
+    sel = torch.zeros((B, Hkv * G, 128))
+    sel[..., 0] = 1.0 if mode == "raw_sum" else 0.5
+    sel = sel.to(TD[dt])
+    Kd = K.to(DEV)
+    Kc = _kc_for(Kd, [T] * B, dt)
+    S = to_np(sel)
+    sampled = list(range(0, B, 37))
+    Kc_ref = {b: oracle_kc(K[b:b + 1].float().numpy(), [T], dt, Kc.shape[2])[0] for b in sampled}
+    for k in (1, 10, 20):
+        idx, cnt, _ = sa.select(sel.to(DEV), Kc, lens_t([T] * B), T, k, 1, 2, mode)
+        assert torch.all(cnt.cpu() == k + 3)
+        rows = gpu_rows(idx, cnt)
+        p = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=mode)
+        for b in sampled:
+            for h in range(Hkv):
+                ref = oracle.select_blocks(S[b, h * G:(h + 1) * G], Kc_ref[b][h], T, p)
+                assert rows[(b, h)] == ref, (pattern, k, b, h, rows[(b, h)], ref)
+
+
 # ------------------------------------------------------------------ decode
 
 def _decode_case(dt, lens, T_cap, blocks_of, n_split, out=torch.float32, seed=10):
