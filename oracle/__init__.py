@@ -10,7 +10,10 @@ Decoupled Attention for Efficient Long-Context LLM Inference" (picx.dev
 summary), section "Theoretical Foundation" (Eq. 1 block union, Eq. 2
 mean-pooled compressed keys) and section "Methodology" (Eq. 4 Forecast-driven
 top-k, Eq. 5 attention over the chosen blocks, "Compact Forecast Indexer", and
-the Eq. 6 group-summed softmax form of the query-driven selector). Arithmetic is
+the Eq. 6 group-summed softmax form of the query-driven selector), plus the
+token-level variant with one index shared across layers (oracle.token: the
+CLSA abstract and the JSSA item) and the selection-quality measures
+(oracle.quality). Arithmetic is
 fp64 from the compressed keys onward; the compressed keys themselves are formed
 in a fixed fp32 order and rounded to the key dtype, so they are one exact value.
 
@@ -28,6 +31,8 @@ from .decode import decode_step, decode_unit
 from .prefill import prefill_tile_select, prefill_attention, prefill_chunk
 from .crosslayer import crosslayer_step
 from .quality import block_mass, recall, rest_bucket_distribution, mass_optimal_blocks
+from .token import (token_candidates, token_scores, top_k_tokens, select_tokens,
+                    token_decode_unit, token_crosslayer_step)
 
 __all__ = [
     "bf16_round", "round_to", "n_compressed", "n_blocks", "compressed_keys",
@@ -36,4 +41,6 @@ __all__ = [
     "sparse_attention", "lse_merge", "split_attention_partials", "decode_step", "decode_unit",
     "prefill_tile_select", "prefill_attention", "prefill_chunk", "crosslayer_step",
     "block_mass", "recall", "rest_bucket_distribution", "mass_optimal_blocks",
+    "token_candidates", "token_scores", "top_k_tokens", "select_tokens", "token_decode_unit",
+    "token_crosslayer_step",
 ]
