@@ -44,6 +44,8 @@ EXPORTS = [
     "sparse_attn_prefill_chunk", "sparse_attn_prefill_attend",
     "sparse_attn_block_mass_workspace_size", "sparse_attn_block_mass",
     "sparse_attn_stream_read_blocks", "sparse_attn_stream_read",
+    "sparse_attn_token_select_workspace_size", "sparse_attn_token_select",
+    "sparse_attn_token_decode_workspace_size", "sparse_attn_token_decode",
 ]
 
 
@@ -117,6 +119,17 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_stream_read_blocks.argtypes = []
     L.sparse_attn_stream_read.restype = _int
     L.sparse_attn_stream_read.argtypes = [_vp, _sz, _vp, _vp]
+    L.sparse_attn_token_select_workspace_size.restype = _sz
+    L.sparse_attn_token_select_workspace_size.argtypes = [_int, _int, _i64]
+    L.sparse_attn_token_select.restype = _int
+    L.sparse_attn_token_select.argtypes = [_vp, _int, _vp, _int, _int, _int, _int, _i64, _vp, _i32,
+                                           _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+    L.sparse_attn_token_decode_workspace_size.restype = _sz
+    L.sparse_attn_token_decode_workspace_size.argtypes = [_int, _int, _int, _i32, _i32]
+    L.sparse_attn_token_decode.restype = _int
+    L.sparse_attn_token_decode.argtypes = [_vp, _vp, _vp, _int, _int, _int, _int, _int, _i64, _vp,
+                                           _vp, _vp, _i32, _f32, _vp, _int, _vp, _i32, _vp, _sz,
+                                           _vp]
     _lib = L
     return L
 
@@ -354,3 +367,69 @@ def block_mass(Q: torch.Tensor, K: torch.Tensor, seq_lens: torch.Tensor, scale: 
                                       _dev(workspace, "workspace"), workspace.numel(), _stream(Q, stream))
     _check("sparse_attn_block_mass", st)
     return mass, recall
+
+
+# ------------------------------------------------------------------ token-level index
+
+def token_select_workspace_size(B, Hkv, T_cap) -> int:
+    return lib().sparse_attn_token_select_workspace_size(B, Hkv, T_cap)
+
+
+def token_select(sel: torch.Tensor, Ki: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
+                 n_init: int = 64, n_local: int = 128, idx: Optional[torch.Tensor] = None,
+                 cnt: Optional[torch.Tensor] = None, scores=None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Token-level index per (sequence, KV head): kept initial/local tokens and
+    the top_k scored tokens, ascending. Returns (idx, cnt, scores or None)."""
+    B, H_sel, d_i = sel.shape
+    _, Hkv, T_cap, _ = Ki.shape
+    dev = sel.device
+    if idx is None:
+        idx = torch.empty((B, Hkv, top_k + n_init + n_local), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if scores is True:
+        scores = torch.empty((B, Hkv, T_cap), dtype=torch.float32, device=dev)
+    need = token_select_workspace_size(B, Hkv, T_cap)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    sc = scores if isinstance(scores, torch.Tensor) else None
+    st = lib().sparse_attn_token_select(_dev(sel, "sel"), H_sel, _dev(Ki, "Ki"), _dtype_code(Ki), B,
+                                        Hkv, d_i, T_cap, _dev(seq_lens, "seq_lens"), int(top_k),
+                                        int(n_init), int(n_local), _dev(idx, "idx"), idx.shape[-1],
+                                        _dev(cnt, "cnt"), _opt(sc, "scores"),
+                                        _dev(workspace, "workspace"), ws_bytes, _stream(sel, stream))
+    _check("sparse_attn_token_select", st)
+    return idx, cnt, sc
+
+
+def token_decode_workspace_size(B, Hq, Hkv, idx_cap, n_split=0) -> int:
+    return lib().sparse_attn_token_decode_workspace_size(B, Hq, Hkv, idx_cap, n_split)
+
+
+def token_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                 idx: torch.Tensor, cnt: torch.Tensor, scale: float = 1.0,
+                 out_dtype=torch.float32, O: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = True, n_split: int = 0,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse decode attention over token lists (gathered rows). Returns (O, lse)."""
+    B, Hq, d = Q.shape
+    _, Hkv, T_cap, _ = K.shape
+    dev = Q.device
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = token_decode_workspace_size(B, Hq, Hkv, idx.shape[-1], n_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_token_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(K), B,
+                                        Hq, Hkv, d, T_cap, _dev(seq_lens, "seq_lens"),
+                                        _dev(idx, "idx"), _dev(cnt, "cnt"), idx.shape[-1],
+                                        float(scale), _dev(O, "O"), _dtype_code(O), _opt(lse, "lse"),
+                                        int(n_split), _opt(workspace, "workspace"), ws_bytes,
+                                        _stream(Q, stream))
+    _check("sparse_attn_token_decode", st)
+    return O, lse

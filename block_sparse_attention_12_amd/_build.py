@@ -15,7 +15,8 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(LIBDIR, "libsparse_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["compress.hip", "select.hip", "decode.hip", "prefill.hip", "quality.hip", "stream.hip", "sparse_attn_api.hip"]
+SOURCES = ["compress.hip", "select.hip", "decode.hip", "prefill.hip", "quality.hip", "stream.hip",
+           "token.hip", "sparse_attn_api.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           # packed fp32 instructions stay off in every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

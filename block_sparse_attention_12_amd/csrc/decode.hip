@@ -99,9 +99,18 @@ template <typename T>
 struct BlockRegs {
     Raw8<T> k[4], v[4];
     int64_t t0;
+    int ids[4];     // token lists: ids of this lane's 4 rows of the next tile this buffer loads
+    int tmy;        // token lists: id of the row whose logit this lane holds (loaded tile)
 };
 
-template <typename T, bool DIRECT>
+// ROWS = false: idx lists 64-token blocks (contiguous rows). ROWS = true: idx
+// lists single tokens (the token-level index); 64 consecutive list entries
+// form a tile that is processed exactly like a block, except that each lane
+// loads its 4 rows from the token ids of its entries. A lane's ids are
+// prefetched three tiles ahead, together with the buffer that will use them,
+// so waiting for them never waits for K/V loads that are still needed in
+// flight.
+template <typename T, bool DIRECT, bool ROWS>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
@@ -122,9 +131,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
     int n = cnt[unit];
     n = n < 0 ? 0 : (n > idx_cap ? idx_cap : n);
-    const int per = (n + n_split - 1) / n_split;
-    const int e_lo = split * per < n ? split * per : n;
-    const int nblk = (e_lo + per < n ? e_lo + per : n) - e_lo;
+    const int n_items = ROWS ? (n + 63) / 64 : n;      // blocks, or 64-entry tiles of tokens
+    const int per = (n_items + n_split - 1) / n_split;
+    const int e_lo = split * per < n_items ? split * per : n_items;
+    const int nblk = (e_lo + per < n_items ? e_lo + per : n_items) - e_lo;
 
     QFrag<T> q;
     load_q(Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + lane16 * kLaneElems, q);
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
-    const int32_t *irow = idx + (int64_t)unit * idx_cap + e_lo;
+    const int32_t *irow = idx + (int64_t)unit * idx_cap + (ROWS ? 0 : e_lo);
     const int my_row = 16 * wave + 4 * (lane16 >> 2) + rgrp;   // row of the logit this lane holds
     const int row0 = 16 * wave + rgrp;                          // first row this lane loads
     const uint32_t row_lane_off = row0 * kRowBytes + lane_off;
@@ -164,6 +174,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             load_raw(rV, off, r.v[i]);
         }
     };
+    // token lists: ids of this lane's rows (entries 64*tile + row0 + 4i) of
+    // split tile it, or -1 past the split or the list
+    auto load_ids = [&](int (&ids)[4], int it) {
+        const int e0 = 64 * (e_lo + it) + row0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = e0 + 4 * i;
+            ids[i] = (it < nblk && e < n) ? irow[e] : -1;
+        }
+    };
+    // token lists: rows from the ids loaded for tile it (ids outside [0, L)
+    // read zeros and are masked), then the ids of tile it + 3
+    auto issue_rows = [&](BlockRegs<T> &r, int it) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int id = r.ids[i];
+            const uint32_t off = (id >= 0 && id < L) ? (uint32_t)id * kRowBytes + lane_off : 0xffffffffu;
+            load_raw(rK, off, r.k[i]);
+            load_raw(rV, off, r.v[i]);
+        }
+        const int a = lane16 >> 2;                  // the logit this lane holds is row i = a
+        r.tmy = a == 0 ? r.ids[0] : (a == 1 ? r.ids[1] : (a == 2 ? r.ids[2] : r.ids[3]));
+        load_ids(r.ids, it + 3);
+    };
     auto process = [&](const BlockRegs<T> &r) {
         float v[16];
 #pragma unroll
@@ -171,7 +205,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
             for (int g = 0; g < G; ++g) v[i * G + g] = qk(q, g, r.k[i]);
         transpose_reduce16<16>(v, lane);
-        const int64_t my_t = r.t0 + my_row;
+        const int64_t my_t = ROWS ? (int64_t)r.tmy : r.t0 + my_row;
         const float x = (my_t >= 0 && my_t < L) ? v[0] * qscale : -INFINITY;
         // block max per head over the wave (lanes sharing lane & 3)
         float mx = fmaxf(x, dpp<kDppRowRor4>(x));
@@ -226,17 +260,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     // is computed. sched_barrier keeps the compiler from sinking a prefetch
     // below the compute it is meant to overlap.
     BlockRegs<T> bufA, bufB, bufC;
-    issue(bufA, block_id(0));
-    issue(bufB, block_id(1));
+    auto start = [&](BlockRegs<T> &r, int it) {
+        if constexpr (ROWS) issue_rows(r, it);
+        else issue(r, block_id(it));
+    };
+    if constexpr (ROWS) {
+        load_ids(bufA.ids, 0);
+        load_ids(bufB.ids, 1);
+        load_ids(bufC.ids, 2);
+    }
+    start(bufA, 0);
+    start(bufB, 1);
 #pragma unroll 1
     for (int it = 0; it < nblk; it += 3) {
-        issue(bufC, block_id(it + 2));
+        start(bufC, it + 2);
         __builtin_amdgcn_sched_barrier(0);
         process(bufA);
-        issue(bufA, block_id(it + 3));
+        start(bufA, it + 3);
         __builtin_amdgcn_sched_barrier(0);
         if (it + 1 < nblk) process(bufB);
-        issue(bufB, block_id(it + 4));
+        start(bufB, it + 4);
         __builtin_amdgcn_sched_barrier(0);
         if (it + 2 < nblk) process(bufC);
     }
@@ -363,7 +406,7 @@ __global__ __launch_bounds__(kDecThreads) void combine_kernel(
     if (lse && (tid & 63) == 0) lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
-template <typename T>
+template <typename T, bool ROWS>
 static void launch_decode_t(const void *Q, const void *K, const void *V, int B, int Hq, int Hkv,
                             int64_t T_cap, const int32_t *seq_lens, const int32_t *idx,
                             const int32_t *cnt, int32_t idx_cap, float scale, void *O,
@@ -372,11 +415,11 @@ static void launch_decode_t(const void *Q, const void *K, const void *V, int B, 
     const dim3 grid((unsigned)n_split, (unsigned)(B * Hkv));
     const float qscale = scale * kLog2e;
     if (n_split == 1) {
-        hipLaunchKernelGGL((decode_kernel<T, true>), grid, dim3(kDecThreads), 0, stream,
+        hipLaunchKernelGGL((decode_kernel<T, true, ROWS>), grid, dim3(kDecThreads), 0, stream,
                            (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens, idx,
                            cnt, idx_cap, qscale, 1, (float *)nullptr, O, out_bf16, lse);
     } else {
-        hipLaunchKernelGGL((decode_kernel<T, false>), grid, dim3(kDecThreads), 0, stream,
+        hipLaunchKernelGGL((decode_kernel<T, false, ROWS>), grid, dim3(kDecThreads), 0, stream,
                            (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens, idx,
                            cnt, idx_cap, qscale, n_split, (float *)ws, O, out_bf16, lse);
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(B * Hkv)), dim3(kDecThreads), 0, stream,
@@ -390,11 +433,25 @@ int launch_decode(const void *Q, const void *K, const void *V, int dtype, int B,
                   int32_t n_split, void *workspace, hipStream_t stream) {
     const int out_bf16 = out_dtype == SA_BF16 ? 1 : 0;
     if (dtype == SA_BF16)
-        launch_decode_t<bf16_t>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale, O,
-                                out_bf16, lse_out, n_split, workspace, stream);
+        launch_decode_t<bf16_t, false>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
+                                       scale, O, out_bf16, lse_out, n_split, workspace, stream);
     else
-        launch_decode_t<float>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale, O,
-                               out_bf16, lse_out, n_split, workspace, stream);
+        launch_decode_t<float, false>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
+                                      scale, O, out_bf16, lse_out, n_split, workspace, stream);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+int launch_decode_rows(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                       int Hkv, int64_t T_cap, const int32_t *seq_lens, const int32_t *idx,
+                       const int32_t *cnt, int32_t idx_cap, float scale, void *O, int out_dtype,
+                       float *lse_out, int32_t n_split, void *workspace, hipStream_t stream) {
+    const int out_bf16 = out_dtype == SA_BF16 ? 1 : 0;
+    if (dtype == SA_BF16)
+        launch_decode_t<bf16_t, true>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
+                                      scale, O, out_bf16, lse_out, n_split, workspace, stream);
+    else
+        launch_decode_t<float, true>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
+                                     scale, O, out_bf16, lse_out, n_split, workspace, stream);
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

@@ -182,4 +182,40 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // Full-wave helpers (64 lanes)
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// A visible length clamped into [0, T_cap].
+__device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
+    return L < 0 ? 0 : (L > T_cap ? T_cap : L);
+}
+
+// 32-bit key whose unsigned order is the order of the fp32 value (-0 and +0 tie).
+__device__ __forceinline__ uint32_t orderable(float x) {
+    if (x == 0.f) x = 0.f;                               // -0 and +0 tie
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of one int per thread over the workgroup; also returns the total.
+template <int NT>
+__device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int v = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    if (lane == 63) s_wave[wave] = v;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int sw = s_wave[w];
+        if (w < wave) base += sw;
+        total += sw;
+    }
+    __syncthreads();
+    return base + v - x;
+}
+
 }  // namespace sa

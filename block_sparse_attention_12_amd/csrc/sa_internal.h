@@ -44,6 +44,27 @@ int launch_decode(const void *Q, const void *K, const void *V, int dtype, int B,
                   int32_t idx_cap, float scale, void *O, int out_dtype, float *lse_out,
                   int32_t n_split, void *workspace, hipStream_t stream);
 
+// Token-level selection: scratch layout and launcher (offsets in bytes).
+struct TokenWorkspace {
+    size_t keys_off;                   // [units][t_pad] uint32 orderable keys
+    size_t hist_off;                   // [4 passes][units][256] uint32
+    size_t counts_off;                 // [units][n_chunks][2] int32
+    size_t info_off;                   // [units][2] uint32 (k-th key, equal keys taken)
+    size_t total;
+    int64_t t_pad;
+    int n_chunks;
+};
+TokenWorkspace token_workspace_layout(int B, int Hkv, int64_t T_cap);
+int launch_token_select(const void *sel, int H_sel, const void *Ki, int dtype, int B, int Hkv,
+                        int d_i, int64_t T_cap, const int32_t *seq_lens, int top_k, int n_init,
+                        int n_local, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                        float *scores_out, void *workspace, hipStream_t stream);
+// Decode attention over per-(b, kvh) token lists (gathered single rows).
+int launch_decode_rows(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                       int Hkv, int64_t T_cap, const int32_t *seq_lens, const int32_t *idx,
+                       const int32_t *cnt, int32_t idx_cap, float scale, void *O, int out_dtype,
+                       float *lse_out, int32_t n_split, void *workspace, hipStream_t stream);
+
 int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p);
 size_t prefill_workspace_bytes(int Hq, int Hkv, int64_t q_start, int64_t Tq,
                                const sa_select_params &p);

@@ -66,10 +66,6 @@ SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, in
     return w;
 }
 
-__device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
-    return L < 0 ? 0 : (L > T_cap ? T_cap : L);
-}
-
 // ---------------------------------------------------------------- raw scores
 
 template <typename T>
@@ -276,36 +272,6 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
 }
 
 // ---------------------------------------------------------------- top-k + union
-
-__device__ __forceinline__ uint32_t orderable(float x) {
-    if (x == 0.f) x = 0.f;                               // -0 and +0 tie
-    const uint32_t u = __float_as_uint(x);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix sum of one int per thread over the workgroup; also returns the total.
-template <int NT>
-__device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int v = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
-    if (lane == 63) s_wave[wave] = v;
-    __syncthreads();
-    int base = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const int sw = s_wave[w];
-        if (w < wave) base += sw;
-        total += sw;
-    }
-    __syncthreads();
-    return base + v - x;
-}
 
 // Thread t owns PER consecutive blocks [t*PER, t*PER + PER): their 32-bit
 // orderable keys stay in registers for the whole kernel, so the bucket (and,

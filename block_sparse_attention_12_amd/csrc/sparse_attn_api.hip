@@ -177,6 +177,63 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                  tile_cnt, scale, O, out_dtype, lse_out, (hipStream_t)stream);
 }
 
+size_t sparse_attn_token_select_workspace_size(int B, int Hkv, int64_t T_cap) {
+    if (B <= 0 || Hkv <= 0 || T_cap < 0) return 0;
+    return token_workspace_layout(B, Hkv, T_cap).total;
+}
+
+int sparse_attn_token_select(const void *sel, int H_sel, const void *Ki, int dtype, int B, int Hkv,
+                             int d_i, int64_t T_cap, const int32_t *seq_lens, int32_t top_k,
+                             int32_t n_init, int32_t n_local, int32_t *idx_out, int32_t idx_cap,
+                             int32_t *cnt_out, float *scores_out, void *workspace,
+                             size_t ws_bytes, void *stream) {
+    if (!sel || !Ki || !seq_lens || !idx_out || !cnt_out) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hkv <= 0 || H_sel <= 0 || d_i <= 0 || T_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    if (top_k < 0 || n_init < 0 || n_local < 0 || H_sel % Hkv) return SA_ERR_INVALID_ARG;
+    if (d_i != 64 && d_i != 128) return SA_ERR_UNSUPPORTED;
+    if (H_sel / Hkv > 64 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
+    if (T_cap * d_i * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (idx_cap <= 0 || idx_cap < (int64_t)top_k + n_init + n_local) return SA_ERR_CAPACITY;
+    const size_t need = token_workspace_layout(B, Hkv, T_cap).total;
+    if (!workspace || ws_bytes < need) return SA_ERR_WORKSPACE;
+    return launch_token_select(sel, H_sel, Ki, dtype, B, Hkv, d_i, T_cap, seq_lens, top_k, n_init,
+                               n_local, idx_out, idx_cap, cnt_out, scores_out, workspace,
+                               (hipStream_t)stream);
+}
+
+size_t sparse_attn_token_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap,
+                                               int32_t n_split) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || idx_cap <= 0) return 0;
+    const int32_t tiles = (idx_cap + 63) / 64;
+    int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, tiles);
+    if (s < decode_min_split(tiles)) s = decode_min_split(tiles);
+    return decode_workspace_bytes(B, Hq, s);
+}
+
+int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                             int Hkv, int d, int64_t T_cap, const int32_t *seq_lens,
+                             const int32_t *idx, const int32_t *cnt, int32_t idx_cap, float scale,
+                             void *O, int out_dtype, float *lse_out, int32_t n_split,
+                             void *workspace, size_t ws_bytes, void *stream) {
+    if (!Q || !K || !V || !seq_lens || !idx || !cnt || !O) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 ||
+        T_cap < 0 || idx_cap <= 0)
+        return SA_ERR_INVALID_ARG;
+    if (Hq % Hkv) return SA_ERR_INVALID_ARG;
+    if (!(scale == scale)) return SA_ERR_INVALID_ARG;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    const int32_t tiles = (int32_t)(((int64_t)idx_cap + 63) / 64);
+    if (n_split > kMaxSplit || tiles > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
+    if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, tiles);
+    if (s < decode_min_split(tiles)) s = decode_min_split(tiles);
+    const size_t need = decode_workspace_bytes(B, Hq, s);
+    if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
+    return launch_decode_rows(Q, K, V, dtype, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale,
+                              O, out_dtype, lse_out, s, workspace, (hipStream_t)stream);
+}
+
 size_t sparse_attn_block_mass_workspace_size(int B, int Hq, int64_t mass_cap) {
     if (B <= 0 || Hq <= 0 || mass_cap <= 0) return 0;
     return block_mass_workspace_bytes(B, Hq, mass_cap);

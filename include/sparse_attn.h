@@ -250,6 +250,71 @@ int sparse_attn_prefill_attend(const void *Q, int64_t q_start, int64_t Tq, const
                                const int32_t *tile_cnt, float scale, void *O, int out_dtype,
                                float *lse_out, void *stream);
 
+/* Workspace bytes needed by sparse_attn_token_select. */
+size_t sparse_attn_token_select_workspace_size(int B, int Hkv, int64_t T_cap);
+
+/*
+ * sparse_attn_token_select - token-level index, computed once and meant to be
+ * reused by every layer that shares the KV cache (CLSA abstract on the page
+ * "HySparse2: Hybrid Sparse Attention with Two-Level KV Sharing"; tokens
+ * scored in a shared low-dimensional query-key space with one token set per
+ * KV head: JSSA item on the "Sparse Attention" topic page).
+ *
+ * Per (sequence b, KV head kvh) at visible length L = seq_lens[b]: every
+ * token t < L gets the raw score of Eq. 4 (SparDA summary page, one vector per
+ * group, no softmax) against its index key, s_t = sum over the group's
+ * selector vectors of sel . Ki_t, summed in fp32. The first n_init and the
+ * last n_local visible tokens are always kept; the top_k of the other visible
+ * tokens by score (exact; ties to the lower token index) are added.
+ *
+ *   sel        [B, H_sel, d_i] device: H_sel = Hkv (one Forecast per group) or
+ *              a multiple of Hkv (the group's query heads, summed; at most 64)
+ *   Ki         [B, Hkv, T_cap, d_i] device: index keys (the keys themselves
+ *              with d_i = 128, or a 64-dimensional projection of them),
+ *              valid for t < L
+ *   idx_out    [B, Hkv, idx_cap] device int32: the kept and chosen token ids
+ *              ascending, padded with -1; idx_cap >= top_k + n_init + n_local
+ *   cnt_out    [B, Hkv] device int32: number of valid entries of each row
+ *   scores_out optional [B, Hkv, T_cap] device fp32: s_t (-inf for t >= L)
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d_i not 64 or 128, more
+ *         than 64 selector heads per group, B * Hkv > 65535, a (b, kvh) slice
+ *         of T_cap * d_i elements taking 2 GiB or more), SA_ERR_CAPACITY,
+ *         SA_ERR_WORKSPACE.
+ */
+int sparse_attn_token_select(const void *sel, int H_sel, const void *Ki, int dtype, int B, int Hkv,
+                             int d_i, int64_t T_cap, const int32_t *seq_lens, int32_t top_k,
+                             int32_t n_init, int32_t n_local, int32_t *idx_out, int32_t idx_cap,
+                             int32_t *cnt_out, float *scores_out, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by sparse_attn_token_decode for this split count
+ * (n_split <= 0 asks the library's choice for this shape). */
+size_t sparse_attn_token_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap,
+                                               int32_t n_split);
+
+/*
+ * sparse_attn_token_decode - Eq. 5 for one new token per sequence over a
+ * token list: the query heads of KV head kvh attend, with softmax scale
+ * `scale`, to the tokens idx[b, kvh, 0 .. cnt[b, kvh]) (any order, no
+ * duplicates; ids outside [0, L) are ignored), e.g. the list written by
+ * sparse_attn_token_select and shared by several layers. Rows are gathered
+ * one token at a time; 64 list entries form a tile, and tiles are split over
+ * n_split workgroups per (b, kvh) whose partials are merged with log-sum-exp
+ * weights, as in sparse_attn_decode.
+ *
+ *   Q [B, Hq, d], K/V [B, Hkv, T_cap, d] device; idx [B, Hkv, idx_cap] and
+ *   cnt [B, Hkv] device int32; O [B, Hq, d] (out_dtype); lse_out optional
+ *   [B, Hq] fp32 natural log of the softmax denominator (-inf when empty).
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4,
+ *         n_split > 64, idx_cap > 262144, a (b, kvh) cache slice of
+ *         T_cap * d elements taking 2 GiB or more), SA_ERR_WORKSPACE.
+ */
+int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                             int Hkv, int d, int64_t T_cap, const int32_t *seq_lens,
+                             const int32_t *idx, const int32_t *cnt, int32_t idx_cap, float scale,
+                             void *O, int out_dtype, float *lse_out, int32_t n_split,
+                             void *workspace, size_t ws_bytes, void *stream);
+
 /*
  * sparse_attn_block_mass - selection quality, not a step of the sparse path:
  * the exact attention mass of every 64-token block for the decode query of

@@ -104,3 +104,24 @@ def tile_union_ok(gpu_union, ref_union, per_query, k, cand):
         if not explained:
             return False, f"block {b} differs outside any near-tie band"
     return True, "near tie"
+
+
+def token_selection_ok(gpu_tokens, ref_tokens, s, bound, k, cand):
+    """Token sets: exact, or of the same size and ascending with every token
+    in which they differ scoring (oracle, fp64) within the fp32 rounding band
+    of the k-th candidate score: |s_t - s_k| <= bound_t + bound_k, where
+    bound_t bounds the fp32 error of token t's score."""
+    gpu_tokens = list(gpu_tokens)
+    if gpu_tokens == list(ref_tokens):
+        return True, "exact"
+    if len(gpu_tokens) != len(ref_tokens) or gpu_tokens != sorted(set(gpu_tokens)):
+        return False, "wrong size, order or duplicates"
+    cand = np.asarray(cand, dtype=np.int64)
+    if k <= 0 or cand.size <= k:
+        return False, "mismatch with no tie possible"
+    order = oracle.top_k_tokens(s, cand, k)
+    kth = order[-1]
+    diff = set(gpu_tokens) ^ set(ref_tokens)
+    if all(abs(s[t] - s[kth]) <= bound[t] + bound[kth] for t in diff):
+        return True, "near tie"
+    return False, "a differing token is outside the rounding band of the k-th score"

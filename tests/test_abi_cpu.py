@@ -212,3 +212,56 @@ def test_block_mass_validation():
     assert need == 2 * 2 * 8 * 16 * 4
     assert call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
     assert call(ws=None) == sa.SA_ERR_WORKSPACE
+
+
+def test_token_select_validation():
+    L = sa.lib()
+
+    def call(**kw):
+        a = dict(sel=FAKE, H_sel=2, Ki=FAKE, dtype=sa.SA_BF16, B=2, Hkv=2, d_i=64, T_cap=10000,
+                 lens=FAKE, k=256, ni=64, nl=128, idx=FAKE, idx_cap=448, cnt=FAKE, scores=None,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sparse_attn_token_select(a["sel"], a["H_sel"], a["Ki"], a["dtype"], a["B"], a["Hkv"],
+                                          a["d_i"], a["T_cap"], a["lens"], a["k"], a["ni"], a["nl"],
+                                          a["idx"], a["idx_cap"], a["cnt"], a["scores"], a["ws"],
+                                          a["ws_bytes"], None)
+    assert call(sel=None) == sa.SA_ERR_INVALID_ARG
+    assert call(cnt=None) == sa.SA_ERR_INVALID_ARG
+    assert call(dtype=5) == sa.SA_ERR_INVALID_ARG
+    assert call(k=-1) == sa.SA_ERR_INVALID_ARG
+    assert call(H_sel=3) == sa.SA_ERR_INVALID_ARG                     # not a multiple of Hkv
+    assert call(d_i=96) == sa.SA_ERR_UNSUPPORTED
+    assert call(H_sel=2 * 65) == sa.SA_ERR_UNSUPPORTED                # 65 selectors per group
+    assert call(T_cap=1 << 24, d_i=128, dtype=sa.SA_F32) == sa.SA_ERR_UNSUPPORTED   # 8 GiB slice
+    assert call(idx_cap=447) == sa.SA_ERR_CAPACITY
+    need = L.sparse_attn_token_select_workspace_size(2, 2, 10000)
+    chunks = 3                                                       # ceil(10000 / 4096)
+    assert need >= 4 * chunks * 4096 * 4 + 4 * 4 * 256 * 4
+    assert call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+    assert call(ws=None) == sa.SA_ERR_WORKSPACE
+    assert L.sparse_attn_token_select_workspace_size(2, 2, 0) > 0      # one chunk even when empty
+
+
+def test_token_decode_validation():
+    L = sa.lib()
+
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, dtype=sa.SA_BF16, B=2, Hq=8, Hkv=2, d=128, T_cap=10000,
+                 lens=FAKE, idx=FAKE, cnt=FAKE, idx_cap=448, O=FAKE, out=sa.SA_F32, lse=None,
+                 n_split=0, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sparse_attn_token_decode(a["Q"], a["K"], a["V"], a["dtype"], a["B"], a["Hq"],
+                                          a["Hkv"], a["d"], a["T_cap"], a["lens"], a["idx"], a["cnt"],
+                                          a["idx_cap"], 1.0, a["O"], a["out"], a["lse"], a["n_split"],
+                                          a["ws"], a["ws_bytes"], None)
+    assert call(Q=None) == sa.SA_ERR_INVALID_ARG
+    assert call(idx_cap=0) == sa.SA_ERR_INVALID_ARG
+    assert call(Hq=7) == sa.SA_ERR_INVALID_ARG
+    assert call(d=64) == sa.SA_ERR_UNSUPPORTED
+    assert call(Hq=16) == sa.SA_ERR_UNSUPPORTED                       # G = 8
+    assert call(n_split=65) == sa.SA_ERR_UNSUPPORTED
+    assert call(idx_cap=64 * 64 * 64 + 1) == sa.SA_ERR_UNSUPPORTED    # more than 4096 tiles
+    need = L.sparse_attn_token_decode_workspace_size(2, 8, 2, 448, 4)
+    assert need == 2 * 8 * 4 * 132 * 4                                 # partials of 4 splits
+    assert call(n_split=4, ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
