@@ -13,7 +13,8 @@ Prints one JSON line: throughput (tokens/s = batch / step time), the achieved
 HBM bandwidth of the dominant kernel (decode attention) on its algorithmic
 bytes against the 8 TB/s peak, and the CPU oracle timed on the same inputs.
 Other workloads: --workload decode_gqa_bf16_32k | decode_tiny_f32_8k |
-crosslayer_bf16_64k | prefill_chunk_bf16_128k.
+crosslayer_bf16_64k | lookahead_forecast_bf16_128k | tokenindex_forecast_bf16_128k |
+prefill_chunk_bf16_128k.
 """
 from __future__ import annotations
 
@@ -61,6 +62,8 @@ def main():
         return copy_calibration(args)
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
+    if args.workload in synth.TOKEN_WORKLOADS:
+        return bench_token(args, synth.TOKEN_WORKLOADS[args.workload])
     w = synth.WORKLOADS[args.workload]
     if w.lookahead:
         return bench_lookahead(args, w)
@@ -452,6 +455,149 @@ def cpu_baseline_decode(w, inp, lens, budget_s):
             "sample": f"{done} full decode steps of {w.name} (all {len(units)} units: append, "
                       f"select, attend), numpy fp64, BLAS threads = {n_threads} (CPU affinity, "
                       f"at most 16), {t_units:.1f} s"}
+
+
+def bench_token(args, w):
+    """One decode step of the token-index workload: the anchor's token index is
+    computed once (scores of every visible token's index key, exact top-k, kept
+    initial/local tokens) and w.layers layers attend over that token list.
+    value = sequences / step time."""
+    import numpy as np
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import TokenIndexDecoder
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_token_inputs(w, device=dev)
+    lens = inp["seq_lens"]
+    dec = TokenIndexDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, device=dev,
+                            n_split=args.n_split)
+    reps = [inp]
+    for r in range(1, args.replicas):
+        reps.append(dict(Ki=inp["Ki"].clone(), Fi=inp["Fi"].clone(),
+                         layers=[{k: v.clone() for k, v in lay.items()} for lay in inp["layers"]]))
+    outs = [(torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev),
+             torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)) for _ in range(w.layers)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    steps_fn = [lambda rep=rep: dec.step(rep["Fi"], rep["Ki"], rep["layers"], lens, outs)
+                for rep in reps]
+    for i in range(args.warmup):
+        steps_fn[i % len(reps)]()
+    torch.cuda.synchronize()
+    ev0, ev1 = _events(2)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        steps_fn[i % len(reps)]()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-phase GPU time (events on the launch stream around each call)
+    n_ph = max(10, min(args.steps, 100))
+    phases = {
+        "select": [lambda rep=rep: dec.select(rep["Fi"], rep["Ki"], lens) for rep in reps],
+        "attend_one_layer": [lambda rep=rep: dec.attend(rep["layers"][0]["Q"], rep["layers"][0]["K"],
+                                                        rep["layers"][0]["V"], lens, *outs[0])
+                             for rep in reps],
+    }
+    mean = {}
+    for name, fns in phases.items():
+        for i in range(3):
+            fns[i % len(fns)]()
+        evs = [_events(2) for _ in range(n_ph)]
+        for i in range(n_ph):
+            evs[i][0].record(stream)
+            fns[i % len(fns)]()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        mean[name] = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ph
+
+    # algorithmic bytes: every visible token's index key (plus the selector),
+    # and per layer the selected tokens' K and V rows, Q in, O + LSE out
+    elem = inp["Ki"].element_size()
+    L = [int(x) for x in lens.cpu()]
+    sel_bytes = sum(L) * w.Hkv * w.d_i * elem + inp["Fi"].numel() * elem
+    cnt = dec.cnt.cpu().numpy()
+    attn_bytes = int(cnt.sum()) * 2 * w.d * elem + w.B * w.Hq * (w.d * elem + w.d * 4 + 4)
+    step_bytes = sel_bytes + w.layers * attn_bytes
+    sel_gbs = sel_bytes / (mean["select"] * 1e-3) / 1e9
+    attn_gbs = attn_bytes / (mean["attend_one_layer"] * 1e-3) / 1e9
+    # planted tokens recovered by the index (quality check of the synthetic setup)
+    idx = dec.idx.cpu().numpy()
+    hit = tot = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            got = set(idx[b, h, :int(cnt[b, h])].tolist())
+            hit += sum(1 for t in inp["planted"][b][h] if t in got)
+            tot += len(inp["planted"][b][h])
+    ceil = measured_stream_read_gbs(dev)
+    out = {
+        "metric": "decode tokens/s through 4 layers sharing one token-level index at 128K, 1 GPU",
+        "value": round(w.B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), planted tokens)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.T, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "index_dim": w.d_i, "layers": w.layers,
+                   "top_k_tokens": w.top_k, "n_init_tokens": w.n_init,
+                   "n_local_tokens": w.n_local, "replicas": args.replicas,
+                   "launch": "eager, one stream", "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "phase_ms": {k: round(v, 5) for k, v in mean.items()},
+        "step_bytes": step_bytes, "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm",
+                     "kernel": "sparse_attn_token_select (index-key scan, 3 radix passes, count, "
+                               "write)",
+                     "achieved": round(sel_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(sel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"{w.name}_score"),
+                     "bytes_per_launch": sel_bytes,
+                     "measured_ceiling": {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
+                                          "GB/s": ceil, "frac": round(sel_gbs / ceil, 4)}},
+        "attend": {"kernel": "sparse_attn_token_decode (gathered rows + combine), one layer",
+                   "GB/s": round(attn_gbs, 1), "frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
+                   "frac_of_ceiling": round(attn_gbs / ceil, 4), "bytes": attn_bytes},
+        "planted_tokens_recovered": round(hit / max(tot, 1), 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_token(w, inp, L, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_token(w, inp, lens, budget_s):
+    """The CPU oracle on the same inputs: whole units (select + every layer's
+    attention) until the budget, scaled to a step of all B * Hkv units."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+
+    Fi = inp["Fi"].float().cpu().numpy()
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    n_threads = min(len(os.sched_getaffinity(0)), 16)
+    done, t_run = 0, 0.0
+    with threadpoolctl.threadpool_limits(n_threads):
+        while t_run < budget_s and done < len(units):
+            b, h = units[done]
+            Ki = inp["Ki"][b, h].float().cpu().numpy()          # host copies: not timed
+            lay = [(l["Q"][b, h * w.G:(h + 1) * w.G].float().cpu().numpy(),
+                    l["K"][b, h].float().cpu().numpy(), l["V"][b, h].float().cpu().numpy())
+                   for l in inp["layers"]]
+            t0 = time.perf_counter()
+            toks = oracle.select_tokens(Fi[b, h:h + 1], Ki, lens[b], w.top_k, w.n_init, w.n_local)
+            for q, K, V in lay:
+                oracle.token_decode_unit(q, K, V, toks, 1.0)
+            t_run += time.perf_counter() - t0
+            done += 1
+    sec_per_step = t_run / done * len(units)
+    return {"value": round(w.B / sec_per_step, 3), "unit": "tokens/s", "cores": n_threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV head) units of {w.name} (token select "
+                      f"+ {w.layers} layers' attention), numpy fp64, BLAS threads = {n_threads}, "
+                      f"{t_run:.1f} s, scaled to a whole step"}
 
 
 def bench_crosslayer(args, w):

@@ -13,7 +13,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
-               select_workspace_size,
+               select_workspace_size, token_select, token_decode, token_select_workspace_size,
+               token_decode_workspace_size,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
 
@@ -175,6 +176,41 @@ class LookaheadDecoder:
             if l + 1 < n:
                 sel_done = next_done
         main.wait_stream(side)                     # join: the side stream is idle after the step
+        return outs
+
+
+class TokenIndexDecoder:
+    """A decode step in which one token-level index, computed once from the
+    anchor's index keys and selector, serves every layer (the CLSA routing
+    index shared across layers): token_select once, then token_decode per
+    layer over the same list. Buffers are allocated once."""
+
+    def __init__(self, B: int, Hq: int, Hkv: int, T_cap: int, top_k: int, n_init: int = 64,
+                 n_local: int = 128, device="cuda", n_split: int = 0, out_dtype=torch.float32):
+        self.B, self.Hq, self.Hkv, self.T_cap = B, Hq, Hkv, T_cap
+        self.top_k, self.n_init, self.n_local, self.n_split = top_k, n_init, n_local, n_split
+        dev = torch.device(device)
+        self.cap = top_k + n_init + n_local
+        self.idx = torch.empty((B, Hkv, self.cap), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        self.sel_ws = torch.empty(max(token_select_workspace_size(B, Hkv, T_cap), 1),
+                                  dtype=torch.uint8, device=dev)
+        dws = token_decode_workspace_size(B, Hq, Hkv, self.cap, n_split)
+        self.dec_ws = torch.empty(max(dws, 1), dtype=torch.uint8, device=dev)
+
+    def select(self, sel, Ki, seq_lens):
+        return token_select(sel, Ki, seq_lens, self.top_k, self.n_init, self.n_local,
+                            idx=self.idx, cnt=self.cnt, workspace=self.sel_ws)
+
+    def attend(self, Q, K, V, seq_lens, O, lse=None, scale=1.0):
+        return token_decode(Q, K, V, seq_lens, self.idx, self.cnt, scale, O=O, lse=lse,
+                            want_lse=lse is not None, n_split=self.n_split, workspace=self.dec_ws)
+
+    def step(self, sel, Ki, layers: Sequence[dict], seq_lens, outs, scale=1.0):
+        """layers: dicts with Q, K, V; outs: list of (O, lse) per layer."""
+        self.select(sel, Ki, seq_lens)
+        for lay, (O, lse) in zip(layers, outs):
+            self.attend(lay["Q"], lay["K"], lay["V"], seq_lens, O, lse, scale)
         return outs
 
 

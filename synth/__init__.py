@@ -17,7 +17,9 @@ Recipe (the same for every workload):
     taken in fp32 before the cast.
   * Finally every tensor is cast to the workload dtype (fp32 or bf16).
 Lengths may be ragged: positions at or beyond a sequence's length hold random
-values that no step may read.
+values that no step may read. Token-index workloads (``make_token_inputs``)
+follow the same recipe with index keys and index vectors of their own
+dimension, planted tokens instead of planted blocks.
 """
 from __future__ import annotations
 
@@ -80,6 +82,38 @@ class PrefillWorkload:
     def G(self) -> int:
         return self.Hq // self.Hkv
 
+
+@dataclass(frozen=True)
+class TokenWorkload:
+    """One decode step through several layers that share one token-level index."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    d_i: int                # index-key dimension
+    T: int
+    dtype: str
+    top_k: int              # tokens chosen by score
+    n_init: int             # first tokens always kept
+    n_local: int            # last tokens always kept
+    planted: int            # planted tokens per (sequence, KV head)
+    layers: int             # layers attending with the shared index
+    seed: int
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+TOKEN_WORKLOADS = {
+    # the 128K Forecast decode shape with a 64-dimensional token index: one
+    # index per step (4096 + 64 + 128 tokens per KV head, the token budget of
+    # 64 + 1 + 2 blocks) shared by 4 layers
+    "tokenindex_forecast_bf16_128k": TokenWorkload(
+        "tokenindex_forecast_bf16_128k", B=8, Hq=32, Hkv=8, d=128, d_i=64, T=131072, dtype="bf16",
+        top_k=4096, n_init=64, n_local=128, planted=512, layers=4, seed=6),
+}
 
 WORKLOADS = {
     # tiny single-layer decode, fp32, 4 planted blocks per KV head
@@ -220,6 +254,57 @@ def make_prefill_inputs(w: PrefillWorkload, device="cpu"):
     for h in range(w.Hkv):
         V[0, h].copy_(_randn((w.T, w.d), g, device))
     return dict(Q=Q, K=K, V=V, q_start=w.q_start, scale=1.0)
+
+
+def make_token_inputs(w: TokenWorkload, device="cpu", seq_lens: Optional[Sequence[int]] = None,
+                      T_cap: Optional[int] = None, layers: Optional[int] = None):
+    """Draw a token-index decode step's inputs.
+
+    Index side: Ki [B, Hkv, T_cap, d_i] index keys and one Forecast-style
+    index vector per group Fi [B, Hkv, d_i] (scaled by 1/sqrt(d_i)); in each
+    (sequence, KV head) ``planted`` distinct tokens outside the kept initial /
+    local windows get +2 * u added to their index key, u the unit vector of
+    that group's Fi (fp32, before the cast). Attention side, per layer: Q
+    [B, Hq, d] (scaled by 1/sqrt(d)), K, V [B, Hkv, T_cap, d]. Returns a dict
+    with Ki, Fi, seq_lens, planted, layers (list of dicts) and scale 1.0.
+    """
+    device = torch.device(device)
+    lens = list(seq_lens) if seq_lens is not None else [w.T] * w.B
+    cap = T_cap if T_cap is not None else max(lens)
+    n_layers = w.layers if layers is None else layers
+    g = _generator(w.seed, device)
+    dt = torch_dtype(w.dtype)
+    Fi = _randn((w.B, w.Hkv, w.d_i), g, device) / math.sqrt(w.d_i)
+    Ki = torch.empty((w.B, w.Hkv, cap, w.d_i), dtype=dt, device=device)
+    planted = []
+    for b in range(w.B):
+        Kb = _randn((w.Hkv, cap, w.d_i), g, device)
+        pl_b = []
+        lo, hi = min(w.n_init, lens[b]), max(min(w.n_init, lens[b]), lens[b] - w.n_local)
+        for h in range(w.Hkv):
+            toks = []
+            if w.planted > 0 and hi > lo:
+                n = min(w.planted, hi - lo)
+                toks = sorted((lo + torch.randperm(hi - lo, generator=g, device=device)[:n]).tolist())
+                u = Fi[b, h] / Fi[b, h].norm()
+                Kb[h, toks] += 2.0 * u
+            pl_b.append(toks)
+        planted.append(pl_b)
+        Ki[b].copy_(Kb)
+        del Kb
+    inv = 1.0 / math.sqrt(w.d)
+    lay = []
+    for l in range(n_layers):
+        gl = _generator(w.seed + 1 + l, device)
+        Q = (_randn((w.B, w.Hq, w.d), gl, device) * inv).to(dt)
+        K = torch.empty((w.B, w.Hkv, cap, w.d), dtype=dt, device=device)
+        V = torch.empty((w.B, w.Hkv, cap, w.d), dtype=dt, device=device)
+        for b in range(w.B):
+            K[b].copy_(_randn((w.Hkv, cap, w.d), gl, device))
+            V[b].copy_(_randn((w.Hkv, cap, w.d), gl, device))
+        lay.append(dict(Q=Q, K=K, V=V))
+    return dict(Ki=Ki, Fi=Fi.to(dt), seq_lens=torch.tensor(lens, dtype=torch.int32, device=device),
+                planted=planted, layers=lay, scale=1.0)
 
 
 def scaled(w, **kw):
