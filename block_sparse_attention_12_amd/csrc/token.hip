@@ -91,6 +91,10 @@ __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, ui
                                           uint32_t *s_above) {
     const int tid = threadIdx.x;
     if (tid < 64) {
+        if (tid == 0) {                 // defined even if no bin qualifies (inconsistent counts)
+            *s_digit = 0;
+            *s_above = 0;
+        }
         const uint32_t hb[4] = {s_h[4 * tid], s_h[4 * tid + 1], s_h[4 * tid + 2], s_h[4 * tid + 3]};
         const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
         uint32_t incl = c;
@@ -129,6 +133,7 @@ __device__ __forceinline__ void tok_prefix(const uint32_t *hist_unit, int64_t hi
         prefix |= *s_digit << shift;
         mask |= 255u << shift;
         remaining -= (int)*s_above;
+        remaining = remaining < 0 ? 0 : remaining;
         __syncthreads();                                               // s_h reused
     }
 }
@@ -372,7 +377,8 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     const int64_t t0 = (int64_t)blockIdx.x * kTokChunk;
     const int n_used = (int)((w.L + kTokChunk - 1) / kTokChunk);
     const uint32_t thr = w.choose ? info[unit * 2] : 0u;
-    const int take_eq = w.choose ? (int)info[unit * 2 + 1] : 0;
+    int take_eq = w.choose ? (int)info[unit * 2 + 1] : 0;
+    take_eq = take_eq < 0 ? 0 : take_eq;
     int32_t *row = idx_out + (int64_t)unit * idx_cap;
     const int32_t *cu = counts + (int64_t)unit * n_chunks * 2;
 
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
         int sure, eq;
         chunk_sums(n_used, sure, eq);
         int total = sure + (eq < take_eq ? eq : take_eq);
-        total = total < idx_cap ? total : idx_cap;
+        total = total < 0 ? 0 : (total < idx_cap ? total : idx_cap);
         for (int i = total + tid; i < idx_cap; i += kTokThreads) row[i] = -1;
         if (tid == 0) cnt_out[unit] = total;
     }
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
 #pragma unroll
     for (int i = 0; i < kTokPer; ++i)
         if (in[i]) {
-            if (pos < idx_cap) row[pos] = (int32_t)(tb + i);
+            if (pos >= 0 && pos < idx_cap) row[pos] = (int32_t)(tb + i);
             ++pos;
         }
 }
