@@ -13,14 +13,17 @@ top-k, Eq. 5 attention over the chosen blocks, "Compact Forecast Indexer", and
 the Eq. 6 group-summed softmax form of the query-driven selector), plus the
 token-level variant with one index shared across layers (oracle.token: the
 CLSA abstract and the JSSA item) and the selection-quality measures
-(oracle.quality). Arithmetic is
+(oracle.quality), and the second-order block statistic read from the COBS
+abstract (oracle.cobs, parity unpinned by the pages). Arithmetic is
 fp64 from the compressed keys onward; the compressed keys themselves are formed
 in a fixed fp32 order and rounded to the key dtype, so they are one exact value.
 
 Pinned by the tests under tests/ marked "not gpu" (closed forms, library
-special cases, invariants and brute force). One reading has no pin of its own
-beyond brute force over its definition: which compressed entries belong to a
-64-token block ("parity unpinned" for that choice, see oracle.select).
+special cases, invariants and brute force). Parity unpinned by the pages: which
+compressed entries belong to a 64-token block (pinned only by brute force over
+that definition, see oracle.select), and the whole of oracle.cobs (the pages
+give no formula for the second-order statistic; pinned only by the mathematics
+of the cumulant expansion and by the first-order block path).
 """
 from .numerics import bf16_round, round_to
 from .compress import n_compressed, n_blocks, compressed_keys, append_compressed_keys
@@ -33,6 +36,7 @@ from .crosslayer import crosslayer_step
 from .quality import block_mass, recall, rest_bucket_distribution, mass_optimal_blocks
 from .token import (token_candidates, token_scores, top_k_tokens, select_tokens,
                     token_decode_unit, token_crosslayer_step)
+from .cobs import block_stats, cobs_log_mass, cobs_block_scores, select_blocks_cobs
 
 __all__ = [
     "bf16_round", "round_to", "n_compressed", "n_blocks", "compressed_keys",
@@ -42,5 +46,6 @@ __all__ = [
     "prefill_tile_select", "prefill_attention", "prefill_chunk", "crosslayer_step",
     "block_mass", "recall", "rest_bucket_distribution", "mass_optimal_blocks",
     "token_candidates", "token_scores", "top_k_tokens", "select_tokens", "token_decode_unit",
-    "token_crosslayer_step",
+    "token_crosslayer_step", "block_stats", "cobs_log_mass", "cobs_block_scores",
+    "select_blocks_cobs",
 ]

@@ -1,0 +1,138 @@
+"""Pins of the second-order block statistic oracle (oracle.cobs).
+
+The pages give no formula for the statistic (parity unpinned by the pages), so
+these pin the reading against the mathematics it rests on: the block mean and
+variance against closed forms and numpy, the first- and second-order terms of
+the cumulant expansion of the block's log-mass against an exactly computed
+mass, and the first-order selection against the block path's own oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import SelectParams
+
+
+def test_block_stats_closed_forms():
+    d = 8
+    L = 64 * 3 + 17                                   # the partial last block has no statistics
+    K = np.zeros((L, d), dtype=np.float32)
+    K[:64] = 1.5                                      # constant block
+    K[64:128, 0] = np.arange(64)                      # ramp 0..63 in channel 0
+    K[128:192, 1] = np.tile([2.0, -2.0], 32)          # two-point block: mean 0, variance 4
+    mu, var = oracle.block_stats(K, L, "f32")
+    assert mu.shape == var.shape == (3, d)
+    assert np.all(mu[0] == 1.5) and np.all(var[0] == 0)
+    assert mu[1, 0] == 31.5 and var[1, 0] == (64 * 64 - 1) / 12.0      # 341.25, exact
+    assert np.all(var[1, 1:] == 0)
+    assert mu[2, 1] == 0 and var[2, 1] == 4.0
+    assert oracle.block_stats(K, 63, "f32")[0].shape == (0, d)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_stats_match_numpy_and_grow_by_prefix(dtype):
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((64 * 10, 16)).astype(np.float32) * 3 + 1
+    mu, var = oracle.block_stats(K, 64 * 10, dtype)
+    blocks = K.reshape(10, 64, 16).astype(np.float64)
+    tol = 1e-5 if dtype == "f32" else 8e-3
+    assert np.allclose(mu, blocks.mean(axis=1), rtol=tol, atol=tol)
+    assert np.allclose(var, blocks.var(axis=1), rtol=tol, atol=tol)
+    mu6, var6 = oracle.block_stats(K, 64 * 6 + 5, dtype)
+    assert np.array_equal(mu6, mu[:6]) and np.array_equal(var6, var[:6])
+
+
+def _exact_log_mass(q, K):
+    z = K.astype(np.float64) @ q
+    m = z.max()
+    return m + np.log(np.exp(z - m).sum()) - np.log(64.0)
+
+
+def test_expansion_orders_on_a_two_point_block():
+    """Keys mu +- a e_0 (32 each): the exact log-mass is q.mu + log cosh(q_0 a).
+    First order misses x^2 / 2 (x = q_0 a), second order only x^4 / 12 + ...:
+    halving a divides the errors by 4 and by 16."""
+    rng = np.random.default_rng(2)
+    d = 8
+    mu_true = rng.integers(-4, 5, d).astype(np.float32) / 4
+    q = rng.standard_normal(d)
+    q[0] = 1.0
+    errs1, errs2 = [], []
+    for k in range(2, 7):
+        a = np.float32(2.0 ** -k)
+        K = np.tile(mu_true, (64, 1))
+        K[0::2, 0] += a
+        K[1::2, 0] -= a
+        mu, var = oracle.block_stats(K, 64, "f32")
+        exact = _exact_log_mass(q, K)
+        assert np.isclose(exact, q @ mu_true + np.log(np.cosh(q[0] * a)), rtol=0, atol=1e-12)
+        e1 = oracle.cobs_log_mass(q[None], mu, var, order=1)[0, 0]
+        e2 = oracle.cobs_log_mass(q[None], mu, var, order=2)[0, 0]
+        errs1.append(exact - e1)
+        errs2.append(exact - e2)
+        x = q[0] * a
+        # log cosh x = x^2/2 - x^4/12 + x^6/45 - ... (alternating, decreasing terms)
+        assert abs(errs1[-1] - x * x / 2) <= x ** 4 / 12 * 1.001
+        assert abs(errs2[-1] + x ** 4 / 12) <= x ** 6 / 45 * 1.001 + 1e-15
+    r1 = np.array(errs1[:-1]) / np.array(errs1[1:])
+    r2 = np.array(errs2[:-1]) / np.array(errs2[1:])
+    assert np.all(np.diff(r1) > 0) and abs(r1[-1] - 4) < 2e-3      # second order in a
+    assert abs(r2[-1] - 16) < 2e-2                                # fourth order in a
+
+
+def test_constant_blocks_estimate_is_exact():
+    rng = np.random.default_rng(3)
+    d, nb = 16, 12
+    w = rng.integers(-8, 9, (nb, d)).astype(np.float32) / 4    # block sums exact in fp32
+    K = np.repeat(w, 64, axis=0)
+    mu, var = oracle.block_stats(K, 64 * nb, "f32")
+    q = rng.standard_normal((2, d))
+    est = oracle.cobs_log_mass(q, mu, var, order=2)
+    for h in range(2):
+        for b in range(nb):
+            assert np.isclose(est[h, b], _exact_log_mass(q[h], K[64 * b:64 * (b + 1)]),
+                              rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_raw_selection_on_constant_blocks_equals_the_block_path(seed):
+    """Constant blocks: zero variance, and every compressed entry inside a
+    block is the block's key, so the COBS raw selection (either order) is the
+    block path's Eq. 4 selection."""
+    rng = np.random.default_rng(seed)
+    nb, d = 40, 16
+    L = 64 * nb - 20                                  # partial last block (local)
+    w = rng.integers(-3, 4, (nb, d)).astype(np.float32)
+    K = np.repeat(w, 64, axis=0)[:L]
+    sel = rng.integers(-2, 3, (1, d)).astype(np.float32)
+    mu, var = oracle.block_stats(K, L, "f32")
+    Kc = oracle.compressed_keys(K, L, "f32")
+    for k in (1, 5, 20, 50):
+        p = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=oracle.RAW_SUM)
+        ref = oracle.select_blocks(sel, Kc, L, p)
+        assert oracle.select_blocks_cobs(sel, mu, var, L, p, order=1) == ref
+        assert oracle.select_blocks_cobs(sel, mu, var, L, p, order=2) == ref
+
+
+def test_second_order_finds_high_spread_blocks_the_first_order_misses():
+    """Blocks whose keys spread along q (same mean) hold more attention mass;
+    only the second-order score sees them, and its selection captures more of
+    the exact mass (oracle.quality)."""
+    rng = np.random.default_rng(4)
+    nb, d = 64, 32
+    L = 64 * nb
+    K = rng.standard_normal((L, d)).astype(np.float32) * 0.5
+    q = rng.standard_normal(d)
+    q /= np.linalg.norm(q)
+    u = q.astype(np.float32)
+    spread = [7, 19, 33, 48]
+    for b in spread:
+        K[64 * b:64 * (b + 1)] += np.tile([2.0, -2.0], 32)[:, None].astype(np.float32) * u
+    mu, var = oracle.block_stats(K, L, "f32")
+    p = SelectParams(top_k=4, n_init=1, n_local=2, score_mode=oracle.SOFTMAX_SUM)
+    s1 = oracle.select_blocks_cobs(q[None], mu, var, L, p, order=1)
+    s2 = oracle.select_blocks_cobs(q[None], mu, var, L, p, order=2)
+    assert set(spread) <= set(s2)
+    assert not set(spread) <= set(s1)
+    mass = oracle.block_mass(q, K, L, 1.0)
+    assert oracle.recall(mass, s2) > oracle.recall(mass, s1) + 0.1
