@@ -46,6 +46,7 @@ EXPORTS = [
     "sparse_attn_stream_read_blocks", "sparse_attn_stream_read",
     "sparse_attn_token_select_workspace_size", "sparse_attn_token_select",
     "sparse_attn_token_decode_workspace_size", "sparse_attn_token_decode",
+    "sparse_attn_cobs_stats", "sparse_attn_cobs_select_workspace_size", "sparse_attn_cobs_select",
 ]
 
 
@@ -124,6 +125,14 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_token_select.restype = _int
     L.sparse_attn_token_select.argtypes = [_vp, _int, _vp, _int, _int, _int, _int, _i64, _vp, _i32,
                                            _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+    L.sparse_attn_cobs_stats.restype = _int
+    L.sparse_attn_cobs_stats.argtypes = [_vp, _vp, _int, _int, _int, _int, _i64, _i64, _vp, _vp, _i32,
+                                         _vp]
+    L.sparse_attn_cobs_select_workspace_size.restype = _sz
+    L.sparse_attn_cobs_select_workspace_size.argtypes = [_int, _int, _int, _i64, _PP]
+    L.sparse_attn_cobs_select.restype = _int
+    L.sparse_attn_cobs_select.argtypes = [_vp, _int, _vp, _int, _int, _int, _int, _i64, _i64, _vp,
+                                          _PP, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
     L.sparse_attn_token_decode_workspace_size.restype = _sz
     L.sparse_attn_token_decode_workspace_size.argtypes = [_int, _int, _int, _i32, _i32]
     L.sparse_attn_token_decode.restype = _int
@@ -433,3 +442,58 @@ def token_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: to
                                         _stream(Q, stream))
     _check("sparse_attn_token_decode", st)
     return O, lse
+
+
+# ------------------------------------------------------------------ second-order block statistic
+
+def cobs_stats(K: torch.Tensor, stats: torch.Tensor, lens_prev: torch.Tensor, lens_now: torch.Tensor,
+               max_new_blocks: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Write the mean and per-channel variance rows of the blocks completed
+    between lens_prev and lens_now into stats [B, Hkv, nb_cap, 2, d] (in place)."""
+    B, Hkv, T_cap, d = K.shape
+    nb_cap = stats.shape[2]
+    if stats.dtype != K.dtype or stats.shape[:2] != K.shape[:2] or stats.shape[3:] != (2, d):
+        raise ValueError("stats must be [B, Hkv, nb_cap, 2, d] with K's dtype")
+    if max_new_blocks is None:
+        max_new_blocks = nb_cap
+    st = lib().sparse_attn_cobs_stats(_dev(K, "K"), _dev(stats, "stats"), _dtype_code(K), B, Hkv, d,
+                                      T_cap, nb_cap, _dev(lens_prev, "lens_prev"),
+                                      _dev(lens_now, "lens_now"), int(max_new_blocks),
+                                      _stream(K, stream))
+    _check("sparse_attn_cobs_stats", st)
+    return stats
+
+
+def cobs_select_workspace_size(B, Hkv, H_sel, T_cap, params: SelectParams) -> int:
+    return lib().sparse_attn_cobs_select_workspace_size(B, Hkv, H_sel, T_cap, ctypes.byref(params))
+
+
+def cobs_select(sel: torch.Tensor, stats: torch.Tensor, seq_lens: torch.Tensor, T_cap: int, top_k: int,
+                n_init: int = 1, n_local: int = 2, score_mode="softmax_sum", order: int = 2,
+                idx: Optional[torch.Tensor] = None, cnt: Optional[torch.Tensor] = None,
+                block_scores=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Block selection by the first- or second-order block-mass estimate.
+    Returns (idx, cnt, block_scores or None)."""
+    B, H_sel, d = sel.shape
+    Hkv, nb_cap = stats.shape[1], stats.shape[2]
+    p = make_params(top_k, n_init, n_local, score_mode)
+    dev = sel.device
+    if idx is None:
+        idx = torch.empty((B, Hkv, top_k + n_init + n_local), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if block_scores is True:
+        block_scores = torch.empty((B, Hkv, n_blocks(T_cap)), dtype=torch.float32, device=dev)
+    bs = block_scores if isinstance(block_scores, torch.Tensor) else None
+    need = cobs_select_workspace_size(B, Hkv, H_sel, T_cap, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_cobs_select(_dev(sel, "sel"), H_sel, _dev(stats, "stats"),
+                                       _dtype_code(stats), B, Hkv, d, T_cap, nb_cap,
+                                       _dev(seq_lens, "seq_lens"), ctypes.byref(p), int(order),
+                                       _dev(idx, "idx"), idx.shape[-1], _dev(cnt, "cnt"),
+                                       _opt(bs, "block_scores"), _dev(workspace, "workspace"),
+                                       ws_bytes, _stream(sel, stream))
+    _check("sparse_attn_cobs_select", st)
+    return idx, cnt, bs

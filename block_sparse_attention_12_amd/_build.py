@@ -16,14 +16,14 @@ LIB = os.path.join(LIBDIR, "libsparse_attn.so")
 ARCH = "gfx950"
 
 SOURCES = ["compress.hip", "select.hip", "decode.hip", "prefill.hip", "quality.hip", "stream.hip",
-           "token.hip", "sparse_attn_api.hip"]
+           "token.hip", "cobs.hip", "sparse_attn_api.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           # packed fp32 instructions stay off in every kernel
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 # prefill.hip: no NaN inputs are assumed (scores are finite or -inf), so max
 # operations need no quieting of their operands.
-PER_FILE = {"compress.hip": ["-ffp-contract=off"], "prefill.hip": ["-fno-honor-nans"]}
+PER_FILE = {"compress.hip": ["-ffp-contract=off"], "cobs.hip": ["-ffp-contract=off"], "prefill.hip": ["-fno-honor-nans"]}
 
 
 def hipcc():

@@ -1,0 +1,328 @@
+// Block selection with a second-order block statistic.
+//
+// Page: the abstract on "CoSA: Accelerating Long-Context Inference via
+// Proxy-Kernel Co-Designed Sparse Attention" (COBS): ranking blocks by
+// attention mass, a cumulant expansion of that mass, and a compressed
+// second-order statistic stored per block. The pages give no formula; the
+// reading implemented here: for a query q and block B the log-mass is
+// log 64 + q . mu_B + 1/2 q^T Sigma_B q + ..., and the stored statistic is the
+// per-channel variance (the diagonal of Sigma_B), so a block's estimate is
+//   q . mu_B + 1/2 sum_c q_c^2 var_{B,c}      (log 64 is common and dropped).
+//
+// Statistics (per complete 64-token block, in the key dtype): mu = fp32 sum of
+// the 64 keys in token order times 2^-6; var = fp32 sum of (k - mu32)^2 in
+// token order times 2^-6. The file is built with -ffp-contract=off, so both
+// are one exact value, reproducible on a CPU. Layout [B, Hkv, nb_cap, 2, d]:
+// mean row, then variance row.
+//
+// Kernels (HBM or latency bound; no matrix cores):
+//   cobs_stats_kernel    one 16-lane row group per block, 8 channels per lane:
+//                        the sum pass streams the 64 keys, the variance pass
+//                        re-reads them (16 KB, from cache)
+//   cobs_score_kernel    one row group per block: the group's estimates for
+//                        every selector head (fp32), reduced over the 16 lanes.
+//                        Raw-sum mode writes the sum over heads as the block
+//                        score; softmax mode writes per-head logits and each
+//                        chunk's (max, sum exp) per head
+//   cobs_softmax_kernel  softmax mode: merges the chunk statistics and writes
+//                        block score = sum over heads of each head's softmax
+//                        over the blocks (Eq. 6 form)
+// The top-k and Eq. 1 union reuse the block path's top-k kernel.
+#include <math.h>
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+constexpr int kCobsThreads = 256;
+constexpr int kCobsGroups = kCobsThreads / kRowLanes;       // 16 blocks in flight per workgroup
+constexpr int kCobsChunk = 256;                             // blocks per scoring workgroup
+
+CobsWorkspace cobs_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
+    CobsWorkspace w{};
+    const int64_t units = (int64_t)B * Hkv;
+    w.nb_cap = n_blocks(T_cap);
+    w.n_chunks = (int)((w.nb_cap + kCobsChunk - 1) / kCobsChunk);
+    if (w.n_chunks < 1) w.n_chunks = 1;
+    w.nb_pad = (int64_t)w.n_chunks * kCobsChunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    w.bscore_off = take((size_t)units * w.nb_cap * sizeof(float) + 4);
+    if (score_mode == SA_SCORE_SOFTMAX_SUM) {
+        w.logits_off = take((size_t)units * G * w.nb_pad * sizeof(float));
+        w.stats_off = take((size_t)units * G * w.n_chunks * sizeof(float2));
+    }
+    w.total = off;
+    return w;
+}
+
+// ---------------------------------------------------------------- statistics
+
+template <typename T>
+__global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
+    const T *__restrict__ K, T *__restrict__ stats, int64_t T_cap, int64_t nb_cap,
+    const int32_t *__restrict__ lens_prev, const int32_t *__restrict__ lens_now, int Hkv) {
+    const int unit = blockIdx.y;
+    const int b = unit / Hkv;
+    const int lane16 = threadIdx.x & (kRowLanes - 1), group = threadIdx.x / kRowLanes;
+    const int64_t L0 = clamp_len(lens_prev[b], T_cap), L1 = clamp_len(lens_now[b], T_cap);
+    const int64_t lo = L0 / kBlock, hi = L1 / kBlock;       // complete blocks only
+    const int64_t blk = lo + (int64_t)blockIdx.x * kCobsGroups + group;
+    if (blk >= hi || blk >= nb_cap) return;                 // no barrier in this kernel
+    const T *src = K + ((int64_t)unit * T_cap + blk * kBlock) * kD + lane16 * kLaneElems;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int t0 = 0; t0 < kBlock; t0 += 16) {
+        Raw8<T> r[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)(t0 + t) * kD, r[t]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float x[8];
+            unpack(r[t], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
+        }
+    }
+    float m[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        m[e] = s[e] * 0.015625f;                            // 2^-6, exact
+        q[e] = 0.f;
+    }
+#pragma unroll 1
+    for (int t0 = 0; t0 < kBlock; t0 += 16) {
+        Raw8<T> r[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)(t0 + t) * kD, r[t]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float x[8];
+            unpack(r[t], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float dv = x[e] - m[e];
+                q[e] = q[e] + dv * dv;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = q[e] * 0.015625f;
+    T *dst = stats + ((int64_t)unit * nb_cap + blk) * 2 * kD + lane16 * kLaneElems;
+    store8(dst, m);
+    store8(dst + kD, q);
+}
+
+// ---------------------------------------------------------------- scores
+
+template <typename T, int G, bool SOFTMAX, int ORDER>
+__global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
+    const T *__restrict__ sel, int H_sel, const T *__restrict__ stats, int64_t stats_nb,
+    int Hkv, int64_t nb_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens,
+    float *__restrict__ bscore,
+    float *__restrict__ logits, int64_t nb_pad, float2 *__restrict__ cstats, int n_chunks) {
+    __shared__ float2 s_ms[kCobsGroups][G];
+    const int unit = blockIdx.y;
+    const int b = unit / Hkv, kvh = unit % Hkv;
+    const int lane16 = threadIdx.x & (kRowLanes - 1), group = threadIdx.x / kRowLanes;
+    const int64_t L = clamp_len(seq_lens[b], T_cap);
+    const int64_t nbc = L / kBlock;                         // blocks with statistics
+    const int64_t chunk0 = (int64_t)blockIdx.x * kCobsChunk;
+
+    // selector slices: q_h and 1/2 q_h^2 for this lane's 8 channels
+    float qv[G][8], q2[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        load8(sel + ((int64_t)b * H_sel + (int64_t)kvh * G + h) * kD + lane16 * kLaneElems, qv[h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q2[h][e] = 0.5f * (qv[h][e] * qv[h][e]);
+    }
+    float run_m[G], run_s[G];                               // this group's (max, sum exp) per head
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        run_m[h] = -INFINITY;
+        run_s[h] = 0.f;
+    }
+    // the unit's statistics rows of blocks < nbc; rows past them read as zeros
+    constexpr uint32_t kRowBytes = kD * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(stats + (int64_t)unit * stats_nb * 2 * kD,
+                                                (uint32_t)(nbc * 2 * kRowBytes));
+    const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
+    constexpr int kPer = kCobsChunk / kCobsGroups;          // 16 blocks per row group
+    constexpr int kBatch = 4;
+#pragma unroll 1
+    for (int i0 = 0; i0 < kPer; i0 += kBatch) {
+        Raw8<T> mu[kBatch], va[kBatch];
+        int64_t blk[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            blk[j] = chunk0 + (int64_t)(i0 + j) * kCobsGroups + group;
+            load_raw(rS, row_offset(2 * blk[j], kRowBytes, lane_off), mu[j]);
+            if constexpr (ORDER == 2) load_raw(rS, row_offset(2 * blk[j] + 1, kRowBytes, lane_off), va[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            float m8[8], v8[8];
+            unpack(mu[j], m8);
+            if constexpr (ORDER == 2) unpack(va[j], v8);
+            float a[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(qv[h][e], m8[e], acc);
+                if constexpr (ORDER == 2) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc = fmaf(q2[h][e], v8[e], acc);
+                }
+                // sum over the 16 lanes of the row (stays inside the row group)
+                acc += __shfl_xor(acc, 8, 64);
+                acc += __shfl_xor(acc, 4, 64);
+                acc += __shfl_xor(acc, 2, 64);
+                acc += __shfl_xor(acc, 1, 64);
+                a[h] = acc;
+            }
+            const int64_t k = blk[j];
+            const bool has = k < nbc;
+            if constexpr (!SOFTMAX) {
+                float tot = a[0];
+#pragma unroll
+                for (int h = 1; h < G; ++h) tot += a[h];
+                if (lane16 == 0 && k < nb_cap) bscore[(int64_t)unit * nb_cap + k] = has ? tot : -INFINITY;
+            } else {
+                if (lane16 < G && k < nb_pad) {
+                    float v = a[0];
+#pragma unroll
+                    for (int h = 1; h < G; ++h)
+                        if (lane16 == h) v = a[h];
+                    logits[((int64_t)unit * G + lane16) * nb_pad + k] = has ? v : -INFINITY;
+                }
+                if (has) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) merge_ms(run_m[h], run_s[h], a[h], 1.f);
+                }
+            }
+        }
+    }
+    if constexpr (SOFTMAX) {
+        if (lane16 == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) s_ms[group][h] = make_float2(run_m[h], run_s[h]);
+        }
+        __syncthreads();
+        if (threadIdx.x < G) {
+            float2 r = s_ms[0][threadIdx.x];
+            for (int g2 = 1; g2 < kCobsGroups; ++g2)
+                merge_ms(r.x, r.y, s_ms[g2][threadIdx.x].x, s_ms[g2][threadIdx.x].y);
+            cstats[((int64_t)unit * G + threadIdx.x) * n_chunks + blockIdx.x] = r;
+        }
+    }
+}
+
+// block score = sum over heads of exp(logit - M_h) / Z_h, from the chunk statistics
+template <int G>
+__global__ __launch_bounds__(kCobsThreads) void cobs_softmax_kernel(
+    const float *__restrict__ logits, int64_t nb_pad, const float2 *__restrict__ cstats,
+    int n_chunks, int64_t nb_cap, float *__restrict__ bscore) {
+    __shared__ float s_M[G], s_Zi[G];
+    const int unit = blockIdx.y;
+    if (threadIdx.x < G) {
+        float M = -INFINITY, Z = 0.f;
+        const float2 *st = cstats + ((int64_t)unit * G + threadIdx.x) * n_chunks;
+        for (int c = 0; c < n_chunks; ++c) merge_ms(M, Z, st[c].x, st[c].y);
+        s_M[threadIdx.x] = M;
+        s_Zi[threadIdx.x] = Z > 0.f ? 1.f / Z : 0.f;
+    }
+    __syncthreads();
+    const int64_t k = (int64_t)blockIdx.x * kCobsChunk + threadIdx.x;
+    if (k >= nb_cap) return;
+    float S = 0.f;
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float x = logits[((int64_t)unit * G + h) * nb_pad + k];
+        if (x != -INFINITY) {
+            S += expf(x - s_M[h]) * s_Zi[h];
+            any = true;
+        }
+    }
+    bscore[(int64_t)unit * nb_cap + k] = any ? S : -INFINITY;
+}
+
+// ---------------------------------------------------------------- launchers
+
+int launch_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int64_t T_cap,
+                      int64_t nb_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                      int32_t max_new_blocks, hipStream_t stream) {
+    const dim3 grid((unsigned)((max_new_blocks + kCobsGroups - 1) / kCobsGroups), (unsigned)(B * Hkv));
+    if (dtype == SA_BF16)
+        hipLaunchKernelGGL(cobs_stats_kernel<bf16_t>, grid, dim3(kCobsThreads), 0, stream,
+                           (const bf16_t *)K, (bf16_t *)stats, T_cap, nb_cap, lens_prev, lens_now, Hkv);
+    else
+        hipLaunchKernelGGL(cobs_stats_kernel<float>, grid, dim3(kCobsThreads), 0, stream,
+                           (const float *)K, (float *)stats, T_cap, nb_cap, lens_prev, lens_now, Hkv);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+template <typename T, int G>
+static void launch_cobs_g(const void *sel, int H_sel, const void *stats, int64_t stats_nb, int B,
+                          int Hkv, int64_t T_cap, const int32_t *seq_lens, const sa_select_params &p,
+                          int order, float *bscore, const CobsWorkspace &w, char *ws,
+                          hipStream_t stream) {
+    const dim3 grid((unsigned)w.n_chunks, (unsigned)(B * Hkv));
+    float *logits = (float *)(ws + w.logits_off);
+    float2 *cst = (float2 *)(ws + w.stats_off);
+#define SA_COBS(SM, ORD)                                                                          \
+    hipLaunchKernelGGL((cobs_score_kernel<T, G, SM, ORD>), grid, dim3(kCobsThreads), 0, stream,    \
+                       (const T *)sel, H_sel, (const T *)stats, stats_nb, Hkv, w.nb_cap, T_cap,     \
+                       seq_lens, bscore, logits, w.nb_pad, cst, w.n_chunks)
+    if (p.score_mode == SA_SCORE_SOFTMAX_SUM) {
+        if (order == 2) SA_COBS(true, 2);
+        else SA_COBS(true, 1);
+        hipLaunchKernelGGL((cobs_softmax_kernel<G>), grid, dim3(kCobsThreads), 0, stream,
+                           (const float *)logits, w.nb_pad, (const float2 *)cst, w.n_chunks,
+                           w.nb_cap, bscore);
+    } else {
+        if (order == 2) SA_COBS(false, 2);
+        else SA_COBS(false, 1);
+    }
+#undef SA_COBS
+}
+
+int launch_cobs_select(const void *sel, int G, const void *stats, int64_t stats_nb, int dtype,
+                       int B, int Hkv, int64_t T_cap, const int32_t *seq_lens,
+                       const sa_select_params &p,
+                       int order, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                       float *block_scores_out, void *workspace, hipStream_t stream) {
+    const CobsWorkspace w = cobs_workspace_layout(B, Hkv, G, T_cap, p.score_mode);
+    char *ws = (char *)workspace;
+    float *bscore = block_scores_out ? block_scores_out : (float *)(ws + w.bscore_off);
+    const int H_sel = G * Hkv;
+#define SA_COBS_CASE(GG)                                                                          \
+    case GG:                                                                                      \
+        if (dtype == SA_BF16)                                                                     \
+            launch_cobs_g<bf16_t, GG>(sel, H_sel, stats, stats_nb, B, Hkv, T_cap, seq_lens, p,    \
+                                      order, bscore, w, ws, stream);                              \
+        else                                                                                      \
+            launch_cobs_g<float, GG>(sel, H_sel, stats, stats_nb, B, Hkv, T_cap, seq_lens, p,     \
+                                     order, bscore, w, ws, stream);                               \
+        break;
+    switch (G) {
+        SA_COBS_CASE(1)
+        SA_COBS_CASE(2)
+        SA_COBS_CASE(4)
+        SA_COBS_CASE(8)
+        default: return SA_ERR_UNSUPPORTED;
+    }
+#undef SA_COBS_CASE
+    launch_topk_raw(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, bscore, idx_out, idx_cap, cnt_out,
+                    stream);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace sa

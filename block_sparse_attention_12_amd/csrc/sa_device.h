@@ -187,6 +187,14 @@ __device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
     return L < 0 ? 0 : (L > T_cap ? T_cap : L);
 }
 
+// Merges a (max, sum of exp(x - max)) pair into another.
+__device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    s = s * expf(m - M) + s2 * expf(m2 - M);
+    m = M;
+}
+
 // 32-bit key whose unsigned order is the order of the fp32 value (-0 and +0 tie).
 __device__ __forceinline__ uint32_t orderable(float x) {
     if (x == 0.f) x = 0.f;                               // -0 and +0 tie

@@ -65,6 +65,25 @@ int launch_decode_rows(const void *Q, const void *K, const void *V, int dtype, i
                        const int32_t *cnt, int32_t idx_cap, float scale, void *O, int out_dtype,
                        float *lse_out, int32_t n_split, void *workspace, hipStream_t stream);
 
+// Second-order block statistic selection: scratch layout and launchers.
+struct CobsWorkspace {
+    size_t bscore_off;                 // [units][nb_cap] fp32 block scores
+    size_t logits_off;                 // [units][G][nb_pad] fp32 (softmax mode)
+    size_t stats_off;                  // [units][G][n_chunks] float2 (max, sum exp)
+    size_t total;
+    int64_t nb_cap, nb_pad;
+    int n_chunks;
+};
+CobsWorkspace cobs_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode);
+int launch_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int64_t T_cap,
+                      int64_t nb_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                      int32_t max_new_blocks, hipStream_t stream);
+int launch_cobs_select(const void *sel, int G, const void *stats, int64_t stats_nb, int dtype,
+                       int B, int Hkv, int64_t T_cap, const int32_t *seq_lens,
+                       const sa_select_params &p,
+                       int order, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                       float *block_scores_out, void *workspace, hipStream_t stream);
+
 int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p);
 size_t prefill_workspace_bytes(int Hq, int Hkv, int64_t q_start, int64_t Tq,
                                const sa_select_params &p);

@@ -185,13 +185,6 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
 
 // ---------------------------------------------------------------- softmax scores
 
-__device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2) {
-    const float M = fmaxf(m, m2);
-    if (M == -INFINITY) return;
-    s = s * expf(m - M) + s2 * expf(m2 - M);
-    m = M;
-}
-
 template <typename T, int G>
 __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     const T *__restrict__ sel, int H_sel, const T *__restrict__ Kc, int Hkv, int64_t nc_cap,

@@ -234,6 +234,52 @@ int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dt
                               O, out_dtype, lse_out, s, workspace, (hipStream_t)stream);
 }
 
+int sparse_attn_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int d,
+                           int64_t T_cap, int64_t nb_cap, const int32_t *lens_prev,
+                           const int32_t *lens_now, int32_t max_new_blocks, void *stream) {
+    if (!K || !stats || !lens_prev || !lens_now) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hkv <= 0 || d <= 0 || T_cap < 0 || nb_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    if (max_new_blocks < 0) return SA_ERR_INVALID_ARG;
+    if (d != kD) return SA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
+    if (nb_cap < T_cap / kBlock) return SA_ERR_CAPACITY;
+    if (max_new_blocks == 0 || T_cap < kBlock) return SA_OK;
+    return launch_cobs_stats(K, stats, dtype, B, Hkv, T_cap, nb_cap, lens_prev, lens_now,
+                             max_new_blocks, (hipStream_t)stream);
+}
+
+size_t sparse_attn_cobs_select_workspace_size(int B, int Hkv, int H_sel, int64_t T_cap,
+                                              const sa_select_params *p) {
+    if (!p || B <= 0 || Hkv <= 0 || H_sel <= 0 || H_sel % Hkv || T_cap < 0) return 0;
+    return cobs_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
+}
+
+int sparse_attn_cobs_select(const void *sel, int H_sel, const void *stats, int dtype, int B,
+                            int Hkv, int d, int64_t T_cap, int64_t nb_cap,
+                            const int32_t *seq_lens, const sa_select_params *p, int32_t order,
+                            int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                            float *block_scores_out, void *workspace, size_t ws_bytes,
+                            void *stream) {
+    if (!sel || !stats || !seq_lens || !idx_out || !cnt_out) return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || B <= 0 || Hkv <= 0 || H_sel <= 0 || d <= 0 || T_cap < 0 || nb_cap < 0)
+        return SA_ERR_INVALID_ARG;
+    int st = check_params(p);
+    if (st) return st;
+    if (H_sel % Hkv || (order != 1 && order != 2)) return SA_ERR_INVALID_ARG;
+    const int G = H_sel / Hkv;
+    if (d != kD) return SA_ERR_UNSUPPORTED;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
+    if (n_blocks(T_cap) > 32768 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
+    if (nb_cap < n_blocks(T_cap)) return SA_ERR_CAPACITY;
+    if (idx_cap < union_cap(p) || idx_cap <= 0) return SA_ERR_CAPACITY;
+    const size_t need = cobs_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total;
+    if (!workspace || ws_bytes < need) return SA_ERR_WORKSPACE;
+    if (T_cap == 0) return SA_ERR_INVALID_ARG;
+    return launch_cobs_select(sel, G, stats, nb_cap, dtype, B, Hkv, T_cap, seq_lens, *p, order, idx_out,
+                              idx_cap, cnt_out, block_scores_out, workspace, (hipStream_t)stream);
+}
+
 size_t sparse_attn_block_mass_workspace_size(int B, int Hq, int64_t mass_cap) {
     if (B <= 0 || Hq <= 0 || mass_cap <= 0) return 0;
     return block_mass_workspace_bytes(B, Hq, mass_cap);

@@ -316,6 +316,68 @@ int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dt
                              void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * sparse_attn_cobs_stats - per-block statistics for selection with a
+ * second-order term (the COBS abstract on the page "CoSA: Accelerating
+ * Long-Context Inference via Proxy-Kernel Co-Designed Sparse Attention":
+ * block selection by attention mass, a cumulant expansion of it, and a
+ * compressed second-order statistic stored per block; the pages give no
+ * formula, and the reading here is the block mean plus the per-channel
+ * variance, i.e. the diagonal of the keys' covariance).
+ *
+ * For every sequence b and every complete 64-token block j with
+ * lens_prev[b] / 64 <= j < lens_now[b] / 64, writes
+ *   stats[b, kvh, j, 0, :] = mean of keys 64j .. 64j+63
+ *   stats[b, kvh, j, 1, :] = mean of (key - mean)^2 over the same keys
+ * each an fp32 sum in token order times 2^-6 (the variance uses the fp32
+ * mean), rounded to the key dtype: one exact value. Other rows are left
+ * untouched. Partial blocks get no statistics.
+ *
+ *   K          [B, Hkv, T_cap, d] device; stats [B, Hkv, nb_cap, 2, d] device,
+ *              K's dtype, nb_cap >= T_cap / 64
+ *   lens_prev, lens_now   device int32 [B]
+ *   max_new_blocks  host hint: an upper bound on the new complete blocks per
+ *              sequence (sizes the launch; pass nb_cap for a bulk build)
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, B * Hkv > 65535),
+ *         SA_ERR_CAPACITY.
+ */
+int sparse_attn_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int d,
+                           int64_t T_cap, int64_t nb_cap, const int32_t *lens_prev,
+                           const int32_t *lens_now, int32_t max_new_blocks, void *stream);
+
+/* Workspace bytes needed by sparse_attn_cobs_select. */
+size_t sparse_attn_cobs_select_workspace_size(int B, int Hkv, int H_sel, int64_t T_cap,
+                                              const sa_select_params *p);
+
+/*
+ * sparse_attn_cobs_select - block selection by the estimated attention mass
+ * of each block (same reading as sparse_attn_cobs_stats): for selector head h
+ * and a block with statistics, the estimated log-mass (less the common log 64)
+ *   order 1:  e_h = sel_h . mean
+ *   order 2:  e_h = sel_h . mean + 1/2 sum_c sel_hc^2 var_c
+ * and the group's block score is, with params->score_mode,
+ *   SOFTMAX_SUM: sum_h softmax over the blocks of e_h   (Eq. 6 form)
+ *   RAW_SUM:     sum_h e_h                             (one Forecast: its e)
+ * Blocks without statistics (the partial last block) score -inf. Then, as in
+ * sparse_attn_select, the top_k candidate blocks (ties to the lower index)
+ * are unioned with the initial and local blocks (Eq. 1 on the SparDA summary
+ * page). idx_out / cnt_out / block_scores_out as in sparse_attn_select.
+ *
+ *   sel        [B, H_sel, d] device (H_sel = G * Hkv, G in {1, 2, 4, 8})
+ *   stats      [B, Hkv, nb_cap, 2, d] device, written by sparse_attn_cobs_stats
+ *              for the complete blocks of seq_lens[b]; nb_cap >= ceil(T_cap/64)
+ *   order      1 or 2
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G, parameters
+ *         other than 64/32/16, ceil(T_cap/64) > 32768), SA_ERR_CAPACITY,
+ *         SA_ERR_WORKSPACE.
+ */
+int sparse_attn_cobs_select(const void *sel, int H_sel, const void *stats, int dtype, int B,
+                            int Hkv, int d, int64_t T_cap, int64_t nb_cap,
+                            const int32_t *seq_lens, const sa_select_params *p, int32_t order,
+                            int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
+                            float *block_scores_out, void *workspace, size_t ws_bytes,
+                            void *stream);
+
+/*
  * sparse_attn_block_mass - selection quality, not a step of the sparse path:
  * the exact attention mass of every 64-token block for the decode query of
  * each head (the sum of the block's dense attention probabilities, the

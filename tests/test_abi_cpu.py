@@ -265,3 +265,40 @@ def test_token_decode_validation():
     need = L.sparse_attn_token_decode_workspace_size(2, 8, 2, 448, 4)
     assert need == 2 * 8 * 4 * 132 * 4                                 # partials of 4 splits
     assert call(n_split=4, ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+
+
+def test_cobs_validation():
+    L = sa.lib()
+
+    def stats_call(**kw):
+        a = dict(K=FAKE, S=FAKE, dtype=sa.SA_BF16, B=2, Hkv=2, d=128, T_cap=1000, nb_cap=16,
+                 lp=FAKE, ln=FAKE, mx=16)
+        a.update(kw)
+        return L.sparse_attn_cobs_stats(a["K"], a["S"], a["dtype"], a["B"], a["Hkv"], a["d"],
+                                        a["T_cap"], a["nb_cap"], a["lp"], a["ln"], a["mx"], None)
+    assert stats_call(K=None) == sa.SA_ERR_INVALID_ARG
+    assert stats_call(mx=-1) == sa.SA_ERR_INVALID_ARG
+    assert stats_call(d=64) == sa.SA_ERR_UNSUPPORTED
+    assert stats_call(nb_cap=14) == sa.SA_ERR_CAPACITY                # 1000 // 64 = 15 complete
+    assert stats_call(mx=0) == sa.SA_OK                               # nothing to do
+
+    def sel_call(**kw):
+        p = kw.pop("params", sa.make_params(8, 1, 2, "softmax_sum"))
+        a = dict(sel=FAKE, H_sel=8, S=FAKE, dtype=sa.SA_BF16, B=2, Hkv=2, d=128, T_cap=1000,
+                 nb_cap=16, lens=FAKE, order=2, idx=FAKE, idx_cap=11, cnt=FAKE, bs=None, ws=FAKE,
+                 ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sparse_attn_cobs_select(a["sel"], a["H_sel"], a["S"], a["dtype"], a["B"], a["Hkv"],
+                                         a["d"], a["T_cap"], a["nb_cap"], a["lens"], ctypes.byref(p),
+                                         a["order"], a["idx"], a["idx_cap"], a["cnt"], a["bs"],
+                                         a["ws"], a["ws_bytes"], None)
+    assert sel_call(sel=None) == sa.SA_ERR_INVALID_ARG
+    assert sel_call(order=3) == sa.SA_ERR_INVALID_ARG
+    assert sel_call(H_sel=7) == sa.SA_ERR_INVALID_ARG
+    assert sel_call(H_sel=6) == sa.SA_ERR_UNSUPPORTED                 # G = 3
+    assert sel_call(params=sa.make_params(8, block_size=32)) == sa.SA_ERR_UNSUPPORTED
+    assert sel_call(nb_cap=15) == sa.SA_ERR_CAPACITY                  # ceil(1000 / 64) = 16
+    assert sel_call(idx_cap=10) == sa.SA_ERR_CAPACITY
+    need = L.sparse_attn_cobs_select_workspace_size(2, 2, 8, 1000, ctypes.byref(sa.make_params(8)))
+    assert need >= 4 * 16 * 4 + 4 * 4 * 256 * 4                       # block scores + logits
+    assert sel_call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE

@@ -1,0 +1,166 @@
+"""GPU parity of the second-order block statistic path against oracle.cobs.
+
+Block statistics: bit-exact. Block scores: elementwise tolerance. Block sets:
+exact (lower index on ties) except for near ties (parity.selection_ok). The
+reading of the statistic itself is not fixed by the pages (oracle.cobs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_12_amd as sa
+import oracle
+from oracle import SelectParams
+from oracle.attention import block_tokens
+from parity import selection_ok, gpu_rows, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+BITS = {"f32": torch.int32, "bf16": torch.int16}
+
+
+def rand(shape, dt, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * scale).to(TD[dt])
+
+
+def lens_t(lens):
+    return torch.tensor(lens, dtype=torch.int32, device=DEV)
+
+
+def _stats_gpu(K, lens, nb_cap=None, fill=1024.0):
+    B, Hkv, T, d = K.shape
+    nb_cap = nb_cap if nb_cap is not None else (T + 63) // 64
+    S = torch.full((B, Hkv, nb_cap, 2, d), fill, dtype=K.dtype, device=DEV)
+    sa.cobs_stats(K.to(DEV), S, lens_t([0] * B), lens_t(lens))
+    return S
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cobs_stats_bulk_and_incremental_bit_exact(dt):
+    B, Hkv, T = 3, 2, 1000
+    lens = [1000, 640, 63]
+    K = rand((B, Hkv, T, 128), dt, 1, scale=2.0) + 0.5
+    S = _stats_gpu(K, lens)
+    got = S.cpu()
+    for b in range(B):
+        for h in range(Hkv):
+            mu, var = oracle.block_stats(K[b, h].float().numpy(), lens[b], dt)
+            n = mu.shape[0]
+            ref = torch.from_numpy(np.stack([mu, var], axis=1)).to(TD[dt])
+            assert torch.equal(got[b, h, :n].view(BITS[dt]), ref.view(BITS[dt])), (b, h)
+            assert torch.all(got[b, h, n:] == 1024.0), "rows of incomplete blocks stay untouched"
+    # incremental: one token at a time across a block edge, then a jump
+    Kd = K.to(DEV)
+    S2 = torch.full_like(S, 1024.0)
+    steps = [[0, 0, 0], [63, 63, 63], [64, 64, 63], [65, 127, 63], [128, 640, 63], [1000, 640, 63]]
+    for i in range(1, len(steps)):
+        sa.cobs_stats(Kd, S2, lens_t(steps[i - 1]), lens_t(steps[i]), max_new_blocks=16)
+    assert torch.equal(S2.cpu().view(BITS[dt]), got.view(BITS[dt]))
+
+
+def _check_cobs_select(sel, K, lens, T_cap, k, n_init, n_local, mode, dt, order, exact=False):
+    S = _stats_gpu(K, lens)
+    idx, cnt, bs = sa.cobs_select(sel.to(DEV), S, lens_t(lens), T_cap, k, n_init, n_local, mode,
+                                  order, block_scores=True)
+    rows = gpu_rows(idx, cnt)
+    bs = bs.cpu().numpy().astype(np.float64)
+    Sel = to_np(sel)
+    B, Hkv = K.shape[:2]
+    Gs = Sel.shape[1] // Hkv
+    p = SelectParams(top_k=k, n_init=n_init, n_local=n_local, score_mode=mode)
+    kinds = []
+    for b in range(B):
+        for h in range(Hkv):
+            L = lens[b]
+            mu, var = oracle.block_stats(K[b, h].float().numpy(), L, dt)
+            ref, BS = oracle.select_blocks_cobs(Sel[b, h * Gs:(h + 1) * Gs], mu, var, L, p, order,
+                                                return_scores=True)
+            nb = oracle.n_blocks(L)
+            fin = np.isfinite(BS)
+            assert np.array_equal(np.isfinite(bs[b, h, :nb]), fin), (b, h)
+            if fin.any():
+                scale = np.abs(BS[fin]).max()
+                assert np.allclose(bs[b, h, :nb][fin], BS[fin], rtol=2e-5, atol=2e-6 * scale), (b, h)
+            assert np.all(np.isneginf(bs[b, h, nb:]))
+            if exact:
+                assert rows[(b, h)] == ref, (b, h, rows[(b, h)], ref)
+                kinds.append("exact")
+            else:
+                ok, why = selection_ok(rows[(b, h)], ref, BS, nb, k, n_init, n_local)
+                assert ok, ((b, h), why, rows[(b, h)], ref)
+                kinds.append(why)
+    return kinds, idx, cnt
+
+
+@pytest.mark.parametrize("mode,G,dt", [("softmax_sum", 4, "bf16"), ("softmax_sum", 4, "f32"),
+                                       ("raw_sum", 1, "bf16"), ("raw_sum", 1, "f32"),
+                                       ("softmax_sum", 1, "bf16"), ("raw_sum", 4, "bf16"),
+                                       ("softmax_sum", 8, "bf16"), ("softmax_sum", 2, "f32")])
+@pytest.mark.parametrize("order", [1, 2])
+def test_cobs_select_parity(mode, G, dt, order):
+    B, Hkv, T = 3, 2, 20000                           # 313 blocks: two scoring chunks
+    lens = [20000, 9000, 700]
+    K = rand((B, Hkv, T, 128), dt, 2)
+    sel = rand((B, Hkv * G, 128), dt, 3, scale=128 ** -0.5)
+    kinds, _, _ = _check_cobs_select(sel, K, lens, T, 24, 1, 2, mode, dt, order)
+    assert kinds.count("exact") >= len(kinds) - 1
+
+
+@pytest.mark.parametrize("L", [0, 10, 63, 64, 65, 127, 128, 129, 192, 260, 16384])
+def test_cobs_select_short_lengths_and_edges(L):
+    dt = "bf16"
+    T = 16384
+    K = rand((1, 2, T, 128), dt, 4)
+    sel = rand((1, 8, 128), dt, 5, scale=128 ** -0.5)
+    for k in (0, 1, 3, 300):
+        _check_cobs_select(sel, K, [L], T, k, 1, 2, "softmax_sum", dt, 2)
+    # no local blocks: the partial last block is a candidate without statistics
+    _check_cobs_select(sel, K, [L], T, 2, 1, 0, "raw_sum", dt, 2)
+
+
+def _hadamard64():
+    H = np.array([[1.0]])
+    while H.shape[0] < 64:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def test_cobs_second_order_finds_spread_blocks_and_decode_runs_on_them():
+    """Blocks whose keys spread in the query's strongest channels (zero-mean,
+    mutually orthogonal sign patterns, so the block mean and the off-diagonal
+    covariance are unchanged) carry far more attention mass: the second-order
+    selection includes them, the first order does not, and decode attention
+    over the second-order set matches the oracle and captures more of the
+    exact mass."""
+    dt = "bf16"
+    B, Hq, Hkv, T = 1, 8, 2, 64 * 128
+    g = torch.Generator().manual_seed(6)
+    K = torch.randn((B, Hkv, T, 128), generator=g) * 0.5
+    V = torch.randn((B, Hkv, T, 128), generator=g)
+    Q = torch.randn((B, Hq, 128), generator=g) * 0.05
+    Q[..., :4] = 1.0                                   # the strongest channels of every head
+    H = torch.from_numpy(_hadamard64()[1:5].T.copy()).float()   # [64 tokens, 4 channels]
+    spread = [11, 40, 77, 100]
+    for h in range(Hkv):
+        for blk in spread:
+            K[0, h, 64 * blk:64 * (blk + 1), :4] += 2.0 * H
+    K, V, Q = K.to(TD[dt]), V.to(TD[dt]), Q.to(TD[dt])
+    lens = [T]
+    k = 8
+    _, idx1, cnt1 = _check_cobs_select(Q, K, lens, T, k, 1, 2, "softmax_sum", dt, 1)
+    _, idx2, cnt2 = _check_cobs_select(Q, K, lens, T, k, 1, 2, "softmax_sum", dt, 2)
+    r1, r2 = gpu_rows(idx1, cnt1), gpu_rows(idx2, cnt2)
+    for h in range(Hkv):
+        assert set(spread) <= set(r2[(0, h)])
+        assert not set(spread) <= set(r1[(0, h)])
+    O, lse = sa.decode(Q.to(DEV), K.to(DEV), V.to(DEV), lens_t(lens), idx2, cnt2, 1.0)
+    Qn, Kn, Vn = to_np(Q), to_np(K), to_np(V)
+    for h in range(Hkv):
+        o, l = oracle.sparse_attention(Qn[0, 4 * h:4 * h + 4], Kn[0, h], Vn[0, h],
+                                       block_tokens(r2[(0, h)], T), 1.0)
+        assert_close(to_np(O)[0, 4 * h:4 * h + 4], o, dt, f"O head group {h}")
+        for g4 in range(4):
+            mass = oracle.block_mass(Qn[0, 4 * h + g4], Kn[0, h], T, 1.0)
+            assert oracle.recall(mass, r2[(0, h)]) > oracle.recall(mass, r1[(0, h)]) + 0.2
