@@ -22,9 +22,10 @@ Reading:
   * statistics exist for complete 64-token blocks only (candidate blocks are
     complete whenever at least one local block is kept), so log n_B = log 64 is
     a common constant and is left out of the score;
-  * mu and var are one exact value each: fp32 sums over the block's 64 keys in
-    token order, times 2^-6, rounded to the key dtype; var uses the fp32 mean:
-    var_c = fp32(sum_t (k_tc - mu32_c)^2) * 2^-6;
+  * mu and var are one exact value each, in a fixed fp32 order: with P_j the
+    sum of keys 16j .. 16j+15 in token order, mu32 = (((P_0 + P_1) + P_2) +
+    P_3) * 2^-6; var the same from quarter sums of (k_t - mu32)^2; both rounded
+    to the key dtype;
   * a group's block score is the Eq. 6 form over the estimated log-masses
     (sum over the group's heads of each head's softmax over the blocks), or,
     in raw-sum mode (one Forecast vector, "Compact Forecast Indexer"), the sum
@@ -40,21 +41,34 @@ from .compress import n_blocks
 BLOCK = 64
 
 
+QUARTER = 16
+
+
+def _quarter_ordered_sum(terms: np.ndarray) -> np.ndarray:
+    """terms [nbc, 64, d] fp32 -> (((P_0 + P_1) + P_2) + P_3), P_j the token-order
+    fp32 sum of terms 16j .. 16j+15 (every block at once)."""
+    parts = []
+    for j in range(BLOCK // QUARTER):
+        p = np.zeros((terms.shape[0], terms.shape[2]), dtype=np.float32)
+        for t in range(j * QUARTER, (j + 1) * QUARTER):
+            p = (p + terms[:, t]).astype(np.float32)
+        parts.append(p)
+    tot = parts[0]
+    for p in parts[1:]:
+        tot = (tot + p).astype(np.float32)
+    return tot
+
+
 def block_stats(K: np.ndarray, L: int, dtype: str):
-    """(mu, var) [L // 64, d] of the complete blocks of K[:L], each an fp32
-    token-order sum times 2^-6, rounded to dtype ("f32" or "bf16")."""
+    """(mu, var) [L // 64, d] of the complete blocks of K[:L], each a sum in the
+    fixed quarter order times 2^-6, rounded to dtype ("f32" or "bf16")."""
     nbc = L // BLOCK
     d = K.shape[1]
     rows = np.asarray(K[:nbc * BLOCK], dtype=np.float32).reshape(nbc, BLOCK, d)
     scale = np.float32(2.0 ** -6)
-    s = np.zeros((nbc, d), dtype=np.float32)
-    for t in range(BLOCK):                           # token order, fp32, every block at once
-        s = (s + rows[:, t]).astype(np.float32)
-    m32 = (s * scale).astype(np.float32)
-    q = np.zeros((nbc, d), dtype=np.float32)
-    for t in range(BLOCK):
-        dv = (rows[:, t] - m32).astype(np.float32)
-        q = (q + (dv * dv).astype(np.float32)).astype(np.float32)
+    m32 = (_quarter_ordered_sum(rows) * scale).astype(np.float32)
+    dv = (rows - m32[:, None, :]).astype(np.float32)
+    q = _quarter_ordered_sum((dv * dv).astype(np.float32))
     return round_to(m32, dtype), round_to((q * scale).astype(np.float32), dtype)
 
 
