@@ -14,7 +14,7 @@ HBM bandwidth of the dominant kernel (decode attention) on its algorithmic
 bytes against the 8 TB/s peak, and the CPU oracle timed on the same inputs.
 Other workloads: --workload decode_gqa_bf16_32k | decode_tiny_f32_8k |
 crosslayer_bf16_64k | lookahead_forecast_bf16_128k | tokenindex_forecast_bf16_128k |
-prefill_chunk_bf16_128k.
+decode_cobs_gqa_bf16_128k | prefill_chunk_bf16_128k.
 """
 from __future__ import annotations
 
@@ -65,6 +65,8 @@ def main():
     if args.workload in synth.TOKEN_WORKLOADS:
         return bench_token(args, synth.TOKEN_WORKLOADS[args.workload])
     w = synth.WORKLOADS[args.workload]
+    if w.cobs:
+        return bench_cobs(args, w)
     if w.lookahead:
         return bench_lookahead(args, w)
     if w.layers > 1:
@@ -455,6 +457,154 @@ def cpu_baseline_decode(w, inp, lens, budget_s):
             "sample": f"{done} full decode steps of {w.name} (all {len(units)} units: append, "
                       f"select, attend), numpy fp64, BLAS threads = {n_threads} (CPU affinity, "
                       f"at most 16), {t_units:.1f} s"}
+
+
+def bench_cobs(args, w):
+    """One decode step selected by block statistics (second order): append the
+    statistics of the block the newest token completes, score every complete
+    block by its estimated attention mass (mean and per-channel variance) with
+    the group's queries, top-k + union, attend. value = batch / step time.
+    Also reports, on the first replica, the dense attention mass captured by
+    the second-order selection, by the first-order one (block mean only) and
+    by the compressed-key selection of the same queries."""
+    import numpy as np
+    import torch
+    import synth
+    from block_sparse_attention_12_amd.pipeline import CobsDecoder, SparseDecoder
+    from block_sparse_attention_12_amd import block_mass, n_blocks
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.make_decode_inputs(w, device=dev)
+    lens_now = inp["seq_lens"]
+    lens_prev = lens_now - 1
+    dec = CobsDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, w.selector,
+                      w.score_mode, device=dev, n_split=args.n_split, order=2)
+    reps = []
+    for r in range(args.replicas):
+        rep = {k: (inp[k] if r == 0 else inp[k].clone()) for k in ("Q", "K", "V")}
+        rep["S"] = dec.new_stats(inp["K"].dtype)
+        dec.build(rep["K"], rep["S"], lens_prev)           # blocks complete before the new token
+        reps.append(rep)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def phases_of(rep):
+        return {
+            "append": lambda: dec.append(rep["K"], rep["S"], lens_prev, lens_now),
+            "select": lambda: dec.select(rep["Q"], rep["S"], lens_now),
+            "attend": lambda: dec.attend(rep["Q"], rep["K"], rep["V"], lens_now),
+        }
+
+    steps_fn = [lambda rep=rep: [f() for f in phases_of(rep).values()] for rep in reps]
+    for i in range(args.warmup):
+        steps_fn[i % len(reps)]()
+    torch.cuda.synchronize()
+    ev0, ev1 = _events(2)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        steps_fn[i % len(reps)]()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    mean = {}
+    n_ph = max(10, min(args.steps, 100))
+    for name in ("append", "select", "attend"):
+        fns = [phases_of(rep)[name] for rep in reps]
+        for i in range(3):
+            fns[i % len(fns)]()
+        evs = [_events(2) for _ in range(n_ph)]
+        for i in range(n_ph):
+            evs[i][0].record(stream)
+            fns[i % len(fns)]()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        mean[name] = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ph
+
+    elem = inp["K"].element_size()
+    lens = [int(x) for x in lens_now.cpu()]
+    row = 128 * elem
+    cnt, idx = dec.cnt.cpu(), dec.idx.cpu()
+    attn_bytes = 0
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for blk in idx[b, h, :int(cnt[b, h])].tolist():
+                attn_bytes += 2 * row * max(0, min(64, lens[b] - 64 * blk))
+    attn_bytes += w.B * w.Hq * 128 * elem + w.B * w.Hq * (128 * 4 + 4)
+    sel_bytes = sum(L // 64 for L in lens) * w.Hkv * 2 * row + inp["Q"].numel() * elem
+    append_bytes = sum((L // 64) - ((L - 1) // 64) for L in lens) * w.Hkv * (64 * row + 2 * row)
+    step_bytes = attn_bytes + sel_bytes + append_bytes
+    attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
+    sel_gbs = sel_bytes / (mean["select"] * 1e-3) / 1e9
+
+    # selection quality on the first replica: second order, first order, compressed keys
+    rep = reps[0]
+    quality = {}
+    sets = {}
+    for order in (2, 1):
+        dec.select(rep["Q"], rep["S"], lens_now, order=order)
+        sets[f"order{order}"] = (dec.idx.clone(), dec.cnt.clone())
+    kc_dec = SparseDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, w.selector,
+                           w.score_mode, device=dev)
+    Kc = kc_dec.new_kc(inp["K"].dtype)
+    kc_dec.build(rep["K"], Kc, lens_now)
+    kc_dec.select(rep["Q"], Kc, lens_now)
+    sets["compressed_keys"] = (kc_dec.idx, kc_dec.cnt)
+    for name, (ix, cn) in sets.items():
+        mass, rec = block_mass(rep["Q"], rep["K"], lens_now, 1.0, idx=ix, cnt=cn)
+        R = rec.cpu().numpy()
+        rows = ix.cpu().numpy()
+        hit = tot = 0
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                got = set(rows[b, h].tolist())
+                hit += sum(1 for x in inp["spread"][b][h] if x in got)
+                tot += len(inp["spread"][b][h])
+        quality[name] = {"recall_mean": round(float(R.mean()), 4),
+                         "recall_min": round(float(R.min()), 4),
+                         "spread_blocks_selected": round(hit / max(tot, 1), 4)}
+    M = mass.cpu().numpy().astype(np.float64)
+    best = []
+    for b in range(w.B):
+        nb = n_blocks(lens[b])
+        cand = np.arange(w.n_init, nb - w.n_local)
+        for hq in range(w.Hq):
+            m = M[b, hq, :nb]
+            best.append(m[:w.n_init].sum() + m[nb - w.n_local:].sum()
+                        + np.sort(m[cand])[::-1][:w.top_k].sum())
+    quality["mass_optimal_recall_mean"] = round(float(np.mean(best)), 4)
+    ceil = measured_stream_read_gbs(dev)
+    out = {
+        "metric": "sparse decode tokens/s at 128K with second-order block-statistic selection, 1 GPU",
+        "value": round(w.B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), planted mean-shifted and high-variance blocks)",
+        "config": {"workload": w.name, "batch": w.B, "context": w.T, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k, "n_init": w.n_init,
+                   "n_local": w.n_local, "selector": w.selector, "score_mode": w.score_mode,
+                   "statistic": "block mean + per-channel variance (second order)",
+                   "replicas": args.replicas, "launch": "eager, one stream",
+                   "parallelism": "none (1 GPU)"},
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "phase_ms": {k: round(v, 5) for k, v in mean.items()},
+        "step_bytes": step_bytes, "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm",
+                     "kernel": "sparse_attn_decode (decode_kernel + combine_kernel)",
+                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"{w.name}_decode"),
+                     "bytes_per_launch": attn_bytes,
+                     "measured_ceiling": {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
+                                          "GB/s": ceil, "frac": round(attn_gbs / ceil, 4)}},
+        "select": {"kernel": "sparse_attn_cobs_select (statistics scan, group softmax, top-k)",
+                   "GB/s": round(sel_gbs, 1), "frac_of_ceiling": round(sel_gbs / ceil, 4),
+                   "bytes": sel_bytes},
+        "selection_quality": quality,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def bench_token(args, w):

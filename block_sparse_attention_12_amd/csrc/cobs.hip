@@ -9,16 +9,17 @@
 // per-channel variance (the diagonal of Sigma_B), so a block's estimate is
 //   q . mu_B + 1/2 sum_c q_c^2 var_{B,c}      (log 64 is common and dropped).
 //
-// Statistics (per complete 64-token block, in the key dtype): mu = fp32 sum of
-// the 64 keys in token order times 2^-6; var = fp32 sum of (k - mu32)^2 in
-// token order times 2^-6. The file is built with -ffp-contract=off, so both
+// Statistics (per complete 64-token block, in the key dtype): with P_j the
+// fp32 sum of keys 16j .. 16j+15 in token order, mu32 = (((P_0 + P_1) + P_2)
+// + P_3) * 2^-6; var likewise from the quarter sums of (k - mu32)^2; both
+// rounded to the key dtype. The file is built with -ffp-contract=off, so both
 // are one exact value, reproducible on a CPU. Layout [B, Hkv, nb_cap, 2, d]:
 // mean row, then variance row.
 //
 // Kernels (HBM or latency bound; no matrix cores):
-//   cobs_stats_kernel    one 16-lane row group per block, 8 channels per lane:
-//                        the sum pass streams the 64 keys, the variance pass
-//                        re-reads them (16 KB, from cache)
+//   cobs_stats_kernel    four 16-lane row groups per block (one per quarter of
+//                        16 keys), 8 channels per lane; the keys stay in
+//                        registers for both passes, partial sums meet in LDS
 //   cobs_score_kernel    one row group per block: the group's estimates for
 //                        every selector head (fp32), reduced over the 16 lanes.
 //                        Raw-sum mode writes the sum over heads as the block
@@ -63,43 +64,52 @@ CobsWorkspace cobs_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int sc
 
 // ---------------------------------------------------------------- statistics
 
+// Four row groups per block, one per quarter (16 consecutive keys); each keeps
+// its 16 keys in registers, so the block is read once. Quarter sums and
+// quarter sums of squared deviations meet in LDS and are combined in quarter
+// order by every group alike.
+constexpr int kStatsBlocksPerWG = kCobsGroups / 4;
+
 template <typename T>
 __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
     const T *__restrict__ K, T *__restrict__ stats, int64_t T_cap, int64_t nb_cap,
     const int32_t *__restrict__ lens_prev, const int32_t *__restrict__ lens_now, int Hkv) {
+    __shared__ float s_part[kStatsBlocksPerWG][4][kRowLanes][8];
     const int unit = blockIdx.y;
     const int b = unit / Hkv;
     const int lane16 = threadIdx.x & (kRowLanes - 1), group = threadIdx.x / kRowLanes;
+    const int slot = group >> 2, quarter = group & 3;
     const int64_t L0 = clamp_len(lens_prev[b], T_cap), L1 = clamp_len(lens_now[b], T_cap);
     const int64_t lo = L0 / kBlock, hi = L1 / kBlock;       // complete blocks only
-    const int64_t blk = lo + (int64_t)blockIdx.x * kCobsGroups + group;
-    if (blk >= hi || blk >= nb_cap) return;                 // no barrier in this kernel
-    const T *src = K + ((int64_t)unit * T_cap + blk * kBlock) * kD + lane16 * kLaneElems;
-    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int t0 = 0; t0 < kBlock; t0 += 16) {
-        Raw8<T> r[16];
+    const int64_t blk = lo + (int64_t)blockIdx.x * kStatsBlocksPerWG + slot;
+    const bool valid = blk < hi && blk < nb_cap;            // uniform per row group
+    const T *src = K + ((int64_t)unit * T_cap + blk * kBlock + quarter * 16) * kD + lane16 * kLaneElems;
+    Raw8<T> r[16];
+    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (valid) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)(t0 + t) * kD, r[t]);
+        for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)t * kD, r[t]);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < 16; ++t) {                      // quarter sum, token order
             float x[8];
             unpack(r[t], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
+            for (int e = 0; e < 8; ++e) p[e] = p[e] + x[e];
         }
     }
-    float m[8], q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_part[slot][quarter][lane16][e] = p[e];
+    __syncthreads();
+    float m[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        m[e] = s[e] * 0.015625f;                            // 2^-6, exact
-        q[e] = 0.f;
+        float t = s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e];
+        t = t + s_part[slot][2][lane16][e];
+        t = t + s_part[slot][3][lane16][e];
+        m[e] = t * 0.015625f;                               // 2^-6, exact
     }
-#pragma unroll 1
-    for (int t0 = 0; t0 < kBlock; t0 += 16) {
-        Raw8<T> r[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)(t0 + t) * kD, r[t]);
+    float q[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (valid) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             float x[8];
@@ -111,14 +121,36 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
             }
         }
     }
+    __syncthreads();                                        // every group has read the sums
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = q[e] * 0.015625f;
+    for (int e = 0; e < 8; ++e) s_part[slot][quarter][lane16][e] = q[e];
+    __syncthreads();
+    if (!valid || quarter != 0) return;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float t = s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e];
+        t = t + s_part[slot][2][lane16][e];
+        t = t + s_part[slot][3][lane16][e];
+        v[e] = t * 0.015625f;
+    }
     T *dst = stats + ((int64_t)unit * nb_cap + blk) * 2 * kD + lane16 * kLaneElems;
     store8(dst, m);
-    store8(dst + kD, q);
+    store8(dst + kD, v);
 }
 
 // ---------------------------------------------------------------- scores
+
+// Sum over the 16 lanes of a row with DPP. The partner sequence (quad xor 1,
+// quad xor 2, half mirror, mirror) pairs only sums of equal terms, so every
+// lane of the row ends with the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+    v += dpp<kDppQuadXor1>(v);
+    v += dpp<kDppQuadXor2>(v);
+    v += dpp<kDppRowHalfMirror>(v);
+    v += dpp<kDppRowMirror>(v);
+    return v;
+}
 
 template <typename T, int G, bool SOFTMAX, int ORDER>
 __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
@@ -154,7 +186,7 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
                                                 (uint32_t)(nbc * 2 * kRowBytes));
     const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
     constexpr int kPer = kCobsChunk / kCobsGroups;          // 16 blocks per row group
-    constexpr int kBatch = 4;
+    constexpr int kBatch = G >= 8 ? 4 : 8;                 // blocks in flight per row group
 #pragma unroll 1
     for (int i0 = 0; i0 < kPer; i0 += kBatch) {
         Raw8<T> mu[kBatch], va[kBatch];
@@ -165,12 +197,12 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
             load_raw(rS, row_offset(2 * blk[j], kRowBytes, lane_off), mu[j]);
             if constexpr (ORDER == 2) load_raw(rS, row_offset(2 * blk[j] + 1, kRowBytes, lane_off), va[j]);
         }
+        float a[kBatch][G];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             float m8[8], v8[8];
             unpack(mu[j], m8);
             if constexpr (ORDER == 2) unpack(va[j], v8);
-            float a[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float acc = 0.f;
@@ -180,32 +212,41 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc = fmaf(q2[h][e], v8[e], acc);
                 }
-                // sum over the 16 lanes of the row (stays inside the row group)
-                acc += __shfl_xor(acc, 8, 64);
-                acc += __shfl_xor(acc, 4, 64);
-                acc += __shfl_xor(acc, 2, 64);
-                acc += __shfl_xor(acc, 1, 64);
-                a[h] = acc;
+                a[j][h] = row_sum16(acc);
             }
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
             const int64_t k = blk[j];
             const bool has = k < nbc;
             if constexpr (!SOFTMAX) {
-                float tot = a[0];
+                float tot = a[j][0];
 #pragma unroll
-                for (int h = 1; h < G; ++h) tot += a[h];
+                for (int h = 1; h < G; ++h) tot += a[j][h];
                 if (lane16 == 0 && k < nb_cap) bscore[(int64_t)unit * nb_cap + k] = has ? tot : -INFINITY;
-            } else {
-                if (lane16 < G && k < nb_pad) {
-                    float v = a[0];
+            } else if (lane16 < G && k < nb_pad) {
+                float v = a[j][0];
 #pragma unroll
-                    for (int h = 1; h < G; ++h)
-                        if (lane16 == h) v = a[h];
-                    logits[((int64_t)unit * G + lane16) * nb_pad + k] = has ? v : -INFINITY;
-                }
-                if (has) {
+                for (int h = 1; h < G; ++h)
+                    if (lane16 == h) v = a[j][h];
+                logits[((int64_t)unit * G + lane16) * nb_pad + k] = has ? v : -INFINITY;
+            }
+        }
+        if constexpr (SOFTMAX) {                            // one rescale per batch and head
 #pragma unroll
-                    for (int h = 0; h < G; ++h) merge_ms(run_m[h], run_s[h], a[h], 1.f);
-                }
+            for (int h = 0; h < G; ++h) {
+                float bm = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (blk[j] < nbc) bm = fmaxf(bm, a[j][h]);
+                if (bm == -INFINITY) continue;
+                const float mn = fmaxf(run_m[h], bm);
+                float ssum = run_m[h] == -INFINITY ? 0.f : run_s[h] * expf(run_m[h] - mn);
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (blk[j] < nbc) ssum += expf(a[j][h] - mn);
+                run_m[h] = mn;
+                run_s[h] = ssum;
             }
         }
     }
@@ -259,7 +300,8 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_softmax_kernel(
 int launch_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int64_t T_cap,
                       int64_t nb_cap, const int32_t *lens_prev, const int32_t *lens_now,
                       int32_t max_new_blocks, hipStream_t stream) {
-    const dim3 grid((unsigned)((max_new_blocks + kCobsGroups - 1) / kCobsGroups), (unsigned)(B * Hkv));
+    const dim3 grid((unsigned)((max_new_blocks + kStatsBlocksPerWG - 1) / kStatsBlocksPerWG),
+                    (unsigned)(B * Hkv));
     if (dtype == SA_BF16)
         hipLaunchKernelGGL(cobs_stats_kernel<bf16_t>, grid, dim3(kCobsThreads), 0, stream,
                            (const bf16_t *)K, (bf16_t *)stats, T_cap, nb_cap, lens_prev, lens_now, Hkv);

@@ -14,7 +14,8 @@ import torch
 
 from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
                select_workspace_size, token_select, token_decode, token_select_workspace_size,
-               token_decode_workspace_size,
+               token_decode_workspace_size, cobs_stats, cobs_select, cobs_select_workspace_size,
+               n_blocks,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
 
@@ -177,6 +178,36 @@ class LookaheadDecoder:
                 sel_done = next_done
         main.wait_stream(side)                     # join: the side stream is idle after the step
         return outs
+
+
+class CobsDecoder(SparseDecoder):
+    """A decode step whose selection uses per-block statistics (block mean and
+    per-channel variance) instead of compressed keys: append writes the
+    statistics of a block when the new token completes it, select scores the
+    blocks by the first- or second-order block-mass estimate, attend is the
+    block decode attention."""
+
+    def __init__(self, *args, order: int = 2, **kw):
+        super().__init__(*args, **kw)
+        self.order = order
+        p = make_params(self.top_k, self.n_init, self.n_local, self.score_mode)
+        ws = cobs_select_workspace_size(self.B, self.Hkv, self.H_sel, self.T_cap, p)
+        self.sel_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
+        self.nb_cap = n_blocks(self.T_cap)
+
+    def new_stats(self, dtype) -> torch.Tensor:
+        return torch.empty((self.B, self.Hkv, self.nb_cap, 2, 128), dtype=dtype, device=self.device)
+
+    def build(self, K, stats, seq_lens):
+        cobs_stats(K, stats, torch.zeros_like(seq_lens), seq_lens, max_new_blocks=self.nb_cap)
+
+    def append(self, K, stats, lens_prev, lens_now, max_new_blocks: int = 1):
+        cobs_stats(K, stats, lens_prev, lens_now, max_new_blocks=max_new_blocks)
+
+    def select(self, sel, stats, seq_lens, block_scores=None, order=None):
+        return cobs_select(sel, stats, seq_lens, self.T_cap, self.top_k, self.n_init, self.n_local,
+                           self.score_mode, self.order if order is None else order, idx=self.idx,
+                           cnt=self.cnt, block_scores=block_scores, workspace=self.sel_ws)
 
 
 class TokenIndexDecoder:

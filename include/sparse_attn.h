@@ -328,7 +328,8 @@ int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dt
  * lens_prev[b] / 64 <= j < lens_now[b] / 64, writes
  *   stats[b, kvh, j, 0, :] = mean of keys 64j .. 64j+63
  *   stats[b, kvh, j, 1, :] = mean of (key - mean)^2 over the same keys
- * each an fp32 sum in token order times 2^-6 (the variance uses the fp32
+ * each a sum in a fixed fp32 order (the four 16-key quarter sums, each in
+ * token order, added in quarter order) times 2^-6 (the variance uses the fp32
  * mean), rounded to the key dtype: one exact value. Other rows are left
  * untouched. Partial blocks get no statistics.
  *

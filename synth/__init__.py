@@ -15,6 +15,11 @@ Recipe (the same for every workload):
     ``+2 * u`` added, where u is the unit vector of the group-summed query
     (query-scored workloads) or of the Forecast vector (Forecast-scored ones),
     taken in fp32 before the cast.
+  * Spread blocks (workloads with ``spread`` > 0): ``spread`` further distinct
+    choosable blocks per (sequence, KV head) get, in the 4 channels where the
+    group-summed query is largest in magnitude, 8 * P[t, c] added, P being
+    zero-mean, mutually orthogonal +-1 patterns over the block's 64 tokens:
+    the block mean is unchanged and only those channels' variance grows.
   * Finally every tensor is cast to the workload dtype (fp32 or bf16).
 Lengths may be ragged: positions at or beyond a sequence's length hold random
 values that no step may read. Token-index workloads (``make_token_inputs``)
@@ -53,6 +58,8 @@ class DecodeWorkload:
     steps: int = 0          # appended decode steps (cross-layer workload only)
     lookahead: bool = False # each layer selects with its own Forecast; layer l+1's selection
                             # runs while layer l attends
+    spread: int = 0         # planted high-variance blocks per (sequence, KV head)
+    cobs: bool = False      # selection by block statistics (first / second order)
 
     @property
     def G(self) -> int:
@@ -137,6 +144,12 @@ WORKLOADS = {
         "lookahead_forecast_bf16_128k", B=8, Hq=32, Hkv=8, d=128, T=131072, dtype="bf16",
         top_k=64, n_init=1, n_local=2, selector="forecast", score_mode="raw_sum",
         planted=8, seed=3, layers=4, lookahead=True),
+    # the 128K GQA decode shape selected by block mean and variance (second
+    # order), with 8 mean-shifted and 8 high-variance planted blocks per KV head
+    "decode_cobs_gqa_bf16_128k": DecodeWorkload(
+        "decode_cobs_gqa_bf16_128k", B=8, Hq=32, Hkv=8, d=128, T=131072, dtype="bf16",
+        top_k=64, n_init=1, n_local=2, selector="query", score_mode="softmax_sum",
+        planted=8, seed=7, spread=8, cobs=True),
     # cross-layer reuse: 4 layers share layer 0's selection, 16 appended steps
     "crosslayer_bf16_64k": DecodeWorkload(
         "crosslayer_bf16_64k", B=32, Hq=32, Hkv=8, d=128, T=65536, dtype="bf16",
@@ -175,6 +188,28 @@ def _plant(Kb: torch.Tensor, u: torch.Tensor, blocks: Sequence[int]):
     """Add 2*u to every key of the listed 64-token blocks (Kb: [T, d] fp32, in place)."""
     for blk in blocks:
         Kb[blk * BLOCK:(blk + 1) * BLOCK] += 2.0 * u
+    return None
+
+
+def _sign_patterns(n: int, device) -> torch.Tensor:
+    """n mutually orthogonal, zero-mean +-1 patterns over the 64 tokens of a
+    block (rows 1..n of the Sylvester Hadamard matrix), as [64, n]."""
+    H = torch.ones((1, 1))
+    while H.shape[0] < BLOCK:
+        H = torch.cat([torch.cat([H, H], 1), torch.cat([H, -H], 1)], 0)
+    return H[1:n + 1].T.contiguous().to(device)
+
+
+def _plant_spread(Kb: torch.Tensor, dirv: torch.Tensor, blocks: Sequence[int], amp: float = 8.0):
+    """Spread the keys of the listed blocks along the 4 channels where dirv is
+    largest in magnitude: channel c of token t gets amp * P[t, c] added, with
+    P zero-mean orthogonal sign patterns, so the block mean and the
+    cross-channel covariance stay as they were and only the per-channel
+    variance of those channels grows (by amp^2)."""
+    ch = torch.topk(dirv.abs(), 4).indices
+    P = _sign_patterns(4, Kb.device)
+    for blk in blocks:
+        Kb[blk * BLOCK:(blk + 1) * BLOCK, ch] += amp * P
 
 
 def make_decode_inputs(w: DecodeWorkload, device="cpu", seq_lens: Optional[Sequence[int]] = None,
@@ -183,8 +218,9 @@ def make_decode_inputs(w: DecodeWorkload, device="cpu", seq_lens: Optional[Seque
 
     Returns a dict with
       Q [B, Hq, d], F [B, Hkv, d] (forecast workloads only), K, V [B, Hkv, T_cap, d]
-      in the workload dtype, seq_lens (int32 [B], same device), planted (list per
-      sequence of lists per KV head of block ids) and the scale (1.0).
+      in the workload dtype, seq_lens (int32 [B], same device), planted and
+      spread (lists per sequence of lists per KV head of block ids; spread is
+      empty without spread blocks) and the scale (1.0).
     """
     device = torch.device(device)
     lens = list(seq_lens) if seq_lens is not None else [w.T] * w.B
@@ -198,11 +234,11 @@ def make_decode_inputs(w: DecodeWorkload, device="cpu", seq_lens: Optional[Seque
     F = _randn((w.B, w.Hkv, w.d), g, device) * inv if w.selector == "forecast" else None
     K = torch.empty((w.B, w.Hkv, cap, w.d), dtype=dt, device=device)
     V = torch.empty((w.B, w.Hkv, cap, w.d), dtype=dt, device=device)
-    planted = []
+    planted, spread = [], []
     for b in range(w.B):
         Kb = _randn((w.Hkv, cap, w.d), g, device)
         Vb = _randn((w.Hkv, cap, w.d), g, device)
-        pl_b = []
+        pl_b, sp_b = [], []
         for h in range(w.Hkv):
             blocks = []
             if w.planted > 0:
@@ -216,12 +252,19 @@ def make_decode_inputs(w: DecodeWorkload, device="cpu", seq_lens: Optional[Seque
                     dirv = Q[b, h * w.G:(h + 1) * w.G].sum(0)
                 u = dirv / dirv.norm()
                 _plant(Kb[h], u, blocks)
+                if w.spread > 0:
+                    rest = [c for c in cand if c not in blocks]
+                    pick = torch.randperm(len(rest), generator=g, device=device)[:w.spread].tolist()
+                    sp = sorted(rest[i] for i in pick)
+                    _plant_spread(Kb[h], dirv, sp)
+                    sp_b.append(sp)
             pl_b.append(blocks)
         planted.append(pl_b)
+        spread.append(sp_b)
         K[b].copy_(Kb)
         V[b].copy_(Vb)
         del Kb, Vb
-    out = dict(Q=Q.to(dt), K=K, V=V, scale=1.0, planted=planted,
+    out = dict(Q=Q.to(dt), K=K, V=V, scale=1.0, planted=planted, spread=spread,
                seq_lens=torch.tensor(lens, dtype=torch.int32, device=device))
     if F is not None:
         out["F"] = F.to(dt)

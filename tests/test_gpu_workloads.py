@@ -170,3 +170,41 @@ def test_tokenindex_forecast_bf16_128k_full_sampled():
             assert_close(to_np(outs[l][0])[b, h * w.G:(h + 1) * w.G], o, w.dtype, f"O {l} {(b, h)}")
             assert_close(outs[l][1].cpu().numpy()[b, h * w.G:(h + 1) * w.G], lse, w.dtype,
                          f"LSE {l} {(b, h)}")
+
+
+def test_decode_cobs_gqa_bf16_128k_full_sampled():
+    """The block-statistic workload at full size (B = 8, 128K, G = 4, softmax
+    form, second order), in the benchmark's launch configuration: statistics
+    bit-exact, selection and attention checked on sampled units."""
+    from block_sparse_attention_12_amd.pipeline import CobsDecoder
+
+    w = synth.WORKLOADS["decode_cobs_gqa_bf16_128k"]
+    inp = synth.make_decode_inputs(w, device=DEV)
+    lens = inp["seq_lens"]
+    dec = CobsDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, w.selector,
+                      w.score_mode, order=2)
+    S = dec.new_stats(inp["K"].dtype)
+    dec.build(inp["K"], S, lens - 1)
+    dec.append(inp["K"], S, lens - 1, lens)
+    dec.select(inp["Q"], S, lens)
+    O, lse = dec.attend(inp["Q"], inp["K"], inp["V"], lens)
+    torch.cuda.synchronize()
+    rows = gpu_rows(dec.idx, dec.cnt)
+    Q = to_np(inp["Q"])
+    p = SelectParams(w.top_k, w.n_init, w.n_local, w.score_mode)
+    for (b, h) in [(0, 0), (2, 5), (7, 7)]:
+        L = int(lens[b])
+        Kbh = inp["K"][b, h].float().cpu().numpy()
+        mu, var = oracle.block_stats(Kbh, L, w.dtype)
+        got = S[b, h, :mu.shape[0]].float().cpu().numpy()
+        assert np.array_equal(got[:, 0], mu) and np.array_equal(got[:, 1], var), (b, h)
+        ref, BS = oracle.select_blocks_cobs(Q[b, h * w.G:(h + 1) * w.G], mu, var, L, p, 2, True)
+        ok, why = selection_ok(rows[(b, h)], ref, BS, oracle.n_blocks(L), w.top_k, w.n_init,
+                               w.n_local)
+        assert ok, ((b, h), why)
+        assert set(inp["spread"][b][h]) <= set(rows[(b, h)]), "spread block missed"
+        o, l = oracle.sparse_attention(Q[b, h * w.G:(h + 1) * w.G], Kbh,
+                                       inp["V"][b, h].float().cpu().numpy(),
+                                       block_tokens(rows[(b, h)], L), 1.0)
+        assert_close(to_np(O)[b, h * w.G:(h + 1) * w.G], o, w.dtype, f"O {(b, h)}")
+        assert_close(lse.cpu().numpy()[b, h * w.G:(h + 1) * w.G], l, w.dtype, f"LSE {(b, h)}")
