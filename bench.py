@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--n-split", type=int, default=0)
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time a decode step as three library calls (compress, select, decode) "
+                         "instead of one sparse_attn_decode_step call")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step as a captured HIP graph (slower on this stack: a graph "
                          "launch costs more than the launch gaps it removes)")
@@ -193,8 +196,12 @@ def bench_decode(args, w):
         }
 
     def whole_step(rep):
-        for f in phases_of(rep).values():
-            f()
+        if args.separate_calls:
+            for f in phases_of(rep).values():
+                f()
+        else:                                   # sparse_attn_decode_step: one call
+            dec.fused_step(rep["Q"], rep[sel_name], rep["K"], rep["V"], rep["Kc"], lens_prev,
+                           lens_now)
 
     if not args.graph:
         steps_fn = [lambda rep=rep: whole_step(rep) for rep in reps]
@@ -273,7 +280,9 @@ def bench_decode(args, w):
                    "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k, "n_init": w.n_init,
                    "n_local": w.n_local, "selector": w.selector, "score_mode": w.score_mode,
                    "replicas": args.replicas, "n_split": args.n_split or "auto",
-                   "launch": "hip graph per step" if args.graph else "eager, one stream",
+                   "launch": ("hip graph per step" if args.graph else "eager, one stream") + (
+                       ", compress + select + decode calls" if args.separate_calls
+                       else ", one sparse_attn_decode_step call"),
                    "parallelism": "none (1 GPU)"},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "phase_ms": {k: round(v, 5) for k, v in mean.items()},

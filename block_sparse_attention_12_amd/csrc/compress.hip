@@ -12,6 +12,7 @@
 // flight. Consecutive entries share a half-window, which is carried in
 // registers. HBM bound: every key is read once (the half-window at a run
 // boundary is read twice, usually from L2).
+#include "compress_device.h"
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -20,21 +21,6 @@ namespace sa {
 constexpr int kCompressThreads = 256;
 constexpr int kCompressRun = 4;                              // entries per row group
 constexpr int kCompressEntriesPerWG = (kCompressThreads / kRowLanes) * kCompressRun;
-
-template <typename T>
-__device__ __forceinline__ void half_window_sum(const T *__restrict__ p, float (&acc)[8]) {
-    Raw8<T> r[kCmpStride];
-#pragma unroll
-    for (int t = 0; t < kCmpStride; ++t) load_raw(p + (int64_t)t * kD, r[t]);
-    unpack(r[0], acc);
-#pragma unroll
-    for (int t = 1; t < kCmpStride; ++t) {
-        float x[8];
-        unpack(r[t], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
-    }
-}
 
 template <typename T>
 __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
@@ -55,21 +41,7 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
     for (int64_t j0 = j_begin + ((int64_t)blockIdx.y * (kCompressThreads / kRowLanes) + group) *
                                     kCompressRun;
          j0 < j_end; j0 += step) {
-        float prev[8];
-        half_window_sum(Ku + j0 * kCmpStride * kD, prev);
-#pragma unroll
-        for (int r = 0; r < kCompressRun; ++r) {
-            const int64_t j = j0 + r;
-            if (j >= j_end) break;
-            float next[8];
-            half_window_sum(Ku + (j + 1) * kCmpStride * kD, next);
-            float e[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) e[c] = (prev[c] + next[c]) * 0.03125f;
-            store8(Kcu + j * kD, e);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) prev[c] = next[c];
-        }
+        compress_run<T, kCompressRun>(Ku, Kcu, j0, j_end);
     }
 }
 

@@ -27,10 +27,13 @@ int launch_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int64_t 
                     int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
                     int32_t max_new_entries, hipStream_t stream);
 
+// With K and lens_prev (raw-sum mode only), the compressed entries completed
+// between lens_prev and seq_lens are written by the scoring launch itself.
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
                   int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
-                  float *block_scores_out, void *workspace, hipStream_t stream);
+                  float *block_scores_out, void *workspace, hipStream_t stream,
+                  const void *K = nullptr, const int32_t *lens_prev = nullptr);
 
 void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
                      const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,

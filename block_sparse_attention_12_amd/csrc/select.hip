@@ -28,6 +28,7 @@
 #include <float.h>
 #include <math.h>
 
+#include "compress_device.h"
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -73,11 +74,18 @@ struct RawIter {                         // one iteration: 4 blocks x 3 inside e
     Raw8<T> r[12];
 };
 
-template <typename T>
+// APPEND: the launch has one more column of workgroups, which write the
+// compressed entries completed between lens_prev and seq_lens (the decode
+// step's append) while the other columns score. Scoring then reads only the
+// entries that existed before (j < n_c(lens_prev)) from Kc and forms any newer
+// entry it needs from K itself, with the same arithmetic, so it never depends
+// on the concurrent writes.
+template <typename T, bool APPEND>
 __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const T *__restrict__ sel, int H_sel, int Gs, const T *__restrict__ Kc, int Hkv,
     int64_t nc_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ bscore,
-    int64_t nb_cap) {
+    int64_t nb_cap, const T *__restrict__ K, T *__restrict__ Kc_w,
+    const int32_t *__restrict__ lens_prev, int n_local) {
     const int unit = blockIdx.y;
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int64_t L = clamp_len(seq_lens[b], T_cap);
@@ -86,9 +94,25 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const int lane16 = threadIdx.x & 15;
     const int group = threadIdx.x >> 4;                 // 0..15
     constexpr uint32_t kRowBytes = kD * sizeof(T);
-    // rows at or past n_c(L) read as zeros
+    int64_t nc_old = nc;                                // entries readable from Kc
+    if constexpr (APPEND) {
+        int64_t Lp = lens_prev[b];
+        Lp = Lp < 0 ? 0 : (Lp > L ? L : Lp);
+        nc_old = n_compressed(Lp);
+        if (blockIdx.x == gridDim.x - 1) {              // the append column
+            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+            T *Kcu = Kc_w + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
+            for (int64_t j = nc_old + group; j < nc; j += 16) {   // few keys in flight
+                Raw8<T> r;
+                compress_entry_raw(Ku, j, r);
+                store_raw(Kcu + j * kD, r);
+            }
+            return;
+        }
+    }
+    // rows at or past the readable entries read as zeros
     const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)unit * nc_cap * kD,
-                                                (uint32_t)(nc * kRowBytes));
+                                                (uint32_t)(nc_old * kRowBytes));
     const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
     const int64_t chunk0 = (int64_t)blockIdx.x * kRawChunkBlocks;
     auto issue = [&](RawIter<T> &it, int64_t blk0) {
@@ -179,6 +203,42 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
             if (it + 2 < kIters) issue(bufA, b0 + 128);
             __builtin_amdgcn_sched_barrier(0);
             process(bufB, b0 + 64);
+        }
+    }
+    if constexpr (APPEND) {
+        // Blocks holding entries of this step's append were scored above with
+        // those entries read as zeros. Each row group rescores its affected
+        // candidate 4-block groups (rare: a single token's new window lies in
+        // the local blocks) with the new entries formed from the keys (same
+        // arithmetic as the append), through the same reduction, and
+        // overwrites their scores. The scores of affected local blocks stay
+        // provisional: the top-k never reads them, and this launch is used
+        // without a block-score output. Runs after the main loop, so its
+        // registers do not add to the loop's.
+        // blocks with an inside entry in [nc_old, nc), below the local window
+        // (local blocks are kept whatever their score; only top-k candidates
+        // need exact scores)
+        const int64_t b_lo = (nc_old + 1) / 4;                  // 4b + 2 >= nc_old
+        int64_t b_hi = (nc - 1) / 4 + 1;                         // 4b <= nc - 1
+        const int64_t cand_hi = n_blocks(L) - n_local;
+        b_hi = b_hi < cand_hi ? b_hi : cand_hi;
+        if (nc > nc_old && b_lo < b_hi) {
+            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+#pragma unroll 1
+            for (int it = 0; it < kIters; ++it) {
+                const int64_t b0 = chunk0 + it * 64 + group * 4;
+                if (b0 + 3 < b_lo || b0 >= b_hi) continue;            // uniform per row group
+                RawIter<T> fix;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 3; ++e) {
+                        const int64_t j = 4 * (b0 + q) + e;
+                        if (j >= nc_old && j < nc) compress_entry_raw(Ku, j, fix.r[q * 3 + e]);
+                        else load_raw(rKc, row_offset(j, kRowBytes, lane_off), fix.r[q * 3 + e]);
+                    }
+                process(fix, b0);
+            }
         }
     }
 }
@@ -616,14 +676,20 @@ static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B
                        int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
                        const sa_select_params &p, int32_t *idx_out, int32_t idx_cap,
                        int32_t *cnt_out, float *bs_out, const SelectWorkspace &w, char *ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, const void *K = nullptr,
+                       const int32_t *lens_prev = nullptr) {
     float *bscore = (float *)(ws + w.bscore_off);
     const unsigned units = (unsigned)(B * Hkv);
     const unsigned chunks = (unsigned)((w.nb_cap + kRawChunkBlocks - 1) / kRawChunkBlocks);
-    if (chunks > 0)
-        hipLaunchKernelGGL(score_raw_kernel<T>, dim3(chunks, units), dim3(kSelThreads), 0, stream,
-                           (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap, seq_lens,
-                           bscore, w.nb_cap);
+    if (lens_prev)                                      // scoring + the step's append in one launch
+        hipLaunchKernelGGL((score_raw_kernel<T, true>), dim3(chunks + 1, units), dim3(kSelThreads), 0,
+                           stream, (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap,
+                           seq_lens, bscore, w.nb_cap, (const T *)K, (T *)Kc, lens_prev, p.n_local);
+    else if (chunks > 0)
+        hipLaunchKernelGGL((score_raw_kernel<T, false>), dim3(chunks, units), dim3(kSelThreads), 0,
+                           stream, (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap,
+                           seq_lens, bscore, w.nb_cap, (const T *)nullptr, (T *)nullptr,
+                           (const int32_t *)nullptr, 0);
     launch_topk<1, false>(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, nullptr, 0, nullptr, 0,
                           bscore, bs_out, idx_out, idx_cap, cnt_out, stream);
 }
@@ -631,7 +697,8 @@ static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
                   int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
-                  float *block_scores_out, void *workspace, hipStream_t stream) {
+                  float *block_scores_out, void *workspace, hipStream_t stream, const void *K,
+                  const int32_t *lens_prev) {
     const SelectWorkspace w = select_workspace_layout(B, Hkv, G, T_cap, p.score_mode);
     if (w.nb_cap > kMaxTopkBlocks) return SA_ERR_UNSUPPORTED;
     char *ws = (char *)workspace;
@@ -639,10 +706,10 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
     if (p.score_mode == SA_SCORE_RAW_SUM) {
         if (dtype == SA_BF16)
             launch_raw<bf16_t>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
-                               cnt_out, block_scores_out, w, ws, stream);
+                               cnt_out, block_scores_out, w, ws, stream, K, lens_prev);
         else
             launch_raw<float>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
-                              cnt_out, block_scores_out, w, ws, stream);
+                              cnt_out, block_scores_out, w, ws, stream, K, lens_prev);
     } else {
 #define SA_SOFTMAX_CASE(GG)                                                                       \
     case GG:                                                                                      \

@@ -119,6 +119,71 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
                          out_dtype, lse_out, s, workspace, (hipStream_t)stream);
 }
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int decode_splits(int B, int Hkv, int32_t idx_cap, int32_t n_split) {
+    int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
+    return s < decode_min_split(idx_cap) ? decode_min_split(idx_cap) : s;
+}
+}  // namespace
+
+size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel, int64_t T_cap,
+                                              const sa_select_params *p, int32_t idx_cap,
+                                              int32_t n_split) {
+    if (!p || B <= 0 || Hq <= 0 || Hkv <= 0 || H_sel <= 0 || H_sel % Hkv || T_cap < 0 ||
+        idx_cap <= 0)
+        return 0;
+    const size_t sel = select_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
+    return align256(sel) + decode_workspace_bytes(B, Hq, decode_splits(B, Hkv, idx_cap, n_split));
+}
+
+int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const void *K, const void *V,
+                            void *Kc, int dtype, int B, int Hq, int Hkv, int d, int64_t T_cap,
+                            int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                            int32_t max_new_tokens, const sa_select_params *p, float scale,
+                            int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, void *O,
+                            int out_dtype, float *lse_out, int32_t n_split, void *workspace,
+                            size_t ws_bytes, void *stream) {
+    if (!Q || !sel || !K || !V || !Kc || !lens_prev || !lens_now || !idx_out || !cnt_out || !O)
+        return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || H_sel <= 0 ||
+        d <= 0 || T_cap <= 0 || nc_cap < 0 || idx_cap <= 0 || max_new_tokens < 0)
+        return SA_ERR_INVALID_ARG;
+    int st = check_params(p);
+    if (st) return st;
+    if (Hq % Hkv || H_sel % Hkv || !(scale == scale)) return SA_ERR_INVALID_ARG;
+    const int G = H_sel / Hkv;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
+    if (n_blocks(T_cap) > 32768 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
+    if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
+    if (T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (nc_cap < n_compressed(T_cap)) return SA_ERR_CAPACITY;
+    if (idx_cap < union_cap(p)) return SA_ERR_CAPACITY;
+    const size_t sel_bytes = align256(select_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total);
+    const int s = decode_splits(B, Hkv, idx_cap, n_split);
+    const size_t need = sel_bytes + decode_workspace_bytes(B, Hq, s);
+    if (!workspace || ws_bytes < need) return SA_ERR_WORKSPACE;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (p->score_mode == SA_SCORE_RAW_SUM) {
+        // the append rides in the scoring launch (the scorer forms new entries itself)
+        st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
+                           cnt_out, nullptr, workspace, hs, K, lens_prev);
+    } else {
+        // every entry enters the softmax denominators: append first
+        if (max_new_tokens > 0) {
+            st = launch_compress(K, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_prev, lens_now,
+                                 max_new_tokens / kCmpStride + 2, hs);
+            if (st) return st;
+        }
+        st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
+                           cnt_out, nullptr, workspace, hs);
+    }
+    if (st) return st;
+    return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, lens_now, idx_out, cnt_out, idx_cap,
+                         scale, O, out_dtype, lse_out, s, (char *)workspace + sel_bytes, hs);
+}
+
 int32_t sparse_attn_prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params *p) {
     if (!p || q_start < 0 || Tq <= 0) return 0;
     return prefill_tile_cap(q_start, Tq, *p);

@@ -15,7 +15,7 @@ import torch
 from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
                select_workspace_size, token_select, token_decode, token_select_workspace_size,
                token_decode_workspace_size, cobs_stats, cobs_select, cobs_select_workspace_size,
-               n_blocks,
+               n_blocks, decode_step, decode_step_workspace_size,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
 
@@ -65,10 +65,25 @@ class SparseDecoder:
                       want_lse=lse is not None, n_split=self.n_split, workspace=self.dec_ws)
 
     def step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0):
-        """One single-layer decode step: append, select, attend."""
+        """One single-layer decode step: append, select, attend (three calls)."""
         self.append(K, Kc, lens_prev, lens_now)
         self.select(sel, Kc, lens_now)
         return self.attend(Q, K, V, lens_now, scale=scale)
+
+    def fused_step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0, max_new_tokens=1):
+        """The same step through sparse_attn_decode_step (one call; in raw-sum
+        mode the append shares the scoring launch)."""
+        if getattr(self, "step_ws", None) is None:
+            p = make_params(self.top_k, self.n_init, self.n_local, self.score_mode)
+            need = decode_step_workspace_size(self.B, self.Hq, self.Hkv, self.H_sel, self.T_cap, p,
+                                              self.cap, self.n_split)
+            self.step_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
+        O, lse, _, _ = decode_step(Q, sel, K, V, Kc, lens_prev, lens_now, self.top_k, self.n_init,
+                                   self.n_local, self.score_mode, scale, max_new_tokens,
+                                   idx=self.idx, cnt=self.cnt, O=self.O, lse=self.lse,
+                                   want_lse=self.lse is not None, n_split=self.n_split,
+                                   workspace=self.step_ws)
+        return O, lse
 
     def capture(self, fn, warmup: int = 2):
         """Capture fn() (a sequence of the calls above on fixed buffers) into a

@@ -188,6 +188,38 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
                        void *O, int out_dtype, float *lse_out, int32_t n_split,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/* Workspace bytes needed by sparse_attn_decode_step (select and decode scratch). */
+size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel, int64_t T_cap,
+                                              const sa_select_params *p, int32_t idx_cap,
+                                              int32_t n_split);
+
+/*
+ * sparse_attn_decode_step - one whole decode step of the hot path in one call:
+ * sparse_attn_compress over [lens_prev, lens_now) (Eq. 2 append), then
+ * sparse_attn_select at L = lens_now (Eq. 1, Eq. 4 / Eq. 6), then
+ * sparse_attn_decode (Eq. 5); results identical to those three calls.
+ * In RAW_SUM mode the append runs inside the scoring launch: the scorer reads
+ * the entries that existed at lens_prev from Kc and forms any newer entry it
+ * needs from K with the same arithmetic, while extra workgroups of the same
+ * launch write the new entries to Kc. In SOFTMAX_SUM mode the new entries
+ * enter every head's softmax denominator, so the append runs first.
+ *
+ *   Q [B, Hq, d]; sel [B, H_sel, d]; K, V [B, Hkv, T_cap, d]; Kc [B, Hkv,
+ *   nc_cap, d] (updated in place); lens_prev, lens_now device int32 [B];
+ *   max_new_tokens host hint: an upper bound on lens_now - lens_prev (sizes
+ *   the separate append launch of SOFTMAX_SUM mode; 0 = no append);
+ *   idx_out / cnt_out as in sparse_attn_select; O / lse_out as in
+ *   sparse_attn_decode. Workspace: sparse_attn_decode_step_workspace_size.
+ * Errors: those of the three calls it stands for.
+ */
+int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const void *K, const void *V,
+                            void *Kc, int dtype, int B, int Hq, int Hkv, int d, int64_t T_cap,
+                            int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
+                            int32_t max_new_tokens, const sa_select_params *p, float scale,
+                            int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, void *O,
+                            int out_dtype, float *lse_out, int32_t n_split, void *workspace,
+                            size_t ws_bytes, void *stream);
+
 /* Columns needed per tile row of the prefill block sets: min(ceil(T/64),
  * 64 * top_k + n_init + n_local) for a context of T = q_start + Tq tokens. */
 int32_t sparse_attn_prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params *p);

@@ -1,0 +1,73 @@
+"""sparse_attn_decode_step (append + select + attend in one call) against the
+three separate calls it stands for: identical block sets, identical outputs,
+identical compressed keys afterwards. Covers the raw-sum path, where the
+append shares the scoring launch and the scorer forms new entries from the
+keys, with jumps that put new entries inside candidate blocks."""
+import pytest
+import torch
+
+import block_sparse_attention_12_amd as sa
+from parity import gpu_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+BITS = {"f32": torch.int32, "bf16": torch.int16}
+
+
+def rand(shape, dt, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * scale).to(TD[dt]).to(DEV)
+
+
+def lens_t(lens):
+    return torch.tensor(lens, dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,G", [("raw_sum", 1), ("raw_sum", 4), ("softmax_sum", 4)])
+@pytest.mark.parametrize("n_local", [2, 1, 0])
+def test_decode_step_equals_separate_calls(dt, mode, G, n_local):
+    B, Hq, Hkv, T = 3, 8, 2, 6000
+    K = rand((B, Hkv, T, 128), dt, 1)
+    V = rand((B, Hkv, T, 128), dt, 2)
+    nc_cap = sa.n_compressed(T)
+    # (lens_prev, lens_now) per step: single tokens across window / block edges,
+    # and jumps whose new entries land inside candidate blocks
+    steps = [([2000, 511, 64], [2001, 512, 65]), ([2001, 512, 65], [2016, 528, 96]),
+             ([2016, 528, 96], [2600, 1500, 97]), ([2600, 1500, 97], [6000, 1501, 700])]
+    Kc_a = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+    Kc_b = torch.zeros_like(Kc_a)
+    first = lens_t(steps[0][0])
+    sa.compress(K, Kc_a, lens_t([0] * B), first)
+    sa.compress(K, Kc_b, lens_t([0] * B), first)
+    k = 24
+    for i, (lp, ln) in enumerate(steps):
+        Q = rand((B, Hq, 128), dt, 10 + i, scale=128 ** -0.5)
+        sel = Q if G == 4 else rand((B, Hkv, 128), dt, 20 + i, scale=128 ** -0.5)
+        Lp, Ln = lens_t(lp), lens_t(ln)
+        mx = max(b - a for a, b in zip(lp, ln))
+        O1, lse1, idx1, cnt1 = sa.decode_step(Q, sel, K, V, Kc_a, Lp, Ln, k, 1, n_local, mode,
+                                              max_new_tokens=mx)
+        sa.compress(K, Kc_b, Lp, Ln, max_new_entries=mx // 16 + 2)
+        idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, 1, n_local, mode)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+        torch.cuda.synchronize()
+        assert gpu_rows(idx1, cnt1) == gpu_rows(idx2, cnt2), (i, mode)
+        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), (i, mode)
+        assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), (i, "compressed keys")
+
+
+def test_decode_step_validation_and_workspace():
+    p = sa.make_params(16, 1, 2, "raw_sum")
+    need = sa.decode_step_workspace_size(2, 8, 2, 2, 4096, p, 19, 4)
+    assert need >= sa.select_workspace_size(2, 2, 2, 4096, p) + sa.decode_workspace_size(2, 8, 2, 19, 4)
+    Q = torch.zeros((2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    K = torch.zeros((2, 2, 4096, 128), dtype=torch.bfloat16, device=DEV)
+    Kc = torch.zeros((2, 2, sa.n_compressed(4096), 128), dtype=torch.bfloat16, device=DEV)
+    L = lens_t([4096, 100])
+    with pytest.raises(sa.SparseAttnError):
+        sa.decode_step(Q, Q[:, :3].contiguous(), K, K, Kc, L, L, 16, 1, 2, "raw_sum")   # H_sel 3
+    with pytest.raises(sa.SparseAttnError):
+        sa.decode_step(Q, Q, K, K, Kc, L, L, 16, 1, 2, "raw_sum",
+                       workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
