@@ -20,16 +20,20 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_decode_workload(w, units=None, check_planted=True):
+def _run_decode_workload(w, units=None, check_planted=True, fused=False):
     inp = synth.make_decode_inputs(w, device=DEV)
     lens = inp["seq_lens"]
     dec = SparseDecoder(w.B, w.Hq, w.Hkv, w.T, w.top_k, w.n_init, w.n_local, w.selector,
                         w.score_mode)
     Kc = dec.new_kc(inp["K"].dtype)
-    dec.build(inp["K"], Kc, lens)
     sel = inp["F"] if w.selector == "forecast" else inp["Q"]
-    dec.select(sel, Kc, lens)
-    O, lse = dec.attend(inp["Q"], inp["K"], inp["V"], lens)
+    if fused:   # the benchmark's step: entries up to L - 1 exist, one call appends, selects, attends
+        dec.build(inp["K"], Kc, lens - 1)
+        O, lse = dec.fused_step(inp["Q"], sel, inp["K"], inp["V"], Kc, lens - 1, lens)
+    else:
+        dec.build(inp["K"], Kc, lens)
+        dec.select(sel, Kc, lens)
+        O, lse = dec.attend(inp["Q"], inp["K"], inp["V"], lens)
     torch.cuda.synchronize()
     rows = gpu_rows(dec.idx, dec.cnt)
     On, Ln = to_np(O), lse.cpu().numpy()
@@ -71,6 +75,17 @@ def test_decode_gqa_bf16_32k_full():
 
 def test_decode_forecast_bf16_128k_full():
     _run_decode_workload(synth.WORKLOADS["decode_forecast_bf16_128k"])
+
+
+def test_decode_forecast_bf16_128k_one_call_step_full():
+    """The benchmark's launch configuration: sparse_attn_decode_step (append
+    inside the scoring launch) on the full workload, every unit against the
+    oracle, compressed keys after the step bit-exact."""
+    _run_decode_workload(synth.WORKLOADS["decode_forecast_bf16_128k"], fused=True)
+
+
+def test_decode_gqa_bf16_32k_one_call_step_full():
+    _run_decode_workload(synth.WORKLOADS["decode_gqa_bf16_32k"], fused=True)
 
 
 def _run_crosslayer(w, units=None, T_cap=None):
