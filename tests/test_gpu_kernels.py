@@ -344,3 +344,40 @@ def test_stream_read_xor_matches_host(nbytes):
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     assert got == want
+
+
+@pytest.mark.parametrize("mode,G", [("softmax_sum", 4), ("raw_sum", 1)])
+def test_select_and_decode_at_the_largest_block_count(mode, G):
+    """2^21 tokens: 32768 blocks, the largest block count the selection takes
+    (1024 threads x 32 blocks per top-k workgroup), one (sequence, KV head)."""
+    dt = "bf16"
+    T = 64 * 32768
+    g = torch.Generator(device=DEV).manual_seed(31)
+    K = torch.randn((1, 1, T, 128), generator=g, device=DEV).to(torch.bfloat16)
+    V = torch.randn((1, 1, T, 128), generator=g, device=DEV).to(torch.bfloat16)
+    Q = (torch.randn((1, 4, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    sel = Q if G == 4 else (torch.randn((1, 1, 128), generator=g, device=DEV) * 128 ** -0.5).to(torch.bfloat16)
+    L = T - 37
+    Kc = torch.zeros((1, 1, oracle.n_compressed(T), 128), dtype=torch.bfloat16, device=DEV)
+    sa.compress(K, Kc, lens_t([0]), lens_t([L]))
+    k = 64
+    idx, cnt, bs = sa.select(sel, Kc, lens_t([L]), T, k, 1, 2, mode, block_scores=True)
+    O, lse = sa.decode(Q, K, V, lens_t([L]), idx, cnt, 1.0)
+    rows = gpu_rows(idx, cnt)
+    Kn = K[0, 0].float().cpu().numpy()
+    Kc_ref = oracle.compressed_keys(Kn, L, dt)
+    assert np.array_equal(Kc[0, 0, :Kc_ref.shape[0]].float().cpu().numpy(), Kc_ref)
+    p = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=mode)
+    ref, BS = oracle.select_blocks(to_np(sel)[0], Kc_ref, L, p, True)
+    nb = oracle.n_blocks(L)
+    ok, why = selection_ok(rows[(0, 0)], ref, BS, nb, k, 1, 2)
+    assert ok, (why, rows[(0, 0)][:10], ref[:10])
+    got_bs = bs[0, 0, :nb].cpu().numpy().astype(np.float64)
+    fin = np.isfinite(BS)
+    assert np.array_equal(np.isfinite(got_bs), fin)
+    scale = np.abs(BS[fin]).max()
+    assert np.allclose(got_bs[fin], BS[fin], rtol=2e-5, atol=2e-6 * scale)
+    o, l = oracle.sparse_attention(to_np(Q)[0], Kn, V[0, 0].float().cpu().numpy(),
+                                   block_tokens(rows[(0, 0)], L), 1.0)
+    assert_close(to_np(O)[0], o, dt, "O")
+    assert_close(lse.cpu().numpy()[0], l, dt, "LSE")
