@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             blk[j] = chunk0 + (int64_t)(i0 + j) * kCobsGroups + group;
-            load_raw(rS, row_offset(2 * blk[j], kRowBytes, lane_off), mu[j]);
-            if constexpr (ORDER == 2) load_raw(rS, row_offset(2 * blk[j] + 1, kRowBytes, lane_off), va[j]);
+            load_raw_nt(rS, row_offset(2 * blk[j], kRowBytes, lane_off), mu[j]);
+            if constexpr (ORDER == 2) load_raw_nt(rS, row_offset(2 * blk[j] + 1, kRowBytes, lane_off), va[j]);
         }
         float a[kBatch][G];
 #pragma unroll

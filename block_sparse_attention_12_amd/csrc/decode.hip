@@ -170,8 +170,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = blk < 0 ? 0xffffffffu : base + row_lane_off + i * (4 * kRowBytes);
-            load_raw(rK, off, r.k[i]);
-            load_raw(rV, off, r.v[i]);
+            load_raw_nt(rK, off, r.k[i]);
+            load_raw_nt(rV, off, r.v[i]);
         }
     };
     // token lists: ids of this lane's rows (entries 64*tile + row0 + 4i) of
@@ -191,8 +191,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         for (int i = 0; i < 4; ++i) {
             const int id = r.ids[i];
             const uint32_t off = (id >= 0 && id < L) ? (uint32_t)id * kRowBytes + lane_off : 0xffffffffu;
-            load_raw(rK, off, r.k[i]);
-            load_raw(rV, off, r.v[i]);
+            load_raw_nt(rK, off, r.k[i]);
+            load_raw_nt(rV, off, r.v[i]);
         }
         const int a = lane16 >> 2;                  // the logit this lane holds is row i = a
         r.tmy = a == 0 ? r.ids[0] : (a == 1 ? r.ids[1] : (a == 2 ? r.ids[2] : r.ids[3]));

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBmThreads) void block_lse_kernel(
         for (int it = 0; it < kBlock / 4; ++it) {
             const int64_t t = (int64_t)blk * kBlock + 4 * it + rg;      // this row group's token
             Raw8<T> k;
-            load_raw(rK, row_offset(t, kRowBytes, lane_off), k);
+            load_raw_nt(rK, row_offset(t, kRowBytes, lane_off), k);
             float s[kBmG];
 #pragma unroll
             for (int g = 0; g < kBmG; ++g) {

@@ -165,6 +165,21 @@ __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off,
     x.a = make_float4(__int_as_float(a.x), __int_as_float(a.y), __int_as_float(a.z), __int_as_float(a.w));
     x.b = make_float4(__int_as_float(b.x), __int_as_float(b.y), __int_as_float(b.z), __int_as_float(b.w));
 }
+// The same loads with the non-temporal (streaming) cache policy, for data a
+// launch reads exactly once (gathered K/V rows, index keys, block statistics):
+// it then does not displace cached data (measured: decode attention -4%,
+// token index-key scan -9% time).
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void load_raw_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<bf16_t> &x) {
+    const sa_v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT);
+    x.v = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+__device__ __forceinline__ void load_raw_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, Raw8<float> &x) {
+    const sa_v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT);
+    const sa_v4i b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16), 0, kCachePolicyNT);
+    x.a = make_float4(__int_as_float(a.x), __int_as_float(a.y), __int_as_float(a.z), __int_as_float(a.w));
+    x.b = make_float4(__int_as_float(b.x), __int_as_float(b.y), __int_as_float(b.z), __int_as_float(b.w));
+}
 // byte offset of a row, or an out-of-range offset (reads zeros) if it does not fit
 __device__ __forceinline__ uint32_t row_offset(int64_t row, uint32_t row_bytes, uint32_t lane_off) {
     const int64_t o = row * (int64_t)row_bytes + lane_off;

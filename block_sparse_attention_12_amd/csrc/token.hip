@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_score_kernel(
         Raw8<T> r[S::NR];
 #pragma unroll
         for (int q = 0; q < S::NR; ++q)
-            load_raw(rK, row_offset(base + (int64_t)q * S::NG, kRowBytes, lane_off), r[q]);
+            load_raw_nt(rK, row_offset(base + (int64_t)q * S::NG, kRowBytes, lane_off), r[q]);
         float v[S::NR];
 #pragma unroll
         for (int q = 0; q < S::NR; ++q) {
