@@ -34,6 +34,7 @@
 
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "topk_device.h"
 
 namespace sa {
 
@@ -110,13 +111,18 @@ struct BlockRegs {
 // prefetched three tiles ahead, together with the buffer that will use them,
 // so waiting for them never waits for K/V loads that are still needed in
 // flight.
-template <typename T, bool DIRECT, bool ROWS>
+// SG > 0: the workgroup first takes its own unit's top-k (topk_unit, with SG
+// selector heads per group, SSOFT for the softmax-sum form) from the scoring
+// kernels' output into LDS; every split of a unit computes the same set (the
+// redundant work replaces a separate top-k launch on the critical path) and
+// split 0 writes it out.
+template <typename T, bool DIRECT, bool ROWS, int SG = 0, bool SSOFT = false>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int idx_cap, float qscale, int n_split,
     float *__restrict__ part, void *__restrict__ O, int out_bf16,
-    float *__restrict__ lse) {
+    float *__restrict__ lse, FusedSelect fs) {
     constexpr int G = kDecG;
     __shared__ __align__(16) float s_p[4][64];
     __shared__ float s_m[4][G], s_l[4][G];
@@ -129,7 +135,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int lane16 = lane & 15, rgrp = lane >> 4;
     int64_t L = seq_lens[b];
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
-    int n = cnt[unit];
+    int n;
+    const int32_t *idx_row;
+    if constexpr (SG > 0) {
+        __shared__ int32_t s_list[kFusedMaxCap];
+        __shared__ int32_t s_cnt;
+        topk_unit<SG, SSOFT, kDecThreads, kFusedMaxBlocks / kDecThreads>(
+            unit, Hkv, T_cap, fs.nb_cap, seq_lens, fs.top_k, fs.n_init, fs.n_local, fs.logits,
+            fs.nc_pad, fs.stats, fs.n_chunks, fs.bscore, nullptr, s_list, idx_cap, &s_cnt,
+            fs.use_buckets);
+        __syncthreads();
+        if (split == 0) {
+            for (int i = tid; i < idx_cap; i += kDecThreads)
+                fs.idx_out[(int64_t)unit * idx_cap + i] = s_list[i];
+            if (tid == 0) fs.cnt_out[unit] = s_cnt;
+        }
+        n = s_cnt;
+        idx_row = s_list;
+    } else {
+        n = cnt[unit];
+        idx_row = idx + (int64_t)unit * idx_cap;
+    }
     n = n < 0 ? 0 : (n > idx_cap ? idx_cap : n);
     const int n_items = ROWS ? (n + 63) / 64 : n;      // blocks, or 64-entry tiles of tokens
     const int per = (n_items + n_split - 1) / n_split;
@@ -149,7 +175,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
-    const int32_t *irow = idx + (int64_t)unit * idx_cap + (ROWS ? 0 : e_lo);
+    const int32_t *irow = idx_row + (ROWS ? 0 : e_lo);
     const int my_row = 16 * wave + 4 * (lane16 >> 2) + rgrp;   // row of the logit this lane holds
     const int row0 = 16 * wave + rgrp;                          // first row this lane loads
     const uint32_t row_lane_off = row0 * kRowBytes + lane_off;
@@ -417,11 +443,11 @@ static void launch_decode_t(const void *Q, const void *K, const void *V, int B, 
     if (n_split == 1) {
         hipLaunchKernelGGL((decode_kernel<T, true, ROWS>), grid, dim3(kDecThreads), 0, stream,
                            (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens, idx,
-                           cnt, idx_cap, qscale, 1, (float *)nullptr, O, out_bf16, lse);
+                           cnt, idx_cap, qscale, 1, (float *)nullptr, O, out_bf16, lse, FusedSelect{});
     } else {
         hipLaunchKernelGGL((decode_kernel<T, false, ROWS>), grid, dim3(kDecThreads), 0, stream,
                            (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens, idx,
-                           cnt, idx_cap, qscale, n_split, (float *)ws, O, out_bf16, lse);
+                           cnt, idx_cap, qscale, n_split, (float *)ws, O, out_bf16, lse, FusedSelect{});
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(B * Hkv)), dim3(kDecThreads), 0, stream,
                            (const float *)ws, n_split, Hq, Hkv, O, out_bf16, lse);
     }
@@ -452,6 +478,54 @@ int launch_decode_rows(const void *Q, const void *K, const void *V, int dtype, i
     else
         launch_decode_t<float, true>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
                                      scale, O, out_bf16, lse_out, n_split, workspace, stream);
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+template <typename T, int SG, bool SSOFT>
+static void launch_decode_select_t(const void *Q, const void *K, const void *V, int B, int Hq,
+                                   int Hkv, int64_t T_cap, const int32_t *seq_lens,
+                                   int32_t idx_cap, float scale, void *O, int out_bf16, float *lse,
+                                   int32_t n_split, void *ws, const FusedSelect &fs,
+                                   hipStream_t stream) {
+    const dim3 grid((unsigned)n_split, (unsigned)(B * Hkv));
+    const float qscale = scale * kLog2e;
+    if (n_split == 1) {
+        hipLaunchKernelGGL((decode_kernel<T, true, false, SG, SSOFT>), grid, dim3(kDecThreads), 0,
+                           stream, (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens,
+                           (const int32_t *)nullptr, (const int32_t *)nullptr, idx_cap, qscale, 1,
+                           (float *)nullptr, O, out_bf16, lse, fs);
+    } else {
+        hipLaunchKernelGGL((decode_kernel<T, false, false, SG, SSOFT>), grid, dim3(kDecThreads), 0,
+                           stream, (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens,
+                           (const int32_t *)nullptr, (const int32_t *)nullptr, idx_cap, qscale,
+                           n_split, (float *)ws, O, out_bf16, lse, fs);
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(B * Hkv)), dim3(kDecThreads), 0, stream,
+                           (const float *)ws, n_split, Hq, Hkv, O, out_bf16, lse);
+    }
+}
+
+int launch_decode_select(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                         int Hkv, int64_t T_cap, const int32_t *seq_lens, int32_t idx_cap,
+                         float scale, void *O, int out_dtype, float *lse_out, int32_t n_split,
+                         void *workspace, const FusedSelect &fs, int G, bool softmax,
+                         hipStream_t stream) {
+    const int out_bf16 = out_dtype == SA_BF16 ? 1 : 0;
+#define SA_DS(TT, SGV, SM)                                                                        \
+    launch_decode_select_t<TT, SGV, SM>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx_cap, scale, O,  \
+                                        out_bf16, lse_out, n_split, workspace, fs, stream)
+#define SA_DS_T(TT)                                                                               \
+    if (!softmax) SA_DS(TT, 1, false);                                                            \
+    else if (G == 1) SA_DS(TT, 1, true);                                                          \
+    else if (G == 2) SA_DS(TT, 2, true);                                                          \
+    else if (G == 4) SA_DS(TT, 4, true);                                                          \
+    else return SA_ERR_UNSUPPORTED;
+    if (dtype == SA_BF16) {
+        SA_DS_T(bf16_t)
+    } else {
+        SA_DS_T(float)
+    }
+#undef SA_DS_T
+#undef SA_DS
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

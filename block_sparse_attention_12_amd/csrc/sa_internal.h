@@ -27,13 +27,41 @@ int launch_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int64_t 
                     int64_t nc_cap, const int32_t *lens_prev, const int32_t *lens_now,
                     int32_t max_new_entries, hipStream_t stream);
 
+// What a decode kernel needs to take the top-k of its own (sequence, KV head)
+// from the scoring kernels' output (raw-sum block scores, or softmax-mode
+// entry logits and chunk statistics), and where to write the block sets.
+struct FusedSelect {
+    int64_t nb_cap;
+    int top_k, n_init, n_local;
+    const float *bscore;               // raw-sum mode
+    const float *logits;               // softmax mode
+    int64_t nc_pad;
+    const float2 *stats;
+    int n_chunks;
+    int32_t *idx_out, *cnt_out;
+    int use_buckets;
+};
+
 // With K and lens_prev (raw-sum mode only), the compressed entries completed
 // between lens_prev and seq_lens are written by the scoring launch itself.
+// With fs, only the scoring kernel(s) run and fs describes their output (the
+// top-k is left to the caller's next launch).
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
                   int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
                   float *block_scores_out, void *workspace, hipStream_t stream,
-                  const void *K = nullptr, const int32_t *lens_prev = nullptr);
+                  const void *K = nullptr, const int32_t *lens_prev = nullptr,
+                  FusedSelect *fs = nullptr);
+// Decode attention whose workgroups first take their unit's top-k themselves
+// (fs from launch_select): needs ceil(T_cap / 64) <= 2048, idx_cap <= 1024 and,
+// for the softmax-sum form, G <= 4.
+constexpr int64_t kFusedMaxBlocks = 2048;
+constexpr int kFusedMaxCap = 1024;
+int launch_decode_select(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
+                         int Hkv, int64_t T_cap, const int32_t *seq_lens, int32_t idx_cap,
+                         float scale, void *O, int out_dtype, float *lse_out, int32_t n_split,
+                         void *workspace, const FusedSelect &fs, int G, bool softmax,
+                         hipStream_t stream);
 
 void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
                      const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,

@@ -165,10 +165,18 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
     const size_t need = sel_bytes + decode_workspace_bytes(B, Hq, s);
     if (!workspace || ws_bytes < need) return SA_ERR_WORKSPACE;
     const hipStream_t hs = (hipStream_t)stream;
+    // up to 2048 blocks, each decode workgroup takes its unit's top-k itself
+    // from the block scores (no separate top-k launch between scoring and
+    // attention); not for 8 selector heads a group, whose softmax top-k would
+    // take the attention kernel past 256 VGPRs
+    FusedSelect fs{};
+    const bool fused = n_blocks(T_cap) <= kFusedMaxBlocks && idx_cap <= kFusedMaxCap &&
+                       (p->score_mode == SA_SCORE_RAW_SUM || G <= 4);
+    FusedSelect *fsp = fused ? &fs : nullptr;
     if (p->score_mode == SA_SCORE_RAW_SUM) {
         // the append rides in the scoring launch (the scorer forms new entries itself)
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
-                           cnt_out, nullptr, workspace, hs, K, lens_prev);
+                           cnt_out, nullptr, workspace, hs, K, lens_prev, fsp);
     } else {
         // every entry enters the softmax denominators: append first
         if (max_new_tokens > 0) {
@@ -177,9 +185,13 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
             if (st) return st;
         }
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
-                           cnt_out, nullptr, workspace, hs);
+                           cnt_out, nullptr, workspace, hs, nullptr, nullptr, fsp);
     }
     if (st) return st;
+    if (fused)
+        return launch_decode_select(Q, K, V, dtype, B, Hq, Hkv, T_cap, lens_now, idx_cap, scale, O,
+                                    out_dtype, lse_out, s, (char *)workspace + sel_bytes, fs, G,
+                                    p->score_mode != SA_SCORE_RAW_SUM, hs);
     return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, lens_now, idx_out, cnt_out, idx_cap,
                          scale, O, out_dtype, lse_out, s, (char *)workspace + sel_bytes, hs);
 }

@@ -1,0 +1,324 @@
+// Block top-k and union (Eq. 1 of the SparDA summary page, "Theoretical
+// Foundation"; ties to the lower block index) for one (sequence, KV head) by
+// one workgroup: from precomputed block scores (raw-sum mode) or from the
+// entry logits and per-chunk softmax statistics (softmax-sum mode, Eq. 6
+// form). Shared by the selection kernels and the decode kernel that selects
+// its own blocks.
+#pragma once
+
+#include <float.h>
+#include <math.h>
+
+#include "sa_device.h"
+
+namespace sa {
+
+constexpr int kSoftmaxChunk = 512;                  // entries per scoring workgroup (softmax mode)
+constexpr int kBoundaryCap = 512;                   // boundary-bucket candidates ranked in LDS
+constexpr int kBucketMinUnits = 1024;               // top-k grids this large take the bucket path
+
+// Top-k + union of one (sequence, KV head) by one workgroup of NT threads:
+// writes the ascending union (-1 padded to idx_cap) to row (global or LDS)
+// and its count to *cnt_slot. Used by topk_kernel and by the decode kernel
+// that selects its own unit's blocks.
+//
+// Thread t owns PER consecutive blocks [t*PER, t*PER + PER): their 32-bit
+// orderable keys stay in registers for the whole kernel, so the bucket (and,
+// when needed, radix) passes are register compares plus LDS histogram atomics,
+// and the ascending compaction is one workgroup prefix scan.
+template <int G, bool SOFTMAX, int NT, int PER>
+__device__ __forceinline__ void topk_unit(
+    int unit, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens,
+    int top_k, int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
+    const float2 *__restrict__ stats, int n_chunks, const float *__restrict__ bscore_in,
+    float *__restrict__ bscore_out, int32_t *row, int idx_cap, int32_t *cnt_slot,
+    int use_buckets) {
+    __shared__ uint32_t s_hist[256];
+    __shared__ float s_M[G], s_Zinv[G];
+    __shared__ float2 s_st[G * 64];
+    constexpr int kSelWords = NT * PER / 32;        // one bit per block this workgroup covers
+    __shared__ int s_wave[NT / 64];
+    __shared__ uint32_t s_digit, s_above, s_nbnd;
+    __shared__ float s_lo[NT / 64], s_hi[NT / 64];
+    __shared__ uint32_t s_sel[kSelWords];
+    __shared__ uint32_t s_bkey[kBoundaryCap];
+    __shared__ int s_bblk[kBoundaryCap];
+    const int b = unit / Hkv;
+    const int tid = threadIdx.x;
+    const int64_t L = clamp_len(seq_lens[b], T_cap);
+    const int64_t nc = n_compressed(L);
+    const int nb = (int)n_blocks(L);
+    const int init_hi = n_init < nb ? n_init : nb;
+    const int local_lo = nb - n_local > 0 ? nb - n_local : 0;
+    const int cand_lo = init_hi;
+    const int cand_hi = local_lo > cand_lo ? local_lo : cand_lo;
+    const int n_cand = cand_hi - cand_lo;
+    const int blk0 = tid * PER;                     // first block of this thread
+
+    float score[PER];
+    if constexpr (SOFTMAX) {
+        // per-head softmax max / denominator from the chunk partials (<= 64 chunks)
+        const int used = (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk);
+        if (used <= 64) {
+            for (int i = tid; i < G * used; i += NT)
+                s_st[i] = stats[((int64_t)unit * G + i / used) * n_chunks + i % used];
+            __syncthreads();
+        }
+        if (tid < G) {
+            float M = -INFINITY, Z = 0.f;
+            const float2 *st = stats + ((int64_t)unit * G + tid) * n_chunks;
+            for (int c = 0; c < used; ++c) {
+                const float2 v = used <= 64 ? s_st[tid * used + c] : st[c];   // > 64: long contexts
+                merge_ms(M, Z, v.x, v.y);
+            }
+            s_M[tid] = M;
+            s_Zinv[tid] = Z > 0.f ? 1.f / Z : 0.f;
+        }
+        __syncthreads();
+        // entries 4*blk0 .. 4*blk0 + 4*PER - 1, eight blocks (32 entries) at a time
+#pragma unroll
+        for (int sub = 0; sub < PER; sub += 8) {
+            float S[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) S[k] = 0.f;
+            const int64_t j0 = 4 * (int64_t)(blk0 + sub);
+#pragma unroll
+            for (int g0 = 0; g0 < G; g0 += (G >= 8 ? 2 : (G < 4 ? G : 4))) {
+                constexpr int GC = G >= 8 ? 2 : (G < 4 ? G : 4);   // heads per load group
+                float4 lg[GC][8];
+#pragma unroll
+                for (int gg = 0; gg < GC; ++gg)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        lg[gg][q] = (j0 + 4 * q < nc)
+                                        ? *reinterpret_cast<const float4 *>(
+                                              logits + ((int64_t)unit * G + g0 + gg) * nc_pad + j0 + 4 * q)
+                                        : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+                for (int gg = 0; gg < GC; ++gg) {
+                    const float Mg = s_M[g0 + gg], Zi = s_Zinv[g0 + gg];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        S[4 * q + 0] += expf(lg[gg][q].x - Mg) * Zi;
+                        S[4 * q + 1] += expf(lg[gg][q].y - Mg) * Zi;
+                        S[4 * q + 2] += expf(lg[gg][q].z - Mg) * Zi;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                float best = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                    if (j0 + 4 * q + e < nc) best = fmaxf(best, S[4 * q + e]);
+                score[sub + q] = (blk0 + sub + q < nb) ? best : -INFINITY;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < PER; q += 4) {
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (blk0 + q + 3 < nb_cap)
+                v = *reinterpret_cast<const float4 *>(bscore_in + (int64_t)unit * nb_cap + blk0 + q);
+            else {
+                float t[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    t[e] = (blk0 + q + e < nb_cap) ? bscore_in[(int64_t)unit * nb_cap + blk0 + q + e] : -INFINITY;
+                v = make_float4(t[0], t[1], t[2], t[3]);
+            }
+            score[q] = v.x; score[q + 1] = v.y; score[q + 2] = v.z; score[q + 3] = v.w;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (blk0 + q >= nb) score[q] = -INFINITY;
+    }
+    uint32_t key[PER];
+    bool cand[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int blk = blk0 + q;
+        if (bscore_out && blk < nb_cap) bscore_out[(int64_t)unit * nb_cap + blk] = score[q];
+        key[q] = orderable(score[q]);
+        cand[q] = blk >= cand_lo && blk < cand_hi;
+    }
+
+    const bool take_all = top_k >= n_cand;
+    const bool take_none = top_k <= 0;
+    const bool choose = !take_all && !take_none;
+
+    // Bin of the histogram that holds the `remaining`-th largest counted key
+    // (bins scanned from the top), and the count of keys in the bins above it.
+    auto boundary_bin = [&](int remaining) {
+        if (tid < 64) {
+            // lane l owns bins 4l .. 4l+3; counts above each bin, from the top
+            const uint32_t hb[4] = {s_hist[4 * tid], s_hist[4 * tid + 1], s_hist[4 * tid + 2],
+                                    s_hist[4 * tid + 3]};
+            const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
+            uint32_t incl = c;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t t = __shfl_down(incl, off, 64);
+                if (tid + off < 64) incl += t;
+            }
+            uint32_t above = incl - c;                   // keys in bins owned by higher lanes
+#pragma unroll
+            for (int k = 3; k >= 0; --k) {
+                if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
+                    s_digit = 4 * tid + k;
+                    s_above = above;
+                }
+                above += hb[k];
+            }
+        }
+        __syncthreads();
+    };
+
+    // Fast path (grids of many units, where the kernel is throughput bound;
+    // with few units its longer chain of dependent steps costs more than the
+    // radix passes it saves): 256 equal-width value buckets over the
+    // candidates' [min, max].
+    // A bucket index is a monotone function of the score (fp32 subtraction of
+    // a constant and multiplication by a positive constant are monotone under
+    // rounding), so every candidate in a bucket above the one holding the k-th
+    // largest score is taken, and only that boundary bucket's candidates are
+    // ranked exactly (score, then lower block id) in LDS. Degenerate ranges
+    // (all scores equal, non-finite) and boundary buckets above kBoundaryCap
+    // fall back to the radix select of the exact k-th key below.
+    int bin[PER];
+    bool fast = false;
+    int bstar = 0;
+    if (choose && use_buckets) {
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (cand[q]) {
+                lo = fminf(lo, score[q]);
+                hi = fmaxf(hi, score[q]);
+            }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            lo = fminf(lo, shfl_xor(lo, off));
+            hi = fmaxf(hi, shfl_xor(hi, off));
+        }
+        if ((tid & 63) == 0) {
+            s_lo[tid >> 6] = lo;
+            s_hi[tid >> 6] = hi;
+        }
+        for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+        for (int i = tid; i < kSelWords; i += NT) s_sel[i] = 0;
+        if (tid == 0) s_nbnd = 0;
+        __syncthreads();
+        lo = s_lo[0];
+        hi = s_hi[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) {
+            lo = fminf(lo, s_lo[w]);
+            hi = fmaxf(hi, s_hi[w]);
+        }
+        const float range = hi - lo;
+        const float inv = 256.f / range;
+        fast = range > 0.f && range <= FLT_MAX && inv <= FLT_MAX;   // same on every thread
+        if (fast) {
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                int bq = -1;
+                if (cand[q]) {
+                    bq = (int)((score[q] - lo) * inv);
+                    bq = bq < 0 ? 0 : (bq > 255 ? 255 : bq);
+                    atomicAdd(&s_hist[bq], 1u);
+                }
+                bin[q] = bq;
+            }
+            __syncthreads();
+            boundary_bin(top_k);
+            bstar = (int)s_digit;
+            const int c = (int)s_hist[bstar];
+            const int r = top_k - (int)s_above;             // taken from the boundary bucket, >= 1
+            if (c <= kBoundaryCap) {
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if (bin[q] == bstar) {
+                        const uint32_t slot = atomicAdd(&s_nbnd, 1u);
+                        s_bkey[slot] = key[q];
+                        s_bblk[slot] = blk0 + q;
+                    }
+                __syncthreads();
+                for (int i = tid; i < c; i += NT) {
+                    const uint32_t ki = s_bkey[i];
+                    const int bi = s_bblk[i];
+                    int rank = 0;
+                    for (int j = 0; j < c; ++j) {
+                        const uint32_t kj = s_bkey[j];
+                        rank += (kj > ki || (kj == ki && s_bblk[j] < bi)) ? 1 : 0;
+                    }
+                    if (rank < r) atomicOr(&s_sel[bi >> 5], 1u << (bi & 31));
+                }
+                __syncthreads();
+            } else {
+                fast = false;
+            }
+        }
+    }
+
+    // Fallback: radix select of the top_k-th largest key among the candidates
+    // (four 8-bit digits of the orderable key, most significant first).
+    uint32_t prefix = 0, mask = 0;
+    int remaining = top_k;
+    if (choose && !fast) {
+#pragma unroll 1
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < PER; ++q)
+                if (cand[q] && (key[q] & mask) == prefix) atomicAdd(&s_hist[(key[q] >> shift) & 255u], 1u);
+            __syncthreads();
+            boundary_bin(remaining);
+            prefix |= s_digit << shift;
+            mask |= 255u << shift;
+            remaining -= (int)s_above;
+        }
+    }
+    const uint32_t thr = prefix;        // exact key of the k-th largest candidate
+    const int take_eq = remaining;      // keys equal to thr that are taken, lowest ids first
+    int rank = 0;
+    if (choose && !fast) {
+        int n_eq = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) n_eq += (cand[q] && key[q] == thr) ? 1 : 0;
+        int unused;
+        rank = wg_exclusive_scan<NT>(n_eq, s_wave, unused);
+    }
+
+    // ascending compaction over this thread's consecutive blocks
+    bool in[PER];
+    int n_in = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int blk = blk0 + q;
+        bool x;
+        if (blk >= nb) x = false;
+        else if (blk < init_hi || blk >= local_lo) x = true;
+        else if (take_none) x = false;
+        else if (take_all) x = true;
+        else if (fast) x = bin[q] > bstar || (bin[q] == bstar && ((s_sel[blk >> 5] >> (blk & 31)) & 1u));
+        else if (key[q] > thr) x = true;
+        else if (key[q] == thr) x = rank++ < take_eq;
+        else x = false;
+        in[q] = x;
+        n_in += x ? 1 : 0;
+    }
+    int total;
+    int pos = wg_exclusive_scan<NT>(n_in, s_wave, total);
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+        if (in[q]) {
+            if (pos < idx_cap) row[pos] = blk0 + q;
+            ++pos;
+        }
+    for (int i = total + tid; i < idx_cap; i += NT) row[i] = -1;
+    if (tid == 0) *cnt_slot = total < idx_cap ? total : idx_cap;
+}
+
+}  // namespace sa

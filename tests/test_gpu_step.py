@@ -71,3 +71,45 @@ def test_decode_step_validation_and_workspace():
     with pytest.raises(sa.SparseAttnError):
         sa.decode_step(Q, Q, K, K, Kc, L, L, 16, 1, 2, "raw_sum",
                        workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+
+
+# Up to 2048 blocks and 1024 list entries, the attention workgroups take their
+# unit's top-k themselves from the block scores; past either limit, and for 8
+# selector heads a group in the softmax-sum form, a separate top-k launch does.
+# Both sides must give the separate calls' sets and outputs bit for bit.
+@pytest.mark.parametrize("case", [
+    dict(mode="raw_sum", G=1, B=1, Hkv=2, T=64 * 2048, lens=[64 * 2048], k=1000, n_split=0),
+    dict(mode="softmax_sum", G=4, B=2, Hkv=2, T=64 * 2048, lens=[64 * 2048 - 5, 3000], k=1021,
+         n_split=7),
+    dict(mode="raw_sum", G=1, B=1, Hkv=2, T=64 * 2048 + 1, lens=[64 * 2048 + 1], k=100, n_split=0),
+    dict(mode="softmax_sum", G=4, B=1, Hkv=2, T=70000, lens=[70000], k=1022, n_split=3),
+    dict(mode="softmax_sum", G=8, B=2, Hkv=2, T=6000, lens=[6000, 777], k=40, n_split=0),
+    dict(mode="softmax_sum", G=2, B=2, Hkv=2, T=6000, lens=[6000, 0], k=40, n_split=1),
+    dict(mode="raw_sum", G=1, B=128, Hkv=8, T=2000, lens=None, k=12, n_split=0),
+    dict(mode="softmax_sum", G=4, B=128, Hkv=8, T=2000, lens=None, k=12, n_split=2),
+], ids=["raw-2048blk-k1000", "soft-2048blk-cap1024", "raw-2049blk", "soft-cap1025",
+        "soft-G8", "soft-G2-empty", "raw-1024units", "soft-1024units"])
+def test_decode_step_fused_and_separate_topk(case):
+    dt = "bf16"
+    B, Hkv, T, G, k = case["B"], case["Hkv"], case["T"], case["G"], case["k"]
+    Hq = 4 * Hkv
+    lens = case["lens"] or [T - 13 * b for b in range(B)]
+    K = rand((B, Hkv, T, 128), dt, 31)
+    V = rand((B, Hkv, T, 128), dt, 32)
+    Q = rand((B, Hq, 128), dt, 33, scale=128 ** -0.5)
+    sel = Q if G == 4 else rand((B, Hkv * G, 128), dt, 34, scale=128 ** -0.5)
+    nc_cap = sa.n_compressed(T)
+    lp = [max(0, L - 1) for L in lens]
+    Kc_a = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+    sa.compress(K, Kc_a, lens_t([0] * B), lens_t(lp))
+    Kc_b = Kc_a.clone()
+    Lp, Ln = lens_t(lp), lens_t(lens)
+    O1, lse1, idx1, cnt1 = sa.decode_step(Q, sel, K, V, Kc_a, Lp, Ln, k, 1, 2, case["mode"],
+                                          n_split=case["n_split"])
+    sa.compress(K, Kc_b, Lp, Ln)
+    idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, 1, 2, case["mode"])
+    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=case["n_split"])
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+    assert torch.equal(O1, O2) and torch.equal(lse1, lse2)
+    assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt]))
