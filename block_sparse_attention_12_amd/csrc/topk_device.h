@@ -38,7 +38,7 @@ __device__ __forceinline__ void topk_unit(
     __shared__ float2 s_st[G * 64];
     constexpr int kSelWords = NT * PER / 32;        // one bit per block this workgroup covers
     __shared__ int s_wave[NT / 64];
-    __shared__ uint32_t s_digit, s_above, s_nbnd;
+    __shared__ uint32_t s_digit, s_above, s_bcnt, s_nbnd;
     __shared__ float s_lo[NT / 64], s_hi[NT / 64];
     __shared__ uint32_t s_sel[kSelWords];
     __shared__ uint32_t s_bkey[kBoundaryCap];
@@ -148,7 +148,8 @@ __device__ __forceinline__ void topk_unit(
     const bool choose = !take_all && !take_none;
 
     // Bin of the histogram that holds the `remaining`-th largest counted key
-    // (bins scanned from the top), and the count of keys in the bins above it.
+    // (bins scanned from the top), the count of keys in the bins above it and
+    // the bin's own count.
     auto boundary_bin = [&](int remaining) {
         if (tid < 64) {
             // lane l owns bins 4l .. 4l+3; counts above each bin, from the top
@@ -167,6 +168,7 @@ __device__ __forceinline__ void topk_unit(
                 if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
                     s_digit = 4 * tid + k;
                     s_above = above;
+                    s_bcnt = hb[k];
                 }
                 above += hb[k];
             }
@@ -262,9 +264,13 @@ __device__ __forceinline__ void topk_unit(
     }
 
     // Fallback: radix select of the top_k-th largest key among the candidates
-    // (four 8-bit digits of the orderable key, most significant first).
+    // (four 8-bit digits of the orderable key, most significant first). The
+    // passes stop early once the boundary bin holds exactly the keys still to
+    // take: every key whose digits so far match (prefix under mask) is then
+    // taken, so the classes compared below are those of the masked key.
     uint32_t prefix = 0, mask = 0;
     int remaining = top_k;
+    bool whole_class = false;           // every key of the boundary class is taken
     if (choose && !fast) {
 #pragma unroll 1
         for (int shift = 24; shift >= 0; shift -= 8) {
@@ -278,12 +284,16 @@ __device__ __forceinline__ void topk_unit(
             prefix |= s_digit << shift;
             mask |= 255u << shift;
             remaining -= (int)s_above;
+            if ((int)s_bcnt == remaining) {
+                whole_class = true;
+                break;
+            }
         }
     }
-    const uint32_t thr = prefix;        // exact key of the k-th largest candidate
-    const int take_eq = remaining;      // keys equal to thr that are taken, lowest ids first
+    const uint32_t thr = prefix;        // masked key of the k-th largest candidate
+    const int take_eq = remaining;      // keys of thr's class taken, lowest ids first
     int rank = 0;
-    if (choose && !fast) {
+    if (choose && !fast && !whole_class) {
         int n_eq = 0;
 #pragma unroll
         for (int q = 0; q < PER; ++q) n_eq += (cand[q] && key[q] == thr) ? 1 : 0;
@@ -303,8 +313,8 @@ __device__ __forceinline__ void topk_unit(
         else if (take_none) x = false;
         else if (take_all) x = true;
         else if (fast) x = bin[q] > bstar || (bin[q] == bstar && ((s_sel[blk >> 5] >> (blk & 31)) & 1u));
-        else if (key[q] > thr) x = true;
-        else if (key[q] == thr) x = rank++ < take_eq;
+        else if ((key[q] & mask) > thr) x = true;
+        else if ((key[q] & mask) == thr) x = whole_class || rank++ < take_eq;
         else x = false;
         in[q] = x;
         n_in += x ? 1 : 0;
