@@ -10,8 +10,8 @@
 // One sequence, queries q_start .. q_start+Tq-1 (q_start a multiple of 64).
 // Tile t = queries q_start+64t .. +63, all inside block bt = q_start/64 + t.
 // A workgroup owns one (tile, KV head): 64 queries x 4 heads = 256 rows
-// (row = 4 * query + head). The scoring kernel gives each of 4 waves 64 rows;
-// the attention kernel gives each of 8 waves (two per SIMD) 32 rows.
+// (row = 4 * query + head). Both the scoring and the attention kernel give
+// each of 8 waves (two per SIMD) 32 rows.
 //
 // Both dense contractions use v_mfma_f32_16x16x32_bf16 in the transposed form
 // S^T = K Q^T (keys as M, rows as N), so each lane ends up with the scores of a
@@ -29,12 +29,12 @@
 // does not depend on the reference, only overflow does).
 //
 // Kernels:
-//   prefill_score_kernel  per (tile, KV head), two sweeps over the compressed
-//                         keys: per-row softmax max / sum over the entries the
-//                         row's query can see, then the group-summed
-//                         probabilities, max-reduced over each block's three
-//                         inside entries, written as one score per (query,
-//                         KV head, block).
+//   prefill_score_kernel  per (tile, KV head), two software-pipelined sweeps
+//                         over the compressed keys: per-row softmax sum over
+//                         the entries the row's query can see (lazy per-lane
+//                         references), then the group-summed probabilities,
+//                         max-reduced over each block's three inside entries,
+//                         written as one score per (query, KV head, block).
 //   topk (select.hip)     per (query, KV head): top-k among the blocks that
 //                         are neither initial nor in the local window, plus
 //                         init and local.
@@ -186,12 +186,26 @@ __device__ __forceinline__ void half_scores(f32x4_t (&s)[2][kAtRt], const bf16_t
 // ------------------------------------------------------------------ scoring
 
 // Visible compressed entries for a query at position p: n_c(p + 1). The
-// compressed keys go through a 2-stage LDS ring of 64-entry chunks (the next
-// chunk's loads held in registers during the current one). Chunks below what
-// the tile's first query sees need no visibility mask; the rest take it.
+// compressed keys go through a 2-stage LDS ring of 64-entry chunks, and each
+// sweep is software-pipelined: the matrix products of chunk c + 1 sit in the
+// same straight-line block as the vector work on chunk c's scores, so one
+// wave keeps its matrix and vector pipes busy together (chunk c + 2's loads
+// are in registers meanwhile). Chunks below what the tile's first query sees
+// need no visibility mask; the rest take it.
+//
+// Softmax denominators (sweep 1) use a lazy reference per lane: the max of the
+// lane's scores in chunk 0 (log2 units); every term is exp2(x - ref) with no
+// running max. The sum does not depend on the reference beyond rounding; only
+// overflow does, so a lane whose sum exceeds 2^64 (some later score above its
+// reference by more than 64) makes the workgroup rerun sweep 1 with a running
+// max. Sweep 2 takes each probability as exp2(x - (m + log2 z)) of the row's
+// merged (m, z).
+constexpr float kScoreSumLimit = 18446744073709551616.f;   // 2^64
+
+template <bool RAW>
 __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_score_kernel(
     const bf16_t *__restrict__ Q, const bf16_t *__restrict__ Kc, int Hq, int Hkv, int64_t q_start,
-    int64_t Tq, int64_t nc_cap, int raw_mode, float *__restrict__ bscore, int64_t nb_cap,
+    int64_t Tq, int64_t nc_cap, float *__restrict__ bscore, int64_t nb_cap,
     int32_t *__restrict__ qlens) {
     __shared__ __align__(16) bf16_t ring[2 * kPfTileElems];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
@@ -212,13 +226,22 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)kvh * nc_cap * kD,
                                                 (uint32_t)(nc_cap * kD * 2));
+    // block scores of this tile's queries for this KV head: query qloc at byte
+    // qloc * Hkv * nb_cap * 4 (the launcher checks the span fits 31 bits);
+    // queries past the chunk fall outside the resource and are not written
+    const int64_t nq = Tq - q_first < 64 ? Tq - q_first : 64;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(
+        bscore + (q_first * Hkv + kvh) * nb_cap, (uint32_t)(((nq - 1) * Hkv + 1) * nb_cap * 4));
+    uint32_t qoff[kAtRt];
+#pragma unroll
+    for (int rt = 0; rt < kAtRt; ++rt) qoff[rt] = (uint32_t)((int64_t)qloc[rt] * Hkv * nb_cap * 4);
     const int n_chunks = (int)(bt / 16) + 1;                     // every block <= bt is covered
     const int vis_min = (int)n_compressed(q_start + q_first + 1);
     const int n_full = vis_min / 64 < n_chunks ? vis_min / 64 : n_chunks;
+    const int nbc = (int)nb_cap;                                 // <= 32768 blocks
 
-    // scores of chunk c: s[mt][rt][i] for entry 64c + 16 mt + 4g + i; masked
-    // entries (past the row's visible count) are -inf
-    auto chunk_scores = [&](f32x4_t (&s)[4][kAtRt], const bf16_t *sK, int c, bool masked) {
+    // scores of a staged chunk: s[mt][rt][i] for entry 16 mt + 4g + i of it
+    auto chunk_scores = [&](f32x4_t (&s)[4][kAtRt], const bf16_t *sK) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             f32x4_t h[2][kAtRt];
@@ -228,70 +251,111 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
                 for (int rt = 0; rt < kAtRt; ++rt) s[2 * hh + j][rt] = h[j][rt];
         }
-        if (masked) {
+    };
+    // entries of chunk c past the row's visible count become -inf
+    auto mask = [&](f32x4_t (&s)[4][kAtRt], int c) {
 #pragma unroll
-            for (int rt = 0; rt < kAtRt; ++rt) {
-                const int lim = nvis[rt] - 64 * c - 4 * g;
+        for (int rt = 0; rt < kAtRt; ++rt) {
+            const int lim = nvis[rt] - 64 * c - 4 * g;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * mt + i >= lim) s[mt][rt][i] = -INFINITY;
-            }
+                for (int i = 0; i < 4; ++i)
+                    if (16 * mt + i >= lim) s[mt][rt][i] = -INFINITY;
         }
     };
-    // one sweep over the chunks: body(s, c) per chunk
-    auto sweep = [&](auto body) {
+    // one sweep: first(s) on chunk 0's scores, then body(s, c) for every chunk
+    auto sweep = [&](auto first, auto body) {
         TileRegs rk;
         load_tile_regs<false>(rk, rKc, 0, tid);
         store_tile_lds(ring, rk, tid);
+        load_tile_regs<false>(rk, rKc, 64, tid);                 // rows past the buffer read zeros
+        __syncthreads();
+        f32x4_t cur[4][kAtRt];
+        chunk_scores(cur, ring);
+        if (n_full == 0) mask(cur, 0);
+        first(cur);
+        store_tile_lds(ring + kPfTileElems, rk, tid);
+        // Loads, stores and products past the last chunk are not skipped (rows
+        // past the buffer read zeros; their slots and scores go unused), which
+        // keeps the products and the vector work in one branch-free block.
         for (int c = 0; c < n_chunks; ++c) {
-            __syncthreads();
-            const bf16_t *sK = ring + (c & 1) * kPfTileElems;
-            const bool more = c + 1 < n_chunks;
-            if (more) load_tile_regs<false>(rk, rKc, (int64_t)(c + 1) * 64, tid);
-            f32x4_t s[4][kAtRt];
-            if (c < n_full) {
-                chunk_scores(s, sK, c, false);
-                body(s, c);
-            } else {
-                chunk_scores(s, sK, c, true);
-                body(s, c);
-            }
-            if (more) store_tile_lds(ring + ((c + 1) & 1) * kPfTileElems, rk, tid);
+            __syncthreads();                       // chunk c + 1 staged; chunk c's slot is free
+            load_tile_regs<false>(rk, rKc, (int64_t)(c + 2) * 64, tid);
+            if (c >= n_full) mask(cur, c);
+            f32x4_t nxt[4][kAtRt];
+            chunk_scores(nxt, ring + ((c + 1) & 1) * kPfTileElems);
+            body(cur, c);
+            store_tile_lds(ring + (c & 1) * kPfTileElems, rk, tid);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int rt = 0; rt < kAtRt; ++rt) cur[mt][rt] = nxt[mt][rt];
         }
         __syncthreads();                           // ring free for the next sweep
     };
 
     // sweep 1 (softmax mode): per-row max and sum of exp over visible entries
-    // (base 2), online per lane, then merged over the 4 lanes sharing a row
+    // (base 2), per lane, then merged over the 4 lanes sharing a row
     float m[kAtRt], z[kAtRt];
 #pragma unroll
     for (int rt = 0; rt < kAtRt; ++rt) { m[rt] = -INFINITY; z[rt] = 0.f; }
-    if (!raw_mode) {
-        sweep([&](f32x4_t (&s)[4][kAtRt], int) {
+    if constexpr (!RAW) {
+        sweep([&](f32x4_t (&s)[4][kAtRt]) {
 #pragma unroll
             for (int rt = 0; rt < kAtRt; ++rt) {
-                float x[16];
-                float mx = m[rt];
+                float mx = -INFINITY;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        x[4 * mt + i] = s[mt][rt][i] * kLog2eF;
-                        mx = fmaxf(mx, x[4 * mt + i]);
-                    }
-                if (mx != -INFINITY) {
-                    float acc = z[rt] * __builtin_amdgcn_exp2f(m[rt] - mx);
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][rt][i]);
+                m[rt] = mx == -INFINITY ? 0.f : mx * kLog2eF;        // lane with nothing visible: z stays 0
+            }
+        }, [&](f32x4_t (&s)[4][kAtRt], int) {
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) acc += __builtin_amdgcn_exp2f(x[k] - mx);
-                    z[rt] = acc;
-                    m[rt] = mx;
-                }
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                float acc = z[rt];
+                const float nm = -m[rt];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc += __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][rt][i], kLog2eF, nm));
+                z[rt] = acc;
             }
         });
+        bool over = false;
+#pragma unroll
+        for (int rt = 0; rt < kAtRt; ++rt) over |= !(z[rt] <= kScoreSumLimit);
+        if (__syncthreads_or(over)) {
+            // rerun with a running max (scores spread far beyond the references)
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt) { m[rt] = -INFINITY; z[rt] = 0.f; }
+            sweep([&](f32x4_t (&)[4][kAtRt]) {}, [&](f32x4_t (&s)[4][kAtRt], int) {
+#pragma unroll
+                for (int rt = 0; rt < kAtRt; ++rt) {
+                    float x[16];
+                    float mx = m[rt];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            x[4 * mt + i] = s[mt][rt][i] * kLog2eF;
+                            mx = fmaxf(mx, x[4 * mt + i]);
+                        }
+                    if (mx != -INFINITY) {
+                        float acc = z[rt] * __builtin_amdgcn_exp2f(m[rt] - mx);
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) acc += __builtin_amdgcn_exp2f(x[k] - mx);
+                        z[rt] = acc;
+                        m[rt] = mx;
+                    }
+                }
+            });
+        }
 #pragma unroll
         for (int rt = 0; rt < kAtRt; ++rt) {
+            if (!(z[rt] > 0.f)) m[rt] = -INFINITY;                      // nothing visible in this lane
 #pragma unroll
             for (int sh = 16; sh <= 32; sh <<= 1) {
                 const float m2 = shfl_xor(m[rt], sh), z2 = shfl_xor(z[rt], sh);
@@ -303,35 +367,37 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
         }
     }
-    float zinv[kAtRt];
+    // probability of a score: exp2(x log2 e - bias), bias = m + log2 z (+inf
+    // for a row that sees nothing, so every probability is 0)
+    float nbias[kAtRt];
 #pragma unroll
-    for (int rt = 0; rt < kAtRt; ++rt) zinv[rt] = z[rt] > 0.f ? 1.f / z[rt] : 0.f;
+    for (int rt = 0; rt < kAtRt; ++rt) nbias[rt] = z[rt] > 0.f ? -(m[rt] + log2f(z[rt])) : -INFINITY;
 
     // sweep 2: probabilities (or raw scores) summed over the 4 heads of a query
     // (lanes 4k .. 4k+3 of a row group), max over each block's inside entries
     // 4b, 4b+1, 4b+2 (lane g holds block 16c + 4mt + g), one score per
-    // (query, KV head, block)
-    sweep([&](f32x4_t (&s)[4][kAtRt], int c) {
+    // (query, KV head, block). Masked entries give probability 0 (raw: -inf in
+    // every head's sum); a block whose first inside entry is masked is -inf.
+    sweep([&](f32x4_t (&)[4][kAtRt]) {}, [&](f32x4_t (&s)[4][kAtRt], int c) {
 #pragma unroll
         for (int rt = 0; rt < kAtRt; ++rt) {
-            const int64_t qi = q_first + qloc[rt];
-            const float nm = -m[rt];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 float v[3];
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
-                    const float x = s[mt][rt][i];
-                    float pv = raw_mode ? (x == -INFINITY ? 0.f : x)
-                                        : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2eF, nm)) * zinv[rt];
+                    float pv = RAW ? s[mt][rt][i]
+                                   : __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][rt][i], kLog2eF, nbias[rt]));
                     pv += dpp<kDppQuadXor1>(pv);
                     pv += dpp<kDppQuadXor2>(pv);
-                    v[i] = x == -INFINITY ? -INFINITY : pv;
+                    v[i] = pv;
                 }
-                const float bs = fmaxf(fmaxf(v[0], v[1]), v[2]);
-                const int64_t blk = (int64_t)c * 16 + 4 * mt + g;
-                if ((c16 & 3) == 0 && qi < Tq && blk < nb_cap)
-                    bscore[(qi * Hkv + kvh) * nb_cap + blk] = bs;
+                const int blk = 16 * c + 4 * mt + g;
+                float bs = fmaxf(fmaxf(v[0], v[1]), v[2]);
+                if (!RAW) bs = 4 * blk >= nvis[rt] ? -INFINITY : bs;
+                const uint32_t off = ((c16 & 3) == 0 && blk < nbc) ? qoff[rt] + 4u * (uint32_t)blk
+                                                                     : 0xffffffffu;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bs), rB, (int)off, 0, 0);
             }
         }
     });
@@ -653,9 +719,14 @@ int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, co
     int32_t *qcnt = (int32_t *)(ws + w.qcnt_off);
     const int n_tiles = (int)((Tq + 63) / 64);
     const dim3 grid((unsigned)(n_tiles * Hkv));
-    const int raw = p.score_mode == SA_SCORE_RAW_SUM ? 1 : 0;
-    hipLaunchKernelGGL(prefill_score_kernel, grid, dim3(kAtThreads), 0, stream, (const bf16_t *)Q,
-                       (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, raw, bscore, w.nb_cap, qlens);
+    // a tile's block scores are addressed by 32-bit offsets
+    if ((63 * (int64_t)Hkv + 1) * w.nb_cap * 4 > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (p.score_mode == SA_SCORE_RAW_SUM)
+        hipLaunchKernelGGL(prefill_score_kernel<true>, grid, dim3(kAtThreads), 0, stream, (const bf16_t *)Q,
+                           (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, bscore, w.nb_cap, qlens);
+    else
+        hipLaunchKernelGGL(prefill_score_kernel<false>, grid, dim3(kAtThreads), 0, stream, (const bf16_t *)Q,
+                           (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, bscore, w.nb_cap, qlens);
     launch_topk_raw((int)(Tq * Hkv), Hkv, q_start + Tq, w.nb_cap, qlens, p, bscore, qidx, w.qcap,
                     qcnt, stream);
     hipLaunchKernelGGL(prefill_union_kernel, grid, dim3(kPfThreads), 0, stream, (const int32_t *)qidx,

@@ -185,3 +185,40 @@ def test_prefill_attend_large_logit_jump_between_blocks():
             assert_close(On[i, 4 * h:4 * h + 4], o, "bf16", f"jump query {i} kvh {h}")
             assert_close(Ln[i, 4 * h:4 * h + 4], l, "bf16", f"jump lse {i} kvh {h}")
     assert jumped > 50, jumped                    # the case really exercises the raised references
+
+
+def test_prefill_select_scores_far_above_the_first_chunk():
+    """Compressed entries in a later 64-entry chunk whose scores exceed every
+    score of the first chunk by ~56 nats (~80 log2 units): the scoring kernel's
+    per-lane references (taken from the first chunk) are then too low for its
+    softmax sums, so the workgroup must rerun the denominator sweep with a
+    running max. Tile sets and attention must still match the oracle."""
+    T, q_start = 4096, 3584
+    Q, K, V, _ = _inputs(T=T, q_start=q_start, seed=11)
+    gen = torch.Generator().manual_seed(110)
+    u = torch.randn(128, generator=gen, dtype=torch.float64)
+    u = (u / u.norm()).to(DEV)
+    Q = (Q.double() + 2.0 * u).to(torch.bfloat16).contiguous()
+    K = K.clone()
+    jump = 30                                    # tokens 1920..1983: entries 120..122 (chunk 1)
+    K[:, 64 * jump:64 * jump + 64] = (28.0 * u + 0.05 * K[:, 64 * jump:64 * jump + 64].double()
+                                      ).to(torch.bfloat16)
+    Hkv = K.shape[0]
+    Kc = torch.zeros((1, Hkv, oracle.n_compressed(T), 128), dtype=torch.bfloat16, device=DEV)
+    lens = torch.tensor([T], dtype=torch.int32, device=DEV)
+    sa.compress(K[None].contiguous(), Kc, torch.zeros_like(lens), lens)
+    Kc = Kc[0].contiguous()
+    # the case is what it claims: per row, max over entries 120..122 minus the
+    # max over entries 0..63 exceeds 64 log2 units (and stays below fp32 range)
+    Qn, Kcn = to_np(Q), to_np(Kc)
+    for h in range(Hkv):
+        s = Qn[:, 4 * h:4 * h + 4].reshape(-1, 128).astype(np.float64) @ Kcn[h].astype(np.float64).T
+        gap = (s[:, 120:123].max(axis=1) - s[:, :64].max(axis=1)) / np.log(2)
+        assert gap.min() > 64 and gap.max() < 120, (gap.min(), gap.max())
+    kinds = _check(Q, K, V, Kc, q_start, 5, 4, "softmax_sum")
+    assert kinds.count("exact") >= len(kinds) - 1
+    _, _, tidx, tcnt = sa.prefill_chunk(Q, q_start, K, V, Kc, 5, 1, 4, "softmax_sum")
+    ti, tc = tidx.cpu().numpy(), tcnt.cpu().numpy()
+    for t in range(ti.shape[0]):
+        for h in range(Hkv):
+            assert jump in ti[t, h, :tc[t, h]].tolist()
