@@ -482,8 +482,8 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    // two stages, each the K tile then the V tile of one block
-    __shared__ __align__(16) bf16_t ring[2 * 2 * kPfTileElems];
+    // three stages, each the K tile then the V tile of one block
+    __shared__ __align__(16) bf16_t ring[3 * 2 * kPfTileElems];
     __shared__ int s_redo[kPfMaxPasses];
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -545,17 +545,17 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
     };
-    // One block: scores and probabilities of both halves, then the value
-    // product O^T += V^T P^T with each accumulator's two steps back to back.
-    auto block_compute = [&](const bf16_t *sK, const bf16_t *sV, bool diag) {
+    // Scores of both halves of a staged block: s[hh][j][rt].
+    auto block_scores = [&](f32x4_t (&s)[2][2][kAtRt], const bf16_t *sK) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) half_scores(s[hh], sK, qf, hh, g, c16);
+    };
+    // Probabilities of a block's scores, then the value product O^T += V^T P^T
+    // with each accumulator's two steps back to back.
+    auto block_values = [&](const f32x4_t (&s)[2][2][kAtRt], const bf16_t *sV) {
         bf16x8_t pb[2][kAtRt];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            f32x4_t s[2][kAtRt];
-            half_scores(s, sK, qf, hh, g, c16);
-            if (diag) mask_causal(s, hh);
-            half_probs(pb[hh], s);
-        }
+        for (int hh = 0; hh < 2; ++hh) half_probs(pb[hh], s[hh]);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
@@ -567,18 +567,21 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
         }
     };
+    auto stage = [&](int e) { return ring + (e % 3) * 2 * kPfTileElems; };
 
-    // Blocks go through a 2-stage LDS ring: block e sits in stage e % 2. Step e:
-    // barrier (block e staged by every wave; every wave done with block e-1),
-    // issue the loads of block e+1 into registers, compute block e, then store
-    // block e+1 into the other stage. The loop body has no branches: the
-    // reference of a row is the max of its first half block; a row whose running
-    // max later exceeds it by more than the slack (checked once per pass) gets
-    // the larger reference and the workgroup runs its blocks again (the pass's
-    // sums are void; accumulators are never rescaled). The tile's own block,
-    // last in the ascending set, takes the causal mask after the loop.
+    // Blocks go through a 3-stage LDS ring (block e in stage e % 3), and the
+    // loop is software-pipelined: step e computes block e + 1's scores (matrix
+    // products) in the same straight-line block as block e's probabilities
+    // (vector work) and value product, with block e + 2's loads in registers
+    // meanwhile; block e + 2 then goes into the stage block e - 1 used, and one
+    // barrier ends the step. Loads, products and stores past the last block
+    // are not skipped (they repeat the last block; their results go unused).
+    // The reference of a row is the max of its first half block; a row whose
+    // running max later exceeds it by more than the slack (checked once per
+    // pass) gets the larger reference and the workgroup runs its blocks again
+    // (the pass's sums are void; accumulators are never rescaled). The tile's
+    // own block, last in the ascending set, takes the causal mask.
     const bool last_diag = n > 0 && blk_at(n - 1) == bt;
-    const int n_main = last_diag ? n - 1 : n;
     for (int pass = 0; pass < kPfMaxPasses; ++pass) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
@@ -591,16 +594,20 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             load_tile_regs<false>(rk, rK, blk * kBlock, tid);
             load_tile_regs<true>(rv, rV, blk * kBlock, tid);
         };
-        auto store_block = [&](bf16_t *stage) {
-            store_tile_lds(stage, rk, tid);
-            store_tile_lds(stage + kPfTileElems, rv, tid);
+        auto store_block = [&](bf16_t *st) {
+            store_tile_lds(st, rk, tid);
+            store_tile_lds(st + kPfTileElems, rv, tid);
         };
         if (n > 0) {
             load_block(blk_at(0));
-            store_block(ring);
+            store_block(stage(0));
         }
+        if (n > 1) {
+            load_block(blk_at(1));
+            store_block(stage(1));
+        }
+        __syncthreads();
         if (pass == 0 && n > 0) {                  // references from the first half block
-            __syncthreads();
             f32x4_t s[2][kAtRt];
             half_scores(s, ring, qf, 0, g, c16);
             if (n == 1 && last_diag) mask_causal(s, 0);
@@ -613,19 +620,25 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 m[rt] = mx == -INFINITY ? 0.f : mx;
             }
         }
-        for (int e = 0; e < n_main; ++e) {
-            __syncthreads();
-            const bf16_t *sK = ring + (e & 1) * 2 * kPfTileElems;
-            const bf16_t *sV = sK + kPfTileElems;
-            const bool more = e + 1 < n;
-            if (more) load_block(blk_at(e + 1));
-            block_compute(sK, sV, false);
-            if (more) store_block(ring + ((e + 1) & 1) * 2 * kPfTileElems);
-        }
-        if (last_diag) {                           // block n-1, staged by the loop (or the prologue)
-            __syncthreads();
-            const bf16_t *sK = ring + (n_main & 1) * 2 * kPfTileElems;
-            block_compute(sK, sK + kPfTileElems, true);
+        f32x4_t sc[2][2][kAtRt];
+        block_scores(sc, stage(0));
+        for (int e = 0; e < n; ++e) {
+            if (e == n - 1 && last_diag) {
+                mask_causal(sc[0], 0);
+                mask_causal(sc[1], 1);
+            }
+            load_block(blk_at(e + 2 < n ? e + 2 : n - 1));
+            f32x4_t sn[2][2][kAtRt];
+            block_scores(sn, stage(e + 1));
+            block_values(sc, stage(e) + kPfTileElems);
+            store_block(stage(e + 2));
+            __syncthreads();                       // block e + 2 staged; stage e % 3 free
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int rt = 0; rt < kAtRt; ++rt) sc[hh][j][rt] = sn[hh][j][rt];
         }
         // end of pass: raise references a row outgrew; workgroup-wide redo
         bool redo = false;
