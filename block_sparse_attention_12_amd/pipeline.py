@@ -70,9 +70,11 @@ class SparseDecoder:
         self.select(sel, Kc, lens_now)
         return self.attend(Q, K, V, lens_now, scale=scale)
 
-    def fused_step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0, max_new_tokens=1):
+    def fused_step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0, max_new_tokens=1,
+                   O=None, lse=None):
         """The same step through sparse_attn_decode_step (one call; in raw-sum
-        mode the append shares the scoring launch)."""
+        mode the append shares the scoring launch). O / lse: output buffers
+        other than the decoder's own."""
         if getattr(self, "step_ws", None) is None:
             p = make_params(self.top_k, self.n_init, self.n_local, self.score_mode)
             need = decode_step_workspace_size(self.B, self.Hq, self.Hkv, self.H_sel, self.T_cap, p,
@@ -80,9 +82,10 @@ class SparseDecoder:
             self.step_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
         O, lse, _, _ = decode_step(Q, sel, K, V, Kc, lens_prev, lens_now, self.top_k, self.n_init,
                                    self.n_local, self.score_mode, scale, max_new_tokens,
-                                   idx=self.idx, cnt=self.cnt, O=self.O, lse=self.lse,
-                                   want_lse=self.lse is not None, n_split=self.n_split,
-                                   workspace=self.step_ws)
+                                   idx=self.idx, cnt=self.cnt, O=self.O if O is None else O,
+                                   lse=self.lse if lse is None else lse,
+                                   want_lse=self.lse is not None or lse is not None,
+                                   n_split=self.n_split, workspace=self.step_ws)
         return O, lse
 
     def capture(self, fn, warmup: int = 2):
@@ -192,6 +195,16 @@ class LookaheadDecoder:
             if l + 1 < n:
                 sel_done = next_done
         main.wait_stream(side)                     # join: the side stream is idle after the step
+        return outs
+
+    def step_one_call(self, layers: Sequence[dict], lens_prev, lens_now, outs, scale=1.0):
+        """The same step in order on the current stream with one
+        sparse_attn_decode_step call per layer (append, selection and attention
+        of a layer in one call, so no selection is left to overlap)."""
+        d = self.dec[0]
+        for l, lay in enumerate(layers):
+            d.fused_step(lay["Q"], lay["F"], lay["K"], lay["V"], lay["Kc"], lens_prev, lens_now,
+                         scale, O=outs[l][0], lse=outs[l][1])
         return outs
 
 

@@ -118,3 +118,34 @@ def test_lookahead_layers_match_oracle():
                                                  block_tokens(rows[(b, h)], L), 1.0)
                 assert_close(On[b, h * w.G:(h + 1) * w.G], o, "bf16", f"O layer {l} {(b, h)}")
                 assert_close(Ln[b, h * w.G:(h + 1) * w.G], lse, "bf16", f"LSE layer {l} {(b, h)}")
+
+
+def test_one_call_schedule_equals_in_order():
+    """One sparse_attn_decode_step call per layer gives every layer's output,
+    compressed keys and block set bit for bit as the three-call in-order step
+    (eagerly and replayed as a captured graph)."""
+    w, la, layers, inps, lens = _setup()
+    n = len(layers)
+    kc0 = [lay["Kc"].clone() for lay in layers]
+    ref = _snapshot(la, layers, lens, _outs(w, n), lookahead=False)
+    last = (la.dec[(n - 1) % 2].idx.clone(), la.dec[(n - 1) % 2].cnt.clone())
+    kc_after = [lay["Kc"].clone() for lay in layers]
+    outs = _outs(w, n)
+    g = la.dec[0].capture(lambda: la.step_one_call(layers, lens - 1, lens, outs))
+    for mode in ("eager", "graph", "graph"):
+        for lay, kc in zip(layers, kc0):
+            lay["Kc"].copy_(kc)
+        for o, s in outs:
+            o.fill_(float("nan"))
+            s.fill_(float("nan"))
+        torch.cuda.synchronize()
+        if mode == "eager":
+            la.step_one_call(layers, lens - 1, lens, outs)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        for l in range(n):
+            assert torch.equal(outs[l][0], ref[l][0]), (mode, l)
+            assert torch.equal(outs[l][1], ref[l][1]), (mode, l)
+            assert torch.equal(layers[l]["Kc"], kc_after[l]), (mode, l)
+        assert torch.equal(la.dec[0].idx, last[0]) and torch.equal(la.dec[0].cnt, last[1]), mode
