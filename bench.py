@@ -771,7 +771,8 @@ def cpu_baseline_token(w, inp, lens, budget_s):
 
 def bench_crosslayer(args, w):
     """One decode step of the cross-layer workload: layer 0 appends its compressed
-    keys and selects; all layers attend over that selection. The 16 appended
+    keys, selects and attends in one sparse_attn_decode_step call; the other
+    layers attend over that selection. The 16 appended
     tokens' keys and values are in the cache from the start; a step advances
     the lengths by one, and the 16-step cycle repeats."""
     import torch
@@ -834,7 +835,8 @@ def bench_crosslayer(args, w):
         "data": "synthetic (seeded N(0,1))",
         "config": {"workload": w.name, "batch": w.B, "context": f"{w.T}..{w.T + w.steps}",
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "layers": w.layers,
-                   "top_k": w.top_k, "parallelism": "none (1 GPU)"},
+                   "top_k": w.top_k, "launch": "eager, one stream; anchor layer in one decode-step call",
+                   "parallelism": "none (1 GPU)"},
         "gpu_ms_per_step": round(gpu_ms, 5), "step_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
     }

@@ -106,21 +106,28 @@ class SparseDecoder:
         return g
 
     def crosslayer_step(self, layers: Sequence[dict], Kc, lens_prev, lens_now, outs=None,
-                        scale=1.0):
+                        scale=1.0, one_call: bool = True):
         """One decode step where layer 0 (the anchor) selects for every layer.
 
         layers: dicts with Q, K, V (K/V already hold the appended token).
-        outs: optional list of (O, lse) buffers per layer.
+        outs: optional list of (O, lse) buffers per layer. one_call: the anchor
+        layer's append, selection and attention through one
+        sparse_attn_decode_step call (its block set is left in self.idx /
+        self.cnt for the other layers), else three calls.
         """
-        a = layers[0]
-        self.append(a["K"], Kc, lens_prev, lens_now)
-        self.select(a["Q"], Kc, lens_now)
         res = []
         for i, lay in enumerate(layers):
             O, lse = (outs[i] if outs is not None else (None, None))
             if O is None:
                 O = torch.empty_like(self.O)
                 lse = torch.empty_like(self.lse) if self.lse is not None else None
+            if i == 0 and one_call:
+                res.append(self.fused_step(lay["Q"], lay["Q"], lay["K"], lay["V"], Kc, lens_prev,
+                                           lens_now, scale, O=O, lse=lse))
+                continue
+            if i == 0:
+                self.append(lay["K"], Kc, lens_prev, lens_now)
+                self.select(lay["Q"], Kc, lens_now)
             res.append(self.attend(lay["Q"], lay["K"], lay["V"], lens_now, O=O, lse=lse,
                                    scale=scale))
         return res
