@@ -135,6 +135,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int lane16 = lane & 15, rgrp = lane >> 4;
     int64_t L = seq_lens[b];
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
+    // the group's queries: loaded first, so the load overlaps the top-k below
+    QFrag<T> q;
+    load_q(Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + lane16 * kLaneElems, q);
     int n;
     const int32_t *idx_row;
     if constexpr (SG > 0) {
@@ -162,8 +165,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int e_lo = split * per < n_items ? split * per : n_items;
     const int nblk = (e_lo + per < n_items ? e_lo + per : n_items) - e_lo;
 
-    QFrag<T> q;
-    load_q(Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + lane16 * kLaneElems, q);
     float acc[G][8];
     float m_my = -INFINITY, l_lane = 0.f;     // this lane's head: running max, partial sum
 #pragma unroll
