@@ -21,7 +21,9 @@
 //                        16 keys), 8 channels per lane; the keys stay in
 //                        registers for both passes, partial sums meet in LDS
 //   cobs_score_kernel    one row group per block: the group's estimates for
-//                        every selector head (fp32), reduced over the 16 lanes.
+//                        every selector head (fp32; bf16 mean terms by dot2
+//                        products), reduced over the 16 lanes; exponentials on
+//                        the hardware exp2.
 //                        Raw-sum mode writes the sum over heads as the block
 //                        score; softmax mode writes per-head logits and each
 //                        chunk's (max, sum exp) per head
@@ -152,6 +154,11 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
+// e^x of a non-positive argument as 2^(x log2 e) on the hardware exp2
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
+}
+
 template <typename T, int G, bool SOFTMAX, int ORDER>
 __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
     const T *__restrict__ sel, int H_sel, const T *__restrict__ stats, int64_t stats_nb,
@@ -166,11 +173,20 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
     const int64_t nbc = L / kBlock;                         // blocks with statistics
     const int64_t chunk0 = (int64_t)blockIdx.x * kCobsChunk;
 
-    // selector slices: q_h and 1/2 q_h^2 for this lane's 8 channels
+    // selector slices: q_h and 1/2 q_h^2 for this lane's 8 channels (bf16:
+    // q_h also as packed pairs for the mean term's dot2 products, which are
+    // exact in fp32 and leave the mean row unconverted)
+    constexpr bool kBf16 = sizeof(T) == 2;
     float qv[G][8], q2[G][8];
+    uint32_t qp[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        load8(sel + ((int64_t)b * H_sel + (int64_t)kvh * G + h) * kD + lane16 * kLaneElems, qv[h]);
+        const T *qs = sel + ((int64_t)b * H_sel + (int64_t)kvh * G + h) * kD + lane16 * kLaneElems;
+        load8(qs, qv[h]);
+        if constexpr (kBf16) {
+            const uint4 r = *reinterpret_cast<const uint4 *>(qs);
+            qp[h][0] = r.x; qp[h][1] = r.y; qp[h][2] = r.z; qp[h][3] = r.w;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) q2[h][e] = 0.5f * (qv[h][e] * qv[h][e]);
     }
@@ -201,13 +217,21 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
             float m8[8], v8[8];
-            unpack(mu[j], m8);
+            if constexpr (!kBf16) unpack(mu[j], m8);
             if constexpr (ORDER == 2) unpack(va[j], v8);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float acc = 0.f;
+                if constexpr (kBf16) {
+                    const uint4 &r = reinterpret_cast<const uint4 &>(mu[j]);
+                    acc = dot2_bf16(qp[h][0], r.x, acc);
+                    acc = dot2_bf16(qp[h][1], r.y, acc);
+                    acc = dot2_bf16(qp[h][2], r.z, acc);
+                    acc = dot2_bf16(qp[h][3], r.w, acc);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(qv[h][e], m8[e], acc);
+                    for (int e = 0; e < 8; ++e) acc = fmaf(qv[h][e], m8[e], acc);
+                }
                 if constexpr (ORDER == 2) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc = fmaf(q2[h][e], v8[e], acc);
@@ -241,10 +265,10 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
                     if (blk[j] < nbc) bm = fmaxf(bm, a[j][h]);
                 if (bm == -INFINITY) continue;
                 const float mn = fmaxf(run_m[h], bm);
-                float ssum = run_m[h] == -INFINITY ? 0.f : run_s[h] * expf(run_m[h] - mn);
+                float ssum = run_m[h] == -INFINITY ? 0.f : run_s[h] * fast_exp(run_m[h] - mn);
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j)
-                    if (blk[j] < nbc) ssum += expf(a[j][h] - mn);
+                    if (blk[j] < nbc) ssum += fast_exp(a[j][h] - mn);
                 run_m[h] = mn;
                 run_s[h] = ssum;
             }
@@ -288,7 +312,7 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_softmax_kernel(
     for (int h = 0; h < G; ++h) {
         const float x = logits[((int64_t)unit * G + h) * nb_pad + k];
         if (x != -INFINITY) {
-            S += expf(x - s_M[h]) * s_Zi[h];
+            S += fast_exp(x - s_M[h]) * s_Zi[h];
             any = true;
         }
     }
