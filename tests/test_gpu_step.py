@@ -85,12 +85,14 @@ def test_decode_step_validation_and_workspace():
     dict(mode="softmax_sum", G=4, B=1, Hkv=2, T=70000, lens=[70000], k=1022, n_split=3),
     dict(mode="softmax_sum", G=8, B=2, Hkv=2, T=6000, lens=[6000, 777], k=40, n_split=0),
     dict(mode="softmax_sum", G=2, B=2, Hkv=2, T=6000, lens=[6000, 0], k=40, n_split=1),
+    dict(mode="softmax_sum", G=1, B=3, Hkv=2, T=9000, lens=[9000, 4100, 70], k=30, n_split=0),
+    dict(mode="raw_sum", G=4, B=2, Hkv=2, T=9000, lens=[8999, 64], k=30, n_split=5, dt="f32"),
     dict(mode="raw_sum", G=1, B=128, Hkv=8, T=2000, lens=None, k=12, n_split=0),
     dict(mode="softmax_sum", G=4, B=128, Hkv=8, T=2000, lens=None, k=12, n_split=2),
 ], ids=["raw-2048blk-k1000", "soft-2048blk-cap1024", "raw-2049blk", "soft-cap1025",
-        "soft-G8", "soft-G2-empty", "raw-1024units", "soft-1024units"])
+        "soft-G8", "soft-G2-empty", "soft-G1", "raw-G4-f32", "raw-1024units", "soft-1024units"])
 def test_decode_step_fused_and_separate_topk(case):
-    dt = "bf16"
+    dt = case.get("dt", "bf16")
     B, Hkv, T, G, k = case["B"], case["Hkv"], case["T"], case["G"], case["k"]
     Hq = 4 * Hkv
     lens = case["lens"] or [T - 13 * b for b in range(B)]
