@@ -732,8 +732,6 @@ int launch_prefill(const void *Q, int64_t q_start, int64_t Tq, const void *K, co
     int32_t *qcnt = (int32_t *)(ws + w.qcnt_off);
     const int n_tiles = (int)((Tq + 63) / 64);
     const dim3 grid((unsigned)(n_tiles * Hkv));
-    // a tile's block scores are addressed by 32-bit offsets
-    if ((63 * (int64_t)Hkv + 1) * w.nb_cap * 4 > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     if (p.score_mode == SA_SCORE_RAW_SUM)
         hipLaunchKernelGGL(prefill_score_kernel<true>, grid, dim3(kAtThreads), 0, stream, (const bf16_t *)Q,
                            (const bf16_t *)Kc, Hq, Hkv, q_start, Tq, nc_cap, bscore, w.nb_cap, qlens);

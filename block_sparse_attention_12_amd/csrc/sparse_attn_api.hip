@@ -225,6 +225,8 @@ int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const 
     if (d != kD || Hq / Hkv != 4 || dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
     if (n_blocks(q_start + Tq) > 32768) return SA_ERR_UNSUPPORTED;
     if (T_cap * d * 2 > 0x7fffffffLL || nc_cap * d * 2 > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    // a tile's per-query block scores (64 queries x Hkv x blocks, fp32) take 32-bit offsets
+    if ((63 * (int64_t)Hkv + 1) * n_blocks(q_start + Tq) * 4 > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     if (T_cap < q_start + Tq) return SA_ERR_CAPACITY;
     if (nc_cap < n_compressed(q_start + Tq)) return SA_ERR_CAPACITY;
     if (tile_idx_cap < prefill_tile_cap(q_start, Tq, *p)) return SA_ERR_CAPACITY;

@@ -251,8 +251,10 @@ size_t sparse_attn_prefill_workspace_size(int Hq, int Hkv, int64_t q_start, int6
  *              -1 padded); tile_cnt_out [n_tiles, Hkv] device int32, written;
  *              tile_idx_cap >= sparse_attn_prefill_tile_cap(...)
  * Errors: SA_ERR_INVALID_ARG (incl. q_start % 64 != 0), SA_ERR_UNSUPPORTED
- *         (d != 128, G != 4, dtype != SA_BF16, parameters other than 64/32/16),
- *         SA_ERR_CAPACITY, SA_ERR_WORKSPACE.
+ *         (d != 128, G != 4, dtype != SA_BF16, parameters other than 64/32/16,
+ *         more than 32768 blocks, or (63 Hkv + 1) * nb * 4 bytes of one tile's
+ *         per-query block scores beyond 2^31 - 1), SA_ERR_CAPACITY,
+ *         SA_ERR_WORKSPACE.
  */
 int sparse_attn_prefill_chunk(const void *Q, int64_t q_start, int64_t Tq, const void *K,
                               const void *V, const void *Kc, int dtype, int Hq, int Hkv, int d,

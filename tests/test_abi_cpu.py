@@ -148,6 +148,9 @@ def test_prefill_validation():
     assert _prefill(tidx=None) == sa.SA_ERR_INVALID_ARG
     assert _prefill(dtype=sa.SA_F32) == sa.SA_ERR_UNSUPPORTED
     assert _prefill(Hq=16) == sa.SA_ERR_UNSUPPORTED
+    # a tile's block scores (64 queries x Hkv x blocks, fp32) must fit 31-bit offsets
+    assert _prefill(Hq=2048, Hkv=512, q_start=64 * 32767, Tq=64, T_cap=64 * 32768,
+                    nc_cap=4 * 32768) == sa.SA_ERR_UNSUPPORTED
     assert _prefill(T_cap=1279) == sa.SA_ERR_CAPACITY
     assert _prefill(nc_cap=78) == sa.SA_ERR_CAPACITY                             # n_c(1280) = 79
     assert _prefill(tcap=19) == sa.SA_ERR_CAPACITY
