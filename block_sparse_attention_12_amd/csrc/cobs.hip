@@ -154,11 +154,6 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-// e^x of a non-positive argument as 2^(x log2 e) on the hardware exp2
-__device__ __forceinline__ float fast_exp(float x) {
-    return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
-}
-
 template <typename T, int G, bool SOFTMAX, int ORDER>
 __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
     const T *__restrict__ sel, int H_sel, const T *__restrict__ stats, int64_t stats_nb,
@@ -265,10 +260,10 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
                     if (blk[j] < nbc) bm = fmaxf(bm, a[j][h]);
                 if (bm == -INFINITY) continue;
                 const float mn = fmaxf(run_m[h], bm);
-                float ssum = run_m[h] == -INFINITY ? 0.f : run_s[h] * fast_exp(run_m[h] - mn);
+                float ssum = run_m[h] == -INFINITY ? 0.f : run_s[h] * hw_exp(run_m[h] - mn);
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j)
-                    if (blk[j] < nbc) ssum += fast_exp(a[j][h] - mn);
+                    if (blk[j] < nbc) ssum += hw_exp(a[j][h] - mn);
                 run_m[h] = mn;
                 run_s[h] = ssum;
             }
@@ -312,7 +307,7 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_softmax_kernel(
     for (int h = 0; h < G; ++h) {
         const float x = logits[((int64_t)unit * G + h) * nb_pad + k];
         if (x != -INFINITY) {
-            S += fast_exp(x - s_M[h]) * s_Zi[h];
+            S += hw_exp(x - s_M[h]) * s_Zi[h];
             any = true;
         }
     }

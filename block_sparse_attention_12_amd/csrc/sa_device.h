@@ -202,6 +202,13 @@ __device__ __forceinline__ int64_t clamp_len(int64_t L, int64_t T_cap) {
     return L < 0 ? 0 : (L > T_cap ? T_cap : L);
 }
 
+// e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32): a few ulp of
+// relative error for the arguments here (x <= 0, softmax terms), against a
+// longer libm-style sequence for expf.
+__device__ __forceinline__ float hw_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896340736f);
+}
+
 // Merges a (max, sum of exp(x - max)) pair into another.
 __device__ __forceinline__ void merge_ms(float &m, float &s, float m2, float s2) {
     const float M = fmaxf(m, m2);

@@ -299,10 +299,10 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
             const float x = v[0];
             lrow[j] = x;
             if (x > m) {
-                ssum = ssum * expf(m - x) + 1.f;
+                ssum = ssum * hw_exp(m - x) + 1.f;
                 m = x;
             } else {
-                ssum += expf(x - m);
+                ssum += hw_exp(x - m);
             }
         }
     }

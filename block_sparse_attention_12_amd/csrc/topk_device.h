@@ -99,9 +99,9 @@ __device__ __forceinline__ void topk_unit(
                     const float Mg = s_M[g0 + gg], Zi = s_Zinv[g0 + gg];
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
-                        S[4 * q + 0] += expf(lg[gg][q].x - Mg) * Zi;
-                        S[4 * q + 1] += expf(lg[gg][q].y - Mg) * Zi;
-                        S[4 * q + 2] += expf(lg[gg][q].z - Mg) * Zi;
+                        S[4 * q + 0] += hw_exp(lg[gg][q].x - Mg) * Zi;
+                        S[4 * q + 1] += hw_exp(lg[gg][q].y - Mg) * Zi;
+                        S[4 * q + 2] += hw_exp(lg[gg][q].z - Mg) * Zi;
                     }
                 }
             }
