@@ -203,6 +203,12 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  * needs from K with the same arithmetic, while extra workgroups of the same
  * launch write the new entries to Kc. In SOFTMAX_SUM mode the new entries
  * enter every head's softmax denominator, so the append runs first.
+ * With at most 2048 blocks (T_cap <= 131072), idx_cap <= 1024 and, in
+ * SOFTMAX_SUM mode, at most 4 selector heads per KV head, there is no
+ * separate top-k launch: every attention workgroup of a (b, kvh) takes that
+ * unit's top-k and union from the block scores itself (the same device code
+ * as the top-k kernel, so the same sets), and the unit's first workgroup
+ * writes idx_out / cnt_out.
  *
  *   Q [B, Hq, d]; sel [B, H_sel, d]; K, V [B, Hkv, T_cap, d]; Kc [B, Hkv,
  *   nc_cap, d] (updated in place); lens_prev, lens_now device int32 [B];
