@@ -515,7 +515,14 @@ def bench_cobs(args, w):
             "attend": lambda: dec.attend(rep["Q"], rep["K"], rep["V"], lens_now),
         }
 
-    steps_fn = [lambda rep=rep: [f() for f in phases_of(rep).values()] for rep in reps]
+    def whole_step(rep):
+        if args.separate_calls:
+            for f in phases_of(rep).values():
+                f()
+        else:                                   # sparse_attn_cobs_decode_step: one call
+            dec.fused_step(rep["Q"], rep["Q"], rep["K"], rep["V"], rep["S"], lens_prev, lens_now)
+
+    steps_fn = [lambda rep=rep: whole_step(rep) for rep in reps]
     for i in range(args.warmup):
         steps_fn[i % len(reps)]()
     torch.cuda.synchronize()
@@ -605,7 +612,9 @@ def bench_cobs(args, w):
                    "kv_heads": w.Hkv, "head_dim": w.d, "top_k": w.top_k, "n_init": w.n_init,
                    "n_local": w.n_local, "selector": w.selector, "score_mode": w.score_mode,
                    "statistic": "block mean + per-channel variance (second order)",
-                   "replicas": args.replicas, "launch": "eager, one stream",
+                   "replicas": args.replicas,
+                   "launch": ("eager, one stream, three calls" if args.separate_calls else
+                              "eager, one stream, one sparse_attn_cobs_decode_step call"),
                    "parallelism": "none (1 GPU)"},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "phase_ms": {k: round(v, 5) for k, v in mean.items()},

@@ -48,6 +48,7 @@ EXPORTS = [
     "sparse_attn_token_decode_workspace_size", "sparse_attn_token_decode",
     "sparse_attn_cobs_stats", "sparse_attn_cobs_select_workspace_size", "sparse_attn_cobs_select",
     "sparse_attn_decode_step_workspace_size", "sparse_attn_decode_step",
+    "sparse_attn_cobs_decode_step_workspace_size", "sparse_attn_cobs_decode_step",
 ]
 
 
@@ -140,6 +141,13 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_cobs_select.restype = _int
     L.sparse_attn_cobs_select.argtypes = [_vp, _int, _vp, _int, _int, _int, _int, _i64, _i64, _vp,
                                           _PP, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
+    L.sparse_attn_cobs_decode_step_workspace_size.restype = _sz
+    L.sparse_attn_cobs_decode_step_workspace_size.argtypes = [_int, _int, _int, _int, _i64, _PP, _i32,
+                                                              _i32]
+    L.sparse_attn_cobs_decode_step.restype = _int
+    L.sparse_attn_cobs_decode_step.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _int, _int, _int, _int,
+                                               _int, _i64, _i64, _vp, _vp, _i32, _PP, _i32, _f32,
+                                               _vp, _i32, _vp, _vp, _int, _vp, _i32, _vp, _sz, _vp]
     L.sparse_attn_token_decode_workspace_size.restype = _sz
     L.sparse_attn_token_decode_workspace_size.argtypes = [_int, _int, _int, _i32, _i32]
     L.sparse_attn_token_decode.restype = _int
@@ -504,6 +512,52 @@ def cobs_select(sel: torch.Tensor, stats: torch.Tensor, seq_lens: torch.Tensor, 
                                        ws_bytes, _stream(sel, stream))
     _check("sparse_attn_cobs_select", st)
     return idx, cnt, bs
+
+
+def cobs_decode_step_workspace_size(B, Hq, Hkv, H_sel, T_cap, params: SelectParams, idx_cap,
+                                    n_split=0) -> int:
+    return lib().sparse_attn_cobs_decode_step_workspace_size(B, Hq, Hkv, H_sel, T_cap,
+                                                             ctypes.byref(params), idx_cap, n_split)
+
+
+def cobs_decode_step(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                     stats: torch.Tensor, lens_prev: torch.Tensor, lens_now: torch.Tensor,
+                     top_k: int, n_init: int = 1, n_local: int = 2, score_mode="softmax_sum",
+                     order: int = 2, scale: float = 1.0, max_new_blocks: int = 1, idx=None,
+                     cnt=None, O=None, lse=None, want_lse=True, out_dtype=torch.float32,
+                     n_split: int = 0, workspace=None, stream=None):
+    """Statistics append + selection by block statistics + decode attention in
+    one call. Returns (O, lse, idx, cnt)."""
+    B, Hq, d = Q.shape
+    _, H_sel, _ = sel.shape
+    _, Hkv, T_cap, _ = K.shape
+    nb_cap = stats.shape[2]
+    p = make_params(top_k, n_init, n_local, score_mode)
+    dev = Q.device
+    cap = top_k + n_init + n_local
+    if idx is None:
+        idx = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = cobs_decode_step_workspace_size(B, Hq, Hkv, H_sel, T_cap, p, idx.shape[-1], n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_cobs_decode_step(_dev(Q, "Q"), _dev(sel, "sel"), H_sel, _dev(K, "K"),
+                                            _dev(V, "V"), _dev(stats, "stats"), _dtype_code(K), B,
+                                            Hq, Hkv, d, T_cap, nb_cap, _dev(lens_prev, "lens_prev"),
+                                            _dev(lens_now, "lens_now"), int(max_new_blocks),
+                                            ctypes.byref(p), int(order), float(scale),
+                                            _dev(idx, "idx"), idx.shape[-1], _dev(cnt, "cnt"),
+                                            _dev(O, "O"), _dtype_code(O), _opt(lse, "lse"),
+                                            int(n_split), _dev(workspace, "workspace"), ws_bytes,
+                                            _stream(Q, stream))
+    _check("sparse_attn_cobs_decode_step", st)
+    return O, lse, idx, cnt
 
 
 # ------------------------------------------------------------------ whole decode step

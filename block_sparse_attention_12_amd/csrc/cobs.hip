@@ -27,20 +27,21 @@
 //                        Raw-sum mode writes the sum over heads as the block
 //                        score; softmax mode writes per-head logits and each
 //                        chunk's (max, sum exp) per head
-//   cobs_softmax_kernel  softmax mode: merges the chunk statistics and writes
-//                        block score = sum over heads of each head's softmax
-//                        over the blocks (Eq. 6 form)
-// The top-k and Eq. 1 union reuse the block path's top-k kernel.
+// The top-k and Eq. 1 union reuse the block path's top-k (in softmax mode it
+// merges the chunk statistics and forms block score = sum over heads of each
+// head's softmax over the blocks, the Eq. 6 form, from the logits), either as
+// its own launch or inside the decode step's attention workgroups.
 #include <math.h>
 
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "topk_device.h"
 
 namespace sa {
 
 constexpr int kCobsThreads = 256;
 constexpr int kCobsGroups = kCobsThreads / kRowLanes;       // 16 blocks in flight per workgroup
-constexpr int kCobsChunk = 256;                             // blocks per scoring workgroup
+constexpr int kCobsChunk = kStatChunk;                      // blocks per scoring workgroup
 
 CobsWorkspace cobs_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
     CobsWorkspace w{};
@@ -284,36 +285,6 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_score_kernel(
     }
 }
 
-// block score = sum over heads of exp(logit - M_h) / Z_h, from the chunk statistics
-template <int G>
-__global__ __launch_bounds__(kCobsThreads) void cobs_softmax_kernel(
-    const float *__restrict__ logits, int64_t nb_pad, const float2 *__restrict__ cstats,
-    int n_chunks, int64_t nb_cap, float *__restrict__ bscore) {
-    __shared__ float s_M[G], s_Zi[G];
-    const int unit = blockIdx.y;
-    if (threadIdx.x < G) {
-        float M = -INFINITY, Z = 0.f;
-        const float2 *st = cstats + ((int64_t)unit * G + threadIdx.x) * n_chunks;
-        for (int c = 0; c < n_chunks; ++c) merge_ms(M, Z, st[c].x, st[c].y);
-        s_M[threadIdx.x] = M;
-        s_Zi[threadIdx.x] = Z > 0.f ? 1.f / Z : 0.f;
-    }
-    __syncthreads();
-    const int64_t k = (int64_t)blockIdx.x * kCobsChunk + threadIdx.x;
-    if (k >= nb_cap) return;
-    float S = 0.f;
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float x = logits[((int64_t)unit * G + h) * nb_pad + k];
-        if (x != -INFINITY) {
-            S += hw_exp(x - s_M[h]) * s_Zi[h];
-            any = true;
-        }
-    }
-    bscore[(int64_t)unit * nb_cap + k] = any ? S : -INFINITY;
-}
-
 // ---------------------------------------------------------------- launchers
 
 int launch_cobs_stats(const void *K, void *stats, int dtype, int B, int Hkv, int64_t T_cap,
@@ -345,9 +316,6 @@ static void launch_cobs_g(const void *sel, int H_sel, const void *stats, int64_t
     if (p.score_mode == SA_SCORE_SOFTMAX_SUM) {
         if (order == 2) SA_COBS(true, 2);
         else SA_COBS(true, 1);
-        hipLaunchKernelGGL((cobs_softmax_kernel<G>), grid, dim3(kCobsThreads), 0, stream,
-                           (const float *)logits, w.nb_pad, (const float2 *)cst, w.n_chunks,
-                           w.nb_cap, bscore);
     } else {
         if (order == 2) SA_COBS(false, 2);
         else SA_COBS(false, 1);
@@ -359,10 +327,15 @@ int launch_cobs_select(const void *sel, int G, const void *stats, int64_t stats_
                        int B, int Hkv, int64_t T_cap, const int32_t *seq_lens,
                        const sa_select_params &p,
                        int order, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
-                       float *block_scores_out, void *workspace, hipStream_t stream) {
+                       float *block_scores_out, void *workspace, hipStream_t stream,
+                       FusedSelect *fs) {
     const CobsWorkspace w = cobs_workspace_layout(B, Hkv, G, T_cap, p.score_mode);
     char *ws = (char *)workspace;
-    float *bscore = block_scores_out ? block_scores_out : (float *)(ws + w.bscore_off);
+    const bool softmax = p.score_mode == SA_SCORE_SOFTMAX_SUM;
+    // raw sum: the scorer writes block scores (to the caller's buffer when one
+    // is given); softmax: the top-k forms them from the logits and writes them
+    // out when asked
+    float *bscore = (block_scores_out && !softmax) ? block_scores_out : (float *)(ws + w.bscore_off);
     const int H_sel = G * Hkv;
 #define SA_COBS_CASE(GG)                                                                          \
     case GG:                                                                                      \
@@ -381,8 +354,30 @@ int launch_cobs_select(const void *sel, int G, const void *stats, int64_t stats_
         default: return SA_ERR_UNSUPPORTED;
     }
 #undef SA_COBS_CASE
-    launch_topk_raw(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, bscore, idx_out, idx_cap, cnt_out,
-                    stream);
+    float *logits = (float *)(ws + w.logits_off);
+    const float2 *cst = (const float2 *)(ws + w.stats_off);
+    if (fs) {                                       // the decode workgroups take the top-k
+        fs->nb_cap = w.nb_cap;
+        fs->top_k = p.top_k;
+        fs->n_init = p.n_init;
+        fs->n_local = p.n_local;
+        fs->bscore = softmax ? nullptr : bscore;
+        fs->logits = softmax ? logits : nullptr;
+        fs->nc_pad = softmax ? w.nb_pad : 0;
+        fs->stats = softmax ? cst : nullptr;
+        fs->n_chunks = softmax ? w.n_chunks : 0;
+        fs->idx_out = idx_out;
+        fs->cnt_out = cnt_out;
+        fs->use_buckets = B * Hkv >= kBucketMinUnits ? 1 : 0;
+        fs->epb = 1;
+    } else if (softmax) {
+        launch_topk_block_softmax(B * Hkv, G, Hkv, T_cap, w.nb_cap, seq_lens, p, logits, w.nb_pad,
+                                  cst, w.n_chunks, block_scores_out, idx_out, idx_cap, cnt_out,
+                                  stream);
+    } else {
+        launch_topk_raw(B * Hkv, Hkv, T_cap, w.nb_cap, seq_lens, p, bscore, idx_out, idx_cap,
+                        cnt_out, stream);
+    }
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 

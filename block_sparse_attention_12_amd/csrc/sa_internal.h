@@ -29,17 +29,18 @@ int launch_compress(const void *K, void *Kc, int dtype, int B, int Hkv, int64_t 
 
 // What a decode kernel needs to take the top-k of its own (sequence, KV head)
 // from the scoring kernels' output (raw-sum block scores, or softmax-mode
-// entry logits and chunk statistics), and where to write the block sets.
+// logits and chunk statistics), and where to write the block sets.
 struct FusedSelect {
     int64_t nb_cap;
     int top_k, n_init, n_local;
     const float *bscore;               // raw-sum mode
     const float *logits;               // softmax mode
-    int64_t nc_pad;
+    int64_t nc_pad;                    // logits row stride
     const float2 *stats;
     int n_chunks;
     int32_t *idx_out, *cnt_out;
     int use_buckets;
+    int epb;                           // softmax logits per block: 4 (compressed entries) or 1
 };
 
 // With K and lens_prev (raw-sum mode only), the compressed entries completed
@@ -53,8 +54,8 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   const void *K = nullptr, const int32_t *lens_prev = nullptr,
                   FusedSelect *fs = nullptr);
 // Decode attention whose workgroups first take their unit's top-k themselves
-// (fs from launch_select): needs ceil(T_cap / 64) <= 2048, idx_cap <= 1024 and,
-// for the softmax-sum form, G <= 4.
+// (fs from launch_select or launch_cobs_select): needs ceil(T_cap / 64) <= 2048,
+// idx_cap <= 1024 and, for the softmax-sum form, G <= 4.
 constexpr int64_t kFusedMaxBlocks = 2048;
 constexpr int kFusedMaxCap = 1024;
 int launch_decode_select(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
@@ -63,6 +64,11 @@ int launch_decode_select(const void *Q, const void *K, const void *V, int dtype,
                          void *workspace, const FusedSelect &fs, int G, bool softmax,
                          hipStream_t stream);
 
+void launch_topk_block_softmax(int n_units, int G, int Hkv, int64_t T_cap, int64_t nb_cap,
+                               const int32_t *seq_lens, const sa_select_params &p,
+                               const float *logits, int64_t nb_pad, const float2 *stats,
+                               int n_chunks, float *bs_out, int32_t *idx_out, int idx_cap,
+                               int32_t *cnt_out, hipStream_t stream);
 void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
                      const sa_select_params &p, const float *bscore, int32_t *idx_out, int idx_cap,
                      int32_t *cnt_out, hipStream_t stream);
@@ -113,7 +119,8 @@ int launch_cobs_select(const void *sel, int G, const void *stats, int64_t stats_
                        int B, int Hkv, int64_t T_cap, const int32_t *seq_lens,
                        const sa_select_params &p,
                        int order, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
-                       float *block_scores_out, void *workspace, hipStream_t stream);
+                       float *block_scores_out, void *workspace, hipStream_t stream,
+                       FusedSelect *fs = nullptr);
 
 int32_t prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params &p);
 size_t prefill_workspace_bytes(int Hq, int Hkv, int64_t q_start, int64_t Tq,

@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
 
 // ---------------------------------------------------------------- top-k + union
 
-template <int G, bool SOFTMAX, int NT, int PER>
+template <int G, bool SOFTMAX, int NT, int PER, int EPB>
 __global__ __launch_bounds__(NT) void topk_kernel(
     int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens, int top_k,
     int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
@@ -332,21 +332,21 @@ __global__ __launch_bounds__(NT) void topk_kernel(
     float *__restrict__ bscore_out, int32_t *__restrict__ idx_out, int idx_cap,
     int32_t *__restrict__ cnt_out, int use_buckets) {
     const int unit = blockIdx.x;
-    topk_unit<G, SOFTMAX, NT, PER>(unit, Hkv, T_cap, nb_cap, seq_lens, top_k, n_init, n_local,
+    topk_unit<G, SOFTMAX, NT, PER, EPB>(unit, Hkv, T_cap, nb_cap, seq_lens, top_k, n_init, n_local,
                                    logits, nc_pad, stats, n_chunks, bscore_in, bscore_out,
                                    idx_out + (int64_t)unit * idx_cap, idx_cap, cnt_out + unit,
                                    use_buckets);
 }
 
 // Launch shape for the block count: keys of PER consecutive blocks per thread.
-template <int G, bool SOFTMAX>
+template <int G, bool SOFTMAX, int EPB = 4>
 static void launch_topk(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *seq_lens,
                         const sa_select_params &p, const float *logits, int64_t nc_pad,
                         const float2 *stats, int n_chunks, const float *bscore, float *bs_out,
                         int32_t *idx_out, int idx_cap, int32_t *cnt_out, hipStream_t stream) {
     const int use_buckets = n_units >= kBucketMinUnits ? 1 : 0;
 #define SA_TOPK(NT, PER)                                                                          \
-    hipLaunchKernelGGL((topk_kernel<G, SOFTMAX, NT, PER>), dim3((unsigned)n_units), dim3(NT), 0,   \
+    hipLaunchKernelGGL((topk_kernel<G, SOFTMAX, NT, PER, EPB>), dim3((unsigned)n_units), dim3(NT), 0, \
                        stream, Hkv, T_cap, nb_cap, seq_lens, p.top_k, p.n_init, p.n_local, logits, \
                        nc_pad, stats, n_chunks, bscore, bs_out, idx_out, idx_cap, cnt_out,          \
                        use_buckets)
@@ -364,6 +364,23 @@ void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const 
                      int32_t *cnt_out, hipStream_t stream) {
     launch_topk<1, false>(n_units, Hkv, T_cap, nb_cap, seq_lens, p, nullptr, 0, nullptr, 0, bscore,
                           nullptr, idx_out, idx_cap, cnt_out, stream);
+}
+
+// Top-k + union over per-head logits of whole blocks (one logit per block and
+// head, chunk partials of kStatChunk blocks): the second-order selection.
+void launch_topk_block_softmax(int n_units, int G, int Hkv, int64_t T_cap, int64_t nb_cap,
+                               const int32_t *seq_lens, const sa_select_params &p,
+                               const float *logits, int64_t nb_pad, const float2 *stats,
+                               int n_chunks, float *bs_out, int32_t *idx_out, int idx_cap,
+                               int32_t *cnt_out, hipStream_t stream) {
+#define SA_TBS(GG)                                                                                \
+    launch_topk<GG, true, 1>(n_units, Hkv, T_cap, nb_cap, seq_lens, p, logits, nb_pad, stats,     \
+                             n_chunks, nullptr, bs_out, idx_out, idx_cap, cnt_out, stream)
+    if (G == 1) SA_TBS(1);
+    else if (G == 2) SA_TBS(2);
+    else if (G == 4) SA_TBS(4);
+    else SA_TBS(8);
+#undef SA_TBS
 }
 
 template <typename T, int G>
@@ -439,6 +456,7 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
         fs->idx_out = idx_out;
         fs->cnt_out = cnt_out;
         fs->use_buckets = B * Hkv >= kBucketMinUnits ? 1 : 0;
+        fs->epb = 4;
     }
     if (p.score_mode == SA_SCORE_RAW_SUM) {
         if (dtype == SA_BF16)

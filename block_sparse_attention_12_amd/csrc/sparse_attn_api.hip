@@ -359,6 +359,71 @@ int sparse_attn_cobs_select(const void *sel, int H_sel, const void *stats, int d
                               idx_cap, cnt_out, block_scores_out, workspace, (hipStream_t)stream);
 }
 
+size_t sparse_attn_cobs_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
+                                                   int64_t T_cap, const sa_select_params *p,
+                                                   int32_t idx_cap, int32_t n_split) {
+    if (!p || B <= 0 || Hq <= 0 || Hkv <= 0 || H_sel <= 0 || H_sel % Hkv || T_cap < 0 ||
+        idx_cap <= 0)
+        return 0;
+    const size_t sel = cobs_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
+    return align256(sel) + decode_workspace_bytes(B, Hq, decode_splits(B, Hkv, idx_cap, n_split));
+}
+
+int sparse_attn_cobs_decode_step(const void *Q, const void *sel, int H_sel, const void *K,
+                                 const void *V, void *stats, int dtype, int B, int Hq, int Hkv,
+                                 int d, int64_t T_cap, int64_t nb_cap, const int32_t *lens_prev,
+                                 const int32_t *lens_now, int32_t max_new_blocks,
+                                 const sa_select_params *p, int32_t order, float scale,
+                                 int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, void *O,
+                                 int out_dtype, float *lse_out, int32_t n_split, void *workspace,
+                                 size_t ws_bytes, void *stream) {
+    if (!Q || !sel || !K || !V || !stats || !lens_prev || !lens_now || !idx_out || !cnt_out || !O)
+        return SA_ERR_INVALID_ARG;
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || H_sel <= 0 ||
+        d <= 0 || T_cap <= 0 || nb_cap < 0 || idx_cap <= 0 || max_new_blocks < 0)
+        return SA_ERR_INVALID_ARG;
+    int st = check_params(p);
+    if (st) return st;
+    if (Hq % Hkv || H_sel % Hkv || (order != 1 && order != 2) || !(scale == scale))
+        return SA_ERR_INVALID_ARG;
+    const int G = H_sel / Hkv;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
+    if (n_blocks(T_cap) > 32768 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
+    if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
+    if (T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
+    if (nb_cap < n_blocks(T_cap)) return SA_ERR_CAPACITY;
+    if (idx_cap < union_cap(p)) return SA_ERR_CAPACITY;
+    const size_t sel_bytes =
+        align256(cobs_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total);
+    const int s = decode_splits(B, Hkv, idx_cap, n_split);
+    if (!workspace || ws_bytes < sel_bytes + decode_workspace_bytes(B, Hq, s))
+        return SA_ERR_WORKSPACE;
+    const hipStream_t hs = (hipStream_t)stream;
+    if (max_new_blocks > 0 && T_cap >= kBlock) {     // statistics of newly completed blocks
+        st = launch_cobs_stats(K, stats, dtype, B, Hkv, T_cap, nb_cap, lens_prev, lens_now,
+                               max_new_blocks, hs);
+        if (st) return st;
+    }
+    // raw sum: the attention workgroups take the top-k from the block scores
+    // (as in sparse_attn_decode_step). Softmax sum: every workgroup would read
+    // all G heads' logits (G x 8 KB at 2048 blocks) and exponentiate them, which
+    // measured slower than the separate top-k launch (64 workgroups).
+    const bool softmax = p->score_mode != SA_SCORE_RAW_SUM;
+    FusedSelect fs{};
+    const bool fused = n_blocks(T_cap) <= kFusedMaxBlocks && idx_cap <= kFusedMaxCap && !softmax;
+    st = launch_cobs_select(sel, G, stats, nb_cap, dtype, B, Hkv, T_cap, lens_now, *p, order,
+                            idx_out, idx_cap, cnt_out, nullptr, workspace, hs,
+                            fused ? &fs : nullptr);
+    if (st) return st;
+    if (fused)
+        return launch_decode_select(Q, K, V, dtype, B, Hq, Hkv, T_cap, lens_now, idx_cap, scale, O,
+                                    out_dtype, lse_out, s, (char *)workspace + sel_bytes, fs, G,
+                                    softmax, hs);
+    return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, lens_now, idx_out, cnt_out, idx_cap,
+                         scale, O, out_dtype, lse_out, s, (char *)workspace + sel_bytes, hs);
+}
+
 size_t sparse_attn_block_mass_workspace_size(int B, int Hq, int64_t mass_cap) {
     if (B <= 0 || Hq <= 0 || mass_cap <= 0) return 0;
     return block_mass_workspace_bytes(B, Hq, mass_cap);

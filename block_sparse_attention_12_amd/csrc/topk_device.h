@@ -14,6 +14,7 @@
 namespace sa {
 
 constexpr int kSoftmaxChunk = 512;                  // entries per scoring workgroup (softmax mode)
+constexpr int kStatChunk = 256;                     // blocks per second-order scoring workgroup
 constexpr int kBoundaryCap = 512;                   // boundary-bucket candidates ranked in LDS
 constexpr int kBucketMinUnits = 1024;               // top-k grids this large take the bucket path
 
@@ -26,7 +27,14 @@ constexpr int kBucketMinUnits = 1024;               // top-k grids this large ta
 // orderable keys stay in registers for the whole kernel, so the bucket (and,
 // when needed, radix) passes are register compares plus LDS histogram atomics,
 // and the ascending compaction is one workgroup prefix scan.
-template <int G, bool SOFTMAX, int NT, int PER>
+//
+// SOFTMAX: scores are the Eq. 6 form, the sum over the group's heads of each
+// head's softmax, from per-head logits and per-chunk (max, sum exp) partials.
+// EPB = 4: logits of compressed entries (4 per block; a block's score is the
+// max over its 3 inside entries), chunks of kSoftmaxChunk entries. EPB = 1:
+// one logit per block (block statistics), chunks of kStatChunk blocks; a
+// block whose every head's logit is -inf has no score.
+template <int G, bool SOFTMAX, int NT, int PER, int EPB = 4>
 __device__ __forceinline__ void topk_unit(
     int unit, int Hkv, int64_t T_cap, int64_t nb_cap, const int32_t *__restrict__ seq_lens,
     int top_k, int n_init, int n_local, const float *__restrict__ logits, int64_t nc_pad,
@@ -55,10 +63,13 @@ __device__ __forceinline__ void topk_unit(
     const int n_cand = cand_hi - cand_lo;
     const int blk0 = tid * PER;                     // first block of this thread
 
+    static_assert(EPB == 4 || EPB == 1, "entries per block");
     float score[PER];
     if constexpr (SOFTMAX) {
-        // per-head softmax max / denominator from the chunk partials (<= 64 chunks)
-        const int used = (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk);
+        // per-head softmax max / denominator from the chunk partials (<= 64 chunks
+        // staged in LDS)
+        const int used = EPB == 4 ? (int)((nc + kSoftmaxChunk - 1) / kSoftmaxChunk)
+                                  : (int)((L / kBlock + kStatChunk - 1) / kStatChunk);
         if (used <= 64) {
             for (int i = tid; i < G * used; i += NT)
                 s_st[i] = stats[((int64_t)unit * G + i / used) * n_chunks + i % used];
@@ -75,6 +86,32 @@ __device__ __forceinline__ void topk_unit(
             s_Zinv[tid] = Z > 0.f ? 1.f / Z : 0.f;
         }
         __syncthreads();
+        if constexpr (EPB == 1) {
+            // blocks blk0 .. blk0 + PER - 1, four at a time (rows padded to a
+            // multiple of 4 blocks; nc_pad is the row stride)
+#pragma unroll
+            for (int q0 = 0; q0 < PER; q0 += 4) {
+                float S[4] = {0.f, 0.f, 0.f, 0.f};
+                bool any[4] = {false, false, false, false};
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                    if (blk0 + q0 < nc_pad)
+                        v = *reinterpret_cast<const float4 *>(logits + ((int64_t)unit * G + h) * nc_pad +
+                                                              blk0 + q0);
+                    const float x[4] = {v.x, v.y, v.z, v.w};
+                    const float Mh = s_M[h], Zi = s_Zinv[h];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (x[e] != -INFINITY) {
+                            S[e] += hw_exp(x[e] - Mh) * Zi;
+                            any[e] = true;
+                        }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) score[q0 + e] = (blk0 + q0 + e < nb && any[e]) ? S[e] : -INFINITY;
+            }
+        } else {
         // entries 4*blk0 .. 4*blk0 + 4*PER - 1, eight blocks (32 entries) at a time
 #pragma unroll
         for (int sub = 0; sub < PER; sub += 8) {
@@ -113,6 +150,7 @@ __device__ __forceinline__ void topk_unit(
                     if (j0 + 4 * q + e < nc) best = fmaxf(best, S[4 * q + e]);
                 score[sub + q] = (blk0 + sub + q < nb) ? best : -INFINITY;
             }
+        }
         }
     } else {
 #pragma unroll

@@ -15,7 +15,8 @@ import torch
 from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
                select_workspace_size, token_select, token_decode, token_select_workspace_size,
                token_decode_workspace_size, cobs_stats, cobs_select, cobs_select_workspace_size,
-               n_blocks, decode_step, decode_step_workspace_size,
+               n_blocks, decode_step, decode_step_workspace_size, cobs_decode_step,
+               cobs_decode_step_workspace_size,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
 
@@ -243,6 +244,23 @@ class CobsDecoder(SparseDecoder):
         return cobs_select(sel, stats, seq_lens, self.T_cap, self.top_k, self.n_init, self.n_local,
                            self.score_mode, self.order if order is None else order, idx=self.idx,
                            cnt=self.cnt, block_scores=block_scores, workspace=self.sel_ws)
+
+    def fused_step(self, Q, sel, K, V, stats, lens_prev, lens_now, scale=1.0, max_new_blocks=1,
+                   O=None, lse=None):
+        """The same step through sparse_attn_cobs_decode_step (one call)."""
+        if getattr(self, "cobs_step_ws", None) is None:
+            p = make_params(self.top_k, self.n_init, self.n_local, self.score_mode)
+            need = cobs_decode_step_workspace_size(self.B, self.Hq, self.Hkv, self.H_sel,
+                                                   self.T_cap, p, self.cap, self.n_split)
+            self.cobs_step_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
+        O, lse, _, _ = cobs_decode_step(Q, sel, K, V, stats, lens_prev, lens_now, self.top_k,
+                                        self.n_init, self.n_local, self.score_mode, self.order,
+                                        scale, max_new_blocks, idx=self.idx, cnt=self.cnt,
+                                        O=self.O if O is None else O,
+                                        lse=self.lse if lse is None else lse,
+                                        want_lse=self.lse is not None or lse is not None,
+                                        n_split=self.n_split, workspace=self.cobs_step_ws)
+        return O, lse
 
 
 class TokenIndexDecoder:

@@ -418,6 +418,39 @@ int sparse_attn_cobs_select(const void *sel, int H_sel, const void *stats, int d
                             float *block_scores_out, void *workspace, size_t ws_bytes,
                             void *stream);
 
+/* Workspace bytes needed by sparse_attn_cobs_decode_step (select and decode scratch). */
+size_t sparse_attn_cobs_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
+                                                   int64_t T_cap, const sa_select_params *p,
+                                                   int32_t idx_cap, int32_t n_split);
+
+/*
+ * sparse_attn_cobs_decode_step - one decode step selected by block statistics
+ * in one call: sparse_attn_cobs_stats over [lens_prev, lens_now) (statistics
+ * of the blocks the new tokens complete), then sparse_attn_cobs_select at
+ * L = lens_now, then sparse_attn_decode (Eq. 5); results identical to those
+ * three calls. In RAW_SUM mode with at most 2048 blocks (T_cap <= 131072)
+ * and idx_cap <= 1024 there is no separate top-k launch: every attention
+ * workgroup of a (b, kvh) takes that unit's top-k and union from the block
+ * scores itself (the same device code as the top-k kernel), and the unit's
+ * first workgroup writes idx_out / cnt_out.
+ *
+ *   Q [B, Hq, d]; sel [B, H_sel, d]; K, V [B, Hkv, T_cap, d]; stats
+ *   [B, Hkv, nb_cap, 2, d] (updated in place); lens_prev, lens_now device
+ *   int32 [B]; max_new_blocks host hint as in sparse_attn_cobs_stats (0 = no
+ *   statistics update); order 1 or 2; idx_out / cnt_out as in
+ *   sparse_attn_cobs_select; O / lse_out / n_split as in sparse_attn_decode.
+ *   Workspace: sparse_attn_cobs_decode_step_workspace_size.
+ * Errors: those of the three calls it stands for.
+ */
+int sparse_attn_cobs_decode_step(const void *Q, const void *sel, int H_sel, const void *K,
+                                 const void *V, void *stats, int dtype, int B, int Hq, int Hkv,
+                                 int d, int64_t T_cap, int64_t nb_cap, const int32_t *lens_prev,
+                                 const int32_t *lens_now, int32_t max_new_blocks,
+                                 const sa_select_params *p, int32_t order, float scale,
+                                 int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, void *O,
+                                 int out_dtype, float *lse_out, int32_t n_split, void *workspace,
+                                 size_t ws_bytes, void *stream);
+
 /*
  * sparse_attn_block_mass - selection quality, not a step of the sparse path:
  * the exact attention mass of every 64-token block for the decode query of

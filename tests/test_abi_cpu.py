@@ -305,3 +305,33 @@ def test_cobs_validation():
     need = L.sparse_attn_cobs_select_workspace_size(2, 2, 8, 1000, ctypes.byref(sa.make_params(8)))
     assert need >= 4 * 16 * 4 + 4 * 4 * 256 * 4                       # block scores + logits
     assert sel_call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+
+
+def test_cobs_decode_step_validation():
+    L = sa.lib()
+    p8 = sa.make_params(8, 1, 2, "softmax_sum")
+
+    def step_call(**kw):
+        p = kw.pop("params", p8)
+        a = dict(Q=FAKE, sel=FAKE, H_sel=8, K=FAKE, V=FAKE, S=FAKE, dtype=sa.SA_BF16, B=2, Hq=8,
+                 Hkv=2, d=128, T_cap=1000, nb_cap=16, lp=FAKE, ln=FAKE, mx=1, order=2, scale=1.0,
+                 idx=FAKE, idx_cap=11, cnt=FAKE, O=FAKE, out_dtype=sa.SA_F32, lse=None, n_split=0,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sparse_attn_cobs_decode_step(
+            a["Q"], a["sel"], a["H_sel"], a["K"], a["V"], a["S"], a["dtype"], a["B"], a["Hq"],
+            a["Hkv"], a["d"], a["T_cap"], a["nb_cap"], a["lp"], a["ln"], a["mx"], ctypes.byref(p),
+            a["order"], a["scale"], a["idx"], a["idx_cap"], a["cnt"], a["O"], a["out_dtype"],
+            a["lse"], a["n_split"], a["ws"], a["ws_bytes"], None)
+    assert step_call(S=None) == sa.SA_ERR_INVALID_ARG
+    assert step_call(mx=-1) == sa.SA_ERR_INVALID_ARG
+    assert step_call(order=0) == sa.SA_ERR_INVALID_ARG
+    assert step_call(scale=float("nan")) == sa.SA_ERR_INVALID_ARG
+    assert step_call(H_sel=6) == sa.SA_ERR_UNSUPPORTED                # G = 3
+    assert step_call(Hq=16) == sa.SA_ERR_UNSUPPORTED                  # 8 query heads per KV head
+    assert step_call(n_split=65) == sa.SA_ERR_UNSUPPORTED
+    assert step_call(nb_cap=15) == sa.SA_ERR_CAPACITY
+    assert step_call(idx_cap=10) == sa.SA_ERR_CAPACITY
+    need = L.sparse_attn_cobs_decode_step_workspace_size(2, 8, 2, 8, 1000, ctypes.byref(p8), 11, 0)
+    assert need >= L.sparse_attn_cobs_select_workspace_size(2, 2, 8, 1000, ctypes.byref(p8))
+    assert step_call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE

@@ -164,3 +164,76 @@ def test_cobs_second_order_finds_spread_blocks_and_decode_runs_on_them():
         for g4 in range(4):
             mass = oracle.block_mass(Qn[0, 4 * h + g4], Kn[0, h], T, 1.0)
             assert oracle.recall(mass, r2[(0, h)]) > oracle.recall(mass, r1[(0, h)]) + 0.2
+
+
+# ------------------------------------------------------------------ one-call step
+
+@pytest.mark.parametrize("mode,G,dt,order", [("softmax_sum", 4, "bf16", 2), ("softmax_sum", 4, "f32", 1),
+                                              ("softmax_sum", 1, "bf16", 2), ("softmax_sum", 2, "bf16", 1),
+                                              ("softmax_sum", 8, "bf16", 2), ("raw_sum", 1, "bf16", 2),
+                                              ("raw_sum", 4, "f32", 2)])
+def test_cobs_decode_step_equals_separate_calls(mode, G, dt, order):
+    """sparse_attn_cobs_decode_step (statistics append + selection + attention,
+    with the top-k inside the attention workgroups where it applies) gives the
+    three calls' statistics, block sets and outputs bit for bit, over steps
+    whose new tokens complete blocks, cross several blocks, or complete none."""
+    B, Hkv, T = 3, 2, 9000
+    Hq = 4 * Hkv
+    K = rand((B, Hkv, T, 128), dt, 40).to(DEV)
+    V = rand((B, Hkv, T, 128), dt, 41).to(DEV)
+    nb = (T + 63) // 64
+    steps = [([4000, 700, 64], [4001, 704, 65]), ([4001, 704, 65], [4096, 705, 128]),
+             ([4096, 705, 128], [5000, 1300, 129]), ([5000, 1300, 129], [9000, 1301, 190])]
+    S_a = torch.full((B, Hkv, nb, 2, 128), 7.0, dtype=TD[dt], device=DEV)
+    sa.cobs_stats(K, S_a, lens_t([0] * B), lens_t(steps[0][0]))
+    S_b = S_a.clone()
+    k = 20
+    for i, (lp, ln) in enumerate(steps):
+        Q = rand((B, Hq, 128), dt, 50 + i, scale=128 ** -0.5).to(DEV)
+        sel = Q if G == 4 else rand((B, Hkv * G, 128), dt, 60 + i, scale=128 ** -0.5).to(DEV)
+        Lp, Ln = lens_t(lp), lens_t(ln)
+        mxb = max(b // 64 - a // 64 for a, b in zip(lp, ln)) + 1
+        O1, lse1, idx1, cnt1 = sa.cobs_decode_step(Q, sel, K, V, S_a, Lp, Ln, k, 1, 2, mode, order,
+                                                   max_new_blocks=mxb)
+        sa.cobs_stats(K, S_b, Lp, Ln, max_new_blocks=mxb)
+        idx2, cnt2, _ = sa.cobs_select(sel, S_b, Ln, T, k, 1, 2, mode, order)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(S_a.view(BITS[dt]), S_b.view(BITS[dt])), (i, "statistics")
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), (i, mode)
+        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), (i, mode)
+
+
+def test_cobs_decode_step_at_and_past_the_fused_limits():
+    """2048 blocks (top-k inside the attention workgroups) and 2049 blocks
+    (separate top-k launch), softmax mode, against the separate calls and the
+    oracle's selection."""
+    for T in (64 * 2048, 64 * 2048 + 64):
+        B, Hkv, G = 1, 2, 4
+        K = rand((B, Hkv, T, 128), "bf16", 70).to(DEV)
+        V = rand((B, Hkv, T, 128), "bf16", 71).to(DEV)
+        Q = rand((B, 4 * Hkv, 128), "bf16", 72, scale=128 ** -0.5).to(DEV)
+        nb = (T + 63) // 64
+        S = _stats_gpu(K.cpu(), [T - 1], nb_cap=nb)
+        S2 = S.clone()
+        Lp, Ln = lens_t([T - 1]), lens_t([T])
+        O1, lse1, idx1, cnt1 = sa.cobs_decode_step(Q, Q, K, V, S, Lp, Ln, 60, 1, 2, "softmax_sum", 2)
+        sa.cobs_stats(K, S2, Lp, Ln)
+        idx2, cnt2, bs = sa.cobs_select(Q, S2, Ln, T, 60, 1, 2, "softmax_sum", 2, block_scores=True)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), T
+        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), T
+        Kn = K.float().cpu().numpy()
+        p = SelectParams(top_k=60, n_init=1, n_local=2, score_mode="softmax_sum")
+        rows = gpu_rows(idx1, cnt1)
+        bsn = bs.cpu().numpy().astype(np.float64)
+        for h in range(Hkv):
+            mu, var = oracle.block_stats(Kn[0, h], T, "bf16")
+            ref, BS = oracle.select_blocks_cobs(to_np(Q)[0, h * G:(h + 1) * G], mu, var, T, p, 2,
+                                                return_scores=True)
+            ok, why = selection_ok(rows[(0, h)], ref, BS, oracle.n_blocks(T), 60, 1, 2)
+            assert ok, (T, h, why)
+            fin = np.isfinite(BS)
+            assert np.allclose(bsn[0, h, :nb][fin], BS[fin], rtol=2e-5,
+                               atol=2e-6 * np.abs(BS[fin]).max())
