@@ -116,7 +116,7 @@ struct BlockRegs {
 // kernels' output into LDS; every split of a unit computes the same set (the
 // redundant work replaces a separate top-k launch on the critical path) and
 // split 0 writes it out.
-template <typename T, bool DIRECT, bool ROWS, int SG = 0, bool SSOFT = false, int SEPB = 4>
+template <typename T, bool DIRECT, bool ROWS, int SG = 0, bool SSOFT = false>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if constexpr (SG > 0) {
         __shared__ int32_t s_list[kFusedMaxCap];
         __shared__ int32_t s_cnt;
-        topk_unit<SG, SSOFT, kDecThreads, kFusedMaxBlocks / kDecThreads, SEPB>(
+        topk_unit<SG, SSOFT, kDecThreads, kFusedMaxBlocks / kDecThreads>(
             unit, Hkv, T_cap, fs.nb_cap, seq_lens, fs.top_k, fs.n_init, fs.n_local, fs.logits,
             fs.nc_pad, fs.stats, fs.n_chunks, fs.bscore, nullptr, s_list, idx_cap, &s_cnt,
             fs.use_buckets);
@@ -482,7 +482,7 @@ int launch_decode_rows(const void *Q, const void *K, const void *V, int dtype, i
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
-template <typename T, int SG, bool SSOFT, int SEPB>
+template <typename T, int SG, bool SSOFT>
 static void launch_decode_select_t(const void *Q, const void *K, const void *V, int B, int Hq,
                                    int Hkv, int64_t T_cap, const int32_t *seq_lens,
                                    int32_t idx_cap, float scale, void *O, int out_bf16, float *lse,
@@ -491,12 +491,12 @@ static void launch_decode_select_t(const void *Q, const void *K, const void *V, 
     const dim3 grid((unsigned)n_split, (unsigned)(B * Hkv));
     const float qscale = scale * kLog2e;
     if (n_split == 1) {
-        hipLaunchKernelGGL((decode_kernel<T, true, false, SG, SSOFT, SEPB>), grid, dim3(kDecThreads), 0,
+        hipLaunchKernelGGL((decode_kernel<T, true, false, SG, SSOFT>), grid, dim3(kDecThreads), 0,
                            stream, (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens,
                            (const int32_t *)nullptr, (const int32_t *)nullptr, idx_cap, qscale, 1,
                            (float *)nullptr, O, out_bf16, lse, fs);
     } else {
-        hipLaunchKernelGGL((decode_kernel<T, false, false, SG, SSOFT, SEPB>), grid, dim3(kDecThreads), 0,
+        hipLaunchKernelGGL((decode_kernel<T, false, false, SG, SSOFT>), grid, dim3(kDecThreads), 0,
                            stream, (const T *)Q, (const T *)K, (const T *)V, Hq, Hkv, T_cap, seq_lens,
                            (const int32_t *)nullptr, (const int32_t *)nullptr, idx_cap, qscale,
                            n_split, (float *)ws, O, out_bf16, lse, fs);
@@ -511,19 +511,15 @@ int launch_decode_select(const void *Q, const void *K, const void *V, int dtype,
                          void *workspace, const FusedSelect &fs, int G, bool softmax,
                          hipStream_t stream) {
     const int out_bf16 = out_dtype == SA_BF16 ? 1 : 0;
-#define SA_DS(TT, SGV, SM, EP)                                                                    \
-    launch_decode_select_t<TT, SGV, SM, EP>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx_cap, scale, \
-                                            O, out_bf16, lse_out, n_split, workspace, fs, stream)
+#define SA_DS(TT, SGV, SM)                                                                        \
+    launch_decode_select_t<TT, SGV, SM>(Q, K, V, B, Hq, Hkv, T_cap, seq_lens, idx_cap, scale, O,  \
+                                        out_bf16, lse_out, n_split, workspace, fs, stream)
 #define SA_DS_T(TT)                                                                               \
-    if (!softmax) SA_DS(TT, 1, false, 4);                                                         \
-    else if (fs.epb == 1) {                                                                       \
-        if (G == 1) SA_DS(TT, 1, true, 1);                                                        \
-        else if (G == 2) SA_DS(TT, 2, true, 1);                                                   \
-        else if (G == 4) SA_DS(TT, 4, true, 1);                                                   \
-        else return SA_ERR_UNSUPPORTED;                                                           \
-    } else if (G == 1) SA_DS(TT, 1, true, 4);                                                     \
-    else if (G == 2) SA_DS(TT, 2, true, 4);                                                       \
-    else if (G == 4) SA_DS(TT, 4, true, 4);                                                       \
+    if (!softmax) SA_DS(TT, 1, false);                                                            \
+    else if (fs.epb != 4) return SA_ERR_UNSUPPORTED;                                              \
+    else if (G == 1) SA_DS(TT, 1, true);                                                          \
+    else if (G == 2) SA_DS(TT, 2, true);                                                          \
+    else if (G == 4) SA_DS(TT, 4, true);                                                          \
     else return SA_ERR_UNSUPPORTED;
     if (dtype == SA_BF16) {
         SA_DS_T(bf16_t)

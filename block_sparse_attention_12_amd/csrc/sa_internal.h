@@ -55,7 +55,8 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   FusedSelect *fs = nullptr);
 // Decode attention whose workgroups first take their unit's top-k themselves
 // (fs from launch_select or launch_cobs_select): needs ceil(T_cap / 64) <= 2048,
-// idx_cap <= 1024 and, for the softmax-sum form, G <= 4.
+// idx_cap <= 1024 and, for the softmax-sum form, G <= 4 and logits of
+// compressed entries (epb 4; per-block logits are not taken here).
 constexpr int64_t kFusedMaxBlocks = 2048;
 constexpr int kFusedMaxCap = 1024;
 int launch_decode_select(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
