@@ -115,3 +115,45 @@ def test_decode_step_fused_and_separate_topk(case):
     assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
     assert torch.equal(O1, O2) and torch.equal(lse1, lse2)
     assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt]))
+
+
+def test_decode_step_random_configurations():
+    """Seeded random shapes, lengths, budgets and modes: the one-call step and
+    the three separate calls agree bit for bit (sets, outputs, compressed keys)."""
+    import random
+    rng = random.Random(2024)
+    for trial in range(12):
+        dt = rng.choice(["bf16", "bf16", "f32"])
+        mode, G = rng.choice([("raw_sum", 1), ("raw_sum", 4), ("softmax_sum", 4), ("softmax_sum", 1),
+                              ("softmax_sum", 2), ("softmax_sum", 8)])
+        B, Hkv = rng.randint(1, 4), rng.choice([1, 2, 4])
+        T = rng.choice([700, 3000, 9000, 20000, 64 * 2048])
+        n_init, n_local = rng.randint(0, 3), rng.randint(0, 4)
+        k = rng.choice([0, 1, 7, 30, 200])
+        if k + n_init + n_local == 0:
+            n_local = 1                                  # a set of capacity 0 is not a call
+        n_split = rng.choice([0, 0, 1, 3])
+        new = rng.choice([1, 1, 5, 40])
+        lens = [rng.randint(0, T) for _ in range(B)]
+        lp = [max(0, L - rng.randint(0, new)) for L in lens]
+        K = rand((B, Hkv, T, 128), dt, 100 + trial)
+        V = rand((B, Hkv, T, 128), dt, 200 + trial)
+        Q = rand((B, 4 * Hkv, 128), dt, 300 + trial, scale=128 ** -0.5)
+        sel = Q if G == 4 else rand((B, Hkv * G, 128), dt, 400 + trial, scale=128 ** -0.5)
+        nc_cap = sa.n_compressed(T)
+        Kc_a = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+        sa.compress(K, Kc_a, lens_t([0] * B), lens_t(lp))
+        Kc_b = Kc_a.clone()
+        Lp, Ln = lens_t(lp), lens_t(lens)
+        mx = max(b - a for a, b in zip(lp, lens))
+        case = (trial, dt, mode, G, B, Hkv, T, n_init, n_local, k, n_split, lens, lp)
+        print("case", case, flush=True)
+        O1, lse1, idx1, cnt1 = sa.decode_step(Q, sel, K, V, Kc_a, Lp, Ln, k, n_init, n_local, mode,
+                                              max_new_tokens=mx, n_split=n_split)
+        sa.compress(K, Kc_b, Lp, Ln, max_new_entries=mx // 16 + 2)
+        idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, n_init, n_local, mode)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=n_split)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), case
+        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), case
+        assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), case
