@@ -91,6 +91,32 @@ __device__ __forceinline__ void compress_entry_raw(const float *__restrict__ Ku,
                         (a[6] + b[6]) * 0.03125f, (a[7] + b[7]) * 0.03125f);
 }
 
+// Entry from its 32 keys staged in LDS (rows[t][l] = lane l's 8 channels of
+// key 16j + t, bf16): the same sums in the same order as compress_entry_raw.
+__device__ __forceinline__ void entry_from_rows(const uint4 (*rows)[16], int lane16,
+                                                Raw8<bf16_t> &out) {
+    float a[8], b[8], e[8];
+    unpack(Raw8<bf16_t>{rows[0][lane16]}, a);
+    unpack(Raw8<bf16_t>{rows[kCmpStride][lane16]}, b);
+#pragma unroll
+    for (int t = 1; t < kCmpStride; ++t) {
+        float x[8], y[8];
+        unpack(Raw8<bf16_t>{rows[t][lane16]}, x);
+        unpack(Raw8<bf16_t>{rows[kCmpStride + t][lane16]}, y);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            a[c] = a[c] + x[c];
+            b[c] = b[c] + y[c];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) e[c] = (a[c] + b[c]) * 0.03125f;
+    out.v.x = f32_to_bf16_bits(e[0]) | (f32_to_bf16_bits(e[1]) << 16);
+    out.v.y = f32_to_bf16_bits(e[2]) | (f32_to_bf16_bits(e[3]) << 16);
+    out.v.z = f32_to_bf16_bits(e[4]) | (f32_to_bf16_bits(e[5]) << 16);
+    out.v.w = f32_to_bf16_bits(e[6]) | (f32_to_bf16_bits(e[7]) << 16);
+}
+
 __device__ __forceinline__ void store_raw(bf16_t *p, const Raw8<bf16_t> &r) {
     *reinterpret_cast<uint4 *>(p) = r.v;
 }

@@ -44,7 +44,9 @@ struct FusedSelect {
 };
 
 // With K and lens_prev (raw-sum mode only), the compressed entries completed
-// between lens_prev and seq_lens are written by the scoring launch itself.
+// between lens_prev and seq_lens are written by the scoring launch itself
+// (max_new_tokens: an upper bound on lens_now - lens_prev; up to 16 in bf16,
+// each unit's first scoring workgroup writes the at most one new entry).
 // With fs, only the scoring kernel(s) run and fs describes their output (the
 // top-k is left to the caller's next launch).
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,
@@ -52,7 +54,7 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
                   float *block_scores_out, void *workspace, hipStream_t stream,
                   const void *K = nullptr, const int32_t *lens_prev = nullptr,
-                  FusedSelect *fs = nullptr);
+                  FusedSelect *fs = nullptr, int32_t max_new_tokens = 1 << 30);
 // Decode attention whose workgroups first take their unit's top-k themselves
 // (fs from launch_select or launch_cobs_select): needs ceil(T_cap / 64) <= 2048,
 // idx_cap <= 1024 and, for the softmax-sum form, G <= 4 and logits of

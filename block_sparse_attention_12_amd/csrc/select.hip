@@ -37,6 +37,8 @@ namespace sa {
 
 constexpr int kSelThreads = 256;
 constexpr int kRawChunkBlocks = 256;                // blocks per workgroup (raw mode)
+constexpr int kAppendColumn = 1;                    // the append as an extra column of workgroups
+constexpr int kAppendInFirst = 2;                   // the append by each unit's first workgroup
 constexpr int64_t kMaxTopkBlocks = 32768;           // 1024 threads x 32 blocks
 
 SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const T *__restrict__ sel, int H_sel, int Gs, const T *__restrict__ Kc, int Hkv,
     int64_t nc_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ bscore,
     int64_t nb_cap, const T *__restrict__ K, T *__restrict__ Kc_w,
-    const int32_t *__restrict__ lens_prev, int n_local) {
+    const int32_t *__restrict__ lens_prev, int n_local, int app_mode) {
     const int unit = blockIdx.y;
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int64_t L = clamp_len(seq_lens[b], T_cap);
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
         int64_t Lp = lens_prev[b];
         Lp = Lp < 0 ? 0 : (Lp > L ? L : Lp);
         nc_old = n_compressed(Lp);
-        if (blockIdx.x == gridDim.x - 1) {              // the append column
+        if (app_mode == kAppendColumn && blockIdx.x == gridDim.x - 1) {   // the append column
             const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
             T *Kcu = Kc_w + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
             for (int64_t j = nc_old + group; j < nc; j += 16) {   // few keys in flight
@@ -236,6 +238,30 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
                         else load_raw(rKc, row_offset(j, kRowBytes, lane_off), fix.r[q * 3 + e]);
                     }
                 process(fix, b0);
+            }
+        }
+    }
+    // kAppendInFirst (bf16, at most one new entry per unit): after its own
+    // blocks, the unit's first workgroup loads the new entry's 32 keys (two per
+    // row group, all in flight at once), stages them in LDS and one row group
+    // sums them in token order. (Loads issued before the main loop, under a
+    // condition, cost the loop its exact wait counts.)
+    constexpr bool kInFirst = APPEND && sizeof(T) == 2;
+    if constexpr (kInFirst) {
+        if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old < nc) {   // uniform per workgroup
+            __shared__ uint4 s_rows[2 * kCmpStride][16];
+            const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+            Raw8<T> app_rows[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                load_raw(Ka + (nc_old * kCmpStride + 2 * group + i) * kD, app_rows[i]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) s_rows[2 * group + i][lane16] = app_rows[i].v;
+            __syncthreads();
+            if (group == 0) {
+                Raw8<T> e;
+                entry_from_rows(s_rows, lane16, e);
+                store_raw(Kc_w + ((int64_t)unit * nc_cap + nc_old) * kD + lane16 * kLaneElems, e);
             }
         }
     }
@@ -413,19 +439,28 @@ static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B
                        const sa_select_params &p, int32_t *idx_out, int32_t idx_cap,
                        int32_t *cnt_out, float *bs_out, const SelectWorkspace &w, char *ws,
                        hipStream_t stream, const void *K = nullptr,
-                       const int32_t *lens_prev = nullptr, FusedSelect *fs = nullptr) {
+                       const int32_t *lens_prev = nullptr, FusedSelect *fs = nullptr,
+                       int32_t max_new_tokens = 1 << 30) {
     float *bscore = (float *)(ws + w.bscore_off);
     const unsigned units = (unsigned)(B * Hkv);
     const unsigned chunks = (unsigned)((w.nb_cap + kRawChunkBlocks - 1) / kRawChunkBlocks);
-    if (lens_prev)                                      // scoring + the step's append in one launch
-        hipLaunchKernelGGL((score_raw_kernel<T, true>), dim3(chunks + 1, units), dim3(kSelThreads), 0,
+    if (lens_prev) {
+        // scoring + the step's append in one launch: with at most one new entry
+        // per unit (bf16) the unit's first workgroup writes it; otherwise an
+        // extra column of workgroups does (which leaves the grid uneven over the
+        // CUs: measured ~2.4 us at 128K)
+        const int mode = (sizeof(T) == 2 && max_new_tokens <= kCmpStride) ? kAppendInFirst
+                                                                           : kAppendColumn;
+        const unsigned cols = chunks + (mode == kAppendColumn ? 1 : 0);
+        hipLaunchKernelGGL((score_raw_kernel<T, true>), dim3(cols, units), dim3(kSelThreads), 0,
                            stream, (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap,
-                           seq_lens, bscore, w.nb_cap, (const T *)K, (T *)Kc, lens_prev, p.n_local);
-    else if (chunks > 0)
+                           seq_lens, bscore, w.nb_cap, (const T *)K, (T *)Kc, lens_prev, p.n_local,
+                           mode);
+    } else if (chunks > 0)
         hipLaunchKernelGGL((score_raw_kernel<T, false>), dim3(chunks, units), dim3(kSelThreads), 0,
                            stream, (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap,
                            seq_lens, bscore, w.nb_cap, (const T *)nullptr, (T *)nullptr,
-                           (const int32_t *)nullptr, 0);
+                           (const int32_t *)nullptr, 0, 0);
     if (fs) {
         fs->bscore = bscore;
         return;
@@ -438,7 +473,7 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
                   int64_t T_cap, int64_t nc_cap, const int32_t *seq_lens,
                   const sa_select_params &p, int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out,
                   float *block_scores_out, void *workspace, hipStream_t stream, const void *K,
-                  const int32_t *lens_prev, FusedSelect *fs) {
+                  const int32_t *lens_prev, FusedSelect *fs, int32_t max_new_tokens) {
     const SelectWorkspace w = select_workspace_layout(B, Hkv, G, T_cap, p.score_mode);
     if (w.nb_cap > kMaxTopkBlocks) return SA_ERR_UNSUPPORTED;
     char *ws = (char *)workspace;
@@ -461,10 +496,12 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
     if (p.score_mode == SA_SCORE_RAW_SUM) {
         if (dtype == SA_BF16)
             launch_raw<bf16_t>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
-                               cnt_out, block_scores_out, w, ws, stream, K, lens_prev, fs);
+                               cnt_out, block_scores_out, w, ws, stream, K, lens_prev, fs,
+                               max_new_tokens);
         else
             launch_raw<float>(sel, H_sel, G, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, idx_cap,
-                              cnt_out, block_scores_out, w, ws, stream, K, lens_prev, fs);
+                              cnt_out, block_scores_out, w, ws, stream, K, lens_prev, fs,
+                              max_new_tokens);
     } else {
 #define SA_SOFTMAX_CASE(GG)                                                                       \
     case GG:                                                                                      \

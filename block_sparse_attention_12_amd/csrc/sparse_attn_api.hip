@@ -176,7 +176,7 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
     if (p->score_mode == SA_SCORE_RAW_SUM) {
         // the append rides in the scoring launch (the scorer forms new entries itself)
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
-                           cnt_out, nullptr, workspace, hs, K, lens_prev, fsp);
+                           cnt_out, nullptr, workspace, hs, K, lens_prev, fsp, max_new_tokens);
     } else {
         // every entry enters the softmax denominators: append first
         if (max_new_tokens > 0) {
