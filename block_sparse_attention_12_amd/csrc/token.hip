@@ -61,7 +61,7 @@ TokenWorkspace token_workspace_layout(int B, int Hkv, int64_t T_cap) {
     w.keys_off = take((size_t)units * w.t_pad * sizeof(uint32_t));
     w.hist_off = take((size_t)kTokPasses * units * 256 * sizeof(uint32_t));
     w.counts_off = take((size_t)units * w.n_chunks * 2 * sizeof(int32_t));
-    w.info_off = take((size_t)units * 2 * sizeof(uint32_t));
+    w.info_off = take((size_t)units * 4 * sizeof(uint32_t));
     w.total = off;
     return w;
 }
@@ -84,16 +84,17 @@ __device__ __forceinline__ TokWindows tok_windows(int64_t L, int top_k, int n_in
 }
 
 // Wave 0 finds the bin of the 256-bin LDS histogram s_h that holds the
-// `remaining`-th largest counted key (bins scanned from the top) and the
-// number of keys in the bins above it; every thread reads them after the
-// barrier.
+// `remaining`-th largest counted key (bins scanned from the top), the number
+// of keys in the bins above it and the bin's own count; every thread reads
+// them after the barrier.
 __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, uint32_t *s_digit,
-                                          uint32_t *s_above) {
+                                          uint32_t *s_above, uint32_t *s_bcnt) {
     const int tid = threadIdx.x;
     if (tid < 64) {
         if (tid == 0) {                 // defined even if no bin qualifies (inconsistent counts)
             *s_digit = 0;
             *s_above = 0;
+            *s_bcnt = 0xffffffffu;
         }
         const uint32_t hb[4] = {s_h[4 * tid], s_h[4 * tid + 1], s_h[4 * tid + 2], s_h[4 * tid + 3]};
         const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
@@ -109,6 +110,7 @@ __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, ui
             if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
                 *s_digit = 4 * tid + k;
                 *s_above = above;
+                *s_bcnt = hb[k];
             }
             above += hb[k];
         }
@@ -118,23 +120,32 @@ __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, ui
 
 // The digits chosen by the first `passes` passes of a unit: prefix (the chosen
 // high bits), mask, and how many of the top_k remain to be found below them.
+// The digits stop early (whole = true) once the boundary bin holds exactly the
+// keys still to take: every key whose masked bits equal the prefix is then
+// taken, and later passes have nothing to count.
 __device__ __forceinline__ void tok_prefix(const uint32_t *hist_unit, int64_t hist_stride,
                                            int passes, int top_k, uint32_t *s_h, uint32_t *s_digit,
-                                           uint32_t *s_above, uint32_t &prefix, uint32_t &mask,
-                                           int &remaining) {
+                                           uint32_t *s_above, uint32_t *s_bcnt, uint32_t &prefix,
+                                           uint32_t &mask, int &remaining, bool &whole) {
     prefix = 0;
     mask = 0;
     remaining = top_k;
+    whole = false;
     for (int p = 0; p < passes; ++p) {
         s_h[threadIdx.x] = hist_unit[p * hist_stride + threadIdx.x];   // 256 threads, 256 bins
         __syncthreads();
-        tok_digit(s_h, remaining, s_digit, s_above);
+        tok_digit(s_h, remaining, s_digit, s_above, s_bcnt);
         const int shift = 24 - 8 * p;
         prefix |= *s_digit << shift;
         mask |= 255u << shift;
         remaining -= (int)*s_above;
         remaining = remaining < 0 ? 0 : remaining;
-        __syncthreads();                                               // s_h reused
+        const bool done = *s_bcnt == (uint32_t)remaining;              // same on every thread
+        __syncthreads();                                               // s_h and the scalars reused
+        if (done) {
+            whole = true;
+            break;
+        }
     }
 }
 
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_radix_kernel(
     int n_local, const uint32_t *__restrict__ keys, int64_t t_pad, uint32_t *__restrict__ hist,
     int64_t hist_stride) {
     __shared__ uint32_t s_h[256];
-    __shared__ uint32_t s_digit, s_above;
+    __shared__ uint32_t s_digit, s_above, s_bcnt;
     const int unit = blockIdx.y;
     const int b = unit / Hkv;
     const TokWindows w = tok_windows(clamp_len(seq_lens[b], T_cap), top_k, n_init, n_local);
@@ -286,7 +297,10 @@ __global__ __launch_bounds__(kTokThreads) void tok_radix_kernel(
     const uint32_t *hu = hist + (int64_t)unit * 256;
     uint32_t prefix, mask;
     int remaining;
-    tok_prefix(hu, hist_stride, pass, top_k, s_h, &s_digit, &s_above, prefix, mask, remaining);
+    bool whole;
+    tok_prefix(hu, hist_stride, pass, top_k, s_h, &s_digit, &s_above, &s_bcnt, prefix, mask,
+               remaining, whole);
+    if (whole) return;                                         // the set is already decided
     uint32_t key[kTokPer];
     bool cand[kTokPer];
     tok_load_keys(keys + (int64_t)unit * t_pad, t0, w, key, cand);
@@ -312,18 +326,19 @@ __global__ __launch_bounds__(kTokThreads) void tok_count_kernel(
     const uint32_t *__restrict__ hist, int64_t hist_stride, int n_chunks,
     int32_t *__restrict__ counts, uint32_t *__restrict__ info) {
     __shared__ uint32_t s_h[256];
-    __shared__ uint32_t s_digit, s_above;
+    __shared__ uint32_t s_digit, s_above, s_bcnt;
     __shared__ int s_red[2][kTokThreads / 64];
     const int unit = blockIdx.y;
     const int b = unit / Hkv;
     const TokWindows w = tok_windows(clamp_len(seq_lens[b], T_cap), top_k, n_init, n_local);
     const int64_t t0 = (int64_t)blockIdx.x * kTokChunk;
     if (t0 >= w.L) return;                                     // chunk never read
-    uint32_t thr = 0, mask;
+    uint32_t thr = 0, mask = 0xffffffffu;
     int take_eq = 0;
+    bool whole = false;
     if (w.choose)
         tok_prefix(hist + (int64_t)unit * 256, hist_stride, kTokPasses, top_k, s_h, &s_digit,
-                   &s_above, thr, mask, take_eq);
+                   &s_above, &s_bcnt, thr, mask, take_eq, whole);
     uint32_t key[kTokPer];
     bool cand[kTokPer];
     tok_load_keys(keys + (int64_t)unit * t_pad, t0, w, key, cand);
@@ -334,8 +349,8 @@ __global__ __launch_bounds__(kTokThreads) void tok_count_kernel(
         const int64_t t = tb + i;
         if (t >= w.L) continue;
         if (!cand[i]) ++n_sure;                                 // kept initial / local token
-        else if (w.take_all || (w.choose && key[i] > thr)) ++n_sure;
-        else if (w.choose && key[i] == thr) ++n_eq;
+        else if (w.take_all || (w.choose && (key[i] & mask) > thr)) ++n_sure;
+        else if (w.choose && (key[i] & mask) == thr) ++n_eq;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -357,8 +372,9 @@ __global__ __launch_bounds__(kTokThreads) void tok_count_kernel(
         counts[((int64_t)unit * n_chunks + blockIdx.x) * 2] = a;
         counts[((int64_t)unit * n_chunks + blockIdx.x) * 2 + 1] = e;
         if (blockIdx.x == 0) {
-            info[unit * 2] = thr;
-            info[unit * 2 + 1] = (uint32_t)take_eq;
+            info[unit * 4] = thr;
+            info[unit * 4 + 1] = (uint32_t)take_eq;
+            info[unit * 4 + 2] = mask;
         }
     }
 }
@@ -376,8 +392,9 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     const TokWindows w = tok_windows(clamp_len(seq_lens[b], T_cap), top_k, n_init, n_local);
     const int64_t t0 = (int64_t)blockIdx.x * kTokChunk;
     const int n_used = (int)((w.L + kTokChunk - 1) / kTokChunk);
-    const uint32_t thr = w.choose ? info[unit * 2] : 0u;
-    int take_eq = w.choose ? (int)info[unit * 2 + 1] : 0;
+    const uint32_t thr = w.choose ? info[unit * 4] : 0u;
+    const uint32_t mask = w.choose ? info[unit * 4 + 2] : 0xffffffffu;
+    int take_eq = w.choose ? (int)info[unit * 4 + 1] : 0;
     take_eq = take_eq < 0 ? 0 : take_eq;
     int32_t *row = idx_out + (int64_t)unit * idx_cap;
     const int32_t *cu = counts + (int64_t)unit * n_chunks * 2;
@@ -425,7 +442,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     int n_eq = 0;
 #pragma unroll
     for (int i = 0; i < kTokPer; ++i)
-        n_eq += (w.choose && tb + i < w.L && cand[i] && key[i] == thr) ? 1 : 0;
+        n_eq += (w.choose && tb + i < w.L && cand[i] && (key[i] & mask) == thr) ? 1 : 0;
     int unused;
     int eq_rank = eq_before + wg_exclusive_scan<kTokThreads>(n_eq, s_wave, unused);
     bool in[kTokPer];
@@ -438,8 +455,8 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
         else if (!cand[i]) x = true;
         else if (w.take_all) x = true;
         else if (!w.choose) x = false;
-        else if (key[i] > thr) x = true;
-        else if (key[i] == thr) x = eq_rank++ < take_eq;
+        else if ((key[i] & mask) > thr) x = true;
+        else if ((key[i] & mask) == thr) x = eq_rank++ < take_eq;
         else x = false;
         in[i] = x;
         n_in += x ? 1 : 0;
