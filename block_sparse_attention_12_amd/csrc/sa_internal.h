@@ -43,10 +43,11 @@ struct FusedSelect {
     int epb;                           // softmax logits per block: 4 (compressed entries) or 1
 };
 
-// With K and lens_prev (raw-sum mode only), the compressed entries completed
-// between lens_prev and seq_lens are written by the scoring launch itself
-// (max_new_tokens: an upper bound on lens_now - lens_prev; up to 16 in bf16,
-// each unit's first scoring workgroup writes the at most one new entry).
+// With K and lens_prev, the compressed entries completed between lens_prev
+// and seq_lens are written by the scoring launch itself (raw-sum mode:
+// max_new_tokens is an upper bound on lens_now - lens_prev; up to 16 in bf16,
+// each unit's first scoring workgroup writes the at most one new entry;
+// softmax mode: the workgroup owning a new entry forms, scores and writes it).
 // With fs, only the scoring kernel(s) run and fs describes their output (the
 // top-k is left to the caller's next launch).
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,

@@ -27,6 +27,7 @@
 //                         union in ascending block order with a prefix scan.
 #include <float.h>
 #include <math.h>
+#include <type_traits>
 
 #include "compress_device.h"
 #include "sa_device.h"
@@ -269,11 +270,18 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
 
 // ---------------------------------------------------------------- softmax scores
 
-template <typename T, int G>
+// APPEND (one-call decode step): entries completed between lens_prev and
+// seq_lens are not read from Kc; the group that owns such an entry forms it
+// from the keys (the append's arithmetic), writes it to Kc and scores it in
+// extra iterations after the main loop. A lane's new entries come after all of
+// its old ones in the main loop's order, so every running (max, sum) sees the
+// same values in the same order as with a separate append before the launch.
+template <typename T, int G, bool APPEND>
 __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     const T *__restrict__ sel, int H_sel, const T *__restrict__ Kc, int Hkv, int64_t nc_cap,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ logits, int64_t nc_pad,
-    float2 *__restrict__ stats, int n_chunks) {
+    float2 *__restrict__ stats, int n_chunks, const T *__restrict__ K, T *__restrict__ Kc_w,
+    const int32_t *__restrict__ lens_prev) {
     constexpr int EPI = 16 / G;                         // entries per row group per iteration
     constexpr int PER_IT = 16 * EPI;                     // entries per workgroup iteration
     __shared__ float2 s_ms[4][G];
@@ -281,6 +289,12 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int64_t L = clamp_len(seq_lens[b], T_cap);
     const int64_t nc = n_compressed(L);
+    int64_t nc_old = nc;                                // entries readable from Kc
+    if constexpr (APPEND) {
+        int64_t Lp = lens_prev[b];
+        Lp = Lp < 0 ? 0 : (Lp > L ? L : Lp);
+        nc_old = n_compressed(Lp);
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lane16 = threadIdx.x & 15;
     const int group = threadIdx.x >> 4;
@@ -295,18 +309,41 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     float *lrow = logits + ((int64_t)unit * G + my_g) * nc_pad;
     float m = -INFINITY, ssum = 0.f;
     const int64_t base = (int64_t)blockIdx.x * kSoftmaxChunk;
-#pragma unroll 1
-    for (int it = 0; it < kSoftmaxChunk / PER_IT; ++it) {
+    // one iteration: dot products, reduction, online update over the entries
+    // read from Kc (below nc_old) or, with FORM, the new ones formed from the keys
+    // bf16 with a single new entry: its 32 keys staged in LDS (see below)
+    __shared__ uint4 s_rows[2 * kCmpStride][16];
+    const bool one_new = APPEND && nc == nc_old + 1;
+    auto iteration = [&](int it, auto form) {
+        constexpr bool FORM = decltype(form)::value;
+        auto live = [&](int64_t je) { return FORM ? (je >= nc_old && je < nc) : je < nc_old; };
         const int64_t j0 = base + it * PER_IT + group * EPI;
         Raw8<T> r[EPI];
 #pragma unroll
-        for (int e = 0; e < EPI; ++e)
-            if (j0 + e < nc) load_raw(Kcu + (j0 + e) * kD, r[e]);
+        for (int e = 0; e < EPI; ++e) {
+            const int64_t je = j0 + e;
+            if (live(je)) {
+                if constexpr (APPEND) {
+                    if constexpr (FORM) {
+                        const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+                        if constexpr (sizeof(T) == 2) {
+                            if (one_new) entry_from_rows(s_rows, lane16, r[e]);
+                            else compress_entry_raw(Ku, je, r[e]);
+                        } else {
+                            compress_entry_raw(Ku, je, r[e]);
+                        }
+                        store_raw(Kc_w + ((int64_t)unit * nc_cap + je) * kD + lane16 * kLaneElems, r[e]);
+                        continue;
+                    }
+                }
+                load_raw(Kcu + je * kD, r[e]);
+            }
+        }
         float v[16];
 #pragma unroll
         for (int e = 0; e < EPI; ++e) {
             float x[8];
-            if (j0 + e < nc) unpack(r[e], x);
+            if (live(j0 + e)) unpack(r[e], x);
             else {
 #pragma unroll
                 for (int c = 0; c < 8; ++c) x[c] = 0.f;
@@ -321,7 +358,7 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
         }
         transpose_reduce16<16>(v, lane);
         const int64_t j = j0 + my_e;
-        if (j < nc) {
+        if (live(j)) {
             const float x = v[0];
             lrow[j] = x;
             if (x > m) {
@@ -331,6 +368,31 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
                 ssum += hw_exp(x - m);
             }
         }
+    };
+#pragma unroll 1
+    for (int it = 0; it < kSoftmaxChunk / PER_IT; ++it) iteration(it, std::false_type{});
+    if constexpr (APPEND) {
+        // the iterations of this chunk that hold new entries (uniform per workgroup)
+        const int64_t a = nc_old > base ? nc_old : base;
+        const int64_t z = nc < base + kSoftmaxChunk ? nc : base + kSoftmaxChunk;
+        // bf16, one new entry: the workgroup loads its 32 keys (two per row
+        // group, all in flight at once) into LDS, and the owning group sums
+        // them in token order (per-lane loads of all 32 would wait in turn)
+        if constexpr (sizeof(T) == 2) {
+            if (a < z && one_new) {                      // uniform per workgroup
+                const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+                Raw8<T> rows[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    load_raw(Ka + (nc_old * kCmpStride + 2 * group + i) * kD, rows[i]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) s_rows[2 * group + i][lane16] = rows[i].v;
+                __syncthreads();
+            }
+        }
+#pragma unroll 1
+        for (int it = (int)((a - base) / PER_IT); a < z && it <= (int)((z - 1 - base) / PER_IT); ++it)
+            iteration(it, std::true_type{});
     }
     // merge (max, sum) over lanes holding the same head: lane bits >= log2(G)
 #pragma unroll
@@ -413,15 +475,24 @@ template <typename T, int G>
 static void launch_softmax(const void *sel, int H_sel, const void *Kc, int B, int Hkv, int64_t T_cap,
                            int64_t nc_cap, const int32_t *seq_lens, const sa_select_params &p,
                            int32_t *idx_out, int32_t idx_cap, int32_t *cnt_out, float *bs_out,
-                               const SelectWorkspace &w, char *ws, hipStream_t stream,
-                           FusedSelect *fs) {
+                           const SelectWorkspace &w, char *ws, hipStream_t stream,
+                           FusedSelect *fs, const void *K = nullptr,
+                           const int32_t *lens_prev = nullptr) {
     float *logits = (float *)(ws + w.logits_off);
     float2 *stats = (float2 *)(ws + w.stats_off);
     const unsigned units = (unsigned)(B * Hkv);
-    if (w.n_chunks > 0)
-        hipLaunchKernelGGL((score_softmax_kernel<T, G>), dim3((unsigned)w.n_chunks, units),
-                           dim3(kSelThreads), 0, stream, (const T *)sel, H_sel, (const T *)Kc, Hkv,
-                           nc_cap, T_cap, seq_lens, logits, w.nc_pad, stats, w.n_chunks);
+    if (w.n_chunks > 0) {
+        if (lens_prev)                                  // scoring + the step's append
+            hipLaunchKernelGGL((score_softmax_kernel<T, G, true>), dim3((unsigned)w.n_chunks, units),
+                               dim3(kSelThreads), 0, stream, (const T *)sel, H_sel, (const T *)Kc,
+                               Hkv, nc_cap, T_cap, seq_lens, logits, w.nc_pad, stats, w.n_chunks,
+                               (const T *)K, (T *)Kc, lens_prev);
+        else
+            hipLaunchKernelGGL((score_softmax_kernel<T, G, false>), dim3((unsigned)w.n_chunks, units),
+                               dim3(kSelThreads), 0, stream, (const T *)sel, H_sel, (const T *)Kc,
+                               Hkv, nc_cap, T_cap, seq_lens, logits, w.nc_pad, stats, w.n_chunks,
+                               (const T *)nullptr, (T *)nullptr, (const int32_t *)nullptr);
+    }
     if (fs) {
         fs->logits = logits;
         fs->nc_pad = w.nc_pad;
@@ -507,10 +578,12 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
     case GG:                                                                                      \
         if (dtype == SA_BF16)                                                                     \
             launch_softmax<bf16_t, GG>(sel, H_sel, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out, \
-                                       idx_cap, cnt_out, block_scores_out, w, ws, stream, fs);    \
+                                       idx_cap, cnt_out, block_scores_out, w, ws, stream, fs, K,  \
+                                       lens_prev);                                                \
         else                                                                                      \
             launch_softmax<float, GG>(sel, H_sel, Kc, B, Hkv, T_cap, nc_cap, seq_lens, p, idx_out,  \
-                                      idx_cap, cnt_out, block_scores_out, w, ws, stream, fs);     \
+                                      idx_cap, cnt_out, block_scores_out, w, ws, stream, fs, K,   \
+                                      lens_prev);                                                 \
         break;
         switch (G) {
             SA_SOFTMAX_CASE(1)

@@ -178,14 +178,12 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
                            cnt_out, nullptr, workspace, hs, K, lens_prev, fsp, max_new_tokens);
     } else {
-        // every entry enters the softmax denominators: append first
-        if (max_new_tokens > 0) {
-            st = launch_compress(K, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_prev, lens_now,
-                                 max_new_tokens / kCmpStride + 2, hs);
-            if (st) return st;
-        }
+        // the scorer forms the new entries itself (they enter every head's
+        // softmax denominator in the order a separate append would give) and
+        // writes them to Kc
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
-                           cnt_out, nullptr, workspace, hs, nullptr, nullptr, fsp);
+                           cnt_out, nullptr, workspace, hs, max_new_tokens > 0 ? K : nullptr,
+                           max_new_tokens > 0 ? lens_prev : nullptr, fsp);
     }
     if (st) return st;
     if (fused)

@@ -201,8 +201,10 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  * In RAW_SUM mode the append runs inside the scoring launch: the scorer reads
  * the entries that existed at lens_prev from Kc and forms any newer entry it
  * needs from K with the same arithmetic, while workgroups of the same launch
- * write the new entries to Kc. In SOFTMAX_SUM mode the new entries
- * enter every head's softmax denominator, so the append runs first.
+ * write the new entries to Kc. In SOFTMAX_SUM mode the workgroup that owns
+ * a new entry forms it from K after the entries it read from Kc, scores it
+ * (so every head's running max / sum sees the same values in the same order
+ * as after a separate append) and writes it to Kc.
  * With at most 2048 blocks (T_cap <= 131072), idx_cap <= 1024 and, in
  * SOFTMAX_SUM mode, at most 4 selector heads per KV head, there is no
  * separate top-k launch: every attention workgroup of a (b, kvh) takes that
@@ -212,9 +214,8 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  *
  *   Q [B, Hq, d]; sel [B, H_sel, d]; K, V [B, Hkv, T_cap, d]; Kc [B, Hkv,
  *   nc_cap, d] (updated in place); lens_prev, lens_now device int32 [B];
- *   max_new_tokens host hint: an upper bound on lens_now - lens_prev (sizes
- *   the append: in SOFTMAX_SUM mode the separate append launch, 0 = no
- *   append; in RAW_SUM mode, up to 16 with bf16 keys, each unit's first
+ *   max_new_tokens host hint: an upper bound on lens_now - lens_prev (0 =
+ *   no append; in RAW_SUM mode, up to 16 with bf16 keys, each unit's first
  *   scoring workgroup writes the at most one new entry instead of an extra
  *   column of workgroups);
  *   idx_out / cnt_out as in sparse_attn_select; O / lse_out as in
