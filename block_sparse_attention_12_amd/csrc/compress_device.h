@@ -98,8 +98,8 @@ __device__ __forceinline__ void entry_from_rows(const uint4 (*rows)[16], int lan
     float a[8], b[8], e[8];
     unpack(Raw8<bf16_t>{rows[0][lane16]}, a);
     unpack(Raw8<bf16_t>{rows[kCmpStride][lane16]}, b);
-#pragma unroll
-    for (int t = 1; t < kCmpStride; ++t) {
+#pragma unroll 3
+    for (int t = 1; t < kCmpStride; ++t) {     // partial unroll: few rows live at once
         float x[8], y[8];
         unpack(Raw8<bf16_t>{rows[t][lane16]}, x);
         unpack(Raw8<bf16_t>{rows[kCmpStride + t][lane16]}, y);
