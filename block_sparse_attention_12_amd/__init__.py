@@ -180,11 +180,62 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _dev(t: torch.Tensor, name: str) -> int:
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
     if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+        raise ValueError(f"{name} must be dense row-major (contiguous): the C ABI takes no strides")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
     return t.data_ptr()
+
+
+def _expect(t, name: str, shape=None, dtype=None):
+    """Raises ValueError unless t is a tensor of the given shape (None entries
+    are free) and dtype (one dtype or a tuple of allowed ones)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be dense row-major (contiguous): the C ABI takes no strides")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w)
+                                        for g, w in zip(t.shape, shape)):
+            want = "[" + ", ".join("*" if w is None else str(int(w)) for w in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+    if dtype is not None:
+        allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in allowed:
+            raise ValueError(f"{name} must have dtype {' or '.join(str(a) for a in allowed)}, "
+                             f"got {t.dtype}")
+
+
+_FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _check_kv(K, V, names=("K", "V")):
+    """K, V [B, Hkv, T_cap, d] of one floating dtype; returns (B, Hkv, T_cap, d)."""
+    _expect(K, names[0], (None, None, None, None), _FLOAT)
+    if V is not None:
+        _expect(V, names[1], tuple(K.shape), K.dtype)
+    return tuple(int(x) for x in K.shape)
+
+
+def _check_sets(idx, cnt, B, Hkv):
+    if idx is not None:
+        _expect(idx, "idx", (B, Hkv, None), torch.int32)
+    if cnt is not None:
+        _expect(cnt, "cnt", (B, Hkv), torch.int32)
+
+
+def _check_out(O, lse, rows, Hq, d):
+    if O is not None:
+        _expect(O, "O", (rows, Hq, d), _FLOAT)
+    if lse is not None:
+        _expect(lse, "lse", (rows, Hq), torch.float32)
+
+
+def _check_lens(B, **lens):
+    for name, t in lens.items():
+        _expect(t, name, (B,), torch.int32)
 
 
 def _opt(t: Optional[torch.Tensor], name: str):
@@ -213,6 +264,7 @@ def compress(K: torch.Tensor, Kc: torch.Tensor, lens_prev: torch.Tensor, lens_no
     nc_cap = Kc.shape[2]
     if Kc.dtype != K.dtype or Kc.shape[:2] != K.shape[:2] or Kc.shape[3] != d:
         raise ValueError("Kc must be [B, Hkv, nc_cap, d] with K's dtype")
+    _check_lens(B, lens_prev=lens_prev, lens_now=lens_now)
     if max_new_entries is None:
         max_new_entries = n_compressed(T_cap)
     st = lib().sparse_attn_compress(_dev(K, "K"), _dev(Kc, "Kc"), _dtype_code(K), B, Hkv, d, T_cap,
@@ -234,11 +286,17 @@ def select(sel: torch.Tensor, Kc: torch.Tensor, seq_lens: torch.Tensor, T_cap: i
            block_scores: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream=None):
     """Block selection for every (sequence, KV head). Returns (idx, cnt, block_scores)."""
-    B, H_sel, d = sel.shape
-    _, Hkv, nc_cap, _ = Kc.shape
+    _expect(Kc, "Kc", (None, None, None, None), _FLOAT)
+    B, Hkv, nc_cap, d = Kc.shape
+    _expect(sel, "sel", (B, None, d), Kc.dtype)
+    H_sel = sel.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
     p = make_params(top_k, n_init, n_local, score_mode)
     cap = top_k + n_init + n_local
     dev = sel.device
+    _check_sets(idx, cnt, B, Hkv)
+    if isinstance(block_scores, torch.Tensor):
+        _expect(block_scores, "block_scores", (B, Hkv, None), torch.float32)
     if idx is None:
         idx = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
     if cnt is None:
@@ -271,8 +329,13 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Te
            lse: Optional[torch.Tensor] = None, want_lse: bool = True, n_split: int = 0,
            workspace: Optional[torch.Tensor] = None, stream=None):
     """Sparse decode attention over the selected blocks. Returns (O, lse)."""
-    B, Hq, d = Q.shape
-    _, Hkv, T_cap, _ = K.shape
+    B, Hkv, T_cap, d = _check_kv(K, V)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    Hq = Q.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
+    _expect(idx, "idx", (B, Hkv, None), torch.int32)
+    _expect(cnt, "cnt", (B, Hkv), torch.int32)
+    _check_out(O, lse, B, Hq, d)
     dev = Q.device
     if O is None:
         O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
@@ -280,7 +343,7 @@ def decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Te
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = decode_workspace_size(B, Hq, Hkv, idx.shape[-1], n_split)
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)   # merge counters start at 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().sparse_attn_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(K), B, Hq, Hkv,
                                   d, T_cap, _dev(seq_lens, "seq_lens"), _dev(idx, "idx"),
@@ -306,9 +369,15 @@ def prefill_chunk(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tenso
                   scale: float = 1.0, out_dtype=torch.float32, O=None, lse=None, want_lse=True,
                   tile_idx=None, tile_cnt=None, workspace=None, stream=None):
     """Tile-shared sparse causal prefill of one chunk. Returns (O, lse, tile_idx, tile_cnt)."""
-    Tq, Hq, d = Q.shape
-    Hkv, T_cap = K.shape[-3], K.shape[-2]
+    K3 = K.reshape(K.shape[-3:]) if K.dim() == 4 and K.shape[0] == 1 else K
+    _expect(K3, "K", (None, None, None), _FLOAT)
+    Hkv, T_cap, d = K3.shape
+    _expect(V, "V", tuple(K.shape), K.dtype)
+    _expect(Q, "Q", (None, None, d), K.dtype)
+    Tq, Hq = Q.shape[0], Q.shape[1]
+    _expect(Kc, "Kc", tuple(K.shape[:-2]) + (None, d), K.dtype)
     nc_cap = Kc.shape[-2]
+    _check_out(O, lse, Tq, Hq, d)
     p = make_params(top_k, n_init, n_local, score_mode)
     dev = Q.device
     n_tiles = (Tq + 63) // 64
@@ -321,6 +390,8 @@ def prefill_chunk(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tenso
         tile_idx = torch.empty((n_tiles, Hkv, cap), dtype=torch.int32, device=dev)
     if tile_cnt is None:
         tile_cnt = torch.empty((n_tiles, Hkv), dtype=torch.int32, device=dev)
+    _expect(tile_idx, "tile_idx", (n_tiles, Hkv, None), torch.int32)
+    _expect(tile_cnt, "tile_cnt", (n_tiles, Hkv), torch.int32)
     need = prefill_workspace_size(Hq, Hkv, q_start, Tq, p)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -339,8 +410,16 @@ def prefill_attend(Q: torch.Tensor, q_start: int, K: torch.Tensor, V: torch.Tens
                    tile_idx: torch.Tensor, tile_cnt: torch.Tensor, scale: float = 1.0,
                    out_dtype=torch.float32, O=None, lse=None, want_lse=True, stream=None):
     """Causal attention of a prefill chunk over given tile block sets. Returns (O, lse)."""
-    Tq, Hq, d = Q.shape
-    Hkv, T_cap = K.shape[-3], K.shape[-2]
+    K3 = K.reshape(K.shape[-3:]) if K.dim() == 4 and K.shape[0] == 1 else K
+    _expect(K3, "K", (None, None, None), _FLOAT)
+    Hkv, T_cap, d = K3.shape
+    _expect(V, "V", tuple(K.shape), K.dtype)
+    _expect(Q, "Q", (None, None, d), K.dtype)
+    Tq, Hq = Q.shape[0], Q.shape[1]
+    n_tiles = (Tq + 63) // 64
+    _expect(tile_idx, "tile_idx", (n_tiles, Hkv, None), torch.int32)
+    _expect(tile_cnt, "tile_cnt", (n_tiles, Hkv), torch.int32)
+    _check_out(O, lse, Tq, Hq, d)
     dev = Q.device
     if O is None:
         O = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
@@ -374,8 +453,17 @@ def block_mass(Q: torch.Tensor, K: torch.Tensor, seq_lens: torch.Tensor, scale: 
                workspace: Optional[torch.Tensor] = None, stream=None):
     """Exact attention mass per 64-token block of each head's decode query, and
     the recall of (idx, cnt) if given. Returns (mass [B, Hq, nb], recall or None)."""
-    B, Hq, d = Q.shape
-    Hkv, T_cap = K.shape[1], K.shape[2]
+    B, Hkv, T_cap, d = _check_kv(K, None)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    Hq = Q.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
+    if idx is not None or cnt is not None:
+        _expect(idx, "idx", (B, Hkv, None), torch.int32)
+        _expect(cnt, "cnt", (B, Hkv), torch.int32)
+    if mass is not None:
+        _expect(mass, "mass", (B, Hq, None), torch.float32)
+    if recall is not None:
+        _expect(recall, "recall", (B, Hq), torch.float32)
     nb = n_blocks(T_cap)
     if mass is None:
         mass = torch.empty((B, Hq, nb), dtype=torch.float32, device=Q.device)
@@ -405,8 +493,13 @@ def token_select(sel: torch.Tensor, Ki: torch.Tensor, seq_lens: torch.Tensor, to
                  workspace: Optional[torch.Tensor] = None, stream=None):
     """Token-level index per (sequence, KV head): kept initial/local tokens and
     the top_k scored tokens, ascending. Returns (idx, cnt, scores or None)."""
-    B, H_sel, d_i = sel.shape
-    _, Hkv, T_cap, _ = Ki.shape
+    B, Hkv, T_cap, d_i = _check_kv(Ki, None, ("Ki", ""))
+    _expect(sel, "sel", (B, None, d_i), Ki.dtype)
+    H_sel = sel.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
+    _check_sets(idx, cnt, B, Hkv)
+    if isinstance(scores, torch.Tensor):
+        _expect(scores, "scores", (B, Hkv, T_cap), torch.float32)
     dev = sel.device
     if idx is None:
         idx = torch.empty((B, Hkv, top_k + n_init + n_local), dtype=torch.int32, device=dev)
@@ -438,8 +531,13 @@ def token_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: to
                  lse: Optional[torch.Tensor] = None, want_lse: bool = True, n_split: int = 0,
                  workspace: Optional[torch.Tensor] = None, stream=None):
     """Sparse decode attention over token lists (gathered rows). Returns (O, lse)."""
-    B, Hq, d = Q.shape
-    _, Hkv, T_cap, _ = K.shape
+    B, Hkv, T_cap, d = _check_kv(K, V)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    Hq = Q.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
+    _expect(idx, "idx", (B, Hkv, None), torch.int32)
+    _expect(cnt, "cnt", (B, Hkv), torch.int32)
+    _check_out(O, lse, B, Hq, d)
     dev = Q.device
     if O is None:
         O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
@@ -469,6 +567,7 @@ def cobs_stats(K: torch.Tensor, stats: torch.Tensor, lens_prev: torch.Tensor, le
     nb_cap = stats.shape[2]
     if stats.dtype != K.dtype or stats.shape[:2] != K.shape[:2] or stats.shape[3:] != (2, d):
         raise ValueError("stats must be [B, Hkv, nb_cap, 2, d] with K's dtype")
+    _check_lens(B, lens_prev=lens_prev, lens_now=lens_now)
     if max_new_blocks is None:
         max_new_blocks = nb_cap
     st = lib().sparse_attn_cobs_stats(_dev(K, "K"), _dev(stats, "stats"), _dtype_code(K), B, Hkv, d,
@@ -489,8 +588,14 @@ def cobs_select(sel: torch.Tensor, stats: torch.Tensor, seq_lens: torch.Tensor, 
                 block_scores=None, workspace: Optional[torch.Tensor] = None, stream=None):
     """Block selection by the first- or second-order block-mass estimate.
     Returns (idx, cnt, block_scores or None)."""
-    B, H_sel, d = sel.shape
-    Hkv, nb_cap = stats.shape[1], stats.shape[2]
+    _expect(stats, "stats", (None, None, None, 2, None), _FLOAT)
+    B, Hkv, nb_cap, _, d = stats.shape
+    _expect(sel, "sel", (B, None, d), stats.dtype)
+    H_sel = sel.shape[1]
+    _check_lens(B, seq_lens=seq_lens)
+    _check_sets(idx, cnt, B, Hkv)
+    if isinstance(block_scores, torch.Tensor):
+        _expect(block_scores, "block_scores", (B, Hkv, None), torch.float32)
     p = make_params(top_k, n_init, n_local, score_mode)
     dev = sel.device
     if idx is None:
@@ -528,9 +633,14 @@ def cobs_decode_step(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: tor
                      n_split: int = 0, workspace=None, stream=None):
     """Statistics append + selection by block statistics + decode attention in
     one call. Returns (O, lse, idx, cnt)."""
-    B, Hq, d = Q.shape
-    _, H_sel, _ = sel.shape
-    _, Hkv, T_cap, _ = K.shape
+    B, Hkv, T_cap, d = _check_kv(K, V)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    _expect(sel, "sel", (B, None, d), K.dtype)
+    _expect(stats, "stats", (B, Hkv, None, 2, d), K.dtype)
+    Hq, H_sel = Q.shape[1], sel.shape[1]
+    _check_lens(B, lens_prev=lens_prev, lens_now=lens_now)
+    _check_sets(idx, cnt, B, Hkv)
+    _check_out(O, lse, B, Hq, d)
     nb_cap = stats.shape[2]
     p = make_params(top_k, n_init, n_local, score_mode)
     dev = Q.device
@@ -574,9 +684,14 @@ def decode_step(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: torch.Te
                 max_new_tokens: int = 1, idx=None, cnt=None, O=None, lse=None, want_lse=True,
                 out_dtype=torch.float32, n_split: int = 0, workspace=None, stream=None):
     """Append + select + decode attention in one call. Returns (O, lse, idx, cnt)."""
-    B, Hq, d = Q.shape
-    _, H_sel, _ = sel.shape
-    _, Hkv, T_cap, _ = K.shape
+    B, Hkv, T_cap, d = _check_kv(K, V)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    _expect(sel, "sel", (B, None, d), K.dtype)
+    _expect(Kc, "Kc", (B, Hkv, None, d), K.dtype)
+    Hq, H_sel = Q.shape[1], sel.shape[1]
+    _check_lens(B, lens_prev=lens_prev, lens_now=lens_now)
+    _check_sets(idx, cnt, B, Hkv)
+    _check_out(O, lse, B, Hq, d)
     nc_cap = Kc.shape[2]
     p = make_params(top_k, n_init, n_local, score_mode)
     dev = Q.device

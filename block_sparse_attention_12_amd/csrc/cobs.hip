@@ -9,17 +9,19 @@
 // per-channel variance (the diagonal of Sigma_B), so a block's estimate is
 //   q . mu_B + 1/2 sum_c q_c^2 var_{B,c}      (log 64 is common and dropped).
 //
-// Statistics (per complete 64-token block, in the key dtype): with P_j the
-// fp32 sum of keys 16j .. 16j+15 in token order, mu32 = (((P_0 + P_1) + P_2)
-// + P_3) * 2^-6; var likewise from the quarter sums of (k - mu32)^2; both
-// rounded to the key dtype. The file is built with -ffp-contract=off, so both
-// are one exact value, reproducible on a CPU. Layout [B, Hkv, nb_cap, 2, d]:
-// mean row, then variance row.
+// Statistics (per complete 64-token block, in the key dtype): the fp64 mean
+// and population variance of each channel over the block's 64 keys, each
+// rounded once (to nearest, ties to even) to the key dtype. fp64 sums of 64
+// bf16 or fp32 keys of ordinary range are exact, and the variance's are
+// within about 2^-46 relative, so the stored values are those of the plain
+// definition up to one unit in the last place (in practice identical).
+// Layout [B, Hkv, nb_cap, 2, d]: mean row, then variance row.
 //
 // Kernels (HBM or latency bound; no matrix cores):
 //   cobs_stats_kernel    four 16-lane row groups per block (one per quarter of
 //                        16 keys), 8 channels per lane; the keys stay in
-//                        registers for both passes, partial sums meet in LDS
+//                        registers for both passes, fp64 partial sums meet in
+//                        LDS
 //   cobs_score_kernel    one row group per block: the group's estimates for
 //                        every selector head (fp32; bf16 mean terms by dot2
 //                        products), reduced over the 16 lanes; exponentials on
@@ -67,17 +69,37 @@ CobsWorkspace cobs_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int sc
 
 // ---------------------------------------------------------------- statistics
 
+// fp64 -> key dtype, one rounding to nearest with ties to even. bf16 keeps 8
+// significant bits with fp32's exponent range: the spacing of bf16 values
+// near x is 2^(e - 7) for 2^e <= |x| < 2^(e+1), and 2^-133 below 2^-126; x is
+// scaled by the inverse spacing (exact), rounded to an integer (rint: ties to
+// even) and scaled back, which is then exactly a bf16 value (or past the
+// largest, which the fp32 conversion turns into an infinity).
+__device__ __forceinline__ float round_once_key(double x, float *) { return (float)x; }
+__device__ __forceinline__ float round_once_key(double x, bf16_t *) {
+    int e = ilogb(x);
+    e = (e < -126 ? -126 : e) - 7;
+    return (float)ldexp(rint(ldexp(x, -e)), e);
+}
+template <typename T>
+__device__ __forceinline__ void store_once(T *p, const double (&x)[8]) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = round_once_key(x[e], (T *)nullptr);
+    store8(p, f);                           // exact: each value is already one of T
+}
+
 // Four row groups per block, one per quarter (16 consecutive keys); each keeps
-// its 16 keys in registers, so the block is read once. Quarter sums and
-// quarter sums of squared deviations meet in LDS and are combined in quarter
-// order by every group alike.
+// its 16 keys in registers, so the block is read once. Quarter sums (fp64)
+// meet in LDS and give the block mean; then the quarter sums of squared
+// deviations from it meet the same way.
 constexpr int kStatsBlocksPerWG = kCobsGroups / 4;
 
 template <typename T>
 __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
     const T *__restrict__ K, T *__restrict__ stats, int64_t T_cap, int64_t nb_cap,
     const int32_t *__restrict__ lens_prev, const int32_t *__restrict__ lens_now, int Hkv) {
-    __shared__ float s_part[kStatsBlocksPerWG][4][kRowLanes][8];
+    __shared__ double s_part[kStatsBlocksPerWG][4][kRowLanes][8];
     const int unit = blockIdx.y;
     const int b = unit / Hkv;
     const int lane16 = threadIdx.x & (kRowLanes - 1), group = threadIdx.x / kRowLanes;
@@ -88,30 +110,27 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
     const bool valid = blk < hi && blk < nb_cap;            // uniform per row group
     const T *src = K + ((int64_t)unit * T_cap + blk * kBlock + quarter * 16) * kD + lane16 * kLaneElems;
     Raw8<T> r[16];
-    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    double p[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
     if (valid) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) load_raw(src + (int64_t)t * kD, r[t]);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {                      // quarter sum, token order
+        for (int t = 0; t < 16; ++t) {
             float x[8];
             unpack(r[t], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) p[e] = p[e] + x[e];
+            for (int e = 0; e < 8; ++e) p[e] += (double)x[e];
         }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) s_part[slot][quarter][lane16][e] = p[e];
     __syncthreads();
-    float m[8];
+    double m[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float t = s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e];
-        t = t + s_part[slot][2][lane16][e];
-        t = t + s_part[slot][3][lane16][e];
-        m[e] = t * 0.015625f;                               // 2^-6, exact
-    }
-    float q[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 8; ++e)
+        m[e] = ((s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e]) +
+                (s_part[slot][2][lane16][e] + s_part[slot][3][lane16][e])) * 0.015625;   // 2^-6, exact
+    double q[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
     if (valid) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -119,8 +138,8 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
             unpack(r[t], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float dv = x[e] - m[e];
-                q[e] = q[e] + dv * dv;
+                const double dv = (double)x[e] - m[e];
+                q[e] += dv * dv;
             }
         }
     }
@@ -129,17 +148,14 @@ __global__ __launch_bounds__(kCobsThreads) void cobs_stats_kernel(
     for (int e = 0; e < 8; ++e) s_part[slot][quarter][lane16][e] = q[e];
     __syncthreads();
     if (!valid || quarter != 0) return;
-    float v[8];
+    double v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float t = s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e];
-        t = t + s_part[slot][2][lane16][e];
-        t = t + s_part[slot][3][lane16][e];
-        v[e] = t * 0.015625f;
-    }
+    for (int e = 0; e < 8; ++e)
+        v[e] = ((s_part[slot][0][lane16][e] + s_part[slot][1][lane16][e]) +
+                (s_part[slot][2][lane16][e] + s_part[slot][3][lane16][e])) * 0.015625;
     T *dst = stats + ((int64_t)unit * nb_cap + blk) * 2 * kD + lane16 * kLaneElems;
-    store8(dst, m);
-    store8(dst + kD, v);
+    store_once(dst, m);
+    store_once(dst + kD, v);
 }
 
 // ---------------------------------------------------------------- scores

@@ -40,8 +40,9 @@
 //                         init and local.
 //   prefill_union_kernel  per (tile, KV head): union of its 64 queries' sets.
 //   prefill_attn_kernel   per (tile, KV head): causal attention over the union,
-//                         blocks staged through a 2-stage LDS ring (loads of
-//                         the next block in registers during the current one),
+//                         blocks staged through a 3-stage LDS ring (loads of
+//                         the block after next in registers during the current
+//                         one),
 //                         softmax in fp32, P rounded to bf16 for the value
 //                         product, fp32 accumulation.
 // Workgroups are numbered tile * Hkv + kvh so the tiles of one KV head land on

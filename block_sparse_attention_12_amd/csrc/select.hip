@@ -242,14 +242,24 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
             }
         }
     }
-    // kAppendInFirst (bf16, at most one new entry per unit): after its own
-    // blocks, the unit's first workgroup loads the new entry's 32 keys (two per
-    // row group, all in flight at once), stages them in LDS and one row group
-    // sums them in token order. (Loads issued before the main loop, under a
-    // condition, cost the loop its exact wait counts.)
+    // kAppendInFirst (bf16, chosen when the caller expects at most one new
+    // entry per unit): after its own blocks, the unit's first workgroup loads
+    // the new entry's 32 keys (two per row group, all in flight at once),
+    // stages them in LDS and one row group sums them in token order. (Loads
+    // issued before the main loop, under a condition, cost the loop its exact
+    // wait counts.) If the length grew by more than expected, the workgroup
+    // forms every new entry one row group at a time, so Kc never has gaps.
     constexpr bool kInFirst = APPEND && sizeof(T) == 2;
     if constexpr (kInFirst) {
-        if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old < nc) {   // uniform per workgroup
+        if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old + 1 < nc) {   // uniform
+            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+            T *Kcu = Kc_w + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
+            for (int64_t j = nc_old + group; j < nc; j += 16) {
+                Raw8<T> r;
+                compress_entry_raw(Ku, j, r);
+                store_raw(Kcu + j * kD, r);
+            }
+        } else if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old < nc) {
             __shared__ uint4 s_rows[2 * kCmpStride][16];
             const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
             Raw8<T> app_rows[2];

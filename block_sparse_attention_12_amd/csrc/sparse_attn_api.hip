@@ -13,6 +13,12 @@ namespace {
 
 bool dtype_ok(int dt) { return dt == SA_F32 || dt == SA_BF16; }
 
+// query heads per KV head the decode attention kernels are built for
+bool attn_group_ok(int Hq, int Hkv) {
+    const int G = Hq / Hkv;
+    return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
 int check_params(const sa_select_params *p) {
     if (!p) return SA_ERR_INVALID_ARG;
     if (p->top_k < 0 || p->n_init < 0 || p->n_local < 0) return SA_ERR_INVALID_ARG;
@@ -108,7 +114,7 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
         return SA_ERR_INVALID_ARG;
     if (Hq % Hkv) return SA_ERR_INVALID_ARG;
     if (!(scale == scale)) return SA_ERR_INVALID_ARG;
-    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (d != kD || !attn_group_ok(Hq, Hkv)) return SA_ERR_UNSUPPORTED;
     if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
     if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
@@ -153,7 +159,7 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
     if (st) return st;
     if (Hq % Hkv || H_sel % Hkv || !(scale == scale)) return SA_ERR_INVALID_ARG;
     const int G = H_sel / Hkv;
-    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (d != kD || !attn_group_ok(Hq, Hkv)) return SA_ERR_UNSUPPORTED;
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
     if (n_blocks(T_cap) > 32768 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
     if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
@@ -182,8 +188,7 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
         // softmax denominator in the order a separate append would give) and
         // writes them to Kc
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
-                           cnt_out, nullptr, workspace, hs, max_new_tokens > 0 ? K : nullptr,
-                           max_new_tokens > 0 ? lens_prev : nullptr, fsp);
+                           cnt_out, nullptr, workspace, hs, K, lens_prev, fsp);
     }
     if (st) return st;
     if (fused)
@@ -299,7 +304,7 @@ int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dt
         return SA_ERR_INVALID_ARG;
     if (Hq % Hkv) return SA_ERR_INVALID_ARG;
     if (!(scale == scale)) return SA_ERR_INVALID_ARG;
-    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (d != kD || !attn_group_ok(Hq, Hkv)) return SA_ERR_UNSUPPORTED;
     const int32_t tiles = (int32_t)(((int64_t)idx_cap + 63) / 64);
     if (n_split > kMaxSplit || tiles > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
     if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
@@ -385,7 +390,7 @@ int sparse_attn_cobs_decode_step(const void *Q, const void *sel, int H_sel, cons
     if (Hq % Hkv || H_sel % Hkv || (order != 1 && order != 2) || !(scale == scale))
         return SA_ERR_INVALID_ARG;
     const int G = H_sel / Hkv;
-    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (d != kD || !attn_group_ok(Hq, Hkv)) return SA_ERR_UNSUPPORTED;
     if (!(G == 1 || G == 2 || G == 4 || G == 8)) return SA_ERR_UNSUPPORTED;
     if (n_blocks(T_cap) > 32768 || (int64_t)B * Hkv > 65535) return SA_ERR_UNSUPPORTED;
     if (n_split > kMaxSplit || idx_cap > 64 * kMaxSplit) return SA_ERR_UNSUPPORTED;
@@ -436,7 +441,7 @@ int sparse_attn_block_mass(const void *Q, const void *K, int dtype, int B, int H
     if (!dtype_ok(dtype) || B <= 0 || Hq <= 0 || Hkv <= 0 || T_cap <= 0) return SA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0 || !(scale == scale)) return SA_ERR_INVALID_ARG;
     if (idx && (!cnt || !recall_out || idx_cap <= 0)) return SA_ERR_INVALID_ARG;
-    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;
+    if (d != kD || Hq / Hkv != 4) return SA_ERR_UNSUPPORTED;       // measurement kernel: G = 4
     if (T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     if (mass_cap < n_blocks(T_cap)) return SA_ERR_CAPACITY;
     if (!workspace || ws_bytes < block_mass_workspace_bytes(B, Hq, mass_cap)) return SA_ERR_WORKSPACE;

@@ -38,6 +38,7 @@
 
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "tok_positions.h"
 
 namespace sa {
 
@@ -85,8 +86,8 @@ __device__ __forceinline__ TokWindows tok_windows(int64_t L, int top_k, int n_in
 
 // Wave 0 finds the bin of the 256-bin LDS histogram s_h that holds the
 // `remaining`-th largest counted key (bins scanned from the top), the number
-// of keys in the bins above it and the bin's own count; every thread reads
-// them after the barrier.
+// of keys in the bins above it and the bin's own count (tok_digit_seq states
+// the same search sequentially); every thread reads them after the barrier.
 __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, uint32_t *s_digit,
                                           uint32_t *s_above, uint32_t *s_bcnt) {
     const int tid = threadIdx.x;
@@ -97,19 +98,19 @@ __device__ __forceinline__ void tok_digit(const uint32_t *s_h, int remaining, ui
             *s_bcnt = 0xffffffffu;
         }
         const uint32_t hb[4] = {s_h[4 * tid], s_h[4 * tid + 1], s_h[4 * tid + 2], s_h[4 * tid + 3]};
-        const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
-        uint32_t incl = c;
+        const uint64_t c = (uint64_t)hb[0] + hb[1] + hb[2] + hb[3];
+        uint64_t incl = c;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_down(incl, off, 64);
+            const uint64_t t = __shfl_down(incl, off, 64);
             if (tid + off < 64) incl += t;
         }
-        uint32_t above = incl - c;
+        uint64_t above = incl - c;                   // keys in bins owned by higher lanes
 #pragma unroll
         for (int k = 3; k >= 0; --k) {
-            if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
+            if (tok_bin_holds(above, hb[k], remaining)) {   // at most one bin of the whole wave
                 *s_digit = 4 * tid + k;
-                *s_above = above;
+                *s_above = (uint32_t)above;
                 *s_bcnt = hb[k];
             }
             above += hb[k];
@@ -138,8 +139,7 @@ __device__ __forceinline__ void tok_prefix(const uint32_t *hist_unit, int64_t hi
         const int shift = 24 - 8 * p;
         prefix |= *s_digit << shift;
         mask |= 255u << shift;
-        remaining -= (int)*s_above;
-        remaining = remaining < 0 ? 0 : remaining;
+        remaining = tok_remaining_after(remaining, *s_above);
         const bool done = *s_bcnt == (uint32_t)remaining;              // same on every thread
         __syncthreads();                                               // s_h and the scalars reused
         if (done) {
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     const int32_t *__restrict__ counts, int n_chunks, const uint32_t *__restrict__ info,
     int32_t *__restrict__ idx_out, int idx_cap, int32_t *__restrict__ cnt_out) {
     __shared__ int s_wave[kTokThreads / 64];
-    __shared__ int s_red[2][kTokThreads / 64];
+    __shared__ int64_t s_red[2][kTokThreads / 64];
     const int unit = blockIdx.y;
     const int b = unit / Hkv;
     const int tid = threadIdx.x;
@@ -394,14 +394,13 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     const int n_used = (int)((w.L + kTokChunk - 1) / kTokChunk);
     const uint32_t thr = w.choose ? info[unit * 4] : 0u;
     const uint32_t mask = w.choose ? info[unit * 4 + 2] : 0xffffffffu;
-    int take_eq = w.choose ? (int)info[unit * 4 + 1] : 0;
-    take_eq = take_eq < 0 ? 0 : take_eq;
+    const int take_eq = w.choose ? tok_take_eq(info[unit * 4 + 1]) : 0;
     int32_t *row = idx_out + (int64_t)unit * idx_cap;
     const int32_t *cu = counts + (int64_t)unit * n_chunks * 2;
 
     // sums over chunks [0, upto) of the surely-taken and the equal-key counts
-    auto chunk_sums = [&](int upto, int &sure, int &eq) {
-        int a = 0, e = 0;
+    auto chunk_sums = [&](int upto, int64_t &sure, int64_t &eq) {
+        int64_t a = 0, e = 0;
         for (int c = tid; c < upto; c += kTokThreads) {
             a += cu[2 * c];
             e += cu[2 * c + 1];
@@ -425,15 +424,14 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
         __syncthreads();
     };
     if (blockIdx.x == 0) {                                   // count and padding of the row
-        int sure, eq;
+        int64_t sure, eq;
         chunk_sums(n_used, sure, eq);
-        int total = sure + (eq < take_eq ? eq : take_eq);
-        total = total < 0 ? 0 : (total < idx_cap ? total : idx_cap);
+        const int total = tok_row_total(sure, eq, take_eq, idx_cap);
         for (int i = total + tid; i < idx_cap; i += kTokThreads) row[i] = -1;
         if (tid == 0) cnt_out[unit] = total;
     }
     if (t0 >= w.L) return;
-    int sure_before, eq_before;
+    int64_t sure_before, eq_before;
     chunk_sums((int)blockIdx.x, sure_before, eq_before);
     uint32_t key[kTokPer];
     bool cand[kTokPer];
@@ -444,7 +442,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
     for (int i = 0; i < kTokPer; ++i)
         n_eq += (w.choose && tb + i < w.L && cand[i] && (key[i] & mask) == thr) ? 1 : 0;
     int unused;
-    int eq_rank = eq_before + wg_exclusive_scan<kTokThreads>(n_eq, s_wave, unused);
+    int64_t eq_rank = eq_before + wg_exclusive_scan<kTokThreads>(n_eq, s_wave, unused);
     bool in[kTokPer];
     int n_in = 0;
 #pragma unroll
@@ -461,12 +459,12 @@ __global__ __launch_bounds__(kTokThreads) void tok_write_kernel(
         in[i] = x;
         n_in += x ? 1 : 0;
     }
-    const int taken_eq_before = eq_before < take_eq ? eq_before : take_eq;
-    int pos = sure_before + taken_eq_before + wg_exclusive_scan<kTokThreads>(n_in, s_wave, unused);
+    int64_t pos = tok_first_pos(sure_before, eq_before, take_eq,
+                                wg_exclusive_scan<kTokThreads>(n_in, s_wave, unused));
 #pragma unroll
     for (int i = 0; i < kTokPer; ++i)
         if (in[i]) {
-            if (pos >= 0 && pos < idx_cap) row[pos] = (int32_t)(tb + i);
+            if (tok_slot_ok(pos, idx_cap)) row[pos] = (int32_t)(tb + i);
             ++pos;
         }
 }

@@ -18,7 +18,11 @@
  *    The library never allocates or frees memory; scratch memory is a
  *    caller-provided device workspace whose size the *_workspace_size
  *    functions return (0 means no workspace is needed; then it may be NULL).
- *  - Tensors are dense, row-major, innermost dimension last:
+ *  - Tensors are dense, row-major, innermost dimension last (the ABI takes
+ *    no strides: every kernel addresses a (sequence, KV head) slice as one
+ *    contiguous [T_cap, d] window through a single buffer resource whose
+ *    hardware range check bounds every access; callers with strided caches
+ *    pass a dense copy or a dense per-layer allocation):
  *      K, V  [B, Hkv, T_cap, d]     (prefill: B = 1)
  *      Kc    [B, Hkv, nc_cap, d]    compressed keys, same dtype as K
  *      Q     [B, Hq, d] (decode) or [Tq, Hq, d] (prefill chunk of one sequence)
@@ -29,7 +33,9 @@
  *    Arithmetic is fp32 (products, sums, softmax), outputs O are fp32 or bf16
  *    (out_dtype), log-sum-exp outputs are fp32 natural logarithms.
  *  - GQA: G = Hq / Hkv query heads share a KV head; query head h uses KV head
- *    h / G. Hq must be a multiple of Hkv.
+ *    h / G. Hq must be a multiple of Hkv. Decode attention (sparse_attn_decode,
+ *    the decode steps, sparse_attn_token_decode) takes G in {1, 2, 4, 8};
+ *    prefill and the block-mass measurement take G = 4.
  *  - seq_lens is a DEVICE int32 array [B]: the visible length L of each
  *    sequence, 0 <= L <= T_cap. Kernels clamp values outside that range into
  *    it so that no access leaves the tensors; the results are then undefined.
@@ -177,8 +183,8 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap
  *   workspace  required when the split count is above 1: the split
  *              partials (fp32), merged by a second kernel on the same stream.
  * A (b, kvh) with cnt = 0 yields O = 0 and LSE = -inf.
- * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4,
- *         n_split > 64, idx_cap > 4096, one (b, kvh) cache slice of
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G not 1, 2, 4
+ *         or 8, n_split > 64, idx_cap > 4096, one (b, kvh) cache slice of
  *         T_cap * d elements taking 2 GiB or more),
  *         SA_ERR_WORKSPACE.
  */
@@ -214,10 +220,12 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  *
  *   Q [B, Hq, d]; sel [B, H_sel, d]; K, V [B, Hkv, T_cap, d]; Kc [B, Hkv,
  *   nc_cap, d] (updated in place); lens_prev, lens_now device int32 [B];
- *   max_new_tokens host hint: an upper bound on lens_now - lens_prev (0 =
- *   no append; in RAW_SUM mode, up to 16 with bf16 keys, each unit's first
- *   scoring workgroup writes the at most one new entry instead of an extra
- *   column of workgroups);
+ *   max_new_tokens host hint, the expected bound on lens_now - lens_prev:
+ *   it only picks how the append is scheduled, never what is computed (in
+ *   RAW_SUM mode, up to 16 with bf16 keys, each unit's first scoring
+ *   workgroup writes the new entries instead of an extra column of
+ *   workgroups); every entry in [n_c(lens_prev), n_c(lens_now)) is written in
+ *   both modes whatever the hint;
  *   idx_out / cnt_out as in sparse_attn_select; O / lse_out as in
  *   sparse_attn_decode. Workspace: sparse_attn_decode_step_workspace_size.
  * Errors: those of the three calls it stands for.
@@ -349,8 +357,8 @@ size_t sparse_attn_token_decode_workspace_size(int B, int Hq, int Hkv, int32_t i
  *   Q [B, Hq, d], K/V [B, Hkv, T_cap, d] device; idx [B, Hkv, idx_cap] and
  *   cnt [B, Hkv] device int32; O [B, Hq, d] (out_dtype); lse_out optional
  *   [B, Hq] fp32 natural log of the softmax denominator (-inf when empty).
- * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G != 4,
- *         n_split > 64, idx_cap > 262144, a (b, kvh) cache slice of
+ * Errors: SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED (d != 128, G not 1, 2, 4
+ *         or 8, n_split > 64, idx_cap > 262144, a (b, kvh) cache slice of
  *         T_cap * d elements taking 2 GiB or more), SA_ERR_WORKSPACE.
  */
 int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,

@@ -16,7 +16,8 @@ CLSA abstract and the JSSA item) and the selection-quality measures
 (oracle.quality), and the second-order block statistic read from the COBS
 abstract (oracle.cobs, parity unpinned by the pages). Arithmetic is
 fp64 from the compressed keys onward; the compressed keys themselves are formed
-in a fixed fp32 order and rounded to the key dtype, so they are one exact value.
+in a fixed fp32 order and rounded to the key dtype, so they are one exact value;
+the second-order block statistics are fp64 mean and variance rounded once.
 
 Pinned by the tests under tests/ marked "not gpu" (closed forms, library
 special cases, invariants and brute force). Parity unpinned by the pages: which
@@ -25,7 +26,7 @@ that definition, see oracle.select), and the whole of oracle.cobs (the pages
 give no formula for the second-order statistic; pinned only by the mathematics
 of the cumulant expansion and by the first-order block path).
 """
-from .numerics import bf16_round, round_to
+from .numerics import bf16_round, round_to, round_once
 from .compress import n_compressed, n_blocks, compressed_keys, append_compressed_keys
 from .select import (SOFTMAX_SUM, RAW_SUM, entry_scores, block_scores, block_entries,
                      candidate_sets, top_k_blocks, select_blocks, SelectParams)
@@ -39,7 +40,7 @@ from .token import (token_candidates, token_scores, top_k_tokens, select_tokens,
 from .cobs import block_stats, cobs_log_mass, cobs_block_scores, select_blocks_cobs
 
 __all__ = [
-    "bf16_round", "round_to", "n_compressed", "n_blocks", "compressed_keys",
+    "bf16_round", "round_to", "round_once", "n_compressed", "n_blocks", "compressed_keys",
     "append_compressed_keys", "SOFTMAX_SUM", "RAW_SUM", "entry_scores", "block_scores",
     "block_entries", "candidate_sets", "top_k_blocks", "select_blocks", "SelectParams",
     "sparse_attention", "lse_merge", "split_attention_partials", "decode_step", "decode_unit",

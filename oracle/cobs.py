@@ -22,10 +22,13 @@ Reading:
   * statistics exist for complete 64-token blocks only (candidate blocks are
     complete whenever at least one local block is kept), so log n_B = log 64 is
     a common constant and is left out of the score;
-  * mu and var are one exact value each, in a fixed fp32 order: with P_j the
-    sum of keys 16j .. 16j+15 in token order, mu32 = (((P_0 + P_1) + P_2) +
-    P_3) * 2^-6; var the same from quarter sums of (k_t - mu32)^2; both rounded
-    to the key dtype;
+  * mu and var are the plain fp64 mean and population variance (mean of the
+    squared deviations from the fp64 mean) of each channel over the block's 64
+    keys, each rounded once, to nearest with ties to even, to the key dtype
+    (numerics.round_once). The fp64 arithmetic is exact for the mean of 64 bf16
+    or fp32 keys of ordinary range and within about 2^-46 relative for the
+    variance, far below one unit in the last place of either key dtype, so an
+    implementation that rounds an fp64 (or exact) result once agrees to 1 ulp;
   * a group's block score is the Eq. 6 form over the estimated log-masses
     (sum over the group's heads of each head's softmax over the blocks), or,
     in raw-sum mode (one Forecast vector, "Compact Forecast Indexer"), the sum
@@ -34,42 +37,23 @@ Arithmetic fp64 from the statistics on.
 """
 import numpy as np
 
-from .numerics import round_to
+from .numerics import round_once
 from .select import SOFTMAX_SUM, RAW_SUM, candidate_sets, top_k_blocks, SelectParams
 from .compress import n_blocks
 
 BLOCK = 64
 
 
-QUARTER = 16
-
-
-def _quarter_ordered_sum(terms: np.ndarray) -> np.ndarray:
-    """terms [nbc, 64, d] fp32 -> (((P_0 + P_1) + P_2) + P_3), P_j the token-order
-    fp32 sum of terms 16j .. 16j+15 (every block at once)."""
-    parts = []
-    for j in range(BLOCK // QUARTER):
-        p = np.zeros((terms.shape[0], terms.shape[2]), dtype=np.float32)
-        for t in range(j * QUARTER, (j + 1) * QUARTER):
-            p = (p + terms[:, t]).astype(np.float32)
-        parts.append(p)
-    tot = parts[0]
-    for p in parts[1:]:
-        tot = (tot + p).astype(np.float32)
-    return tot
-
-
 def block_stats(K: np.ndarray, L: int, dtype: str):
-    """(mu, var) [L // 64, d] of the complete blocks of K[:L], each a sum in the
-    fixed quarter order times 2^-6, rounded to dtype ("f32" or "bf16")."""
+    """(mu, var) [L // 64, d] of the complete blocks of K[:L]: fp64 mean and
+    population variance per channel, each rounded once to dtype ("f32" or
+    "bf16")."""
     nbc = L // BLOCK
     d = K.shape[1]
-    rows = np.asarray(K[:nbc * BLOCK], dtype=np.float32).reshape(nbc, BLOCK, d)
-    scale = np.float32(2.0 ** -6)
-    m32 = (_quarter_ordered_sum(rows) * scale).astype(np.float32)
-    dv = (rows - m32[:, None, :]).astype(np.float32)
-    q = _quarter_ordered_sum((dv * dv).astype(np.float32))
-    return round_to(m32, dtype), round_to((q * scale).astype(np.float32), dtype)
+    rows = np.asarray(K[:nbc * BLOCK], dtype=np.float64).reshape(nbc, BLOCK, d)
+    mu = rows.mean(axis=1)
+    var = ((rows - mu[:, None, :]) ** 2).mean(axis=1)
+    return round_once(mu, dtype), round_once(var, dtype)
 
 
 def cobs_log_mass(sel: np.ndarray, mu: np.ndarray, var: np.ndarray, order: int = 2) -> np.ndarray:

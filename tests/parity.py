@@ -125,3 +125,18 @@ def token_selection_ok(gpu_tokens, ref_tokens, s, bound, k, cand):
     if all(abs(s[t] - s[kth]) <= bound[t] + bound[kth] for t in diff):
         return True, "near tie"
     return False, "a differing token is outside the rounding band of the k-th score"
+
+
+def ulp_distance(got: np.ndarray, ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Number of representable values of dtype ("f32" or "bf16") between two
+    arrays of that dtype's values (given as fp32 numbers)."""
+    def ordered(x):
+        bits = np.asarray(x, dtype=np.float32).view(np.int32).astype(np.int64)
+        if dtype == "bf16":
+            assert np.all(bits & 0xFFFF == 0), "not bf16 values"
+            bits = bits >> 16
+            top = 2 ** 15
+        else:
+            top = 2 ** 31
+        return np.where(bits < 0, -(bits & (top - 1)), bits)
+    return np.abs(ordered(got) - ordered(ref))

@@ -118,7 +118,8 @@ def test_decode_validation():
     assert _decode(Hq=7) == sa.SA_ERR_INVALID_ARG
     assert _decode(out_dtype=3) == sa.SA_ERR_INVALID_ARG
     assert _decode(scale=float("nan")) == sa.SA_ERR_INVALID_ARG
-    assert _decode(Hq=16) == sa.SA_ERR_UNSUPPORTED              # G = 8
+    assert _decode(Hq=6) == sa.SA_ERR_UNSUPPORTED               # G = 3
+    assert _decode(Hq=32) == sa.SA_ERR_UNSUPPORTED              # G = 16
     assert _decode(n_split=65) == sa.SA_ERR_UNSUPPORTED
     assert _decode(idx_cap=4097) == sa.SA_ERR_UNSUPPORTED
     assert _decode(d=64) == sa.SA_ERR_UNSUPPORTED
@@ -262,7 +263,8 @@ def test_token_decode_validation():
     assert call(idx_cap=0) == sa.SA_ERR_INVALID_ARG
     assert call(Hq=7) == sa.SA_ERR_INVALID_ARG
     assert call(d=64) == sa.SA_ERR_UNSUPPORTED
-    assert call(Hq=16) == sa.SA_ERR_UNSUPPORTED                       # G = 8
+    assert call(Hq=6) == sa.SA_ERR_UNSUPPORTED                        # G = 3
+    assert call(Hq=32) == sa.SA_ERR_UNSUPPORTED                       # G = 16
     assert call(n_split=65) == sa.SA_ERR_UNSUPPORTED
     assert call(idx_cap=64 * 64 * 64 + 1) == sa.SA_ERR_UNSUPPORTED    # more than 4096 tiles
     need = L.sparse_attn_token_decode_workspace_size(2, 8, 2, 448, 4)
@@ -328,7 +330,7 @@ def test_cobs_decode_step_validation():
     assert step_call(order=0) == sa.SA_ERR_INVALID_ARG
     assert step_call(scale=float("nan")) == sa.SA_ERR_INVALID_ARG
     assert step_call(H_sel=6) == sa.SA_ERR_UNSUPPORTED                # G = 3
-    assert step_call(Hq=16) == sa.SA_ERR_UNSUPPORTED                  # 8 query heads per KV head
+    assert step_call(Hq=6) == sa.SA_ERR_UNSUPPORTED                   # 3 query heads per KV head
     assert step_call(n_split=65) == sa.SA_ERR_UNSUPPORTED
     assert step_call(nb_cap=15) == sa.SA_ERR_CAPACITY
     assert step_call(idx_cap=10) == sa.SA_ERR_CAPACITY

@@ -223,8 +223,9 @@ def test_select_ties_on_a_grid_of_many_units(mode, pattern):
 
 # ------------------------------------------------------------------ decode
 
-def _decode_case(dt, lens, T_cap, blocks_of, n_split, out=torch.float32, seed=10):
-    B, Hq, Hkv = len(lens), 8, 2
+def _decode_case(dt, lens, T_cap, blocks_of, n_split, out=torch.float32, seed=10, G=4):
+    B, Hkv = len(lens), 2
+    Hq = G * Hkv
     Q = rand((B, Hq, 128), dt, seed, scale=128 ** -0.5)
     K = rand((B, Hkv, T_cap, 128), dt, seed + 1)
     V = rand((B, Hkv, T_cap, 128), dt, seed + 2)
@@ -239,16 +240,17 @@ def _decode_case(dt, lens, T_cap, blocks_of, n_split, out=torch.float32, seed=10
     Qn, Kn, Vn = to_np(Q), to_np(K), to_np(V)
     On, Ln = to_np(O), lse.cpu().numpy()
     for (b, h), blk in blocks_of.items():
-        o, l = oracle.sparse_attention(Qn[b, 4 * h:4 * h + 4], Kn[b, h], Vn[b, h],
+        rows = slice(G * h, G * h + G)
+        o, l = oracle.sparse_attention(Qn[b, rows], Kn[b, h], Vn[b, h],
                                        block_tokens(blk, lens[b]), 1.0)
         if len(blk) == 0 or block_tokens(blk, lens[b]).size == 0:
-            assert np.all(On[b, 4 * h:4 * h + 4] == 0) and np.all(np.isneginf(Ln[b, 4 * h:4 * h + 4]))
+            assert np.all(On[b, rows] == 0) and np.all(np.isneginf(Ln[b, rows]))
             continue
         if out == torch.float32:
-            assert_close(On[b, 4 * h:4 * h + 4], o, dt, f"O unit {(b, h)}")
+            assert_close(On[b, rows], o, dt, f"O unit {(b, h)}")
         else:
-            assert np.allclose(On[b, 4 * h:4 * h + 4], o, atol=TOL[dt][0] + 2e-2, rtol=1e-2)
-        assert_close(Ln[b, 4 * h:4 * h + 4], l, dt, f"LSE unit {(b, h)}")
+            assert np.allclose(On[b, rows], o, atol=TOL[dt][0] + 2e-2, rtol=1e-2)
+        assert_close(Ln[b, rows], l, dt, f"LSE unit {(b, h)}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -268,6 +270,26 @@ def test_decode_parity(dt, n_split):
             blocks_of[(b, h)] = pick
     blocks_of[(2, 1)] = []                          # a unit with nothing selected
     _decode_case(dt, lens, 5000, blocks_of, n_split)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 8])
+@pytest.mark.parametrize("n_split", [1, 0, 5])
+def test_decode_parity_other_gqa_ratios(dt, G, n_split):
+    """G query heads per KV head (Eq. 5 with the group's heads sharing the KV
+    head's blocks), for G = 1, 2 and 8."""
+    lens = [5000, 3333, 70]
+    rng = np.random.default_rng(12 + G)
+    blocks_of = {}
+    for b, L in enumerate(lens):
+        nb = oracle.n_blocks(L)
+        for h in range(2):
+            pick = sorted(set(rng.choice(nb, size=min(nb, 23), replace=False).tolist()) | {nb - 1})
+            blocks_of[(b, h)] = pick
+    blocks_of[(2, 1)] = []
+    _decode_case(dt, lens, 5000, blocks_of, n_split, G=G, seed=40 + G)
+    if dt == "bf16":
+        _decode_case(dt, lens, 5000, blocks_of, n_split, out=torch.bfloat16, G=G, seed=50 + G)
 
 
 def test_decode_unsorted_blocks_and_bf16_output():

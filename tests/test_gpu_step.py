@@ -157,3 +157,75 @@ def test_decode_step_random_configurations():
         assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), case
         assert torch.equal(O1, O2) and torch.equal(lse1, lse2), case
         assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), case
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,G", [("raw_sum", 1), ("softmax_sum", 4)])
+@pytest.mark.parametrize("hint", [0, 1])
+def test_decode_step_hint_below_the_real_jump(dt, mode, G, hint):
+    """max_new_tokens only schedules the append: with a hint below the real
+    length jump (0 or 1 for jumps of 1, 37 and 300 tokens) every new entry is
+    still written, and the step equals the three separate calls."""
+    B, Hq, Hkv, T = 3, 8, 2, 4000
+    K = rand((B, Hkv, T, 128), dt, 81)
+    V = rand((B, Hkv, T, 128), dt, 82)
+    nc_cap = sa.n_compressed(T)
+    lp, ln = [1000, 2047, 64], [1001, 2084, 364]
+    Kc_a = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+    sa.compress(K, Kc_a, lens_t([0] * B), lens_t(lp))
+    Kc_b = Kc_a.clone()
+    Q = rand((B, Hq, 128), dt, 83, scale=128 ** -0.5)
+    sel = Q if G == 4 else rand((B, Hkv, 128), dt, 84, scale=128 ** -0.5)
+    Lp, Ln = lens_t(lp), lens_t(ln)
+    O1, lse1, idx1, cnt1 = sa.decode_step(Q, sel, K, V, Kc_a, Lp, Ln, 20, 1, 2, mode,
+                                          max_new_tokens=hint)
+    sa.compress(K, Kc_b, Lp, Ln)
+    idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, 20, 1, 2, mode)
+    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), "compressed keys"
+    assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
+    assert torch.equal(O1, O2) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("Gq", [1, 2, 8])
+@pytest.mark.parametrize("mode,Gs", [("raw_sum", 1), ("softmax_sum", 1), ("softmax_sum", 4)])
+def test_decode_step_other_gqa_ratios_against_the_oracle(Gq, mode, Gs):
+    """Gq query heads per KV head in the attention (1, 2 or 8) with Gs
+    selector heads: the step's sets equal the oracle's (R9 near ties aside)
+    and its outputs the oracle's attention over those sets."""
+    import numpy as np
+    import oracle
+    from oracle import SelectParams
+    from oracle.attention import block_tokens
+    from parity import selection_ok, assert_close, to_np
+    dt = "bf16"
+    B, Hkv, T = 2, 2, 5000
+    Hq = Gq * Hkv
+    K = rand((B, Hkv, T, 128), dt, 91)
+    V = rand((B, Hkv, T, 128), dt, 92)
+    Q = rand((B, Hq, 128), dt, 93, scale=128 ** -0.5)
+    sel = rand((B, Hkv * Gs, 128), dt, 94, scale=128 ** -0.5)
+    lens = [5000, 2222]
+    nc_cap = sa.n_compressed(T)
+    Kc = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+    sa.compress(K, Kc, lens_t([0] * B), lens_t([L - 1 for L in lens]))
+    k = 16
+    O, lse, idx, cnt = sa.decode_step(Q, sel, K, V, Kc, lens_t([L - 1 for L in lens]), lens_t(lens),
+                                      k, 1, 2, mode)
+    torch.cuda.synchronize()
+    rows = gpu_rows(idx, cnt)
+    p = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=mode)
+    Sn, Qn = to_np(sel), to_np(Q)
+    for b, L in enumerate(lens):
+        for h in range(Hkv):
+            Kn = K[b, h].float().cpu().numpy()
+            Kc_ref = oracle.compressed_keys(Kn, L, dt)
+            ref, BS = oracle.select_blocks(Sn[b, h * Gs:(h + 1) * Gs], Kc_ref, L, p, True)
+            ok, why = selection_ok(rows[(b, h)], ref, BS, oracle.n_blocks(L), k, 1, 2)
+            assert ok, ((b, h), why)
+            o, l = oracle.sparse_attention(Qn[b, h * Gq:(h + 1) * Gq], Kn,
+                                           V[b, h].float().cpu().numpy(),
+                                           block_tokens(rows[(b, h)], L), 1.0)
+            assert_close(to_np(O)[b, h * Gq:(h + 1) * Gq], o, dt, f"O {(b, h)}")
+            assert_close(lse.cpu().numpy()[b, h * Gq:(h + 1) * Gq], l, dt, f"LSE {(b, h)}")

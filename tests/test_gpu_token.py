@@ -122,8 +122,9 @@ def test_token_select_many_units_sampled():
 
 # ------------------------------------------------------------------ attention over token lists
 
-def _token_decode_case(dt, lens, T_cap, lists, n_split, out=torch.float32, seed=20):
-    B, Hq, Hkv = len(lens), 8, 2
+def _token_decode_case(dt, lens, T_cap, lists, n_split, out=torch.float32, seed=20, G=4):
+    B, Hkv = len(lens), 2
+    Hq = G * Hkv
     Q = rand((B, Hq, 128), dt, seed, scale=128 ** -0.5)
     K = rand((B, Hkv, T_cap, 128), dt, seed + 1)
     V = rand((B, Hkv, T_cap, 128), dt, seed + 2)
@@ -139,13 +140,13 @@ def _token_decode_case(dt, lens, T_cap, lists, n_split, out=torch.float32, seed=
     On, Ln = to_np(O), lse.cpu().numpy()
     for (b, h), toks in lists.items():
         valid = [t for t in toks if 0 <= t < lens[b]]
-        o, l = oracle.token_decode_unit(Qn[b, 4 * h:4 * h + 4], Kn[b, h], Vn[b, h], valid, 1.0)
+        rows = slice(G * h, G * h + G)
+        o, l = oracle.token_decode_unit(Qn[b, rows], Kn[b, h], Vn[b, h], valid, 1.0)
         if not valid:
-            assert np.all(On[b, 4 * h:4 * h + 4] == 0) and np.all(np.isneginf(Ln[b, 4 * h:4 * h + 4]))
+            assert np.all(On[b, rows] == 0) and np.all(np.isneginf(Ln[b, rows]))
             continue
-        assert_close(On[b, 4 * h:4 * h + 4], o, dt if out == torch.float32 else "bf16",
-                     f"O unit {(b, h)}")
-        assert_close(Ln[b, 4 * h:4 * h + 4], l, dt, f"LSE unit {(b, h)}")
+        assert_close(On[b, rows], o, dt if out == torch.float32 else "bf16", f"O unit {(b, h)}")
+        assert_close(Ln[b, rows], l, dt, f"LSE unit {(b, h)}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -161,6 +162,20 @@ def test_token_decode_parity(dt, n_split):
             toks = rng.choice(L, size=min(n, L), replace=False).tolist()
             lists[(b, h)] = toks                                    # unsorted on purpose
     _token_decode_case(dt, lens, T_cap, lists, n_split)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_token_decode_other_gqa_ratios(dt, G):
+    rng = np.random.default_rng(31 + G)
+    lens = [3000, 1234, 70]
+    lists = {}
+    for b, L in enumerate(lens):
+        for h in range(2):
+            n = [700, 130, 64][b] if h == 0 else [1, 65, 70][b]
+            lists[(b, h)] = rng.choice(L, size=min(n, L), replace=False).tolist()
+    _token_decode_case(dt, lens, 3000, lists, 0, G=G, seed=60 + G)
+    _token_decode_case(dt, lens, 3000, lists, 3, G=G, seed=70 + G)
 
 
 def test_token_decode_ignores_out_of_range_and_empty_lists():

@@ -14,7 +14,7 @@ import synth
 from block_sparse_attention_12_amd.pipeline import SparseDecoder
 from oracle import SelectParams
 from oracle.attention import block_tokens
-from parity import selection_ok, gpu_rows, assert_close, to_np
+from parity import selection_ok, gpu_rows, assert_close, to_np, ulp_distance
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -212,7 +212,8 @@ def test_decode_cobs_gqa_bf16_128k_full_sampled():
         Kbh = inp["K"][b, h].float().cpu().numpy()
         mu, var = oracle.block_stats(Kbh, L, w.dtype)
         got = S[b, h, :mu.shape[0]].float().cpu().numpy()
-        assert np.array_equal(got[:, 0], mu) and np.array_equal(got[:, 1], var), (b, h)
+        assert ulp_distance(got[:, 0], mu, w.dtype).max() <= 1, (b, h)
+        assert ulp_distance(got[:, 1], var, w.dtype).max() <= 1, (b, h)
         ref, BS = oracle.select_blocks_cobs(Q[b, h * w.G:(h + 1) * w.G], mu, var, L, p, 2, True)
         ok, why = selection_ok(rows[(b, h)], ref, BS, oracle.n_blocks(L), w.top_k, w.n_init,
                                w.n_local)

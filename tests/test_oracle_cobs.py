@@ -136,3 +136,133 @@ def test_second_order_finds_high_spread_blocks_the_first_order_misses():
     assert not set(spread) <= set(s1)
     mass = oracle.block_mass(q, K, L, 1.0)
     assert oracle.recall(mass, s2) > oracle.recall(mass, s1) + 0.1
+
+
+# ---- rounding once to the key dtype (numerics.round_once), pinned by
+# construction: points placed between two neighbouring values of the dtype at
+# known fractions of the gap, so the nearest value (ties to the even pattern)
+# is known without any rounding routine.
+
+def _neighbour_cases(dtype, rng, n=400):
+    if dtype == "bf16":
+        pats = rng.integers(0x0001, 0x7F7F, n).astype(np.uint32)      # finite, below the largest
+        lo = (pats << 16).view(np.float32).astype(np.float64)
+        hi = ((pats + 1) << 16).view(np.float32).astype(np.float64)
+        even_lo = (pats & 1) == 0
+    else:
+        pats = rng.integers(0x00000001, 0x7F7FFFFF, n, dtype=np.int64).astype(np.uint32)
+        lo = pats.view(np.float32).astype(np.float64)
+        hi = (pats + 1).view(np.float32).astype(np.float64)
+        even_lo = (pats & 1) == 0
+    return lo, hi, even_lo
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_round_once_nearest_and_ties_to_even(dtype):
+    rng = np.random.default_rng(11)
+    lo, hi, even_lo = _neighbour_cases(dtype, rng)
+    gap = hi - lo
+    for frac, expect_lo in ((0.25, np.ones_like(even_lo)), (0.75, np.zeros_like(even_lo)),
+                            (0.5, even_lo), (0.0, np.ones_like(even_lo)),
+                            (0.5 - 2.0 ** -20, np.ones_like(even_lo)),
+                            (0.5 + 2.0 ** -20, np.zeros_like(even_lo))):
+        x = lo + frac * gap                               # exact in fp64 (dyadic fractions)
+        want = np.where(expect_lo.astype(bool), lo, hi).astype(np.float32)
+        for sign in (1.0, -1.0):
+            got = oracle.round_once(sign * x, dtype)
+            assert np.array_equal(got, (sign * want).astype(np.float32)), (dtype, frac, sign)
+
+
+def test_round_once_special_values():
+    assert oracle.round_once(np.array([0.0]), "bf16")[0] == 0.0
+    # the smallest subnormal bf16 is 2^-133: half of it is a tie to 0, a bit more rounds up
+    assert oracle.round_once(np.array([2.0 ** -134]), "bf16")[0] == 0.0
+    assert oracle.round_once(np.array([1.5 * 2.0 ** -134]), "bf16")[0] == np.float32(2.0 ** -133)
+    assert oracle.round_once(np.array([3 * 2.0 ** -134]), "bf16")[0] == np.float32(2.0 ** -132)
+    big = float(np.float32(3.3895313892515355e38))          # largest bf16 (0x7F7F)
+    assert oracle.round_once(np.array([big]), "bf16")[0] == big
+    assert np.isinf(oracle.round_once(np.array([2.0 ** 128]), "bf16")[0])
+    # a value just above 1 + 2^-8 (the tie between 1 and 1 + 2^-7) goes up, one
+    # rounding only: rounding through fp32 first would make it the tie and go down
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert oracle.round_once(np.array([x]), "bf16")[0] == np.float32(1.0 + 2.0 ** -7)
+    assert oracle.bf16_round(np.float32(x)) == np.float32(1.0)
+
+
+def test_block_stats_equal_exact_rational_mean_and_variance_rounded_once():
+    """Exact rational mean and population variance (fractions), then the
+    nearest value of the dtype by comparing exact distances to the stored
+    value's neighbours."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    d = 6
+    for dtype in ("bf16", "f32"):
+        K = oracle.round_to(rng.standard_normal((64 * 3, d)) * 3 + 0.7, dtype)
+        mu, var = oracle.block_stats(K, 64 * 3, dtype)
+        for b in range(3):
+            for c in range(d):
+                xs = [Fraction(float(v)) for v in K[64 * b:64 * (b + 1), c]]
+                m = sum(xs) / 64
+                v = sum((x - m) ** 2 for x in xs) / 64
+                for got, exact in ((mu[b, c], m), (var[b, c], v)):
+                    g = np.float32(got)
+                    if dtype == "bf16":
+                        bits = int(g.view(np.uint32)) >> 16
+                        nbrs = [np.uint32(p << 16).view(np.float32) for p in (bits - 1, bits + 1)
+                                if 0 <= p < 0xFFFF]
+                    else:
+                        nbrs = [np.nextafter(g, np.float32(np.inf)), np.nextafter(g, np.float32(-np.inf))]
+                    dg = abs(Fraction(float(g)) - exact)
+                    for nb in nbrs:
+                        dn = abs(Fraction(float(nb)) - exact)
+                        assert dg <= dn, (dtype, b, c, float(g), float(nb), float(exact))
+
+
+# ---- the group form of the score for G > 1 heads (Eq. 6 form over the
+# estimates: sum over heads of each head's softmax over the blocks)
+
+def _stats_for_scores(seed, nbc=30, d=16):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((64 * nbc, d)).astype(np.float32)
+    K[64 * 5:64 * 6] += 1.5
+    return oracle.block_stats(K, 64 * nbc, "f32"), rng
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_cobs_softmax_sum_identical_heads_scale_by_G(G):
+    (mu, var), rng = _stats_for_scores(20 + G)
+    q = rng.standard_normal((1, mu.shape[1])) * 0.5
+    nb = mu.shape[0] + 2
+    one = oracle.cobs_block_scores(q, mu, var, nb, oracle.SOFTMAX_SUM)
+    many = oracle.cobs_block_scores(np.repeat(q, G, axis=0), mu, var, nb, oracle.SOFTMAX_SUM)
+    fin = np.isfinite(one)
+    assert np.array_equal(fin, np.isfinite(many)) and not fin[-1] and not fin[-2]
+    assert np.allclose(many[fin], G * one[fin], rtol=1e-13, atol=0)
+    assert np.isclose(many[fin].sum(), G, rtol=1e-12)     # each head's softmax sums to 1
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_cobs_softmax_sum_head_permutation_and_single_head_ranking(order):
+    (mu, var), rng = _stats_for_scores(31)
+    d = mu.shape[1]
+    q = rng.standard_normal((8, d)) * 0.4
+    nb = mu.shape[0]
+    s = oracle.cobs_block_scores(q, mu, var, nb, oracle.SOFTMAX_SUM, order)
+    for perm in (rng.permutation(8), np.arange(8)[::-1]):
+        sp = oracle.cobs_block_scores(q[perm], mu, var, nb, oracle.SOFTMAX_SUM, order)
+        assert np.allclose(sp, s, rtol=1e-13, atol=0)
+    # one head: the softmax is a monotone map of the estimate, so both modes rank alike
+    L = 64 * nb
+    for k in (1, 4, 12):
+        ps = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=oracle.SOFTMAX_SUM)
+        pr = SelectParams(top_k=k, n_init=1, n_local=2, score_mode=oracle.RAW_SUM)
+        assert (oracle.select_blocks_cobs(q[:1], mu, var, L, ps, order)
+                == oracle.select_blocks_cobs(q[:1], mu, var, L, pr, order))
+    # the group sum differs from any single head's ranking in general, and a
+    # head with a dominant direction decides the blocks it prefers
+    spike = np.zeros((2, d))
+    spike[0, 0] = 40.0
+    mu2 = mu.copy()
+    mu2[7, 0] = 3.0
+    s2 = oracle.cobs_block_scores(spike, mu2, np.zeros_like(var), nb, oracle.SOFTMAX_SUM, order)
+    assert np.argmax(s2) == 7 and s2[7] > 1.0                      # head 0 puts ~all its mass there
