@@ -49,7 +49,11 @@ EXPORTS = [
     "sparse_attn_cobs_stats", "sparse_attn_cobs_select_workspace_size", "sparse_attn_cobs_select",
     "sparse_attn_decode_step_workspace_size", "sparse_attn_decode_step",
     "sparse_attn_cobs_decode_step_workspace_size", "sparse_attn_cobs_decode_step",
+    "sparse_attn_decode_step_noalloc",
 ]
+
+# scratch bytes of sparse_attn_decode_step_noalloc's per-GPU array (SA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SelectParams(ctypes.Structure):
@@ -133,6 +137,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_attn_decode_step.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _int, _int, _int, _int, _int,
                                           _i64, _i64, _vp, _vp, _i32, _PP, _f32, _vp, _i32, _vp, _vp,
                                           _int, _vp, _i32, _vp, _sz, _vp]
+    L.sparse_attn_decode_step_noalloc.restype = _int
+    L.sparse_attn_decode_step_noalloc.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _int, _int, _int, _int,
+                                                  _int, _i64, _i64, _vp, _vp, _i32, _PP, _f32, _vp,
+                                                  _i32, _vp, _vp, _int, _vp, _i32, _vp]
     L.sparse_attn_cobs_stats.restype = _int
     L.sparse_attn_cobs_stats.argtypes = [_vp, _vp, _int, _int, _int, _int, _i64, _i64, _vp, _vp, _i32,
                                          _vp]
@@ -716,4 +724,45 @@ def decode_step(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: torch.Te
                                        _dtype_code(O), _opt(lse, "lse"), int(n_split),
                                        _dev(workspace, "workspace"), ws_bytes, _stream(Q, stream))
     _check("sparse_attn_decode_step", st)
+    return O, lse, idx, cnt
+
+
+def decode_step_noalloc(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                        Kc: torch.Tensor, lens_prev: torch.Tensor, lens_now: torch.Tensor,
+                        top_k: int, n_init: int = 1, n_local: int = 2, score_mode="softmax_sum",
+                        scale: float = 1.0, max_new_tokens: int = 1, idx=None, cnt=None, O=None,
+                        lse=None, want_lse=True, out_dtype=torch.float32, n_split: int = 0,
+                        stream=None):
+    """decode_step without a workspace: the library's fixed per-GPU scratch
+    array serves as scratch (nothing is allocated for it). Calls that overlap
+    on one GPU race on that array. Returns (O, lse, idx, cnt)."""
+    B, Hkv, T_cap, d = _check_kv(K, V)
+    _expect(Q, "Q", (B, None, d), K.dtype)
+    _expect(sel, "sel", (B, None, d), K.dtype)
+    _expect(Kc, "Kc", (B, Hkv, None, d), K.dtype)
+    Hq, H_sel = Q.shape[1], sel.shape[1]
+    _check_lens(B, lens_prev=lens_prev, lens_now=lens_now)
+    _check_sets(idx, cnt, B, Hkv)
+    _check_out(O, lse, B, Hq, d)
+    nc_cap = Kc.shape[2]
+    p = make_params(top_k, n_init, n_local, score_mode)
+    dev = Q.device
+    cap = top_k + n_init + n_local
+    if idx is None:
+        idx = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
+    if cnt is None:
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    st = lib().sparse_attn_decode_step_noalloc(_dev(Q, "Q"), _dev(sel, "sel"), H_sel, _dev(K, "K"),
+                                               _dev(V, "V"), _dev(Kc, "Kc"), _dtype_code(K), B, Hq,
+                                               Hkv, d, T_cap, nc_cap, _dev(lens_prev, "lens_prev"),
+                                               _dev(lens_now, "lens_now"), int(max_new_tokens),
+                                               ctypes.byref(p), float(scale), _dev(idx, "idx"),
+                                               idx.shape[-1], _dev(cnt, "cnt"), _dev(O, "O"),
+                                               _dtype_code(O), _opt(lse, "lse"), int(n_split),
+                                               _stream(Q, stream))
+    _check("sparse_attn_decode_step_noalloc", st)
     return O, lse, idx, cnt

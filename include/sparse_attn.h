@@ -238,6 +238,29 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
                             int out_dtype, float *lse_out, int32_t n_split, void *workspace,
                             size_t ws_bytes, void *stream);
 
+/*
+ * sparse_attn_decode_step_noalloc - for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): sparse_attn_decode_step with the same arguments except
+ * the workspace, and the same results. Its scratch memory is a fixed array of
+ * SA_NOALLOC_SCRATCH_BYTES per GPU inside the library (held until the process
+ * ends); the call allocates nothing. Calls that overlap on one GPU (other
+ * streams or host threads) share that array and race: order them.
+ * Errors: those of sparse_attn_decode_step; SA_ERR_WORKSPACE when the step
+ *         needs more scratch than SA_NOALLOC_SCRATCH_BYTES
+ *         (sparse_attn_decode_step_workspace_size tells); SA_ERR_HIP when the
+ *         array's device address cannot be obtained.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int sparse_attn_decode_step_noalloc(const void *Q, const void *sel, int H_sel, const void *K,
+                                    const void *V, void *Kc, int dtype, int B, int Hq, int Hkv,
+                                    int d, int64_t T_cap, int64_t nc_cap,
+                                    const int32_t *lens_prev, const int32_t *lens_now,
+                                    int32_t max_new_tokens, const sa_select_params *p,
+                                    float scale, int32_t *idx_out, int32_t idx_cap,
+                                    int32_t *cnt_out, void *O, int out_dtype, float *lse_out,
+                                    int32_t n_split, void *stream);
+
 /* Columns needed per tile row of the prefill block sets: min(ceil(T/64),
  * 64 * top_k + n_init + n_local) for a context of T = q_start + Tq tokens. */
 int32_t sparse_attn_prefill_tile_cap(int64_t q_start, int64_t Tq, const sa_select_params *p);

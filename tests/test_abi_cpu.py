@@ -337,3 +337,20 @@ def test_cobs_decode_step_validation():
     need = L.sparse_attn_cobs_decode_step_workspace_size(2, 8, 2, 8, 1000, ctypes.byref(p8), 11, 0)
     assert need >= L.sparse_attn_cobs_select_workspace_size(2, 2, 8, 1000, ctypes.byref(p8))
     assert step_call(ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
+
+
+def test_decode_step_noalloc_rejects_steps_beyond_its_scratch():
+    """A step whose scratch exceeds the fixed per-GPU array is refused before
+    any HIP call (softmax-sum logits of 512 units x 4 heads x 8192 entries)."""
+    L = sa.lib()
+    p = sa.make_params(64, 1, 2, "softmax_sum")
+    need = L.sparse_attn_decode_step_workspace_size(64, 256, 8, 32, 131072, ctypes.byref(p), 67, 0)
+    assert need > sa.NOALLOC_SCRATCH_BYTES
+    st = L.sparse_attn_decode_step_noalloc(FAKE, FAKE, 32, FAKE, FAKE, FAKE, sa.SA_BF16, 64, 256, 8,
+                                           128, 131072, 8191, FAKE, FAKE, 1, ctypes.byref(p), 1.0,
+                                           FAKE, 67, FAKE, FAKE, sa.SA_F32, None, 0, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    assert L.sparse_attn_decode_step_noalloc(FAKE, FAKE, 32, FAKE, FAKE, FAKE, sa.SA_BF16, 64, 256,
+                                             8, 128, 131072, 8191, FAKE, FAKE, 1, None, 1.0, FAKE,
+                                             67, FAKE, FAKE, sa.SA_F32, None, 0, None) \
+        == sa.SA_ERR_INVALID_ARG
