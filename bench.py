@@ -222,9 +222,18 @@ def bench_decode(args, w):
     ms_step = wall * 1e3 / args.steps
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # GPU time of each whole step call (events around every call)
+    n_ph = max(10, min(args.steps, 100))
+    evs = [_events(2) for _ in range(n_ph)]
+    for i in range(n_ph):
+        evs[i][0].record(stream)
+        steps_fn[i % len(reps)]()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ph
+
     # per-phase GPU time: each phase captured on its own, replays bracketed by events
     mean = {}
-    n_ph = max(10, min(args.steps, 100))
     for name in ("append", "select", "attend"):
         fns = [phases_of(rep)[name] for rep in reps]
         if args.graph:
@@ -267,6 +276,7 @@ def bench_decode(args, w):
     append_bytes = new_entries * (32 * row + row)
     step_bytes = attn_bytes + sel_bytes + append_bytes
     attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
+    step_gbs = step_bytes / (step_call_ms * 1e-3) / 1e9
 
     out = {
         "metric": "sparse decode attn tokens/s and HBM GB/s (% of peak) at 128K ctx, 1 GPU",
@@ -288,17 +298,33 @@ def bench_decode(args, w):
         "phase_ms": {k: round(v, 5) for k, v in mean.items()},
         "step_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm",
-                     "kernel": "sparse_attn_decode (decode_kernel + combine_kernel)",
-                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"{w.name}_decode"),
-                     "bytes_per_launch": attn_bytes},
+        "step_call_ms": round(step_call_ms, 5),
     }
+    separate = {"kernel": "sparse_attn_decode called alone (decode_kernel + combine_kernel)",
+                "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(f"{w.name}_decode"), "bytes_per_launch": attn_bytes}
+    if not args.separate_calls:
+        # the timed step is one sparse_attn_decode_step call: its launches (the
+        # scorer with the append, then the attention with the top-k prologue
+        # and the in-kernel split merge) timed together with events around
+        # every call, on the step's algorithmic bytes
+        out["roofline"] = {"bound": "hbm",
+                           "kernel": "sparse_attn_decode_step call (score_raw_kernel with the "
+                                     "append; decode_kernel with the top-k and the split merge)",
+                           "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                           "traffic": recorded_traffic(f"{w.name}_step"),
+                           "bytes_per_launch": step_bytes, "call_ms": round(step_call_ms, 5),
+                           "separate_call_attention": separate}
+    else:
+        out["roofline"] = dict(bound="hbm", **separate)
+        out["roofline"]["step_calls_ms"] = round(step_call_ms, 5)
     out["selection_quality"] = selection_quality(w, reps[0], dec, sel_name, lens_now)
     ceil = measured_stream_read_gbs(dev)
     out["roofline"]["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
-                                           "GB/s": ceil, "frac": round(attn_gbs / ceil, 4),
+                                           "GB/s": ceil,
+                                           "frac": round(out["roofline"]["achieved"] / ceil, 4),
                                            "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, inp, lens, args.cpu_seconds)
@@ -563,6 +589,7 @@ def bench_cobs(args, w):
     append_bytes = sum((L // 64) - ((L - 1) // 64) for L in lens) * w.Hkv * (64 * row + 2 * row)
     step_bytes = attn_bytes + sel_bytes + append_bytes
     attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
+    step_gbs = step_bytes / (step_call_ms * 1e-3) / 1e9
     sel_gbs = sel_bytes / (mean["select"] * 1e-3) / 1e9
 
     # selection quality on the first replica: second order, first order, compressed keys
@@ -836,6 +863,21 @@ def bench_crosslayer(args, w):
     attn = attn * w.layers + w.layers * w.B * w.Hq * (128 * 2 + 128 * 4 + 4)
     scan = w.B * w.Hkv * n_compressed(L) * row + w.B * w.Hq * row
     step_bytes = attn + scan
+    # dominant kernel: the attention of a follower layer over the shared sets
+    # (one sparse_attn_decode call: decode_kernel + combine_kernel), timed with
+    # events around each call on the launch stream, at the last step's lengths
+    per_layer_attn = attn // w.layers
+    n_ev = max(10, min(args.steps, 60))
+    evs = [_events(2) for _ in range(n_ev)]
+    for i in range(n_ev):
+        lay = layers[1 + i % (w.layers - 1)]
+        evs[i][0].record(stream)
+        dec.attend(lay["qs"][w.steps - 1], lay["K"], lay["V"], lens[w.steps], O=outs[1][0],
+                   lse=outs[1][1])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    attn_call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ev
+    attn_gbs = per_layer_attn / (attn_call_ms * 1e-3) / 1e9
     out = {
         "metric": "cross-layer sparse decode tokens/s (4 layers share one selection) and HBM GB/s",
         "value": round(w.B / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -849,10 +891,94 @@ def bench_crosslayer(args, w):
         "gpu_ms_per_step": round(gpu_ms, 5), "step_bytes": step_bytes,
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
     }
+    out["roofline"] = {"bound": "hbm",
+                       "kernel": "sparse_attn_decode of a follower layer (decode_kernel + "
+                                 "combine_kernel) over the anchor's block sets",
+                       "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                       "traffic": recorded_traffic(f"{w.name}_decode"),
+                       "bytes_per_launch": per_layer_attn, "launch_ms": round(attn_call_ms, 5)}
     ceil = measured_stream_read_gbs(dev)
     out["measured_ceiling"] = {"what": "stream read (sparse_attn_stream_read, 4 GiB)", "GB/s": ceil,
                                "step_frac": round(out["step_hbm_gbs"] / ceil, 4)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_crosslayer(w, layers, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_crosslayer(w, layers, budget_s):
+    """The CPU oracle, as it is, on the cross-layer workload's first step
+    (L = T -> T + 1): the anchor's append, selection and attention plus the
+    other layers' attention over the shared sets, on a deterministic prefix
+    of the (sequence, KV head) units (units are independent), scaled linearly
+    to all units."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+
+    p = oracle.SelectParams(w.top_k, w.n_init, w.n_local, w.score_mode)
+    L0, L1 = w.T, w.T + 1
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    n_threads = min(len(os.sched_getaffinity(0)), 16)
+    done, spent = 0, 0.0
+    with threadpoolctl.threadpool_limits(n_threads):
+        for (b, h) in units:
+            lay = []
+            for l, L in enumerate(layers):                  # setup, not timed
+                lay.append(dict(Q=L["qs"][0][b:b + 1].float().cpu().numpy(),
+                                K=L["K"][b:b + 1, h:h + 1, :L1].float().cpu().numpy(),
+                                V=L["V"][b:b + 1, h:h + 1, :L1].float().cpu().numpy()))
+            for d in lay:                                    # the unit's query heads only
+                d["Q"] = d["Q"][:, h * w.G:(h + 1) * w.G]
+            kc0 = oracle.compressed_keys(lay[0]["K"][0, 0], L0, w.dtype)
+            Kc = np.zeros((1, 1, max(oracle.n_compressed(L1), 1), kc0.shape[1]), dtype=kc0.dtype)
+            Kc[0, 0, :kc0.shape[0]] = kc0
+            t0 = time.perf_counter()
+            oracle.crosslayer_step(lay, Kc, np.array([L0]), np.array([L1]), p, 1.0, w.dtype)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    sec_per_step = spent / done * len(units)
+    return {"value": round(w.B / sec_per_step, 4), "unit": "tokens/s", "cores": n_threads,
+            "kind": "oracle",
+            "sample": f"first decode step of {w.name} on {done} of {len(units)} (sequence, KV head) "
+                      f"units (4 layers each: anchor append + select + attend, 3 follower "
+                      f"attentions), {spent:.1f} s, scaled linearly to all units; numpy fp64, "
+                      f"BLAS threads = {n_threads}"}
+
+
+def cpu_baseline_prefill(w, inp, Kc, budget_s):
+    """The CPU oracle, as it is, on the prefill chunk: tile selection and causal
+    attention of a deterministic prefix of the (64-query tile, KV head) units
+    (units are independent), scaled linearly to the whole chunk."""
+    import threadpoolctl
+    import oracle
+
+    p = oracle.SelectParams(w.top_k, w.n_init, w.n_local, "softmax_sum")
+    n_tiles = (w.Tq + 63) // 64
+    units = [(t, h) for t in range(n_tiles) for h in range(w.Hkv)]
+    Q = inp["Q"].float().cpu().numpy()
+    K = inp["K"][0].float().cpu().numpy()
+    V = inp["V"][0].float().cpu().numpy()
+    Kcn = Kc.float().cpu().numpy()
+    n_threads = min(len(os.sched_getaffinity(0)), 16)
+    done, spent = 0, 0.0
+    with threadpoolctl.threadpool_limits(n_threads):
+        for u in units:
+            t0 = time.perf_counter()
+            oracle.prefill_chunk(Q, K, V, Kcn, w.q_start, p, 1.0, tiles=[u])
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+    sec_per_chunk = spent / done * len(units)
+    return {"value": round(w.Tq / sec_per_chunk, 4), "unit": "tokens/s", "cores": n_threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(units)} (64-query tile, KV head) units of {w.name} "
+                      f"(per-query selection, tile union, causal attention), {spent:.1f} s, "
+                      f"scaled linearly to the whole {w.Tq}-query chunk; numpy fp64, BLAS "
+                      f"threads = {n_threads}"}
 
 
 def bench_prefill(args):
@@ -945,6 +1071,8 @@ def bench_prefill(args):
     ceil = measured_matmul_tflops(dev)
     out["roofline"]["measured_ceiling"] = {"what": "bf16 GEMM 8192^3 (torch.matmul)",
                                            "TFLOP/s": ceil, "frac": round(attn_tf / ceil, 4)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(w, inp, reps[0]["Kc"], args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -79,7 +79,9 @@ void launch_topk_raw(int n_units, int Hkv, int64_t T_cap, int64_t nb_cap, const 
 
 int decode_auto_split(int B, int Hkv, int32_t idx_cap);
 int decode_min_split(int32_t idx_cap);
-size_t decode_workspace_bytes(int B, int Hq, int32_t n_split);
+// split partials [B * Hq][n_split][132] fp32 and the split-merge hand-off
+// words (0 bytes for one split)
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int32_t n_split);
 int launch_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq, int Hkv,
                   int64_t T_cap, const int32_t *seq_lens, const int32_t *idx, const int32_t *cnt,
                   int32_t idx_cap, float scale, void *O, int out_dtype, float *lse_out,

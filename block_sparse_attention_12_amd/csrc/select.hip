@@ -32,14 +32,12 @@
 #include "compress_device.h"
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "score_raw_device.h"
 #include "topk_device.h"
 
 namespace sa {
 
 constexpr int kSelThreads = 256;
-constexpr int kRawChunkBlocks = 256;                // blocks per workgroup (raw mode)
-constexpr int kAppendColumn = 1;                    // the append as an extra column of workgroups
-constexpr int kAppendInFirst = 2;                   // the append by each unit's first workgroup
 constexpr int64_t kMaxTopkBlocks = 32768;           // 1024 threads x 32 blocks
 
 SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, int score_mode) {
@@ -70,212 +68,16 @@ SelectWorkspace select_workspace_layout(int B, int Hkv, int G, int64_t T_cap, in
 
 // ---------------------------------------------------------------- raw scores
 
-template <typename T>
-struct RawIter {                         // one iteration: 4 blocks x 3 inside entries per row group
-    Raw8<T> r[12];
-};
-
-// APPEND: the launch has one more column of workgroups, which write the
-// compressed entries completed between lens_prev and seq_lens (the decode
-// step's append) while the other columns score. Scoring then reads only the
-// entries that existed before (j < n_c(lens_prev)) from Kc and forms any newer
-// entry it needs from K itself, with the same arithmetic, so it never depends
-// on the concurrent writes.
 template <typename T, bool APPEND>
 __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
     const T *__restrict__ sel, int H_sel, int Gs, const T *__restrict__ Kc, int Hkv,
     int64_t nc_cap, int64_t T_cap, const int32_t *__restrict__ seq_lens, float *__restrict__ bscore,
     int64_t nb_cap, const T *__restrict__ K, T *__restrict__ Kc_w,
     const int32_t *__restrict__ lens_prev, int n_local, int app_mode) {
-    const int unit = blockIdx.y;
-    const int b = unit / Hkv, kvh = unit % Hkv;
-    const int64_t L = clamp_len(seq_lens[b], T_cap);
-    const int64_t nc = n_compressed(L);
-    const int lane = threadIdx.x & 63;
-    const int lane16 = threadIdx.x & 15;
-    const int group = threadIdx.x >> 4;                 // 0..15
-    constexpr uint32_t kRowBytes = kD * sizeof(T);
-    int64_t nc_old = nc;                                // entries readable from Kc
-    if constexpr (APPEND) {
-        int64_t Lp = lens_prev[b];
-        Lp = Lp < 0 ? 0 : (Lp > L ? L : Lp);
-        nc_old = n_compressed(Lp);
-        if (app_mode == kAppendColumn && blockIdx.x == gridDim.x - 1) {   // the append column
-            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-            T *Kcu = Kc_w + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
-            for (int64_t j = nc_old + group; j < nc; j += 16) {   // few keys in flight
-                Raw8<T> r;
-                compress_entry_raw(Ku, j, r);
-                store_raw(Kcu + j * kD, r);
-            }
-            return;
-        }
-    }
-    // rows at or past the readable entries read as zeros
-    const __amdgpu_buffer_rsrc_t rKc = make_rsrc(Kc + (int64_t)unit * nc_cap * kD,
-                                                (uint32_t)(nc_old * kRowBytes));
-    const uint32_t lane_off = lane16 * kLaneElems * sizeof(T);
-    const int64_t chunk0 = (int64_t)blockIdx.x * kRawChunkBlocks;
-    auto issue = [&](RawIter<T> &it, int64_t blk0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 3; ++e)
-                load_raw(rKc, row_offset(4 * (blk0 + q) + e, kRowBytes, lane_off), it.r[q * 3 + e]);
-    };
-    // first rows go out before the selector is even loaded
-    RawIter<T> bufA, bufB;
-    issue(bufA, chunk0 + group * 4);
-
-    // group-summed selector slice (sum in head order)
-    float s[8];
-    uint32_t s_bf[4];                       // the single selector as bf16 pairs (Gs == 1, bf16)
-    {
-        const T *sp = sel + ((int64_t)b * H_sel + (int64_t)kvh * Gs) * kD + lane16 * kLaneElems;
-        Raw8<T> raw[8];
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-            if (g < Gs) load_raw(sp + (int64_t)g * kD, raw[g]);
-        unpack(raw[0], s);
-#pragma unroll
-        for (int g = 1; g < 8; ++g) {
-            if (g < Gs) {
-                float x[8];
-                unpack(raw[g], x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-            }
-        }
-        if constexpr (sizeof(T) == 2) {
-            const Raw8<bf16_t> &r0 = reinterpret_cast<const Raw8<bf16_t> &>(raw[0]);
-            s_bf[0] = r0.v.x; s_bf[1] = r0.v.y; s_bf[2] = r0.v.z; s_bf[3] = r0.v.w;
-        }
-    }
-    const bool use_dot2 = sizeof(T) == 2 && Gs == 1;
-    float *bs = bscore + (int64_t)unit * nb_cap;
-
-    auto process = [&](const RawIter<T> &it, int64_t blk0) {
-        float v[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int e = 0; e < 3; ++e) {
-                float acc = 0.f;
-                if constexpr (sizeof(T) == 2) {
-                    if (use_dot2) {
-                        const Raw8<bf16_t> &k8 = reinterpret_cast<const Raw8<bf16_t> &>(it.r[q * 3 + e]);
-                        acc = dot2_bf16(s_bf[0], k8.v.x, acc);
-                        acc = dot2_bf16(s_bf[1], k8.v.y, acc);
-                        acc = dot2_bf16(s_bf[2], k8.v.z, acc);
-                        acc = dot2_bf16(s_bf[3], k8.v.w, acc);
-                    }
-                }
-                if (!use_dot2) {
-                    float x[8];
-                    unpack(it.r[q * 3 + e], x);
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc = fmaf(s[c], x[c], acc);
-                }
-                v[q * 4 + e] = acc;
-            }
-            v[q * 4 + 3] = 0.f;
-        }
-        transpose_reduce16<16>(v, lane);
-        // lane position i holds block (i >> 2), inside entry (i & 3)
-        const int q = lane16 >> 2, e = lane16 & 3;
-        const int64_t blk = blk0 + q;
-        const int64_t j = 4 * blk + e;
-        float x = (e < 3 && j < nc) ? v[0] : -INFINITY;
-        x = fmaxf(x, dpp<kDppQuadXor1>(x));
-        x = fmaxf(x, dpp<kDppQuadXor2>(x));
-        if (e == 0 && blk < nb_cap) bs[blk] = x;
-    };
-
-    // iterations of 64 blocks; the next iteration's rows are in flight while
-    // the current ones are reduced (sched_barrier keeps the prefetch in place)
-    constexpr int kIters = kRawChunkBlocks / 64;
-#pragma unroll
-    for (int it = 0; it < kIters; it += 2) {
-        const int64_t b0 = chunk0 + it * 64 + group * 4;
-        if (it + 1 < kIters) issue(bufB, b0 + 64);
-        __builtin_amdgcn_sched_barrier(0);
-        process(bufA, b0);
-        if (it + 1 < kIters) {
-            if (it + 2 < kIters) issue(bufA, b0 + 128);
-            __builtin_amdgcn_sched_barrier(0);
-            process(bufB, b0 + 64);
-        }
-    }
-    if constexpr (APPEND) {
-        // Blocks holding entries of this step's append were scored above with
-        // those entries read as zeros. Each row group rescores its affected
-        // candidate 4-block groups (rare: a single token's new window lies in
-        // the local blocks) with the new entries formed from the keys (same
-        // arithmetic as the append), through the same reduction, and
-        // overwrites their scores. The scores of affected local blocks stay
-        // provisional: the top-k never reads them, and this launch is used
-        // without a block-score output. Runs after the main loop, so its
-        // registers do not add to the loop's.
-        // blocks with an inside entry in [nc_old, nc), below the local window
-        // (local blocks are kept whatever their score; only top-k candidates
-        // need exact scores)
-        const int64_t b_lo = (nc_old + 1) / 4;                  // 4b + 2 >= nc_old
-        int64_t b_hi = (nc - 1) / 4 + 1;                         // 4b <= nc - 1
-        const int64_t cand_hi = n_blocks(L) - n_local;
-        b_hi = b_hi < cand_hi ? b_hi : cand_hi;
-        if (nc > nc_old && b_lo < b_hi) {
-            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-#pragma unroll 1
-            for (int it = 0; it < kIters; ++it) {
-                const int64_t b0 = chunk0 + it * 64 + group * 4;
-                if (b0 + 3 < b_lo || b0 >= b_hi) continue;            // uniform per row group
-                RawIter<T> fix;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int e = 0; e < 3; ++e) {
-                        const int64_t j = 4 * (b0 + q) + e;
-                        if (j >= nc_old && j < nc) compress_entry_raw(Ku, j, fix.r[q * 3 + e]);
-                        else load_raw(rKc, row_offset(j, kRowBytes, lane_off), fix.r[q * 3 + e]);
-                    }
-                process(fix, b0);
-            }
-        }
-    }
-    // kAppendInFirst (bf16, chosen when the caller expects at most one new
-    // entry per unit): after its own blocks, the unit's first workgroup loads
-    // the new entry's 32 keys (two per row group, all in flight at once),
-    // stages them in LDS and one row group sums them in token order. (Loads
-    // issued before the main loop, under a condition, cost the loop its exact
-    // wait counts.) If the length grew by more than expected, the workgroup
-    // forms every new entry one row group at a time, so Kc never has gaps.
-    constexpr bool kInFirst = APPEND && sizeof(T) == 2;
-    if constexpr (kInFirst) {
-        if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old + 1 < nc) {   // uniform
-            const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-            T *Kcu = Kc_w + (int64_t)unit * nc_cap * kD + lane16 * kLaneElems;
-            for (int64_t j = nc_old + group; j < nc; j += 16) {
-                Raw8<T> r;
-                compress_entry_raw(Ku, j, r);
-                store_raw(Kcu + j * kD, r);
-            }
-        } else if (app_mode == kAppendInFirst && blockIdx.x == 0 && nc_old < nc) {
-            __shared__ uint4 s_rows[2 * kCmpStride][16];
-            const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-            Raw8<T> app_rows[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                load_raw(Ka + (nc_old * kCmpStride + 2 * group + i) * kD, app_rows[i]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) s_rows[2 * group + i][lane16] = app_rows[i].v;
-            __syncthreads();
-            if (group == 0) {
-                Raw8<T> e;
-                entry_from_rows(s_rows, lane16, e);
-                store_raw(Kc_w + ((int64_t)unit * nc_cap + nc_old) * kD + lane16 * kLaneElems, e);
-            }
-        }
-    }
+    score_raw_chunk<T, APPEND, kSelThreads / 16>(
+        sel, H_sel, Gs, Kc, Hkv, nc_cap, T_cap, seq_lens, bscore, nb_cap, K, Kc_w, lens_prev,
+        n_local, app_mode, (int)blockIdx.x, (int)blockIdx.y,
+        APPEND && app_mode == kAppendColumn && blockIdx.x == gridDim.x - 1);
 }
 
 // ---------------------------------------------------------------- softmax scores

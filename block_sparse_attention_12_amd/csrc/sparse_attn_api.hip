@@ -100,7 +100,7 @@ size_t sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int32_t idx_cap
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || idx_cap <= 0) return 0;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
     if (s < decode_min_split(idx_cap)) s = decode_min_split(idx_cap);
-    return decode_workspace_bytes(B, Hq, s);
+    return decode_workspace_bytes(B, Hq, Hkv, s);
 }
 
 int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
@@ -119,7 +119,7 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
     if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
     if (s < decode_min_split(idx_cap)) s = decode_min_split(idx_cap);
-    const size_t need = decode_workspace_bytes(B, Hq, s);
+    const size_t need = decode_workspace_bytes(B, Hq, Hkv, s);
     if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
     return launch_decode(Q, K, V, dtype, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale, O,
                          out_dtype, lse_out, s, workspace, (hipStream_t)stream);
@@ -127,6 +127,7 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
 
 namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 int decode_splits(int B, int Hkv, int32_t idx_cap, int32_t n_split) {
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
     return s < decode_min_split(idx_cap) ? decode_min_split(idx_cap) : s;
@@ -140,7 +141,7 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
         idx_cap <= 0)
         return 0;
     const size_t sel = select_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
-    return align256(sel) + decode_workspace_bytes(B, Hq, decode_splits(B, Hkv, idx_cap, n_split));
+    return align256(sel) + decode_workspace_bytes(B, Hq, Hkv, decode_splits(B, Hkv, idx_cap, n_split));
 }
 
 int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const void *K, const void *V,
@@ -166,11 +167,11 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
     if (T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     if (nc_cap < n_compressed(T_cap)) return SA_ERR_CAPACITY;
     if (idx_cap < union_cap(p)) return SA_ERR_CAPACITY;
+    const hipStream_t hs = (hipStream_t)stream;
     const size_t sel_bytes = align256(select_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total);
     const int s = decode_splits(B, Hkv, idx_cap, n_split);
-    const size_t need = sel_bytes + decode_workspace_bytes(B, Hq, s);
+    const size_t need = sel_bytes + decode_workspace_bytes(B, Hq, Hkv, s);
     if (!workspace || ws_bytes < need) return SA_ERR_WORKSPACE;
-    const hipStream_t hs = (hipStream_t)stream;
     // up to 2048 blocks, each decode workgroup takes its unit's top-k itself
     // from the block scores (no separate top-k launch between scoring and
     // attention); not for 8 selector heads a group, whose softmax top-k would
@@ -290,7 +291,7 @@ size_t sparse_attn_token_decode_workspace_size(int B, int Hq, int Hkv, int32_t i
     const int32_t tiles = (idx_cap + 63) / 64;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, tiles);
     if (s < decode_min_split(tiles)) s = decode_min_split(tiles);
-    return decode_workspace_bytes(B, Hq, s);
+    return decode_workspace_bytes(B, Hq, Hkv, s);
 }
 
 int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dtype, int B, int Hq,
@@ -310,7 +311,7 @@ int sparse_attn_token_decode(const void *Q, const void *K, const void *V, int dt
     if ((int64_t)T_cap * d * (dtype == SA_BF16 ? 2 : 4) > 0x7fffffffLL) return SA_ERR_UNSUPPORTED;
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, tiles);
     if (s < decode_min_split(tiles)) s = decode_min_split(tiles);
-    const size_t need = decode_workspace_bytes(B, Hq, s);
+    const size_t need = decode_workspace_bytes(B, Hq, Hkv, s);
     if (need > 0 && (!workspace || ws_bytes < need)) return SA_ERR_WORKSPACE;
     return launch_decode_rows(Q, K, V, dtype, B, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap, scale,
                               O, out_dtype, lse_out, s, workspace, (hipStream_t)stream);
@@ -369,7 +370,7 @@ size_t sparse_attn_cobs_decode_step_workspace_size(int B, int Hq, int Hkv, int H
         idx_cap <= 0)
         return 0;
     const size_t sel = cobs_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
-    return align256(sel) + decode_workspace_bytes(B, Hq, decode_splits(B, Hkv, idx_cap, n_split));
+    return align256(sel) + decode_workspace_bytes(B, Hq, Hkv, decode_splits(B, Hkv, idx_cap, n_split));
 }
 
 int sparse_attn_cobs_decode_step(const void *Q, const void *sel, int H_sel, const void *K,
@@ -400,7 +401,7 @@ int sparse_attn_cobs_decode_step(const void *Q, const void *sel, int H_sel, cons
     const size_t sel_bytes =
         align256(cobs_workspace_layout(B, Hkv, G, T_cap, p->score_mode).total);
     const int s = decode_splits(B, Hkv, idx_cap, n_split);
-    if (!workspace || ws_bytes < sel_bytes + decode_workspace_bytes(B, Hq, s))
+    if (!workspace || ws_bytes < sel_bytes + decode_workspace_bytes(B, Hq, Hkv, s))
         return SA_ERR_WORKSPACE;
     const hipStream_t hs = (hipStream_t)stream;
     if (max_new_blocks > 0 && T_cap >= kBlock) {     // statistics of newly completed blocks

@@ -140,3 +140,15 @@ def ulp_distance(got: np.ndarray, ref: np.ndarray, dtype: str) -> np.ndarray:
             top = 2 ** 31
         return np.where(bits < 0, -(bits & (top - 1)), bits)
     return np.abs(ordered(got) - ordered(ref))
+
+
+def assert_same_attention(O1, O2, lse1, lse2, what=""):
+    """Two GPU computations of the same attention over the same block sets that
+    may split and sum the blocks in different orders (the one-call decode step
+    against the separate calls): equal up to fp32 summation order."""
+    a, b = O1.float().cpu(), O2.float().cpu()
+    assert torch.allclose(a, b, rtol=1e-5, atol=1e-6), (what, float((a - b).abs().max()))
+    la, lb = lse1.float().cpu(), lse2.float().cpu()
+    assert torch.equal(torch.isinf(la), torch.isinf(lb)), what
+    fin = torch.isfinite(la)
+    assert torch.allclose(la[fin], lb[fin], rtol=1e-5, atol=1e-6), (what, "lse")

@@ -268,7 +268,8 @@ def test_token_decode_validation():
     assert call(n_split=65) == sa.SA_ERR_UNSUPPORTED
     assert call(idx_cap=64 * 64 * 64 + 1) == sa.SA_ERR_UNSUPPORTED    # more than 4096 tiles
     need = L.sparse_attn_token_decode_workspace_size(2, 8, 2, 448, 4)
-    assert need == 2 * 8 * 4 * 132 * 4                                 # partials of 4 splits
+    part = -(-(2 * 8 * 4 * 132 * 4) // 256) * 256                     # partials of 4 splits
+    assert need == part + (2 + 2 * 2) * 8                             # + split-merge words
     assert call(n_split=4, ws_bytes=need - 1) == sa.SA_ERR_WORKSPACE
 
 

@@ -1,13 +1,13 @@
 """sparse_attn_decode_step (append + select + attend in one call) against the
-three separate calls it stands for: identical block sets, identical outputs,
-identical compressed keys afterwards. Covers the raw-sum path, where the
+three separate calls it stands for: identical block sets, identical compressed
+keys afterwards, and outputs equal up to fp32 summation order. Covers the raw-sum path, where the
 append shares the scoring launch and the scorer forms new entries from the
 keys, with jumps that put new entries inside candidate blocks."""
 import pytest
 import torch
 
 import block_sparse_attention_12_amd as sa
-from parity import gpu_rows
+from parity import gpu_rows, assert_same_attention
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -54,7 +54,7 @@ def test_decode_step_equals_separate_calls(dt, mode, G, n_local):
         O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
         torch.cuda.synchronize()
         assert gpu_rows(idx1, cnt1) == gpu_rows(idx2, cnt2), (i, mode)
-        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), (i, mode)
+        assert_same_attention(O1, O2, lse1, lse2, (i, mode))
         assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), (i, "compressed keys")
 
 
@@ -113,7 +113,7 @@ def test_decode_step_fused_and_separate_topk(case):
     O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=case["n_split"])
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
-    assert torch.equal(O1, O2) and torch.equal(lse1, lse2)
+    assert_same_attention(O1, O2, lse1, lse2, case)
     assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt]))
 
 
@@ -155,7 +155,7 @@ def test_decode_step_random_configurations():
         O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=n_split)
         torch.cuda.synchronize()
         assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), case
-        assert torch.equal(O1, O2) and torch.equal(lse1, lse2), case
+        assert_same_attention(O1, O2, lse1, lse2, case)
         assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), case
 
 
@@ -185,7 +185,7 @@ def test_decode_step_hint_below_the_real_jump(dt, mode, G, hint):
     torch.cuda.synchronize()
     assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), "compressed keys"
     assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
-    assert torch.equal(O1, O2) and torch.equal(lse1, lse2)
+    assert_same_attention(O1, O2, lse1, lse2, (dt, mode, hint))
 
 
 @pytest.mark.parametrize("Gq", [1, 2, 8])
@@ -229,3 +229,73 @@ def test_decode_step_other_gqa_ratios_against_the_oracle(Gq, mode, Gs):
                                            block_tokens(rows[(b, h)], L), 1.0)
             assert_close(to_np(O)[b, h * Gq:(h + 1) * Gq], o, dt, f"O {(b, h)}")
             assert_close(lse.cpu().numpy()[b, h * Gq:(h + 1) * Gq], l, dt, f"LSE {(b, h)}")
+
+
+@pytest.mark.parametrize("Gq", [1, 4])
+def test_step_graph_replays_and_repeated_calls(Gq):
+    """The step's split merge (the last split workgroup of a unit merges, its
+    hand-off words tagged by a call counter kept in the workspace): repeated
+    eager calls on one workspace and replays of a captured graph, with other
+    work in between, all give the first call's sets, compressed keys and
+    outputs bit for bit."""
+    B, Hkv, T = 4, 4, 40000
+    Hq = Gq * Hkv
+    dt = "bf16"
+    K = rand((B, Hkv, T, 128), dt, 101)
+    V = rand((B, Hkv, T, 128), dt, 102)
+    Q = rand((B, Hq, 128), dt, 103, scale=128 ** -0.5)
+    F = rand((B, Hkv, 128), dt, 104, scale=128 ** -0.5)
+    lens = [40000, 39001, 20000, 64]
+    lp = [L - 1 for L in lens]
+    nc_cap = sa.n_compressed(T)
+    Kc0 = torch.zeros((B, Hkv, nc_cap, 128), dtype=TD[dt], device=DEV)
+    sa.compress(K, Kc0, lens_t([0] * B), lens_t(lp))
+    Kc = Kc0.clone()
+    Lp, Ln = lens_t(lp), lens_t(lens)
+    p = sa.make_params(40, 1, 2, "raw_sum")
+    ws = torch.empty(sa.decode_step_workspace_size(B, Hq, Hkv, Hkv, T, p, 43), dtype=torch.uint8,
+                     device=DEV)
+    O = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, Hkv, 43), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+
+    def step():
+        sa.decode_step(Q, F, K, V, Kc, Lp, Ln, 40, 1, 2, "raw_sum", idx=idx, cnt=cnt, O=O, lse=lse,
+                       workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (O.clone(), lse.clone(), idx.clone(), cnt.clone(), Kc.clone())
+    # the separate calls give the same sets and keys, and outputs up to order
+    Kc2 = Kc0.clone()
+    sa.compress(K, Kc2, Lp, Ln)
+    idx2, cnt2, _ = sa.select(F, Kc2, Ln, T, 40, 1, 2, "raw_sum")
+    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, ref[2]) and torch.equal(cnt2, ref[3])
+    assert torch.equal(Kc2.view(torch.int16), ref[4].view(torch.int16))
+    assert_same_attention(O2, ref[0], lse2, ref[1], "separate calls")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        Kc.copy_(Kc0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for r in range(6):
+        Kc.copy_(Kc0)
+        O.fill_(float("nan"))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        if r % 2:
+            g.replay()
+        else:
+            step()
+        torch.cuda.synchronize()
+        got = (O, lse, idx, cnt, Kc)
+        for a, b_ in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_), r
+        _ = (Q.float() * 3).sum().item()          # unrelated eager work between calls
