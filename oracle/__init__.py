@@ -32,7 +32,7 @@ from .select import (SOFTMAX_SUM, RAW_SUM, entry_scores, block_scores, block_ent
                      candidate_sets, top_k_blocks, select_blocks, SelectParams)
 from .attention import sparse_attention, lse_merge, split_attention_partials
 from .decode import decode_step, decode_unit
-from .prefill import prefill_tile_select, prefill_attention, prefill_chunk
+from .prefill import prefill_tile_select, prefill_attention, prefill_chunk, tile_attention
 from .crosslayer import crosslayer_step
 from .quality import block_mass, recall, rest_bucket_distribution, mass_optimal_blocks
 from .token import (token_candidates, token_scores, top_k_tokens, select_tokens,
@@ -44,7 +44,8 @@ __all__ = [
     "append_compressed_keys", "SOFTMAX_SUM", "RAW_SUM", "entry_scores", "block_scores",
     "block_entries", "candidate_sets", "top_k_blocks", "select_blocks", "SelectParams",
     "sparse_attention", "lse_merge", "split_attention_partials", "decode_step", "decode_unit",
-    "prefill_tile_select", "prefill_attention", "prefill_chunk", "crosslayer_step",
+    "prefill_tile_select", "prefill_attention", "prefill_chunk", "tile_attention",
+    "crosslayer_step",
     "block_mass", "recall", "rest_bucket_distribution", "mass_optimal_blocks",
     "token_candidates", "token_scores", "top_k_tokens", "select_tokens", "token_decode_unit",
     "token_crosslayer_step", "block_stats", "cobs_log_mass", "cobs_block_scores",

@@ -50,6 +50,32 @@ def prefill_tile_select(q_tile, Kc, positions, p: SelectParams, return_per_query
     return union
 
 
+def tile_attention(q_tile, K, V, blocks, positions, scale: float):
+    """Eq. 5 for every query of one tile over the tile's block set, causally.
+
+    q_tile: [n_q, G, d] the group's heads of the tile's queries; K, V: [T, d];
+    positions: [n_q] absolute query positions. Query p attends to the tokens
+    t <= p of the listed blocks: one score matrix over the set's tokens with
+    the invisible ones at -inf, the same softmax and weighted sum as
+    attention.sparse_attention per query. Returns (O [n_q, G, d], LSE [n_q, G]).
+    """
+    q64 = np.asarray(q_tile, dtype=np.float64)
+    n_q, G, d = q64.shape
+    toks = block_tokens(blocks, int(positions[-1]) + 1)
+    if toks.size == 0:
+        return np.zeros((n_q, G, d)), np.full((n_q, G), -np.inf)
+    k64 = np.asarray(K, dtype=np.float64)[toks]
+    v64 = np.asarray(V, dtype=np.float64)[toks]
+    z = scale * (q64.reshape(n_q * G, d) @ k64.T).reshape(n_q, G, -1)
+    visible = toks[None, :] <= np.asarray(positions)[:, None]          # [n_q, n]
+    z = np.where(visible[:, None, :], z, -np.inf)
+    m = z.max(axis=2, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=2, keepdims=True)
+    O = (e.reshape(n_q * G, -1) @ v64).reshape(n_q, G, d) / l
+    return O, m[:, :, 0] + np.log(l[:, :, 0])
+
+
 def prefill_attention(Q, K, V, tile_blocks, q_start: int, scale: float, tiles=None):
     """Causal attention of each chunk query over its tile's block set.
 

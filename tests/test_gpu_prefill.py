@@ -103,16 +103,64 @@ def test_prefill_dense_limit_equals_causal_sdpa():
     assert_close(to_np(O), ref, "bf16", "dense causal prefill")
 
 
-def test_prefill_chunk_bf16_128k_full_sampled():
-    w = synth.PREFILL_WORKLOADS["prefill_chunk_bf16_128k"]
-    inp = synth.make_prefill_inputs(w, device=DEV)
-    K, V = inp["K"][0].contiguous(), inp["V"][0].contiguous()
-    Kc = torch.zeros((1, w.Hkv, oracle.n_compressed(w.T), 128), dtype=torch.bfloat16, device=DEV)
-    lens = torch.tensor([w.T], dtype=torch.int32, device=DEV)
-    sa.compress(inp["K"], Kc, torch.zeros_like(lens), lens)
-    kinds = _check(inp["Q"], K, V, Kc[0].contiguous(), w.q_start, w.top_k, w.n_local, "softmax_sum",
-                   tiles=[(0, 0), (13, 3), (31, 7)], queries_per_tile=6)
-    print(f"prefill_chunk_bf16_128k sampled tiles: {kinds}", flush=True)
+_FULL = {}
+
+
+def _full_chunk():
+    """The 128K prefill workload at full size, run once per test process: the
+    chunk's outputs and tile sets, and the host copies the oracle reads."""
+    if not _FULL:
+        w = synth.PREFILL_WORKLOADS["prefill_chunk_bf16_128k"]
+        inp = synth.make_prefill_inputs(w, device=DEV)
+        K, V = inp["K"][0].contiguous(), inp["V"][0].contiguous()
+        Kc = torch.zeros((1, w.Hkv, oracle.n_compressed(w.T), 128), dtype=torch.bfloat16,
+                         device=DEV)
+        lens = torch.tensor([w.T], dtype=torch.int32, device=DEV)
+        sa.compress(inp["K"], Kc, torch.zeros_like(lens), lens)
+        O, lse, tidx, tcnt = sa.prefill_chunk(inp["Q"], w.q_start, K, V, Kc[0].contiguous(),
+                                              w.top_k, w.n_init, w.n_local, "softmax_sum")
+        torch.cuda.synchronize()
+        _FULL.update(w=w, Q=to_np(inp["Q"]), K=to_np(K), V=to_np(V), Kc=to_np(Kc[0]), O=to_np(O),
+                     lse=lse.cpu().numpy(), tidx=tidx.cpu().numpy(), tcnt=tcnt.cpu().numpy())
+    return _FULL
+
+
+@pytest.mark.parametrize("part", ["kvh0_all_tiles", "kvh5_all_tiles", "one_tile_per_kvh"])
+def test_prefill_chunk_bf16_128k_full(part):
+    """The 128K prefill chunk at full size (2048 queries, 32 tiles x 8 KV
+    heads): every tile of KV heads 0 and 5 and one tile of every KV head,
+    each with its tile set against the per-query oracle selection and all 64
+    queries' outputs against the oracle's causal attention over that set."""
+    f = _full_chunk()
+    w = f["w"]
+    G = w.Hq // w.Hkv
+    n_tiles = (w.Tq + 63) // 64
+    if part == "kvh0_all_tiles":
+        todo = [(t, 0) for t in range(n_tiles)]
+    elif part == "kvh5_all_tiles":
+        todo = [(t, 5) for t in range(n_tiles)]
+    else:
+        todo = [((5 * h + 3) % n_tiles, h) for h in range(w.Hkv)]
+    p = SelectParams(top_k=w.top_k, n_init=w.n_init, n_local=w.n_local, score_mode="softmax_sum")
+    kinds = []
+    for (t, h) in todo:
+        n = int(f["tcnt"][t, h])
+        got = f["tidx"][t, h, :n].tolist()
+        assert np.all(f["tidx"][t, h, n:] == -1)
+        lo, hi = 64 * t, min(64 * t + 64, w.Tq)
+        pos = np.arange(w.q_start + lo, w.q_start + hi)
+        qg = f["Q"][lo:hi, G * h:G * h + G]
+        ref, per_q = oracle.prefill_tile_select(qg, f["Kc"][h], pos, p, return_per_query=True)
+        nb = oracle.n_blocks(int(pos[-1]) + 1)
+        _, _, cand = oracle.candidate_sets(nb, w.n_init, w.n_local)
+        ok, why = tile_union_ok(got, ref, per_q, w.top_k, cand)
+        assert ok, ((t, h), why)
+        kinds.append(why)
+        o, l = oracle.tile_attention(qg, f["K"][h], f["V"][h], got, pos, 1.0)
+        assert_close(f["O"][lo:hi, G * h:G * h + G], o, "bf16", f"O tile {t} kvh {h}")
+        assert_close(f["lse"][lo:hi, G * h:G * h + G], l, "bf16", f"LSE tile {t} kvh {h}")
+    print(f"prefill_chunk_bf16_128k {part}: {len(todo)} tiles, {kinds.count('exact')} exact",
+          flush=True)
 
 
 def test_prefill_attend_reuses_tile_sets_across_layers():

@@ -148,8 +148,13 @@ def test_crosslayer_small_all_units():
 
 
 def test_crosslayer_bf16_64k_full_sampled():
+    """The cross-layer workload at full size (B = 32, 64K, 4 layers, 16 steps):
+    32 of the 256 (sequence, KV head) units, two per even sequence on varying
+    KV heads, checked at every step (selection, all 4 layers' outputs)."""
     w = synth.WORKLOADS["crosslayer_bf16_64k"]
-    _run_crosslayer(w, units=[(0, 0), (7, 3), (19, 5), (31, 7)])
+    units = [(b, h) for b in range(0, w.B, 2) for h in sorted({b % w.Hkv, (3 * b + 5) % w.Hkv})]
+    assert len(units) == 32                          # b % 8 and (3b + 5) % 8 differ for even b
+    _run_crosslayer(w, units=units)
 
 
 def test_tokenindex_forecast_bf16_128k_full_sampled():

@@ -167,6 +167,36 @@ def test_prefill_all_blocks_equals_causal_sdpa():
     assert np.allclose(r["O"], ref, rtol=1e-11, atol=1e-12)
 
 
+def test_prefill_tile_attention_equals_per_query_attention_and_causal_sdpa():
+    """oracle.tile_attention (all queries of a tile at once, causal mask) is
+    the per-query Eq. 5 of sparse_attention over each query's visible tokens,
+    and with every block chosen it is causal dense attention (SDPA)."""
+    T, q_start = 1300, 1216                               # a full tile and a partial one
+    Q, K, V, Kc = _prefill_case(T=T, q_start=q_start)
+    G = 4
+    rng = np.random.default_rng(5)
+    for t, n_q in ((0, 64), (1, T - q_start - 64)):
+        lo = 64 * t
+        pos = np.arange(q_start + lo, q_start + lo + n_q)
+        nb = oracle.n_blocks(int(pos[-1]) + 1)
+        for h in range(K.shape[0]):
+            blocks = sorted(set(rng.choice(nb, size=min(nb, 7), replace=False).tolist()) | {nb - 1})
+            O, L = oracle.tile_attention(Q[lo:lo + n_q, G * h:G * h + G], K[h], V[h], blocks, pos, 1.0)
+            for i, p_ in enumerate(pos):
+                o, l = oracle.sparse_attention(Q[lo + i, G * h:G * h + G], K[h], V[h],
+                                               block_tokens(blocks, int(p_) + 1), 1.0)
+                assert np.allclose(O[i], o, rtol=1e-12, atol=1e-13)
+                assert np.allclose(L[i], l, rtol=1e-12, atol=1e-13)
+            O, L = oracle.tile_attention(Q[lo:lo + n_q, G * h:G * h + G], K[h], V[h],
+                                         list(range(nb)), pos, 1.0)
+            qt = torch.from_numpy(Q[lo:lo + n_q, G * h:G * h + G].astype(np.float64)).permute(1, 0, 2)
+            kt = torch.from_numpy(K[h, :int(pos[-1]) + 1].astype(np.float64))[None].expand(G, -1, -1)
+            vt = torch.from_numpy(V[h, :int(pos[-1]) + 1].astype(np.float64))[None].expand(G, -1, -1)
+            mask = torch.arange(int(pos[-1]) + 1)[None, :] <= torch.from_numpy(pos)[:, None]
+            ref = Fn.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=1.0)
+            assert np.allclose(O, ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
 # ---------------------------------------------------------------- cross-layer reuse
 
 def test_crosslayer_step_shares_anchor_selection_and_grows_keys():
