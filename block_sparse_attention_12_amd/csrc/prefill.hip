@@ -79,27 +79,14 @@ __device__ __forceinline__ bf16x8_t lds_frag_rows(const bf16_t *lds, int m_row, 
 // distinct chunks, all 64 banks once.
 __device__ __forceinline__ int vt_swizzle(int row) { return 2 * (row & 7); }
 
-// A operand of V^T for the value product from a swizzled row-major V tile:
-// channel row 16 ct + (l%16), permuted keys of step kk: slots 0..3 hold keys
-// 32kk + 4g .. +3, slots 4..7 keys 32kk + 16 + 4g .. +3. ds_read_b64_tr_b16
-// transposes inside each 16-lane group: output lane i, element j comes from
-// source lane 4j + i/4, element i%4, so source lane s reads key row
-// key0 + s/4 at channels 16 ct + 4 (s%4) .. +3.
+// A operand of V^T for the value product from a swizzled row-major V tile
+// (the attention kernel's v_frag): channel row 16 ct + (l%16), permuted keys
+// of step kk: slots 0..3 hold keys 32kk + 4g .. +3, slots 4..7 keys 32kk + 16
+// + 4g .. +3. ds_read_b64_tr_b16 transposes inside each 16-lane group: output
+// lane i, element j comes from source lane 4j + i/4, element i%4, so source
+// lane s reads key row key0 + s/4 at channels 16 ct + 4 (s%4) .. +3.
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-__device__ __forceinline__ bf16x8_t vt_frag_tr(const bf16_t *lds, int ct, int kk, int g, int c16) {
-    s16x4_t h[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int row = 32 * kk + 16 * half + 4 * g + (c16 >> 2);
-        const int ch = 16 * ct + 4 * (c16 & 3);
-        const int elem = row * kD + (((ch >> 3) ^ vt_swizzle(row)) << 3) + (ch & 7);
-        h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + elem));
-    }
-    typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-    const s16x8_t v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-    return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // Two fp32 values to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
@@ -119,6 +106,7 @@ constexpr int kAtWaves = 8;
 constexpr int kAtThreads = 64 * kAtWaves;
 constexpr int kAtRt = 2;
 constexpr int kPfTileElems = 64 * kD;             // one 64 x 128 bf16 tile (16 KB)
+
 
 // This wave's query rows as B operands: qf[rt][ks] = Q[row 16 rt + (l%16)][32 ks + 8 g .. +8]
 // (zeros for queries past the chunk); qloc[rt] = the lane's query offset in the tile.
@@ -164,6 +152,26 @@ __device__ __forceinline__ void load_tile_regs(TileRegs &tr, __amdgpu_buffer_rsr
 __device__ __forceinline__ void store_tile_lds(bf16_t *lds, const TileRegs &tr, int tid) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) *reinterpret_cast<uint4 *>(lds + (kAtThreads * r + tid) * 8) = tr.c[r].v;
+}
+
+// The attention kernel keeps the K swizzle (measured free of LDS bank
+// conflicts; rows padded to 272 bytes instead measured a 2-way conflict on
+// these 16-byte reads) and stages V unswizzled in rows padded to 288 bytes: a
+// transposed read of 8 rows x 32 bytes then starts 8 banks further per row
+// (measured conflict-free), and every V fragment address is one per-lane base
+// plus a constant.
+constexpr int kAtKRow = 2 * kD;
+constexpr int kAtVRow = 2 * kD + 32;
+// Thread t loads the 16-byte chunks t % 16 of rows t / 16 and 32 + t / 16 of
+// a 64-row block starting blk_bytes into src (the block offset in the scalar
+// offset, the lane part fixed).
+__device__ __forceinline__ void load_tile_rows(TileRegs &tr, __amdgpu_buffer_rsrc_t src, uint32_t blk_bytes,
+                                               uint32_t lane_off) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const sa_v4i v = __builtin_amdgcn_raw_buffer_load_b128(src, (int)lane_off, (int)(blk_bytes + r * 32 * 2 * kD), 0);
+        tr.c[r].v = make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+    }
 }
 
 // Scores S^T = K Q^T of half a tile (keys 32hh .. 32hh+31) for this wave's rows:
@@ -483,9 +491,11 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     int Hq, int Hkv, int64_t q_start, int64_t Tq, int64_t T_cap, const int32_t *__restrict__ tile_idx,
     int tile_cap, const int32_t *__restrict__ tile_cnt, float qscale, void *__restrict__ O,
     int out_bf16, float *__restrict__ lse) {
-    // three stages, each the K tile then the V tile of one block
-    __shared__ __align__(16) bf16_t ring[3 * 2 * kPfTileElems];
+    // three K stages, then three V stages (block e in stage e % 3 of each),
+    // rows of kAtKRow / kAtVRow bytes
+    __shared__ __align__(16) char ring[3 * 64 * (kAtKRow + kAtVRow)];
     __shared__ int s_redo[kPfMaxPasses];
+    constexpr uint32_t kKTile = 64 * kAtKRow, kVTile = 64 * kAtVRow, kVStages = 3 * kKTile;
     const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -509,6 +519,34 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     int n = tile_cnt[blockIdx.x];
     n = n < 0 ? 0 : (n > tile_cap ? tile_cap : n);
     auto blk_at = [&](int e) -> int64_t { return ids[__builtin_amdgcn_readfirstlane(e)]; };
+
+    // Per-lane LDS byte offsets, fixed for the kernel: every fragment read and
+    // staging store below is one of these plus a constant (stage, key rows,
+    // channels), which the LDS instructions take as their immediate offset.
+    // K fragment of channel step ks: key row c16 (+ 32hh + 16j), swizzled
+    // chunk (4ks + g) ^ c16. V^T fragment: key row vrow (+ 32kk + 16 half),
+    // channels 4 (c16 % 4) .. +3 (+ 16ct). Staging: row tid / 16 (+ 32r),
+    // 16-byte chunk slot tid % 16, which for K holds the source chunk the
+    // swizzle puts there.
+    const int vrow = 4 * g + (c16 >> 2);
+    uint32_t koff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = (uint32_t)(c16 * kAtKRow + (((4 * ks + g) ^ c16) << 4));
+    uint32_t voff = kVStages + (uint32_t)(vrow * kAtVRow + 8 * (c16 & 3));
+    uint32_t kst = (uint32_t)(tid * 16);
+    uint32_t vst = kVStages + (uint32_t)((tid >> 4) * kAtVRow + (tid & 15) * 16);
+    // global lane offsets in a block (K: the swizzled source chunk)
+    uint32_t gofs_k = (uint32_t)((tid >> 4) * 2 * kD + (((tid & 15) ^ ((tid >> 4) & 15)) << 4));
+    uint32_t gofs_v = (uint32_t)((tid >> 4) * 2 * kD + (tid & 15) * 16);
+    char *lds = ring;
+    auto k_frag = [&](uint32_t off) { return as_bf16x8(*reinterpret_cast<const uint4 *>(lds + off)); };
+    auto v_frag = [&](uint32_t off) {                  // rows off and off + 16 rows, transposed
+        const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + off));
+        const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + off + 16 * kAtVRow));
+        typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+        const s16x8_t v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
 
     // causal mask inside the tile's own block: key <= query
     auto mask_causal = [&](f32x4_t (&s)[2][kAtRt], int hh) {
@@ -546,37 +584,62 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
     };
-    // Scores of both halves of a staged block: s[hh][j][rt].
-    auto block_scores = [&](f32x4_t (&s)[2][2][kAtRt], const bf16_t *sK) {
+    // Scores of half hh (keys 32hh .. 32hh + 31) of the block staged at K
+    // offsets kb (koff plus the stage): s[j][rt].
+    auto half_scores_at = [&](f32x4_t (&s)[2][kAtRt], const uint32_t (&kb)[4], int hh) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) half_scores(s[hh], sK, qf, hh, g, c16);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8_t a = k_frag(kb[ks] + (uint32_t)(32 * hh + 16 * j) * kAtKRow);
+#pragma unroll
+                for (int rt = 0; rt < kAtRt; ++rt) s[j][rt] = mfma16(a, qf[rt][ks], s[j][rt]);
+            }
     };
-    // Probabilities of a block's scores, then the value product O^T += V^T P^T
-    // with each accumulator's two steps back to back.
-    auto block_values = [&](const f32x4_t (&s)[2][2][kAtRt], const bf16_t *sV) {
-        bf16x8_t pb[2][kAtRt];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) half_probs(pb[hh], s[hh]);
+    // Probabilities of half hh's scores, then the value product O^T += V^T P^T
+    // over its 32 keys from the V tile at offset vb (voff plus the stage).
+    auto half_values = [&](const f32x4_t (&s)[2][kAtRt], uint32_t vb, int hh) {
+        bf16x8_t pb[kAtRt];
+        half_probs(pb, s);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const bf16x8_t a0 = vt_frag_tr(sV, ct, 0, g, c16);
-            const bf16x8_t a1 = vt_frag_tr(sV, ct, 1, g, c16);
+            const bf16x8_t a = v_frag(vb + 32 * ct + (uint32_t)(32 * hh) * kAtVRow);
 #pragma unroll
-            for (int rt = 0; rt < kAtRt; ++rt) {
-                o[ct][rt] = mfma16(a0, pb[0][rt], o[ct][rt]);
-                o[ct][rt] = mfma16(a1, pb[1][rt], o[ct][rt]);
-            }
+            for (int rt = 0; rt < kAtRt; ++rt) o[ct][rt] = mfma16(a, pb[rt], o[ct][rt]);
         }
     };
-    auto stage = [&](int e) { return ring + (e % 3) * 2 * kPfTileElems; };
+    // Issue order of one half step for the scheduler: the score products,
+    // each pair after its K fragment read (reads run two ahead) and followed
+    // by a share of the probabilities' vector work, then the value products
+    // with their V fragment reads.
+    auto half_step_order = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);         // LDS reads
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);     // VALU
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    };
 
     // Blocks go through a 3-stage LDS ring (block e in stage e % 3), and the
-    // loop is software-pipelined: step e computes block e + 1's scores (matrix
-    // products) in the same straight-line block as block e's probabilities
-    // (vector work) and value product, with block e + 2's loads in registers
-    // meanwhile; block e + 2 then goes into the stage block e - 1 used, and one
-    // barrier ends the step. Loads, products and stores past the last block
-    // are not skipped (they repeat the last block; their results go unused).
+    // loop is software-pipelined in half blocks: while one half's scores turn
+    // into probabilities (vector work), the next half's scores are computed
+    // (matrix products) in the same straight-line code, followed by the
+    // first half's value product. Block e + 2's loads are in registers during
+    // block e and go into the stage block e - 1 used; one barrier ends each
+    // block. Loads, products and stores past the last block are not skipped
+    // (they repeat the last block; their results go unused). The stage is one
+    // offset added to the lane bases per block.
     // The reference of a row is the max of its first half block; a row whose
     // running max later exceeds it by more than the slack (checked once per
     // pass) gets the larger reference and the workgroup runs its blocks again
@@ -592,54 +655,74 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int rt = 0; rt < kAtRt; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
         TileRegs rk, rv;
         auto load_block = [&](int64_t blk) {
-            load_tile_regs<false>(rk, rK, blk * kBlock, tid);
-            load_tile_regs<true>(rv, rV, blk * kBlock, tid);
+            const uint32_t bb = (uint32_t)blk * (kBlock * 2 * kD);
+            load_tile_rows(rk, rK, bb, gofs_k);
+            load_tile_rows(rv, rV, bb, gofs_v);
         };
-        auto store_block = [&](bf16_t *st) {
-            store_tile_lds(st, rk, tid);
-            store_tile_lds(st + kPfTileElems, rv, tid);
+        auto store_block = [&](int st) {
+            uint32_t kb = kst + (uint32_t)st * kKTile, vb = vst + (uint32_t)st * kVTile;
+            asm volatile("" : "+v"(kb), "+v"(vb));
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                *reinterpret_cast<uint4 *>(lds + kb + r * 32 * kAtKRow) = rk.c[r].v;
+                *reinterpret_cast<uint4 *>(lds + vb + r * 32 * kAtVRow) = rv.c[r].v;
+            }
         };
         if (n > 0) {
             load_block(blk_at(0));
-            store_block(stage(0));
+            store_block(0);
         }
         if (n > 1) {
             load_block(blk_at(1));
-            store_block(stage(1));
+            store_block(1);
         }
         __syncthreads();
+        f32x4_t sa[2][kAtRt], sb[2][kAtRt];        // scores of the first / second half
+        half_scores_at(sa, koff, 0);
+        if (n == 1 && last_diag) mask_causal(sa, 0);
         if (pass == 0 && n > 0) {                  // references from the first half block
-            f32x4_t s[2][kAtRt];
-            half_scores(s, ring, qf, 0, g, c16);
-            if (n == 1 && last_diag) mask_causal(s, 0);
 #pragma unroll
             for (int rt = 0; rt < kAtRt; ++rt) {
-                float mx = fmaxf(fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), fmaxf(s[0][rt][2], s[0][rt][3])),
-                                 fmaxf(fmaxf(s[1][rt][0], s[1][rt][1]), fmaxf(s[1][rt][2], s[1][rt][3]))) * qscale;
+                float mx = fmaxf(fmaxf(fmaxf(sa[0][rt][0], sa[0][rt][1]), fmaxf(sa[0][rt][2], sa[0][rt][3])),
+                                 fmaxf(fmaxf(sa[1][rt][0], sa[1][rt][1]), fmaxf(sa[1][rt][2], sa[1][rt][3]))) *
+                           qscale;
                 mx = fmaxf(mx, shfl_xor(mx, 16));
                 mx = fmaxf(mx, shfl_xor(mx, 32));
                 m[rt] = mx == -INFINITY ? 0.f : mx;
             }
         }
-        f32x4_t sc[2][2][kAtRt];
-        block_scores(sc, stage(0));
         for (int e = 0; e < n; ++e) {
-            if (e == n - 1 && last_diag) {
-                mask_causal(sc[0], 0);
-                mask_causal(sc[1], 1);
+            const int st = e % 3, st1 = st == 2 ? 0 : st + 1, st2 = st == 0 ? 2 : st - 1;
+            const bool diag = e == n - 1 && last_diag;
+            if (diag) {                            // a branch, not selects in every block
+                asm volatile("");
+                mask_causal(sa, 0);
             }
+            // this block's stage bases, one register each: every read below
+            // is a base plus an immediate (kept opaque so the compiler does
+            // not rebuild each address from the loop counter)
+            uint32_t kb0[4], kb1[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                kb0[ks] = koff[ks] + (uint32_t)st * kKTile;
+                kb1[ks] = koff[ks] + (uint32_t)st1 * kKTile;
+            }
+            uint32_t vb0 = voff + (uint32_t)st * kVTile;
+            asm volatile("" : "+v"(kb0[0]), "+v"(kb0[1]), "+v"(kb0[2]), "+v"(kb0[3]), "+v"(kb1[0]),
+                              "+v"(kb1[1]), "+v"(kb1[2]), "+v"(kb1[3]), "+v"(vb0));
             load_block(blk_at(e + 2 < n ? e + 2 : n - 1));
-            f32x4_t sn[2][2][kAtRt];
-            block_scores(sn, stage(e + 1));
-            block_values(sc, stage(e) + kPfTileElems);
-            store_block(stage(e + 2));
+            half_scores_at(sb, kb0, 1);
+            half_values(sa, vb0, 0);
+            half_step_order();
+            if (diag) {
+                asm volatile("");
+                mask_causal(sb, 1);
+            }
+            half_scores_at(sa, kb1, 0);
+            half_values(sb, vb0, 1);
+            half_step_order();
+            store_block(st2);
             __syncthreads();                       // block e + 2 staged; stage e % 3 free
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int rt = 0; rt < kAtRt; ++rt) sc[hh][j][rt] = sn[hh][j][rt];
         }
         // end of pass: raise references a row outgrew; workgroup-wide redo
         bool redo = false;
