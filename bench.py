@@ -300,7 +300,7 @@ def bench_decode(args, w):
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "step_call_ms": round(step_call_ms, 5),
     }
-    separate = {"kernel": "sparse_attn_decode called alone (decode_kernel + combine_kernel)",
+    separate = {"kernel": "sparse_attn_decode called alone (decode_kernel with the split merge)",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(f"{w.name}_decode"), "bytes_per_launch": attn_bytes}
@@ -309,8 +309,9 @@ def bench_decode(args, w):
         # scorer with the append, then the attention with the top-k prologue
         # and the in-kernel split merge) timed together with events around
         # every call, on the step's algorithmic bytes
+        scorer = "score_softmax_kernel" if w.score_mode == "softmax_sum" else "score_raw_kernel"
         out["roofline"] = {"bound": "hbm",
-                           "kernel": "sparse_attn_decode_step call (score_raw_kernel with the "
+                           "kernel": f"sparse_attn_decode_step call ({scorer} with the "
                                      "append; decode_kernel with the top-k and the split merge)",
                            "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -647,7 +648,7 @@ def bench_cobs(args, w):
         "phase_ms": {k: round(v, 5) for k, v in mean.items()},
         "step_bytes": step_bytes, "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm",
-                     "kernel": "sparse_attn_decode (decode_kernel + combine_kernel)",
+                     "kernel": "sparse_attn_decode (decode_kernel with the split merge)",
                      "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"{w.name}_decode"),
@@ -763,7 +764,7 @@ def bench_token(args, w):
                      "bytes_per_launch": sel_bytes,
                      "measured_ceiling": {"what": "stream read (sparse_attn_stream_read, 4 GiB)",
                                           "GB/s": ceil, "frac": round(sel_gbs / ceil, 4)}},
-        "attend": {"kernel": "sparse_attn_token_decode (gathered rows + combine), one layer",
+        "attend": {"kernel": "sparse_attn_token_decode (gathered rows, split merge in the kernel), one layer",
                    "GB/s": round(attn_gbs, 1), "frac_of_peak": round(attn_gbs / HBM_PEAK_GBS, 4),
                    "frac_of_ceiling": round(attn_gbs / ceil, 4), "bytes": attn_bytes},
         "planted_tokens_recovered": round(hit / max(tot, 1), 4),
@@ -864,7 +865,7 @@ def bench_crosslayer(args, w):
     scan = w.B * w.Hkv * n_compressed(L) * row + w.B * w.Hq * row
     step_bytes = attn + scan
     # dominant kernel: the attention of a follower layer over the shared sets
-    # (one sparse_attn_decode call: decode_kernel + combine_kernel), timed with
+    # (one sparse_attn_decode call: decode_kernel with the split merge), timed with
     # events around each call on the launch stream, at the last step's lengths
     per_layer_attn = attn // w.layers
     n_ev = max(10, min(args.steps, 60))
@@ -892,8 +893,8 @@ def bench_crosslayer(args, w):
         "step_hbm_gbs": round(step_bytes / (gpu_ms * 1e-3) / 1e9, 1),
     }
     out["roofline"] = {"bound": "hbm",
-                       "kernel": "sparse_attn_decode of a follower layer (decode_kernel + "
-                                 "combine_kernel) over the anchor's block sets",
+                       "kernel": "sparse_attn_decode of a follower layer (decode_kernel with "
+                                 "the split merge) over the anchor's block sets",
                        "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                        "traffic": recorded_traffic(f"{w.name}_decode"),
