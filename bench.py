@@ -590,7 +590,6 @@ def bench_cobs(args, w):
     append_bytes = sum((L // 64) - ((L - 1) // 64) for L in lens) * w.Hkv * (64 * row + 2 * row)
     step_bytes = attn_bytes + sel_bytes + append_bytes
     attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
-    step_gbs = step_bytes / (step_call_ms * 1e-3) / 1e9
     sel_gbs = sel_bytes / (mean["select"] * 1e-3) / 1e9
 
     # selection quality on the first replica: second order, first order, compressed keys
