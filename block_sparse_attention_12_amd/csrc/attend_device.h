@@ -161,11 +161,19 @@ __device__ __forceinline__ void attend_share(const QFrag<T, G> &q, const T *__re
 
     // item of this wave set's k-th iteration
     auto item_of = [&](int k) { return wset + k * NWS; };
-    // block id of share item it (a uniform scalar load), or -1 (no rows) past
-    // the share or out of range
+    // The share's block ids, read once: lane i holds item i's id (a share never
+    // has more than 64 items: every split takes at most 64 list entries), so
+    // the loop takes ids with v_readlane and no load of an id waits, in order,
+    // behind the K/V loads in flight. -1 (no rows) past the share or out of range.
+    int id_lane = -1;
+    if constexpr (!ROWS) {
+        if (lane < nblk) {
+            const int blk = irow[lane];
+            id_lane = (blk >= 0 && blk < nb) ? blk : -1;
+        }
+    }
     auto block_id = [&](int it) -> int {
-        const int blk = it < nblk ? irow[it] : -1;
-        return (blk >= 0 && blk < nb) ? blk : -1;
+        return it < nblk ? __builtin_amdgcn_readlane(id_lane, it & 63) : -1;
     };
     // Issues the block's K/V loads unconditionally: id -1 maps every row to an
     // out-of-range offset, which reads zeros and moves no bytes, so the wait
