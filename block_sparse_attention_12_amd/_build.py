@@ -23,7 +23,11 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Wno-unused-command-line-argument"]
 # prefill.hip: no NaN inputs are assumed (scores are finite or -inf), so max
 # operations need no quieting of their operands.
-PER_FILE = {"compress.hip": ["-ffp-contract=off"], "cobs.hip": ["-ffp-contract=off"], "prefill.hip": ["-fno-honor-nans"]}
+# decode.hip: matrix-core accumulators in ordinary VGPRs (the online softmax
+# rescales them with vector instructions; the accumulation registers would
+# need copies around every rescale).
+PER_FILE = {"compress.hip": ["-ffp-contract=off"], "cobs.hip": ["-ffp-contract=off"],
+            "prefill.hip": ["-fno-honor-nans"], "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -26,6 +26,12 @@
 // wave-private LDS slot. Logits are in base-2 units (scaled by scale * log2 e)
 // so each exponential is one exp2. At the end the waves' (max, sum, weighted
 // values) meet in LDS.
+//
+// bf16 block lists take attend_share_mfma instead: the same loads and block
+// ring, with q.k and P.V on the matrix cores (4 + 8 MFMA per wave and block)
+// and the softmax on one head's 4 logits per lane, about a fifth of the vector
+// instructions of the path above. That path still serves fp32 inputs and
+// token lists.
 #pragma once
 
 #include <math.h>
@@ -75,6 +81,45 @@ __device__ __forceinline__ float qk(const QFrag<float, G> &q, int g, const Raw8<
     return a;
 }
 
+// bf16 block lists run both products on the matrix cores (attend_share_mfma).
+typedef __attribute__((ext_vector_type(8))) __bf16 mf_bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short mf_s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float mf_f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float mf_f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 mf_bf16x2_t;
+
+// q of the group as the B operand of S = K q^T on v_mfma_f32_16x16x32_bf16
+// (four steps of 32 channels): lane l holds head l % 16 (zeros from G on),
+// channels 32 s + 8 (l / 16) .. +7 of step s.
+struct QMfma { uint4 w[4]; };
+template <int G>
+__device__ __forceinline__ void load_q_mfma(const bf16_t *group, int lane, QMfma &q) {
+    const int h = lane & 15, c = 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        q.w[s] = h < G ? *reinterpret_cast<const uint4 *>(group + (int64_t)h * kD + 32 * s + c)
+                       : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// x combined with the lane 16 (32) apart, on v_permlane16_swap (32_swap):
+// with both operands x, each lane's two results are x of the lane pair.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Where the reduced logits of a group of G heads live: NV logits per lane;
 // for G < 4 each total sits on REP = 4/G lanes.
 template <int G> struct HeadLayout {
@@ -118,6 +163,62 @@ struct AttendOut {
     float *lse;
 };
 
+// The waves' (max, sum, weighted values) in sm -> the share's result for the
+// G head rows from row_base (O and LSE, or a partial row). Starts and ends
+// with a workgroup barrier.
+template <int G, int NW, int MODE>
+__device__ __forceinline__ void merge_waves(AttendSmem<G, NW> &sm, int64_t row_base,
+                                            const AttendOut &out) {
+    constexpr int NT = 64 * NW;
+    const int tid = threadIdx.x;
+    __syncthreads();
+    // thread -> (head g, channels 2c, 2c+1)
+    for (int pair = tid; pair < G * (kD / 2); pair += NT) {
+        const int g = pair / (kD / 2);
+        const int c2 = (pair % (kD / 2)) * 2;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
+        float lsum = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = sm.m[w][g];
+            const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+            lsum = fmaf(wt, sm.l[w][g], lsum);
+            a0 = fmaf(wt, sm.acc[w][g][c2], a0);
+            a1 = fmaf(wt, sm.acc[w][g][c2 + 1], a1);
+        }
+        const int64_t row = row_base + g;                    // query head row
+        if constexpr (MODE != kAttendDirect) {
+            float *dst = out.part + (row * out.n_split + out.split) * kPartStride;
+            if constexpr (MODE == kAttendPartialCoherent) {
+                store_dev(dst + c2, a0);
+                store_dev(dst + c2 + 1, a1);
+                if (c2 == 0) {
+                    store_dev(dst + kD, M);
+                    store_dev(dst + kD + 1, lsum);
+                }
+            } else {
+                reinterpret_cast<float2 *>(dst)[c2 / 2] = make_float2(a0, a1);
+                if (c2 == 0) {
+                    dst[kD] = M;
+                    dst[kD + 1] = lsum;
+                }
+            }
+            continue;
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        if (out.out_bf16) {
+            const uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
+            reinterpret_cast<uint32_t *>(out.O)[(row * kD + c2) / 2] = w;
+        } else {
+            reinterpret_cast<float2 *>(out.O)[(row * kD + c2) / 2] = make_float2(a0 * inv, a1 * inv);
+        }
+        if (out.lse && c2 == 0) out.lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();                             // sm may be reused by the caller
+}
+
 // One share of a unit: items [e_lo, e_lo + nblk) of the list (ROWS = false:
 // block ids, irow already at entry e_lo; ROWS = true: 64-entry tiles of token
 // ids, irow at the list start, n entries). L is the unit's visible length,
@@ -133,7 +234,6 @@ __device__ __forceinline__ void attend_share(const QFrag<T, G> &q, const T *__re
     constexpr int NV = HL::NV;
     constexpr int NVAL = 4 * G;                  // logits per row group per block (4 rows x G heads)
     constexpr int NWS = NW / 4;                  // wave sets
-    constexpr int NT = 64 * NW;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wq = wave & 3, wset = wave >> 2;
     const int lane16 = lane & 15, rgrp = lane >> 4;
@@ -355,53 +455,153 @@ __device__ __forceinline__ void attend_share(const QFrag<T, G> &q, const T *__re
             }
         }
     }
-    __syncthreads();
+    merge_waves<G, NW, MODE>(sm, row_base, out);
+}
 
-    // ---- merge the waves: thread -> (head g, channels 2c, 2c+1)
-    for (int pair = tid; pair < G * (kD / 2); pair += NT) {
-        const int g = pair / (kD / 2);
-        const int c2 = (pair % (kD / 2)) * 2;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
-        float lsum = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float mw = sm.m[w][g];
-            const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-            lsum = fmaf(wt, sm.l[w][g], lsum);
-            a0 = fmaf(wt, sm.acc[w][g][c2], a0);
-            a1 = fmaf(wt, sm.acc[w][g][c2 + 1], a1);
-        }
-        const int64_t row = row_base + g;                    // query head row
-        if constexpr (MODE != kAttendDirect) {
-            float *dst = out.part + (row * out.n_split + out.split) * kPartStride;
-            if constexpr (MODE == kAttendPartialCoherent) {
-                store_dev(dst + c2, a0);
-                store_dev(dst + c2 + 1, a1);
-                if (c2 == 0) {
-                    store_dev(dst + kD, M);
-                    store_dev(dst + kD + 1, lsum);
-                }
-            } else {
-                reinterpret_cast<float2 *>(dst)[c2 / 2] = make_float2(a0, a1);
-                if (c2 == 0) {
-                    dst[kD] = M;
-                    dst[kD + 1] = lsum;
-                }
-            }
-            continue;
-        }
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        if (out.out_bf16) {
-            const uint32_t w = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
-            reinterpret_cast<uint32_t *>(out.O)[(row * kD + c2) / 2] = w;
-        } else {
-            reinterpret_cast<float2 *>(out.O)[(row * kD + c2) / 2] = make_float2(a0 * inv, a1 * inv);
-        }
-        if (out.lse && c2 == 0) out.lse[row] = lsum > 0.f ? (M + log2f(lsum)) * kLn2 : -INFINITY;
+// One share of a unit's bf16 block list on the matrix cores (same contract as
+// attend_share with ROWS = false). Wave w still owns rows 16 (w % 4) .. +15 of
+// each block; with g = lane / 16 and h = lane % 16:
+//   S = K q^T, v_mfma_f32_16x16x32_bf16 x 4: the A operand's row h is key row
+//     h / 4 + 4 (h % 4) of the wave's 16 (lane l loads channels 32 s + 8 g of
+//     it in step s), so output element j of lane l is the logit of key
+//     g + 4 j for head h: exactly the keys whose V rows the lane loads.
+//   O^T += V^T P^T, v_mfma_f32_16x16x16_bf16 x 8: P^T is the B operand as it
+//     comes out of the softmax (element j = key g + 4 j, head h, rounded to
+//     bf16); tile t's A operand row h is channel 8 h + t, assembled with
+//     v_perm from the lane's four V rows. Lane l accumulates head h,
+//     channels 32 g + 8 j + t (element j of tile t).
+// The softmax runs per lane on its head's 4 logits (max over the wave's 16
+// keys by two lane swaps). The reference is raised only when a block's max
+// exceeds it by more than kSlack (log2 units): after the first block almost
+// never, so the accumulators are rarely touched by vector instructions; the
+// probabilities stay below 2^kSlack (sums far inside the fp32 range). Heads
+// G .. 15 carry zero queries and are discarded. exp2 is the hardware
+// instruction (arguments <= kSlack; results below 2^-126 flush to zero).
+template <int G, int NW, int MODE>
+__device__ __forceinline__ void attend_share_mfma(const QMfma &q, const bf16_t *__restrict__ K,
+                                                  const bf16_t *__restrict__ V, int64_t T_cap,
+                                                  int unit, int64_t L, const int32_t *irow,
+                                                  int nblk, float qscale, int64_t row_base,
+                                                  const AttendOut &out, AttendSmem<G, NW> &sm) {
+    constexpr int NWS = NW / 4;                  // wave sets
+    constexpr float kSlack = 32.f;
+    constexpr uint32_t kRowBytes = kD * sizeof(bf16_t);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wq = wave & 3, wset = wave >> 2;
+    const int h = lane & 15, g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
+    const uint32_t k_lane = (16 * wq + (h >> 2) + 4 * (h & 3)) * kRowBytes + 16 * g;
+    const uint32_t v_lane = (16 * wq + g) * kRowBytes + 16 * h;
+    const int64_t nb = n_blocks(L);
+
+    // block ids as in attend_share: lane i holds item i's id (-1: none)
+    int id_lane = -1;
+    if (lane < nblk) {
+        const int blk = irow[lane];
+        id_lane = (blk >= 0 && blk < nb) ? blk : -1;
     }
-    __syncthreads();                             // sm may be reused by the caller
+    auto item_of = [&](int k) { return wset + k * NWS; };
+    auto block_id = [&](int it) -> int {
+        return it < nblk ? __builtin_amdgcn_readlane(id_lane, it & 63) : -1;
+    };
+    // loads of an absent block (id -1) use an out-of-range offset: zeros, no bytes
+    auto issue = [&](BlockRegs<bf16_t> &r, int blk) {
+        r.t0 = (int64_t)blk * kBlock;
+        const uint32_t base = blk < 0 ? 0xffffffffu : (uint32_t)blk * (kBlock * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            load_raw_nt(rK, blk < 0 ? 0xffffffffu : base + k_lane + 64 * i, r.k[i]);
+            load_raw_nt(rV, blk < 0 ? 0xffffffffu : base + v_lane + i * (4 * kRowBytes), r.v[i]);
+        }
+    };
+
+    float m_ref = -INFINITY, l_lane = 0.f;
+    mf_f32x4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = (mf_f32x4_t){0.f, 0.f, 0.f, 0.f};
+    auto process = [&](const BlockRegs<bf16_t> &r) {
+        if (r.t0 < 0) return;                    // absent block: nothing visible
+        mf_f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mf_bf16x8_t, r.k[st].v),
+                                                      __builtin_bit_cast(mf_bf16x8_t, q.w[st]), s,
+                                                      0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = s[j] * qscale;
+        if (r.t0 + kBlock > L) {                 // the visible length ends inside this block
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (r.t0 + 16 * wq + g + 4 * j >= L) x[j] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = max_xor32(max_xor16(mx));
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + kSlack)) {     // wave-uniform
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            l_lane *= alpha;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+        }
+        const float mref = m_ref == -INFINITY ? 0.f : m_ref;
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[j] - mref);
+        l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+        const uint2 pw = make_uint2(
+            __builtin_bit_cast(uint32_t, __builtin_convertvector((mf_f32x2_t){p[0], p[1]}, mf_bf16x2_t)),
+            __builtin_bit_cast(uint32_t, __builtin_convertvector((mf_f32x2_t){p[2], p[3]}, mf_bf16x2_t)));
+        const mf_s16x4_t pb = __builtin_bit_cast(mf_s16x4_t, pw);
+        const uint32_t vw[4][4] = {{r.v[0].v.x, r.v[0].v.y, r.v[0].v.z, r.v[0].v.w},
+                                   {r.v[1].v.x, r.v[1].v.y, r.v[1].v.z, r.v[1].v.w},
+                                   {r.v[2].v.x, r.v[2].v.y, r.v[2].v.z, r.v[2].v.w},
+                                   {r.v[3].v.x, r.v[3].v.y, r.v[3].v.z, r.v[3].v.w}};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            // channel 8 h + t of keys g, g + 4 (low word) and g + 8, g + 12
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            const uint2 a = make_uint2(__builtin_amdgcn_perm(vw[1][t >> 1], vw[0][t >> 1], sel),
+                                       __builtin_amdgcn_perm(vw[3][t >> 1], vw[2][t >> 1], sel));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mf_s16x4_t, a), pb,
+                                                              acc[t], 0, 0, 0);
+        }
+    };
+
+    // three register buffers, as in attend_share
+    BlockRegs<bf16_t> bufA, bufB, bufC;
+    issue(bufA, block_id(item_of(0)));
+    issue(bufB, block_id(item_of(1)));
+#pragma unroll 1
+    for (int k = 0; item_of(k) < nblk; k += 3) {
+        issue(bufC, block_id(item_of(k + 2)));
+        __builtin_amdgcn_sched_barrier(0);
+        process(bufA);
+        issue(bufA, block_id(item_of(k + 3)));
+        __builtin_amdgcn_sched_barrier(0);
+        if (item_of(k + 1) < nblk) process(bufB);
+        issue(bufB, block_id(item_of(k + 4)));
+        __builtin_amdgcn_sched_barrier(0);
+        if (item_of(k + 2) < nblk) process(bufC);
+    }
+
+    // the wave's (reference, sum, weighted values) of heads 0 .. G-1
+    l_lane = sum_xor32(sum_xor16(l_lane));
+    if (h < G) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float4 *dst = reinterpret_cast<float4 *>(&sm.acc[wave][h][32 * g + 8 * j]);
+            dst[0] = make_float4(acc[0][j], acc[1][j], acc[2][j], acc[3][j]);
+            dst[1] = make_float4(acc[4][j], acc[5][j], acc[6][j], acc[7][j]);
+        }
+        if (g == 0) {
+            sm.m[wave][h] = m_ref;
+            sm.l[wave][h] = l_lane;
+        }
+    }
+    merge_waves<G, NW, MODE>(sm, row_base, out);
 }
 
 }  // namespace sa

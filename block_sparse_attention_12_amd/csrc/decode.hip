@@ -7,8 +7,8 @@
 // 256-thread workgroup streams its share's K and V blocks (64 rows x 256 B
 // each for bf16, contiguous in HBM) once and serves all G query heads of the
 // group from that single read (attend_device.h: GQA packing for G = 1, 2, 4
-// or 8, DPP transposed reductions, online softmax without workgroup
-// barriers inside the block loop).
+// or 8, both products on the matrix cores for bf16 block lists, online
+// softmax without workgroup barriers inside the block loop).
 //
 // Split merge: every workgroup writes (max, sum, weighted values) for its G
 // heads with device-scope stores and counts itself in its unit's counter word
@@ -137,8 +137,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     int64_t L = seq_lens[b];
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
     // the group's queries: loaded first, so the load overlaps the top-k below
+    // (bf16 block lists: in the matrix-core operand layout)
+    constexpr bool kMfma = __is_same(T, bf16_t) && !ROWS;
+    const T *Qg = Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD;
     QFrag<T, G> q;
-    load_q<G>(Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD + (tid & 15) * kLaneElems, q);
+    QMfma qm;
+    if constexpr (kMfma) load_q_mfma<G>(Qg, tid & 63, qm);
+    else load_q<G>(Qg + (tid & 15) * kLaneElems, q);
     int n;
     const int32_t *idx_row;
     if constexpr (SG > 0) {
@@ -167,9 +172,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int nblk = (e_lo + per < n_items ? e_lo + per : n_items) - e_lo;
     const AttendOut out{part, n_split, split, O, out_bf16, lse};
     const int64_t row_base = (int64_t)b * Hq + (int64_t)kvh * G;
-    attend_share<T, G, ROWS, 4, DIRECT ? kAttendDirect : kAttendPartialCoherent>(
-        q, K, V, T_cap, unit, L, idx_row + (ROWS ? 0 : e_lo), n, e_lo, nblk, qscale, row_base,
-        out, sm);
+    constexpr int kMode = DIRECT ? kAttendDirect : kAttendPartialCoherent;
+    if constexpr (kMfma)
+        attend_share_mfma<G, 4, kMode>(qm, K, V, T_cap, unit, L, idx_row + e_lo, nblk, qscale,
+                                       row_base, out, sm);
+    else
+        attend_share<T, G, ROWS, 4, kMode>(q, K, V, T_cap, unit, L, idx_row + (ROWS ? 0 : e_lo), n,
+                                           e_lo, nblk, qscale, row_base, out, sm);
     if constexpr (!DIRECT) {
         wait_own_stores();
         __syncthreads();
