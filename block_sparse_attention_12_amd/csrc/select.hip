@@ -83,11 +83,17 @@ __global__ __launch_bounds__(kSelThreads) void score_raw_kernel(
 // ---------------------------------------------------------------- softmax scores
 
 // APPEND (one-call decode step): entries completed between lens_prev and
-// seq_lens are not read from Kc; the group that owns such an entry forms it
-// from the keys (the append's arithmetic), writes it to Kc and scores it in
-// extra iterations after the main loop. A lane's new entries come after all of
-// its old ones in the main loop's order, so every running (max, sum) sees the
-// same values in the same order as with a separate append before the launch.
+// seq_lens are not read from Kc; they are formed from the keys (the append's
+// arithmetic), written to Kc and scored in extra iterations after the main
+// loop. A lane's new entries come after all of its old ones in the main loop's
+// order, so every running (max, sum) sees the same values in the same order as
+// with a separate append before the launch. bf16: the workgroup stages each
+// new entry's 32 keys in LDS (two per row group, all in flight at once) and the
+// row group that scores the entry sums them in token order, once, before the
+// scoring iterations (formation inside the unrolled iteration would set the
+// register count, and with it the occupancy, of every workgroup of the launch);
+// the group takes the chunk's last new entry from LDS and earlier ones from its
+// own stores. fp32: formed in the iteration from per-lane key loads.
 template <typename T, int G, bool APPEND>
 __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     const T *__restrict__ sel, int H_sel, const T *__restrict__ Kc, int Hkv, int64_t nc_cap,
@@ -123,9 +129,10 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
     const int64_t base = (int64_t)blockIdx.x * kSoftmaxChunk;
     // one iteration: dot products, reduction, online update over the entries
     // read from Kc (below nc_old) or, with FORM, the new ones formed from the keys
-    // bf16 with a single new entry: its 32 keys staged in LDS (see below)
+    // bf16 appends: a new entry's 32 keys staged in LDS, the chunk's last new entry
     __shared__ uint4 s_rows[2 * kCmpStride][16];
-    const bool one_new = APPEND && nc == nc_old + 1;
+    __shared__ uint4 s_last[16];
+    int64_t j_last = -1;
     auto iteration = [&](int it, auto form) {
         constexpr bool FORM = decltype(form)::value;
         auto live = [&](int64_t je) { return FORM ? (je >= nc_old && je < nc) : je < nc_old; };
@@ -137,14 +144,14 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
             if (live(je)) {
                 if constexpr (APPEND) {
                     if constexpr (FORM) {
-                        const T *Ku = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
-                        if constexpr (sizeof(T) == 2) {
-                            if (one_new) entry_from_rows(s_rows, lane16, r[e]);
-                            else compress_entry_raw(Ku, je, r[e]);
+                        T *kw = Kc_w + ((int64_t)unit * nc_cap + je) * kD + lane16 * kLaneElems;
+                        if constexpr (sizeof(T) == 2) {          // formed before the iterations
+                            if (je == j_last) r[e].v = s_last[lane16];
+                            else load_raw(kw, r[e]);
                         } else {
-                            compress_entry_raw(Ku, je, r[e]);
+                            compress_entry_raw(K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems, je, r[e]);
+                            store_raw(kw, r[e]);
                         }
-                        store_raw(Kc_w + ((int64_t)unit * nc_cap + je) * kD + lane16 * kLaneElems, r[e]);
                         continue;
                     }
                 }
@@ -187,20 +194,25 @@ __global__ __launch_bounds__(kSelThreads) void score_softmax_kernel(
         // the iterations of this chunk that hold new entries (uniform per workgroup)
         const int64_t a = nc_old > base ? nc_old : base;
         const int64_t z = nc < base + kSoftmaxChunk ? nc : base + kSoftmaxChunk;
-        // bf16, one new entry: the workgroup loads its 32 keys (two per row
-        // group, all in flight at once) into LDS, and the owning group sums
-        // them in token order (per-lane loads of all 32 would wait in turn)
         if constexpr (sizeof(T) == 2) {
-            if (a < z && one_new) {                      // uniform per workgroup
-                const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+            const T *Ka = K + (int64_t)unit * T_cap * kD + lane16 * kLaneElems;
+#pragma unroll 1
+            for (int64_t j = a; j < z; ++j) {             // uniform per workgroup
                 Raw8<T> rows[2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    load_raw(Ka + (nc_old * kCmpStride + 2 * group + i) * kD, rows[i]);
+                for (int i = 0; i < 2; ++i) load_raw(Ka + (j * kCmpStride + 2 * group + i) * kD, rows[i]);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) s_rows[2 * group + i][lane16] = rows[i].v;
                 __syncthreads();
+                if (group == (int)(((j - base) % PER_IT) / EPI)) {     // the group that scores entry j
+                    Raw8<T> t;
+                    entry_from_rows(s_rows, lane16, t);
+                    store_raw(Kc_w + ((int64_t)unit * nc_cap + j) * kD + lane16 * kLaneElems, t);
+                    if (j == z - 1) s_last[lane16] = t.v;
+                }
+                __syncthreads();                          // s_rows is refilled for the next entry
             }
+            j_last = z - 1;
         }
 #pragma unroll 1
         for (int it = (int)((a - base) / PER_IT); a < z && it <= (int)((z - 1 - base) / PER_IT); ++it)
