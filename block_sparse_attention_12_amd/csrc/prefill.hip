@@ -23,10 +23,11 @@
 // swizzle, read as V^T operands with ds_read_b64_tr_b16.
 //
 // Softmax: a row's reference (log2 units) is the max of its first half block;
-// probabilities are taken against it without rescaling the accumulators. A
-// row whose scores outgrow the reference by more than 2^64 voids the pass and
-// the workgroup runs its blocks again with the raised reference (the result
-// does not depend on the reference, only overflow does).
+// probabilities are taken against it without rescaling the accumulators. In
+// the attention kernel the row sums come from the matrix cores (the value
+// product with an all-ones tile), and a pass whose row sum passes 2^64 is void:
+// a pass that tracks the rows' maxima follows, then one against the raised
+// references (the result does not depend on the reference, only overflow does).
 //
 // Kernels:
 //   prefill_score_kernel  per (tile, KV head), two software-pipelined sweeps
@@ -48,6 +49,8 @@
 // Workgroups are numbered tile * Hkv + kvh so the tiles of one KV head land on
 // the same XCD (round-robin dispatch over 8 XCDs) and share its L2.
 #include <math.h>
+
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -477,13 +480,14 @@ __global__ __launch_bounds__(kPfThreads) void prefill_union_kernel(
 
 // ------------------------------------------------------------------ attention
 
-// A row's softmax reference only moves when a block's row max exceeds it by more
-// than this (log2 units): probabilities then stay below 2^64, far from fp32 /
-// bf16 overflow. The result does not depend on the reference: numerator and
-// denominator share it.
+// A pass is kept when every row sum of probabilities (against the row's
+// reference, log2 units) stays within 2^kRescaleSlack: every probability is then
+// below it too, far from fp32 / bf16 overflow. The result does not depend on the
+// reference: numerator and denominator share it.
 constexpr float kRescaleSlack = 64.f;
-// Passes over a tile's blocks: each redo raises some reference by more than the
-// slack and the second pass can no longer outgrow any (the cap only bounds the loop).
+constexpr float kSumLimit = 18446744073709551616.f;     // 2^kRescaleSlack
+// Passes over a tile's blocks: at most fast, tracking, fast (the cap only
+// bounds the loop).
 constexpr int kPfMaxPasses = 4;
 
 __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
@@ -508,7 +512,11 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     load_q_frags(qf, qloc, Q, Hq, kvh, q_first, Tq, wave, lane);
 
     f32x4_t o[8][kAtRt];
-    float m[kAtRt], lsum[kAtRt], mrun[kAtRt];      // reference (log2 units), partial sum, running max
+    // per row tile: the row sums (every element of a lane holds its row's sum),
+    // reference (log2 units), running max (tracking passes only)
+    f32x4_t osum[kAtRt];
+    float m[kAtRt], mrun[kAtRt];
+    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 #pragma unroll
     for (int rt = 0; rt < kAtRt; ++rt) m[rt] = -INFINITY;
 
@@ -561,10 +569,11 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                     if (16 * j + i > q) s[j][rt][i] = -INFINITY;
         }
     };
-    // Exponents against the row references (running max kept), probabilities as
-    // bf16 B operands (keys 32hh + 4g + i for j = 0, then 32hh + 16 + 4g + i),
-    // row sums.
-    auto half_probs = [&](bf16x8_t (&pb)[kAtRt], const f32x4_t (&s)[2][kAtRt]) {
+    // Exponents against the row references (TRACK: running max kept),
+    // probabilities as bf16 B operands (keys 32hh + 4g + i for j = 0, then
+    // 32hh + 16 + 4g + i). The row sums are taken by the value product.
+    auto half_probs = [&](bf16x8_t (&pb)[kAtRt], const f32x4_t (&s)[2][kAtRt], auto track) {
+        constexpr bool TRACK = decltype(track)::value;
 #pragma unroll
         for (int rt = 0; rt < kAtRt; ++rt) {
             const float nm = -m[rt];
@@ -573,13 +582,13 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) p[j][i] = __builtin_fmaf(s[j][rt][i], qscale, nm);
-            mrun[rt] = fmaxf(fmaxf(fmaxf(mrun[rt], fmaxf(p[0][0], p[0][1])), fmaxf(p[0][2], p[0][3])),
-                             fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
+            if constexpr (TRACK)
+                mrun[rt] = fmaxf(fmaxf(fmaxf(mrun[rt], fmaxf(p[0][0], p[0][1])), fmaxf(p[0][2], p[0][3])),
+                                 fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) p[j][i] = __builtin_amdgcn_exp2f(p[j][i]);
-            lsum[rt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
             pb[rt] = as_bf16x8(make_uint4(cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
                                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])));
         }
@@ -601,16 +610,21 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
             }
     };
     // Probabilities of half hh's scores, then the value product O^T += V^T P^T
-    // over its 32 keys from the V tile at offset vb (voff plus the stage).
-    auto half_values = [&](const f32x4_t (&s)[2][kAtRt], uint32_t vb, int hh) {
+    // over its 32 keys from the V tile at offset vb (voff plus the stage), and
+    // the row sums as one more product with an all-ones V^T tile (the sums of
+    // the bf16 probabilities the value product weighs, on the matrix cores
+    // instead of 16 vector additions per row tile and block).
+    auto half_values = [&](const f32x4_t (&s)[2][kAtRt], uint32_t vb, int hh, auto track) {
         bf16x8_t pb[kAtRt];
-        half_probs(pb, s);
+        half_probs(pb, s, track);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const bf16x8_t a = v_frag(vb + 32 * ct + (uint32_t)(32 * hh) * kAtVRow);
 #pragma unroll
             for (int rt = 0; rt < kAtRt; ++rt) o[ct][rt] = mfma16(a, pb[rt], o[ct][rt]);
         }
+#pragma unroll
+        for (int rt = 0; rt < kAtRt; ++rt) osum[rt] = mfma16(ones, pb[rt], osum[rt]);
     };
     // Issue order of one half step for the scheduler: the score products,
     // each pair after its K fragment read (reads run two ahead) and followed
@@ -640,19 +654,20 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     // block. Loads, products and stores past the last block are not skipped
     // (they repeat the last block; their results go unused). The stage is one
     // offset added to the lane bases per block.
-    // The reference of a row is the max of its first half block; a row whose
-    // running max later exceeds it by more than the slack (checked once per
-    // pass) gets the larger reference and the workgroup runs its blocks again
-    // (the pass's sums are void; accumulators are never rescaled). The tile's
-    // own block, last in the ascending set, takes the causal mask.
+    // The reference of a row is the max of its first half block; a pass in
+    // which some row's sum of probabilities passes 2^64 is void and the
+    // workgroup runs its blocks again (accumulators are never rescaled; see the
+    // end of the pass). The tile's own block, last in the ascending set, takes
+    // the causal mask.
     const bool last_diag = n > 0 && blk_at(n - 1) == bt;
+    bool track = false;                            // this pass keeps the running maxima
     for (int pass = 0; pass < kPfMaxPasses; ++pass) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int rt = 0; rt < kAtRt; ++rt) o[ct][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < kAtRt; ++rt) { lsum[rt] = 0.f; mrun[rt] = -INFINITY; }
+        for (int rt = 0; rt < kAtRt; ++rt) { osum[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f}; mrun[rt] = -INFINITY; }
         TileRegs rk, rv;
         auto load_block = [&](int64_t blk) {
             const uint32_t bb = (uint32_t)blk * (kBlock * 2 * kD);
@@ -691,6 +706,7 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                 m[rt] = mx == -INFINITY ? 0.f : mx;
             }
         }
+        auto blocks = [&](auto trk) {
         for (int e = 0; e < n; ++e) {
             const int st = e % 3, st1 = st == 2 ? 0 : st + 1, st2 = st == 0 ? 2 : st - 1;
             const bool diag = e == n - 1 && last_diag;
@@ -712,39 +728,51 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
                               "+v"(kb1[1]), "+v"(kb1[2]), "+v"(kb1[3]), "+v"(vb0));
             load_block(blk_at(e + 2 < n ? e + 2 : n - 1));
             half_scores_at(sb, kb0, 1);
-            half_values(sa, vb0, 0);
+            half_values(sa, vb0, 0, trk);
             half_step_order();
             if (diag) {
                 asm volatile("");
                 mask_causal(sb, 1);
             }
             half_scores_at(sa, kb1, 0);
-            half_values(sb, vb0, 1);
+            half_values(sb, vb0, 1, trk);
             half_step_order();
             store_block(st2);
             __syncthreads();                       // block e + 2 staged; stage e % 3 free
         }
-        // end of pass: raise references a row outgrew; workgroup-wide redo
+        };
+        if (track) blocks(std::true_type{});
+        else blocks(std::false_type{});
+        // end of pass. A pass whose row sums stay within 2^kRescaleSlack is
+        // final. Otherwise a tracking pass follows (same references, running
+        // maxima kept), after which every row's reference is raised to its
+        // maximum and a last pass runs (probabilities <= 1 there).
         bool redo = false;
+        if (track) {
 #pragma unroll
-        for (int rt = 0; rt < kAtRt; ++rt) {
-            float mx = mrun[rt];
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            if (mx > kRescaleSlack) { m[rt] += mx; redo = true; }
+            for (int rt = 0; rt < kAtRt; ++rt) {
+                float mx = mrun[rt];
+                mx = fmaxf(mx, shfl_xor(mx, 16));
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                if (mx > 0.f) m[rt] += mx;
+            }
+            redo = true;
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < kAtRt; ++rt)
+                if (!(osum[rt][0] <= kSumLimit)) redo = true;         // also catches inf / NaN
         }
         __syncthreads();
         if (redo) s_redo[pass] = 1;
         __syncthreads();
         if (s_redo[pass] == 0) break;
+        track = !track;
     }
 
-    // finish: total sum per row over the 4 lanes sharing it, then write
+    // finish: normalise by the row sums and write
 #pragma unroll
     for (int rt = 0; rt < kAtRt; ++rt) {
-        float l = lsum[rt];
-        l += shfl_xor(l, 16);
-        l += shfl_xor(l, 32);
+        const float l = osum[rt][0];
         const int64_t qi = q_first + qloc[rt];
         if (qi >= Tq) continue;
         const int h = c16 & 3;
