@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kAtThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);     // VALU
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
