@@ -27,11 +27,11 @@
 // so each exponential is one exp2. At the end the waves' (max, sum, weighted
 // values) meet in LDS.
 //
-// bf16 block lists take attend_share_mfma instead: the same loads and block
-// ring, with q.k and P.V on the matrix cores (4 + 8 MFMA per wave and block)
-// and the softmax on one head's 4 logits per lane, about a fifth of the vector
-// instructions of the path above. That path still serves fp32 inputs and
-// token lists.
+// bf16 inputs (block and token lists) take attend_share_mfma instead: the
+// same loads and block ring, with q.k and P.V on the matrix cores (4 + 8 MFMA
+// per wave and block) and the softmax on one head's 4 logits per lane, about a
+// fifth of the vector instructions of the path above. That path still serves
+// fp32 inputs.
 #pragma once
 
 #include <math.h>
@@ -137,7 +137,9 @@ struct BlockRegs {
     Raw8<T> k[4], v[4];
     int64_t t0;
     int ids[4];     // token lists: ids of this lane's 4 rows of the next tile this buffer loads
-    int tmy;        // token lists: id of the row whose logit this lane holds (loaded tile)
+    int tmy;        // token lists: id of the row whose logit this lane holds (loaded tile);
+                    // matrix-core share: visibility bits of the lane's 4 logits
+    int idk;        // token lists, matrix-core share: id of the lane's K row of the next tile
 };
 
 // LDS of attend_share for G heads and NW waves.
@@ -458,9 +460,9 @@ __device__ __forceinline__ void attend_share(const QFrag<T, G> &q, const T *__re
     merge_waves<G, NW, MODE>(sm, row_base, out);
 }
 
-// One share of a unit's bf16 block list on the matrix cores (same contract as
-// attend_share with ROWS = false). Wave w still owns rows 16 (w % 4) .. +15 of
-// each block; with g = lane / 16 and h = lane % 16:
+// One share of a unit's bf16 list on the matrix cores (same contract as
+// attend_share). Wave w still owns rows 16 (w % 4) .. +15 of each block (ROWS:
+// of each 64-entry tile of token ids); with g = lane / 16 and h = lane % 16:
 //   S = K q^T, v_mfma_f32_16x16x32_bf16 x 4: the A operand's row h is key row
 //     h / 4 + 4 (h % 4) of the wave's 16 (lane l loads channels 32 s + 8 g of
 //     it in step s), so output element j of lane l is the logit of key
@@ -477,11 +479,14 @@ __device__ __forceinline__ void attend_share(const QFrag<T, G> &q, const T *__re
 // probabilities stay below 2^kSlack (sums far inside the fp32 range). Heads
 // G .. 15 carry zero queries and are discarded. exp2 is the hardware
 // instruction (arguments <= kSlack; results below 2^-126 flush to zero).
-template <int G, int NW, int MODE>
+// Token lists gather each row by its id (ids of a wave set's tile prefetched
+// three tiles ahead with the buffer that uses them, as in attend_share); ids
+// outside [0, L) read zeros and their logits are masked.
+template <int G, bool ROWS, int NW, int MODE>
 __device__ __forceinline__ void attend_share_mfma(const QMfma &q, const bf16_t *__restrict__ K,
                                                   const bf16_t *__restrict__ V, int64_t T_cap,
-                                                  int unit, int64_t L, const int32_t *irow,
-                                                  int nblk, float qscale, int64_t row_base,
+                                                  int unit, int64_t L, const int32_t *irow, int n,
+                                                  int e_lo, int nblk, float qscale, int64_t row_base,
                                                   const AttendOut &out, AttendSmem<G, NW> &sm) {
     constexpr int NWS = NW / 4;                  // wave sets
     constexpr float kSlack = 32.f;
@@ -491,19 +496,52 @@ __device__ __forceinline__ void attend_share_mfma(const QMfma &q, const bf16_t *
     const int h = lane & 15, g = lane >> 4;
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + (int64_t)unit * T_cap * kD, (uint32_t)(L * kRowBytes));
-    const uint32_t k_lane = (16 * wq + (h >> 2) + 4 * (h & 3)) * kRowBytes + 16 * g;
+    const int k_row = 16 * wq + (h >> 2) + 4 * (h & 3);           // the lane's K row of a block
+    const uint32_t k_lane = k_row * kRowBytes + 16 * g;
     const uint32_t v_lane = (16 * wq + g) * kRowBytes + 16 * h;
     const int64_t nb = n_blocks(L);
 
     // block ids as in attend_share: lane i holds item i's id (-1: none)
     int id_lane = -1;
-    if (lane < nblk) {
-        const int blk = irow[lane];
-        id_lane = (blk >= 0 && blk < nb) ? blk : -1;
+    if constexpr (!ROWS) {
+        if (lane < nblk) {
+            const int blk = irow[lane];
+            id_lane = (blk >= 0 && blk < nb) ? blk : -1;
+        }
     }
     auto item_of = [&](int k) { return wset + k * NWS; };
     auto block_id = [&](int it) -> int {
         return it < nblk ? __builtin_amdgcn_readlane(id_lane, it & 63) : -1;
+    };
+    // token lists: ids of share tile it (entry 64 (e_lo + it) + row) for the
+    // lane's V rows g + 4j and its K row, -1 past the share or the list
+    auto load_ids = [&](BlockRegs<bf16_t> &r, int it) {
+        const int e0 = 64 * (e_lo + it) + 16 * wq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + g + 4 * j;
+            r.ids[j] = (it < nblk && e < n) ? irow[e] : -1;
+        }
+        const int e = e0 + (k_row - 16 * wq);
+        r.idk = (it < nblk && e < n) ? irow[e] : -1;
+    };
+    // token lists: rows of the ids loaded for tile it (ids outside [0, L) read
+    // zeros, no bytes), their visibility bits, then the ids three tiles on
+    auto issue_rows = [&](BlockRegs<bf16_t> &r, int it) {
+        const bool kv = r.idk >= 0 && r.idk < L;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            load_raw_nt(rK, kv ? (uint32_t)r.idk * kRowBytes + 16 * g + 64 * i : 0xffffffffu, r.k[i]);
+        int vis = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = r.ids[j] >= 0 && r.ids[j] < L;
+            load_raw_nt(rV, ok ? (uint32_t)r.ids[j] * kRowBytes + 16 * h : 0xffffffffu, r.v[j]);
+            vis |= ok ? 1 << j : 0;
+        }
+        r.tmy = vis;
+        r.t0 = 0;
+        load_ids(r, it + 3 * NWS);
     };
     // loads of an absent block (id -1) use an out-of-range offset: zeros, no bytes
     auto issue = [&](BlockRegs<bf16_t> &r, int blk) {
@@ -531,7 +569,11 @@ __device__ __forceinline__ void attend_share_mfma(const QMfma &q, const bf16_t *
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = s[j] * qscale;
-        if (r.t0 + kBlock > L) {                 // the visible length ends inside this block
+        if constexpr (ROWS) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (!((r.tmy >> j) & 1)) x[j] = -INFINITY;
+        } else if (r.t0 + kBlock > L) {          // the visible length ends inside this block
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (r.t0 + 16 * wq + g + 4 * j >= L) x[j] = -INFINITY;
@@ -572,17 +614,26 @@ __device__ __forceinline__ void attend_share_mfma(const QMfma &q, const bf16_t *
 
     // three register buffers, as in attend_share
     BlockRegs<bf16_t> bufA, bufB, bufC;
-    issue(bufA, block_id(item_of(0)));
-    issue(bufB, block_id(item_of(1)));
+    auto start = [&](BlockRegs<bf16_t> &r, int k) {
+        if constexpr (ROWS) issue_rows(r, item_of(k));
+        else issue(r, block_id(item_of(k)));
+    };
+    if constexpr (ROWS) {
+        load_ids(bufA, item_of(0));
+        load_ids(bufB, item_of(1));
+        load_ids(bufC, item_of(2));
+    }
+    start(bufA, 0);
+    start(bufB, 1);
 #pragma unroll 1
     for (int k = 0; item_of(k) < nblk; k += 3) {
-        issue(bufC, block_id(item_of(k + 2)));
+        start(bufC, k + 2);
         __builtin_amdgcn_sched_barrier(0);
         process(bufA);
-        issue(bufA, block_id(item_of(k + 3)));
+        start(bufA, k + 3);
         __builtin_amdgcn_sched_barrier(0);
         if (item_of(k + 1) < nblk) process(bufB);
-        issue(bufB, block_id(item_of(k + 4)));
+        start(bufB, k + 4);
         __builtin_amdgcn_sched_barrier(0);
         if (item_of(k + 2) < nblk) process(bufC);
     }

@@ -137,8 +137,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     int64_t L = seq_lens[b];
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
     // the group's queries: loaded first, so the load overlaps the top-k below
-    // (bf16 block lists: in the matrix-core operand layout)
-    constexpr bool kMfma = __is_same(T, bf16_t) && !ROWS;
+    // (bf16: in the matrix-core operand layout)
+    constexpr bool kMfma = __is_same(T, bf16_t);
     const T *Qg = Q + ((int64_t)b * Hq + (int64_t)kvh * G) * kD;
     QFrag<T, G> q;
     QMfma qm;
@@ -174,8 +174,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const int64_t row_base = (int64_t)b * Hq + (int64_t)kvh * G;
     constexpr int kMode = DIRECT ? kAttendDirect : kAttendPartialCoherent;
     if constexpr (kMfma)
-        attend_share_mfma<G, 4, kMode>(qm, K, V, T_cap, unit, L, idx_row + e_lo, nblk, qscale,
-                                       row_base, out, sm);
+        attend_share_mfma<G, ROWS, 4, kMode>(qm, K, V, T_cap, unit, L,
+                                             idx_row + (ROWS ? 0 : e_lo), n, e_lo, nblk, qscale,
+                                             row_base, out, sm);
     else
         attend_share<T, G, ROWS, 4, kMode>(q, K, V, T_cap, unit, L, idx_row + (ROWS ? 0 : e_lo), n,
                                            e_lo, nblk, qscale, row_base, out, sm);
