@@ -55,7 +55,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py runs on one GPU (the kernels work on a single device); run with --gpus 1"}))
         sys.exit(2)
     import torch
     import synth
