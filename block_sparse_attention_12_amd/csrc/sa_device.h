@@ -224,16 +224,49 @@ __device__ __forceinline__ uint32_t orderable(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of one int per thread over the workgroup; also returns the total.
+// ---- whole-wave scans on DPP (no LDS round trips) --------------------------
+// Lane i takes lane i - n of its 16-lane row (row_shr:n), or lane 15 (31) of
+// the previous row(s) (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows
+// 2 and 3); a lane with no source, or in a row outside the row mask, keeps
+// `ident`, the identity of the scan's operation.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t ident, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+// Inclusive scan over the 64 lanes with an associative operation `op` whose
+// identity is `ident` (sum: 0, max: 0, min: ~0u): after six steps lane i
+// holds op over lanes 0..i.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t ident, Op op) {
+    v = op(v, dpp_u32<kDppRowShr1>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr2>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr4>(ident, v));
+    v = op(v, dpp_u32<kDppRowShr8>(ident, v));
+    v = op(v, dpp_u32<kDppRowBcast15, 0xA>(ident, v));
+    v = op(v, dpp_u32<kDppRowBcast31, 0xC>(ident, v));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    return wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// op over the whole wave, the same value on every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = wave_incl_scan(v, ~0u, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exclusive prefix sum of one non-negative int per thread over the workgroup;
+// also returns the total.
 template <int NT>
 __device__ __forceinline__ int wg_exclusive_scan(int x, int *s_wave, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int v = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
+    const int v = (int)wave_incl_sum((uint32_t)x);
     if (lane == 63) s_wave[wave] = v;
     __syncthreads();
     int base = 0;

@@ -42,6 +42,8 @@ __device__ __forceinline__ void topk_unit(
     float *__restrict__ bscore_out, int32_t *row, int idx_cap, int32_t *cnt_slot,
     int use_buckets) {
     __shared__ uint32_t s_hist[256];
+    __shared__ uint32_t s_hist2[256];
+    __shared__ uint32_t s_kmin[NT / 64], s_kmax[NT / 64];
     __shared__ float s_M[G], s_Zinv[G];
     __shared__ float2 s_st[G * 64];
     constexpr int kSelWords = NT * PER / 32;        // one bit per block this workgroup covers
@@ -185,22 +187,17 @@ __device__ __forceinline__ void topk_unit(
     const bool take_none = top_k <= 0;
     const bool choose = !take_all && !take_none;
 
-    // Bin of the histogram that holds the `remaining`-th largest counted key
+    // Bin of histogram h that holds the `remaining`-th largest counted key
     // (bins scanned from the top), the count of keys in the bins above it and
     // the bin's own count.
-    auto boundary_bin = [&](int remaining) {
+    auto boundary_bin = [&](const uint32_t *h, int remaining) {
         if (tid < 64) {
-            // lane l owns bins 4l .. 4l+3; counts above each bin, from the top
-            const uint32_t hb[4] = {s_hist[4 * tid], s_hist[4 * tid + 1], s_hist[4 * tid + 2],
-                                    s_hist[4 * tid + 3]};
+            // lane l owns bins 4l .. 4l+3; keys in bins owned by higher lanes
+            // = wave total - inclusive prefix over lanes 0..l
+            const uint32_t hb[4] = {h[4 * tid], h[4 * tid + 1], h[4 * tid + 2], h[4 * tid + 3]};
             const uint32_t c = hb[0] + hb[1] + hb[2] + hb[3];
-            uint32_t incl = c;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t t = __shfl_down(incl, off, 64);
-                if (tid + off < 64) incl += t;
-            }
-            uint32_t above = incl - c;                   // keys in bins owned by higher lanes
+            const uint32_t incl = wave_incl_sum(c);
+            uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
 #pragma unroll
             for (int k = 3; k >= 0; --k) {
                 if (above < (uint32_t)remaining && above + hb[k] >= (uint32_t)remaining) {
@@ -271,9 +268,9 @@ __device__ __forceinline__ void topk_unit(
                 bin[q] = bq;
             }
             __syncthreads();
-            boundary_bin(top_k);
+            boundary_bin(s_hist, top_k);
             bstar = (int)s_digit;
-            const int c = (int)s_hist[bstar];
+            const int c = (int)s_bcnt;                      // the boundary bucket's count
             const int r = top_k - (int)s_above;             // taken from the boundary bucket, >= 1
             if (c <= kBoundaryCap) {
 #pragma unroll
@@ -301,30 +298,68 @@ __device__ __forceinline__ void topk_unit(
         }
     }
 
-    // Fallback: radix select of the top_k-th largest key among the candidates
-    // (four 8-bit digits of the orderable key, most significant first). The
-    // passes stop early once the boundary bin holds exactly the keys still to
-    // take: every key whose digits so far match (prefix under mask) is then
-    // taken, so the classes compared below are those of the masked key.
+    // Fallback: radix select of the top_k-th largest key among the candidates,
+    // 8-bit digits from the most significant bit in which the candidates'
+    // keys differ (the bits above it are common to every candidate: those of
+    // the smallest and largest key agree there). The passes stop early once
+    // the boundary bin holds exactly the keys still to take: every key whose
+    // digits so far match (prefix under mask) is then taken, so the classes
+    // compared below are those of the masked key. A digit that reaches below
+    // bit 0 starts at bit 0 instead; its upper bits are already fixed by the
+    // prefix, so the bins stay in key order. Two histograms alternate, so a
+    // pass clears the next pass's one and needs two barriers.
     uint32_t prefix = 0, mask = 0;
     int remaining = top_k;
     bool whole_class = false;           // every key of the boundary class is taken
     if (choose && !fast) {
-#pragma unroll 1
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
-            __syncthreads();
+        uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
-            for (int q = 0; q < PER; ++q)
-                if (cand[q] && (key[q] & mask) == prefix) atomicAdd(&s_hist[(key[q] >> shift) & 255u], 1u);
-            __syncthreads();
-            boundary_bin(remaining);
-            prefix |= s_digit << shift;
-            mask |= 255u << shift;
-            remaining -= (int)s_above;
-            if ((int)s_bcnt == remaining) {
-                whole_class = true;
-                break;
+        for (int q = 0; q < PER; ++q)
+            if (cand[q]) {
+                kmin = key[q] < kmin ? key[q] : kmin;
+                kmax = key[q] > kmax ? key[q] : kmax;
+            }
+        kmin = wave_min_u32(kmin);
+        kmax = wave_max_u32(kmax);
+        if ((tid & 63) == 0) {
+            s_kmin[tid >> 6] = kmin;
+            s_kmax[tid >> 6] = kmax;
+        }
+        for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            kmin = s_kmin[w] < kmin ? s_kmin[w] : kmin;
+            kmax = s_kmax[w] > kmax ? s_kmax[w] : kmax;
+        }
+        const uint32_t diff = kmin ^ kmax;               // same on every thread
+        if (diff == 0u) {
+            prefix = kmin;                               // one class: ranked by id below
+            mask = ~0u;
+        } else {
+            const int hb = 31 - __builtin_clz(diff);     // highest differing bit
+            mask = hb == 31 ? 0u : (~0u << (hb + 1));
+            prefix = kmin & mask;
+            int shift = hb - 7 > 0 ? hb - 7 : 0;
+#pragma unroll 1
+            for (int pass = 0;; ++pass) {
+                uint32_t *h = (pass & 1) ? s_hist2 : s_hist;
+                uint32_t *h_next = (pass & 1) ? s_hist : s_hist2;
+                for (int i = tid; i < 256; i += NT) h_next[i] = 0;
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    if (cand[q] && (key[q] & mask) == prefix) atomicAdd(&h[(key[q] >> shift) & 255u], 1u);
+                __syncthreads();
+                boundary_bin(h, remaining);
+                prefix |= s_digit << shift;
+                mask |= 255u << shift;
+                remaining -= (int)s_above;
+                if ((int)s_bcnt == remaining) {
+                    whole_class = true;
+                    break;
+                }
+                if (shift == 0) break;
+                shift = shift - 8 > 0 ? shift - 8 : 0;
             }
         }
     }
