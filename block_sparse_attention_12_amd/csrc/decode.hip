@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include "attend_device.h"
+#include "compress_device.h"
 #include "handoff_device.h"
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -149,11 +150,66 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if constexpr (SG > 0) {
         __shared__ int32_t s_list[kFusedMaxCap];
         __shared__ int32_t s_cnt;
+        // The step's append (raw-sum, bf16): the unit's last split writes the
+        // compressed entries completed between lens_prev and seq_lens (Eq. 2;
+        // the same sums in the same order as the compress kernel). One new
+        // entry: its 32 keys are loaded here, two per 16-lane row group, stay
+        // in flight during the top-k, are staged in LDS and summed in token
+        // order by one row group. More (a length jump beyond the caller's
+        // hint): one entry per row group at a time from per-lane key loads.
+        constexpr bool kApp = !SSOFT && __is_same(T, bf16_t);
+        __shared__ uint4 s_app[kApp ? 2 * kCmpStride : 1][16];
+        const int app_group = tid >> 4, app_lane = tid & 15;
+        const bool app = kApp && fs.app_Kc != nullptr && split == n_split - 1;   // uniform
+        int64_t app_lo = 0, app_hi = 0;
+        Raw8<bf16_t> app_rows[2];
+        if constexpr (kApp) {
+            if (app) {
+                int64_t Lp = fs.app_lens_prev[b];
+                Lp = Lp < 0 ? 0 : (Lp > L ? L : Lp);
+                app_lo = n_compressed(Lp);
+                app_hi = n_compressed(L);
+                if (app_hi == app_lo + 1) {
+                    const bf16_t *Ka = (const bf16_t *)fs.app_K +
+                                       ((int64_t)unit * T_cap + app_lo * kCmpStride + 2 * app_group) * kD +
+                                       app_lane * kLaneElems;
+                    load_raw(Ka, app_rows[0]);
+                    load_raw(Ka + kD, app_rows[1]);
+                }
+            }
+        }
         topk_unit<SG, SSOFT, kDecThreads, kFusedMaxBlocks / kDecThreads>(
             unit, Hkv, T_cap, fs.nb_cap, seq_lens, fs.top_k, fs.n_init, fs.n_local, fs.logits,
             fs.nc_pad, fs.stats, fs.n_chunks, fs.bscore, nullptr, s_list, idx_cap, &s_cnt,
             fs.use_buckets);
+        if constexpr (kApp) {
+            if (app && app_hi == app_lo + 1) {
+                s_app[2 * app_group][app_lane] = app_rows[0].v;
+                s_app[2 * app_group + 1][app_lane] = app_rows[1].v;
+            }
+        }
         __syncthreads();
+        if constexpr (kApp) {
+            if (app) {
+                bf16_t *Kcu = (bf16_t *)fs.app_Kc + (int64_t)unit * fs.app_nc_cap * kD +
+                              app_lane * kLaneElems;
+                if (app_hi == app_lo + 1) {
+                    if (app_group == 0) {
+                        Raw8<bf16_t> e;
+                        entry_from_rows(s_app, app_lane, e);
+                        store_raw(Kcu + app_lo * kD, e);
+                    }
+                } else {
+                    const bf16_t *Ku = (const bf16_t *)fs.app_K + (int64_t)unit * T_cap * kD +
+                                       app_lane * kLaneElems;
+                    for (int64_t j = app_lo + app_group; j < app_hi; j += kDecThreads / 16) {
+                        Raw8<bf16_t> r;
+                        compress_entry_raw(Ku, j, r);
+                        store_raw(Kcu + j * kD, r);
+                    }
+                }
+            }
+        }
         if (split == 0) {
             for (int i = tid; i < idx_cap; i += kDecThreads)
                 fs.idx_out[(int64_t)unit * idx_cap + i] = s_list[i];

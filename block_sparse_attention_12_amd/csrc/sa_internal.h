@@ -41,13 +41,22 @@ struct FusedSelect {
     int32_t *idx_out, *cnt_out;
     int use_buckets;
     int epb;                           // softmax logits per block: 4 (compressed entries) or 1
+    // the step's append by the attention launch (raw-sum, bf16 keys): when
+    // app_Kc is set, the last split workgroup of each unit writes the
+    // compressed entries completed between app_lens_prev and seq_lens, formed
+    // from app_K (the scoring launch read none of them)
+    const void *app_K;
+    void *app_Kc;
+    const int32_t *app_lens_prev;
+    int64_t app_nc_cap;
 };
 
 // With K and lens_prev, the compressed entries completed between lens_prev
-// and seq_lens are written by the scoring launch itself (raw-sum mode:
-// max_new_tokens is an upper bound on lens_now - lens_prev; up to 16 in bf16,
-// each unit's first scoring workgroup writes the at most one new entry;
-// softmax mode: the workgroup owning a new entry forms, scores and writes it).
+// and seq_lens are written in the same step (raw-sum mode: max_new_tokens is
+// an upper bound on lens_now - lens_prev; up to 16 with bf16 keys and fs, the
+// attention launch writes them (fs->app_*) and the scorer reads only older
+// entries; otherwise the scoring launch writes them; softmax mode: the
+// scoring workgroup owning a new entry forms, scores and writes it).
 // With fs, only the scoring kernel(s) run and fs describes their output (the
 // top-k is left to the caller's next launch).
 int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int Hkv,

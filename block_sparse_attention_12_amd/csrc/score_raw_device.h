@@ -20,6 +20,7 @@ namespace sa {
 constexpr int kRawChunkBlocks = 256;                // blocks per chunk
 constexpr int kAppendColumn = 1;                    // the append as an extra column of workgroups
 constexpr int kAppendInFirst = 2;                   // the append by each unit's chunk-0 workgroup
+constexpr int kAppendElsewhere = 3;                 // another launch appends (scores only)
 
 template <typename T>
 struct RawIter {                         // one iteration: 4 blocks x 3 inside entries per row group
@@ -31,7 +32,8 @@ struct RawIter {                         // one iteration: 4 blocks x 3 inside e
 // compressed entries completed between lens_prev and seq_lens are written by
 // this launch itself, either by an extra column of workgroups
 // (append_column) while the others score, or by each unit's chunk-0
-// workgroup after its own blocks (app_mode kAppendInFirst). Scoring then
+// workgroup after its own blocks (app_mode kAppendInFirst), or by the next
+// launch (kAppendElsewhere: this launch writes nothing to Kc). Scoring then
 // reads only the entries that existed before (j < n_c(lens_prev)) from Kc and
 // forms any newer entry it needs from K itself, with the same arithmetic, so
 // it never depends on the concurrent writes.

@@ -340,12 +340,21 @@ static void launch_raw(const void *sel, int H_sel, int Gs, const void *Kc, int B
     const unsigned units = (unsigned)(B * Hkv);
     const unsigned chunks = (unsigned)((w.nb_cap + kRawChunkBlocks - 1) / kRawChunkBlocks);
     if (lens_prev) {
-        // scoring + the step's append in one launch: with at most one new entry
-        // per unit (bf16) the unit's first workgroup writes it; otherwise an
-        // extra column of workgroups does (which leaves the grid uneven over the
-        // CUs: measured ~2.4 us at 128K)
-        const int mode = (sizeof(T) == 2 && max_new_tokens <= kCmpStride) ? kAppendInFirst
-                                                                           : kAppendColumn;
+        // the step's append: with at most one new entry per unit (bf16) and
+        // the attention launch next (fs), that launch's last split workgroup of
+        // each unit writes it, in the shadow of its top-k (in the scoring
+        // launch it made the unit's chunk-0 workgroup the last one: measured
+        // ~2 us of tail at 128K); without fs the unit's first scoring
+        // workgroup writes it; otherwise an extra column of scoring workgroups
+        // does (which leaves the grid uneven over the CUs: ~2.4 us at 128K)
+        const bool small = sizeof(T) == 2 && max_new_tokens <= kCmpStride;
+        const int mode = small ? (fs ? kAppendElsewhere : kAppendInFirst) : kAppendColumn;
+        if (fs && mode == kAppendElsewhere) {
+            fs->app_K = K;
+            fs->app_Kc = const_cast<void *>(Kc);
+            fs->app_lens_prev = lens_prev;
+            fs->app_nc_cap = nc_cap;
+        }
         const unsigned cols = chunks + (mode == kAppendColumn ? 1 : 0);
         hipLaunchKernelGGL((score_raw_kernel<T, true>), dim3(cols, units), dim3(kSelThreads), 0,
                            stream, (const T *)sel, H_sel, Gs, (const T *)Kc, Hkv, nc_cap, T_cap,
@@ -387,6 +396,10 @@ int launch_select(const void *sel, int G, const void *Kc, int dtype, int B, int 
         fs->cnt_out = cnt_out;
         fs->use_buckets = B * Hkv >= kBucketMinUnits ? 1 : 0;
         fs->epb = 4;
+        fs->app_K = nullptr;
+        fs->app_Kc = nullptr;
+        fs->app_lens_prev = nullptr;
+        fs->app_nc_cap = 0;
     }
     if (p.score_mode == SA_SCORE_RAW_SUM) {
         if (dtype == SA_BF16)
