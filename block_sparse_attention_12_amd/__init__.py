@@ -47,7 +47,8 @@ EXPORTS = [
     "sparse_attn_token_select_workspace_size", "sparse_attn_token_select",
     "sparse_attn_token_decode_workspace_size", "sparse_attn_token_decode",
     "sparse_attn_cobs_stats", "sparse_attn_cobs_select_workspace_size", "sparse_attn_cobs_select",
-    "sparse_attn_decode_step_workspace_size", "sparse_attn_decode_step",
+    "sparse_attn_decode_step_workspace_size", "sparse_attn_decode_step_splits",
+    "sparse_attn_decode_step",
     "sparse_attn_cobs_decode_step_workspace_size", "sparse_attn_cobs_decode_step",
     "sparse_attn_decode_step_noalloc",
 ]
@@ -133,6 +134,8 @@ def lib() -> ctypes.CDLL:
                                            _i32, _i32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]
     L.sparse_attn_decode_step_workspace_size.restype = _sz
     L.sparse_attn_decode_step_workspace_size.argtypes = [_int, _int, _int, _int, _i64, _PP, _i32, _i32]
+    L.sparse_attn_decode_step_splits.restype = _i32
+    L.sparse_attn_decode_step_splits.argtypes = [_int, _int, _int, _i64, _PP, _i32, _i32, _i32]
     L.sparse_attn_decode_step.restype = _int
     L.sparse_attn_decode_step.argtypes = [_vp, _vp, _int, _vp, _vp, _vp, _int, _int, _int, _int, _int,
                                           _i64, _i64, _vp, _vp, _i32, _PP, _f32, _vp, _i32, _vp, _vp,
@@ -684,6 +687,15 @@ def decode_step_workspace_size(B, Hq, Hkv, H_sel, T_cap, params: SelectParams, i
                                n_split=0) -> int:
     return lib().sparse_attn_decode_step_workspace_size(B, Hq, Hkv, H_sel, T_cap, ctypes.byref(params),
                                                         idx_cap, n_split)
+
+
+def decode_step_splits(dtype, B, Hkv, T_cap, params: SelectParams, idx_cap, max_new_tokens=1,
+                       n_split=0) -> int:
+    """Split-K workgroups per (b, kvh) of decode_step's attention with these
+    arguments (dtype: the key dtype, torch.bfloat16 or torch.float32)."""
+    code = {torch.bfloat16: 1, torch.float32: 0}[dtype]
+    return lib().sparse_attn_decode_step_splits(code, B, Hkv, T_cap, ctypes.byref(params), idx_cap,
+                                                int(max_new_tokens), int(n_split))
 
 
 def decode_step(Q: torch.Tensor, sel: torch.Tensor, K: torch.Tensor, V: torch.Tensor, Kc: torch.Tensor,

@@ -118,22 +118,21 @@ __device__ __forceinline__ void merge_partials(const float *part, int64_t row_ba
 // kernels' output into LDS; every split of a unit computes the same set (the
 // redundant work replaces a separate top-k launch on the critical path) and
 // split 0 writes it out.
-template <typename T, int G, bool DIRECT, bool ROWS, int SG = 0, bool SSOFT = false>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+// One workgroup's share of a unit: split `split` of unit `unit` out of n_units.
+template <typename T, int G, bool DIRECT, bool ROWS, int SG, bool SSOFT>
+__device__ __forceinline__ void decode_unit(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
     int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ cnt, int idx_cap, float qscale, int n_split,
     float *__restrict__ part, void *__restrict__ O, int out_bf16,
-    float *__restrict__ lse, FusedSelect fs) {
+    float *__restrict__ lse, const FusedSelect &fs, int split, int unit, int n_units) {
     __shared__ AttendSmem<G, 4> sm;
     __shared__ uint32_t s_arrive;
-    const int split = blockIdx.x, unit = blockIdx.y;
     const int b = unit / Hkv, kvh = unit % Hkv;
     const int tid = threadIdx.x;
     // split merge hand-off words after the partials (see decode_workspace_bytes)
     uint64_t *sync = DIRECT ? nullptr
-                            : (uint64_t *)((char *)part + partial_bytes((int)(gridDim.y / Hkv), Hq,
-                                                                        n_split));
+                            : (uint64_t *)((char *)part + partial_bytes(n_units / Hkv, Hq, n_split));
     const uint64_t tag = DIRECT ? 0 : call_tag(sync);
     int64_t L = seq_lens[b];
     L = L < 0 ? 0 : (L > T_cap ? T_cap : L);
@@ -247,11 +246,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         merge_partials<G, kDecThreads>(part, row_base, n_split, O, out_bf16, lse);
         // every workgroup has counted itself (so read the epoch) once the last
         // unit is merged: the call's tag becomes the epoch
-        if (tid == 0 && arrive(sync + 1, tag) == (uint32_t)(gridDim.y - 1)) {
+        if (tid == 0 && arrive(sync + 1, tag) == (uint32_t)(n_units - 1)) {
             arm(sync + 1, tag);
             store_dev(sync, tag);
         }
     }
+}
+
+template <typename T, int G, bool DIRECT, bool ROWS, int SG = 0, bool SSOFT = false>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, int Hq, int Hkv,
+    int64_t T_cap, const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ cnt, int idx_cap, float qscale, int n_split,
+    float *__restrict__ part, void *__restrict__ O, int out_bf16,
+    float *__restrict__ lse, FusedSelect fs) {
+    decode_unit<T, G, DIRECT, ROWS, SG, SSOFT>(Q, K, V, Hq, Hkv, T_cap, seq_lens, idx, cnt, idx_cap,
+                                               qscale, n_split, part, O, out_bf16, lse, fs,
+                                               (int)blockIdx.x, (int)blockIdx.y, (int)gridDim.y);
 }
 
 template <typename T, int G, bool ROWS>

@@ -132,6 +132,7 @@ int decode_splits(int B, int Hkv, int32_t idx_cap, int32_t n_split) {
     int s = n_split > 0 ? n_split : decode_auto_split(B, Hkv, idx_cap);
     return s < decode_min_split(idx_cap) ? decode_min_split(idx_cap) : s;
 }
+
 }  // namespace
 
 size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel, int64_t T_cap,
@@ -142,6 +143,17 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
         return 0;
     const size_t sel = select_workspace_layout(B, Hkv, H_sel / Hkv, T_cap, p->score_mode).total;
     return align256(sel) + decode_workspace_bytes(B, Hq, Hkv, decode_splits(B, Hkv, idx_cap, n_split));
+}
+
+int32_t sparse_attn_decode_step_splits(int dtype, int B, int Hkv, int64_t T_cap,
+                                       const sa_select_params *p, int32_t idx_cap,
+                                       int32_t max_new_tokens, int32_t n_split) {
+    if (!p || !dtype_ok(dtype) || B <= 0 || Hkv <= 0 || T_cap < 0 || idx_cap <= 0 || n_split < 0 ||
+        max_new_tokens < 0)
+        return 0;
+    (void)T_cap;
+    (void)max_new_tokens;
+    return decode_splits(B, Hkv, idx_cap, n_split);
 }
 
 int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const void *K, const void *V,

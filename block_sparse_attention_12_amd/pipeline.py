@@ -15,7 +15,8 @@ import torch
 from . import (compress, select, decode, prefill_chunk, prefill_attend, make_params,
                select_workspace_size, token_select, token_decode, token_select_workspace_size,
                token_decode_workspace_size, cobs_stats, cobs_select, cobs_select_workspace_size,
-               n_blocks, decode_step, decode_step_workspace_size, cobs_decode_step,
+               n_blocks, decode_step, decode_step_workspace_size, decode_step_splits,
+               cobs_decode_step,
                cobs_decode_step_workspace_size,
                decode_workspace_size, prefill_workspace_size, prefill_tile_cap, n_compressed)
 
@@ -59,11 +60,22 @@ class SparseDecoder:
                       self.score_mode, idx=self.idx, cnt=self.cnt, block_scores=block_scores,
                       workspace=self.sel_ws)
 
+    def attn_splits(self, dtype) -> int:
+        """Split-K workgroups per (b, kvh) of the decode step (fused_step) for
+        keys of this dtype; attend uses the same, so step and fused_step agree
+        up to fp32 summation order."""
+        p = make_params(self.top_k, self.n_init, self.n_local, self.score_mode)
+        return decode_step_splits(dtype, self.B, self.Hkv, self.T_cap, p, self.cap, 1, self.n_split)
+
     def attend(self, Q, K, V, seq_lens, O: Optional[torch.Tensor] = None, lse=None, scale=1.0):
         O = self.O if O is None else O
         lse = self.lse if lse is None else lse
+        ns = self.attn_splits(K.dtype)
+        need = decode_workspace_size(self.B, self.Hq, self.Hkv, self.cap, ns)
+        if self.dec_ws.numel() < need:
+            self.dec_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return decode(Q, K, V, seq_lens, self.idx, self.cnt, scale, O=O, lse=lse,
-                      want_lse=lse is not None, n_split=self.n_split, workspace=self.dec_ws)
+                      want_lse=lse is not None, n_split=ns, workspace=self.dec_ws)
 
     def step(self, Q, sel, K, V, Kc, lens_prev, lens_now, scale=1.0):
         """One single-layer decode step: append, select, attend (three calls)."""

@@ -194,6 +194,14 @@ int sparse_attn_decode(const void *Q, const void *K, const void *V, int dtype, i
                        void *O, int out_dtype, float *lse_out, int32_t n_split,
                        void *workspace, size_t ws_bytes, void *stream);
 
+/* Split-K workgroups per (b, kvh) that sparse_attn_decode_step uses for the
+ * attention with these arguments (n_split as passed to it: 0 = automatic); 0
+ * for invalid arguments. sparse_attn_decode with this n_split over the step's
+ * block sets gives the step's outputs up to fp32 summation order. */
+int32_t sparse_attn_decode_step_splits(int dtype, int B, int Hkv, int64_t T_cap,
+                                       const sa_select_params *p, int32_t idx_cap,
+                                       int32_t max_new_tokens, int32_t n_split);
+
 /* Workspace bytes needed by sparse_attn_decode_step (select and decode scratch). */
 size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel, int64_t T_cap,
                                               const sa_select_params *p, int32_t idx_cap,
@@ -203,12 +211,16 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  * sparse_attn_decode_step - one whole decode step of the hot path in one call:
  * sparse_attn_compress over [lens_prev, lens_now) (Eq. 2 append), then
  * sparse_attn_select at L = lens_now (Eq. 1, Eq. 4 / Eq. 6), then
- * sparse_attn_decode (Eq. 5); results identical to those three calls.
- * In RAW_SUM mode the append runs inside the scoring launch: the scorer reads
- * the entries that existed at lens_prev from Kc and forms any newer entry it
- * needs from K with the same arithmetic, while workgroups of the same launch
- * write the new entries to Kc. In SOFTMAX_SUM mode the workgroup that owns
- * a new entry forms it from K after the entries it read from Kc, scores it
+ * sparse_attn_decode (Eq. 5) with n_split = sparse_attn_decode_step_splits:
+ * identical block sets and compressed keys, outputs equal up to fp32
+ * summation order (the same kernels; the attention is one launch with the
+ * top-k, see below).
+ * In RAW_SUM mode the scorer reads the entries that existed at lens_prev
+ * from Kc and forms any newer entry a candidate block needs from K with the
+ * same arithmetic; the new entries are written to Kc by the attention launch
+ * (see max_new_tokens) or by workgroups of the scoring launch. In
+ * SOFTMAX_SUM mode the workgroup that owns a new entry forms it from K after
+ * the entries it read from Kc, scores it
  * (so every head's running max / sum sees the same values in the same order
  * as after a separate append) and writes it to Kc.
  * With at most 2048 blocks (T_cap <= 131072), idx_cap <= 1024 and, in
@@ -222,10 +234,12 @@ size_t sparse_attn_decode_step_workspace_size(int B, int Hq, int Hkv, int H_sel,
  *   nc_cap, d] (updated in place); lens_prev, lens_now device int32 [B];
  *   max_new_tokens host hint, the expected bound on lens_now - lens_prev:
  *   it only picks how the append is scheduled, never what is computed (in
- *   RAW_SUM mode, up to 16 with bf16 keys, each unit's first scoring
- *   workgroup writes the new entries instead of an extra column of
- *   workgroups); every entry in [n_c(lens_prev), n_c(lens_now)) is written in
- *   both modes whatever the hint;
+ *   RAW_SUM mode, up to 16 with bf16 keys and the top-k inside the attention
+ *   launch, each unit's last attention workgroup writes the new entries
+ *   while it takes the top-k; otherwise, up to 16 with bf16 keys, each unit's
+ *   first scoring workgroup, else an extra column of scoring workgroups);
+ *   every entry in [n_c(lens_prev), n_c(lens_now)) is written in both modes
+ *   whatever the hint;
  *   idx_out / cnt_out as in sparse_attn_select; O / lse_out as in
  *   sparse_attn_decode. Workspace: sparse_attn_decode_step_workspace_size.
  * Errors: those of the three calls it stands for.

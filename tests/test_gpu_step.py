@@ -1,8 +1,10 @@
 """sparse_attn_decode_step (append + select + attend in one call) against the
-three separate calls it stands for: identical block sets, identical compressed
-keys afterwards, and outputs equal up to fp32 summation order. Covers the raw-sum path, where the
-append shares the scoring launch and the scorer forms new entries from the
-keys, with jumps that put new entries inside candidate blocks."""
+three separate calls it stands for (the attention with the step's split count,
+sparse_attn_decode_step_splits): identical block sets, identical compressed
+keys afterwards, and outputs equal up to fp32 summation order. Covers the
+raw-sum paths (the one-launch pipelined step with bf16 keys and small hints,
+the append inside the scoring launch otherwise), where the scorer forms new
+entries from the keys, with jumps that put new entries inside candidate blocks."""
 import pytest
 import torch
 
@@ -22,6 +24,12 @@ def rand(shape, dt, seed, scale=1.0):
 
 def lens_t(lens):
     return torch.tensor(lens, dtype=torch.int32, device=DEV)
+
+
+def step_splits(dt, B, Hkv, T, k, n_init, n_local, mode, max_new_tokens, n_split=0):
+    """The split count of the step's attention for these arguments."""
+    return sa.decode_step_splits(TD[dt], B, Hkv, T, sa.make_params(k, n_init, n_local, mode),
+                                 k + n_init + n_local, max_new_tokens, n_split)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -51,7 +59,8 @@ def test_decode_step_equals_separate_calls(dt, mode, G, n_local):
                                               max_new_tokens=mx)
         sa.compress(K, Kc_b, Lp, Ln, max_new_entries=mx // 16 + 2)
         idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, 1, n_local, mode)
-        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0,
+                             n_split=step_splits(dt, B, Hkv, T, k, 1, n_local, mode, mx))
         torch.cuda.synchronize()
         assert gpu_rows(idx1, cnt1) == gpu_rows(idx2, cnt2), (i, mode)
         assert_same_attention(O1, O2, lse1, lse2, (i, mode))
@@ -110,7 +119,8 @@ def test_decode_step_fused_and_separate_topk(case):
                                           n_split=case["n_split"])
     sa.compress(K, Kc_b, Lp, Ln)
     idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, 1, 2, case["mode"])
-    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=case["n_split"])
+    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0,
+                         n_split=step_splits(dt, B, Hkv, T, k, 1, 2, case["mode"], 1, case["n_split"]))
     torch.cuda.synchronize()
     assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
     assert_same_attention(O1, O2, lse1, lse2, case)
@@ -119,7 +129,8 @@ def test_decode_step_fused_and_separate_topk(case):
 
 def test_decode_step_random_configurations():
     """Seeded random shapes, lengths, budgets and modes: the one-call step and
-    the three separate calls agree bit for bit (sets, outputs, compressed keys)."""
+    the three separate calls agree: sets and compressed keys bit for bit,
+    outputs up to fp32 summation order."""
     import random
     rng = random.Random(2024)
     for trial in range(12):
@@ -152,7 +163,8 @@ def test_decode_step_random_configurations():
                                               max_new_tokens=mx, n_split=n_split)
         sa.compress(K, Kc_b, Lp, Ln, max_new_entries=mx // 16 + 2)
         idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, k, n_init, n_local, mode)
-        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0, n_split=n_split)
+        O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0,
+                             n_split=step_splits(dt, B, Hkv, T, k, n_init, n_local, mode, mx, n_split))
         torch.cuda.synchronize()
         assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2), case
         assert_same_attention(O1, O2, lse1, lse2, case)
@@ -181,7 +193,8 @@ def test_decode_step_hint_below_the_real_jump(dt, mode, G, hint):
                                           max_new_tokens=hint)
     sa.compress(K, Kc_b, Lp, Ln)
     idx2, cnt2, _ = sa.select(sel, Kc_b, Ln, T, 20, 1, 2, mode)
-    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0)
+    O2, lse2 = sa.decode(Q, K, V, Ln, idx2, cnt2, 1.0,
+                         n_split=step_splits(dt, B, Hkv, T, 20, 1, 2, mode, hint))
     torch.cuda.synchronize()
     assert torch.equal(Kc_a.view(BITS[dt]), Kc_b.view(BITS[dt])), "compressed keys"
     assert torch.equal(idx1, idx2) and torch.equal(cnt1, cnt2)
