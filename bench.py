@@ -309,10 +309,16 @@ def bench_decode(args, w):
         # scorer with the append, then the attention with the top-k prologue
         # and the in-kernel split merge) timed together with events around
         # every call, on the step's algorithmic bytes
-        scorer = "score_softmax_kernel" if w.score_mode == "softmax_sum" else "score_raw_kernel"
+        if w.score_mode == "softmax_sum":
+            launches = ("score_softmax_kernel with the append; decode_kernel with the top-k and "
+                        "the split merge")
+        elif w.dtype == "bf16":
+            launches = ("score_raw_kernel; decode_kernel with the top-k, the append and the split "
+                        "merge")
+        else:
+            launches = "score_raw_kernel with the append; decode_kernel with the top-k and the split merge"
         out["roofline"] = {"bound": "hbm",
-                           "kernel": f"sparse_attn_decode_step call ({scorer} with the "
-                                     "append; decode_kernel with the top-k and the split merge)",
+                           "kernel": f"sparse_attn_decode_step call ({launches})",
                            "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                            "traffic": recorded_traffic(f"{w.name}_step"),
