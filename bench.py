@@ -276,7 +276,8 @@ def bench_decode(args, w):
     append_bytes = new_entries * (32 * row + row)
     step_bytes = attn_bytes + sel_bytes + append_bytes
     attn_gbs = attn_bytes / (mean["attend"] * 1e-3) / 1e9
-    step_gbs = step_bytes / (step_call_ms * 1e-3) / 1e9
+    step_gbs = step_bytes / (gpu_ms * 1e-3) / 1e9            # timed region, HIP events
+    call_gbs = step_bytes / (step_call_ms * 1e-3) / 1e9
 
     out = {
         "metric": "sparse decode attn tokens/s and HBM GB/s (% of peak) at 128K ctx, 1 GPU",
@@ -306,9 +307,11 @@ def bench_decode(args, w):
                 "traffic": recorded_traffic(f"{w.name}_decode"), "bytes_per_launch": attn_bytes}
     if not args.separate_calls:
         # the timed step is one sparse_attn_decode_step call: its launches (the
-        # scorer with the append, then the attention with the top-k prologue
-        # and the in-kernel split merge) timed together with events around
-        # every call, on the step's algorithmic bytes
+        # scorer, then the attention with the top-k prologue and the in-kernel
+        # split merge) timed together, as the average step time between HIP
+        # events on the launch stream at both ends of the timed region, on the
+        # step's algorithmic bytes; call_ms adds events around every call
+        # (each pair costs ~2 us of its own)
         if w.score_mode == "softmax_sum":
             launches = ("score_softmax_kernel with the append; decode_kernel with the top-k and "
                         "the split merge")
@@ -322,7 +325,8 @@ def bench_decode(args, w):
                            "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                            "traffic": recorded_traffic(f"{w.name}_step"),
-                           "bytes_per_launch": step_bytes, "call_ms": round(step_call_ms, 5),
+                           "bytes_per_launch": step_bytes, "launch_ms": round(gpu_ms, 5),
+                           "call_ms": round(step_call_ms, 5), "call_achieved": round(call_gbs, 1),
                            "separate_call_attention": separate}
     else:
         out["roofline"] = dict(bound="hbm", **separate)
