@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_attention_12_amd as sa
 
@@ -355,3 +356,29 @@ def test_decode_step_noalloc_rejects_steps_beyond_its_scratch():
                                              8, 128, 131072, 8191, FAKE, FAKE, 1, None, 1.0, FAKE,
                                              67, FAKE, FAKE, sa.SA_F32, None, 0, None) \
         == sa.SA_ERR_INVALID_ARG
+
+
+def test_decode_step_splits():
+    """sparse_attn_decode_step_splits: the step's split count is the decode
+    call's for the same arguments (so sparse_attn_decode with it reproduces
+    the step's outputs up to fp32 order), an explicit count is kept (raised to
+    the one that keeps every split within 64 list entries), and invalid
+    arguments give 0."""
+    L = sa.lib()
+    raw = sa.make_params(64, 1, 2, "raw_sum")
+    soft = sa.make_params(64, 1, 2, "softmax_sum")
+    for p in (raw, soft):
+        for dtype in (torch.bfloat16, torch.float32):
+            for B, Hkv in ((8, 8), (16, 8), (1, 2), (32, 8)):
+                s = sa.decode_step_splits(dtype, B, Hkv, 131072, p, 67)
+                assert s >= 1
+                ws = sa.decode_workspace_size(B, 4 * Hkv, Hkv, 67, s)
+                assert ws == sa.decode_workspace_size(B, 4 * Hkv, Hkv, 67, 0)   # = automatic
+                assert sa.decode_step_splits(dtype, B, Hkv, 131072, p, 67, 1, 3) == 3
+    assert sa.decode_step_splits(torch.bfloat16, 1, 2, 131072, raw, 1000, 1, 3) == 16   # 1000 / 64
+    bad = [(-1, 8, 8, 131072, 67, 1, 0), (1, 0, 8, 131072, 67, 1, 0), (1, 8, 0, 131072, 67, 1, 0),
+           (1, 8, 8, -1, 67, 1, 0), (1, 8, 8, 131072, 0, 1, 0), (1, 8, 8, 131072, 67, -1, 0),
+           (1, 8, 8, 131072, 67, 1, -1), (7, 8, 8, 131072, 67, 1, 0)]
+    for dt, B, Hkv, T, cap, mx, ns in bad:
+        assert L.sparse_attn_decode_step_splits(dt, B, Hkv, T, ctypes.byref(raw), cap, mx, ns) == 0
+    assert L.sparse_attn_decode_step_splits(1, 8, 8, 131072, None, 67, 1, 0) == 0
