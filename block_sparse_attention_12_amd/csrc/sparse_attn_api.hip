@@ -193,7 +193,10 @@ int sparse_attn_decode_step(const void *Q, const void *sel, int H_sel, const voi
                        (p->score_mode == SA_SCORE_RAW_SUM || G <= 4);
     FusedSelect *fsp = fused ? &fs : nullptr;
     if (p->score_mode == SA_SCORE_RAW_SUM) {
-        // the append rides in the scoring launch (the scorer forms new entries itself)
+        // the scorer reads only the entries that existed before the step (a
+        // candidate block holding a new one is rescored with it formed from the
+        // keys); the new entries are written by the attention launch (bf16, at
+        // most 16 new tokens, fused top-k: fs->app_*) or by the scoring launch
         st = launch_select(sel, G, Kc, dtype, B, Hkv, T_cap, nc_cap, lens_now, *p, idx_out, idx_cap,
                            cnt_out, nullptr, workspace, hs, K, lens_prev, fsp, max_new_tokens);
     } else {
