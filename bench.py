@@ -39,7 +39,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_forecast_bf16_128k")
-    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=None,
+                    help="input replicas rotated per step (default: 8 for the single-layer decode "
+                         "workloads, whose per-step bytes are about the size of the 256 MB last-level "
+                         "cache; 3 for the token-index workload; prefill takes at most 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--n-split", type=int, default=0)
@@ -63,6 +66,8 @@ def main():
 
     if args.workload == "copy_calibration":
         return copy_calibration(args)
+    if args.replicas is None:
+        args.replicas = 3 if args.workload in synth.TOKEN_WORKLOADS else (2 if args.workload.startswith("prefill") else 8)
     if args.workload.startswith("prefill"):
         return bench_prefill(args)
     if args.workload in synth.TOKEN_WORKLOADS:
